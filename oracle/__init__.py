@@ -1,0 +1,182 @@
+"""CPU oracle for the routed, weight-quantized MoE expert FFN (ctypes front end).
+
+TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the benchmark's CPU
+baseline may import this package; the product package never does, and the HIP
+library shares no code with it. The arithmetic lives in oracle.c (plain loops,
+fp64); this module only marshals numpy arrays.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.oracle_moe_align.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _I64, _P, _P]
+    lib.oracle_moe_align.restype = ctypes.c_int
+    lib.oracle_w4a16_moe.argtypes = [_P] * 7 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
+    lib.oracle_w4a16_moe.restype = ctypes.c_int
+    lib.oracle_fp8_moe.argtypes = [_P] * 8 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
+    lib.oracle_fp8_moe.restype = ctypes.c_int
+    lib.oracle_fp8_quantize_blocks.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P]
+    lib.oracle_fp8_quantize_blocks.restype = ctypes.c_int
+    lib.oracle_f64_to_bf16_array.argtypes = [_P, _I64, _P]
+    lib.oracle_e4m3_to_f64_array.argtypes = [_P, _I64, _P]
+    lib.oracle_f32_to_e4m3_array.argtypes = [_P, _I64, _P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def default_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def align_capacity(P: int, E: int, B: int):
+    """Sorted-id capacity L = P + E*(B-1) and block capacity NB = ceil(L/B)."""
+    L = P + E * (B - 1)
+    return L, (L + B - 1) // B
+
+
+def moe_align(topk_ids, E: int, B: int):
+    """Stable counting sort of flat pair indices by expert, padded per expert to B.
+
+    Returns (sorted_ids [L], expert_ids [NB], num_tokens_padded, expert_offsets [E+1]).
+    """
+    ids = _c(np.asarray(topk_ids).reshape(-1), np.int32)
+    P = ids.size
+    L, NB = align_capacity(P, E, B)
+    sorted_ids = np.empty(L, np.int32)
+    expert_ids = np.empty(NB, np.int32)
+    ntp = np.zeros(1, np.int32)
+    offs = np.empty(E + 1, np.int32)
+    rc = _load().oracle_moe_align(_ptr(ids), P, E, B, _ptr(sorted_ids), L, _ptr(expert_ids), NB,
+                                  _ptr(ntp), _ptr(offs))
+    if rc != 0:
+        raise ValueError("oracle_moe_align: bad arguments")
+    return sorted_ids, expert_ids, int(ntp[0]), offs
+
+
+def w4a16_moe(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=None):
+    """Routed W4A16 MoE FFN in fp64 for the given token rows (all rows if None).
+
+    x [T,H] uint16 (bf16 bits); w13 [E,2I,H/2] uint8; s13 [E,2I,H/32] uint16;
+    w2 [E,H,I/2] uint8; s2 [E,H,I/32] uint16; topk_ids int32 [T,k];
+    topk_weights float32 [T,k]. Returns float64 [nrows, H] (before bf16 rounding).
+    """
+    x = _c(x, np.uint16)
+    w13 = _c(w13, np.uint8)
+    s13 = _c(s13, np.uint16)
+    w2 = _c(w2, np.uint8)
+    s2 = _c(s2, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    wts = _c(topk_weights, np.float32)
+    T, H = x.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    k = ids.shape[1]
+    if rows is None:
+        rows_arr, nrows, rp = None, T, None
+    else:
+        rows_arr = _c(np.asarray(rows, dtype=np.int64), np.int64)
+        nrows, rp = rows_arr.size, _ptr(rows_arr)
+    out = np.zeros((nrows, H), np.float64)
+    rc = _load().oracle_w4a16_moe(_ptr(x), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), _ptr(ids),
+                                  _ptr(wts), T, H, I, E, k, rp, nrows, _ptr(out),
+                                  nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_w4a16_moe: bad arguments")
+    return out
+
+
+def fp8_moe(a_q, a_s, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=None):
+    """Routed W8A8 block-FP8 MoE FFN in fp64 (h requantized per 128 in fp32)."""
+    a_q = _c(a_q, np.uint8)
+    a_s = _c(a_s, np.float32)
+    w13 = _c(w13, np.uint8)
+    s13 = _c(s13, np.float32)
+    w2 = _c(w2, np.uint8)
+    s2 = _c(s2, np.float32)
+    ids = _c(topk_ids, np.int32)
+    wts = _c(topk_weights, np.float32)
+    T, H = a_q.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    k = ids.shape[1]
+    if rows is None:
+        rows_arr, nrows, rp = None, T, None
+    else:
+        rows_arr = _c(np.asarray(rows, dtype=np.int64), np.int64)
+        nrows, rp = rows_arr.size, _ptr(rows_arr)
+    out = np.zeros((nrows, H), np.float64)
+    rc = _load().oracle_fp8_moe(_ptr(a_q), _ptr(a_s), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                                _ptr(ids), _ptr(wts), T, H, I, E, k, rp, nrows, _ptr(out),
+                                nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_fp8_moe: bad arguments")
+    return out
+
+
+def fp8_quantize_blocks(v, br: int, bc: int):
+    """Block E4M3 quantizer on a 2-D fp32 array: returns (codes uint8, scales fp32)."""
+    v = _c(v, np.float32)
+    R, C = v.shape
+    q = np.empty((R, C), np.uint8)
+    s = np.empty(((R + br - 1) // br, (C + bc - 1) // bc), np.float32)
+    rc = _load().oracle_fp8_quantize_blocks(_ptr(v), R, C, br, bc, _ptr(q), _ptr(s))
+    if rc != 0:
+        raise ValueError("oracle_fp8_quantize_blocks: bad arguments")
+    return q, s
+
+
+def f64_to_bf16(x):
+    """fp64 -> bf16 bits (uint16), round to nearest even from the exact value."""
+    x = _c(np.asarray(x, dtype=np.float64), np.float64)
+    out = np.empty(x.shape, np.uint16)
+    _load().oracle_f64_to_bf16_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def bf16_to_f64(b):
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def e4m3_to_f64(codes):
+    c = _c(np.asarray(codes, dtype=np.uint8), np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e4m3_to_f64_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def f32_to_e4m3(x):
+    x = _c(np.asarray(x, dtype=np.float32), np.float32)
+    out = np.empty(x.shape, np.uint8)
+    _load().oracle_f32_to_e4m3_array(_ptr(x), x.size, _ptr(out))
+    return out

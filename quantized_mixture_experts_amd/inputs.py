@@ -1,0 +1,167 @@
+"""Seeded synthetic inputs for the routed MoE expert FFN.
+
+This module only draws random numbers and converts them to the storage dtypes the
+library takes (bf16 bits, packed bytes). It holds none of the FFN's arithmetic: the
+E4M3 block quantizer is passed in by the caller, so tests can use the CPU oracle's
+and the benchmark can use the library's.
+
+Workloads (Kimi K2.x-style serving shapes from "vLLM x Novita AI: Chord W4A16 INT4
+MoE Kernel for Kimi K2.x", summary and Figure 2; block-FP8 format from "SGLang W8A8
+Block FP8 quantization kernel config guide", background section):
+
+  tiny      16 tokens, H 256,  I 128,  8 experts, top-2,  W4A16
+  decode    32 tokens, H 7168, I 2048, 48 experts, top-8, W4A16, uniform routing
+  prefill   8192 tokens, H 7168, I 2048, 48 experts, top-8, W4A16, Zipf(1.0) routing
+  fp8       1024 tokens, H 7168, I 2048, 32 experts, top-8, W8A8 block FP8
+  full384   256 tokens, H 7168, I 2048, 384 experts, top-8, W4A16, uniform routing
+
+Recipe (per case, numpy default_rng(seed), draws in this order):
+  x       bf16(N(0,1)) [T,H]                      (FP8: fp32 N(0,1) source)
+  router  logits N(0,1) [T,E]; Zipf: log(1/(e+1)) + Gumbel(0,1)
+          softmax (fp32, max-subtracted) -> top-k (ties to the lower id) -> renormalize
+  W4A16   w13 uniform bytes [E,2I,H/2]; s13 bf16(|N(0,1)|*0.02) [E,2I,H/32];
+          w2 uniform bytes [E,H,I/2];  s2 bf16(|N(0,1)|*0.02) [E,H,I/32]
+  FP8     per expert: w13 source N(0,1) [2I,H], then w2 source N(0,1) [H,I],
+          each quantized in [128,128] blocks by the caller's quantizer
+"""
+from dataclasses import dataclass
+
+import numpy as np
+
+SEED_BASE = 20260
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    fmt: str  # "w4a16" or "fp8"
+    routing: str  # "uniform" or "zipf"
+    index: int  # 1-based position in the workload list; seeds are SEED_BASE + index
+
+    @property
+    def P(self) -> int:
+        return self.T * self.k
+
+    @property
+    def seed(self) -> int:
+        return SEED_BASE + self.index
+
+
+CONFIGS = {
+    "tiny": MoEConfig("tiny", 16, 256, 128, 8, 2, "w4a16", "uniform", 1),
+    "decode": MoEConfig("decode", 32, 7168, 2048, 48, 8, "w4a16", "uniform", 2),
+    "prefill": MoEConfig("prefill", 8192, 7168, 2048, 48, 8, "w4a16", "zipf", 3),
+    "fp8": MoEConfig("fp8", 1024, 7168, 2048, 32, 8, "fp8", "uniform", 4),
+    "full384": MoEConfig("full384", 256, 7168, 2048, 384, 8, "w4a16", "uniform", 5),
+}
+
+
+def bf16_bits(a) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even (storage conversion)."""
+    f = np.ascontiguousarray(a, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(f)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r[nan] = 0x7FC0
+    return r
+
+
+def bf16_value(b) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def routing(rng: np.random.Generator, T: int, E: int, k: int, kind: str = "uniform"):
+    """Router output: topk_ids int32 [T,k] (descending probability), topk_weights fp32 [T,k].
+
+    uniform: i.i.d. N(0,1) logits, so every k-subset is equally likely.
+    zipf: logits log(p_e) + Gumbel(0,1) with p_e proportional to 1/(e+1); the top-k of
+    Gumbel-perturbed log-probabilities samples k distinct experts without replacement
+    in proportion to p (expert 0 the most popular).
+    """
+    if kind == "uniform":
+        logits = rng.standard_normal((T, E), dtype=np.float32)
+    elif kind == "zipf":
+        logp = -np.log(np.arange(1, E + 1, dtype=np.float64))
+        logp -= np.log(np.exp(logp).sum())
+        g = rng.gumbel(0.0, 1.0, size=(T, E))
+        logits = (logp[None, :] + g).astype(np.float32)
+    else:
+        raise ValueError(kind)
+    z = logits - logits.max(axis=1, keepdims=True)
+    ez = np.exp(z, dtype=np.float32)
+    p = ez / ez.sum(axis=1, keepdims=True, dtype=np.float32)
+    order = np.argsort(-p, axis=1, kind="stable")  # equal values keep the lower id first
+    ids = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(p, ids, axis=1).astype(np.float32)
+    w = (sel / sel.sum(axis=1, keepdims=True, dtype=np.float32)).astype(np.float32)
+    return np.ascontiguousarray(ids), np.ascontiguousarray(w)
+
+
+def _scales(rng, shape):
+    return bf16_bits(np.abs(rng.standard_normal(shape, dtype=np.float32)) * np.float32(0.02))
+
+
+def _bytes(rng, shape):
+    n = int(np.prod(shape))
+    return np.frombuffer(rng.bytes(n), dtype=np.uint8).reshape(shape).copy()
+
+
+def w4a16_case(cfg: MoEConfig, seed=None) -> dict:
+    """All host arrays of one W4A16 case (see the module recipe)."""
+    if cfg.fmt != "w4a16":
+        raise ValueError(cfg.fmt)
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    x = bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    ids, wts = routing(rng, T, E, k, cfg.routing)
+    w13 = _bytes(rng, (E, 2 * I, H // 2))
+    s13 = _scales(rng, (E, 2 * I, H // 32))
+    w2 = _bytes(rng, (E, H, I // 2))
+    s2 = _scales(rng, (E, H, I // 32))
+    return dict(x=x, topk_ids=ids, topk_weights=wts, w13=w13, s13=s13, w2=w2, s2=s2)
+
+
+def fp8_case(cfg: MoEConfig, quantize, seed=None) -> dict:
+    """All host arrays of one W8A8 block-FP8 case.
+
+    quantize(v_fp32_2d, br, bc) -> (codes uint8, scales fp32) is the caller's block
+    quantizer; activations use [1,128] blocks, weights [128,128].
+    """
+    if cfg.fmt != "fp8":
+        raise ValueError(cfg.fmt)
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    x_src = rng.standard_normal((T, H), dtype=np.float32)
+    ids, wts = routing(rng, T, E, k, cfg.routing)
+    a_q, a_s = quantize(x_src, 1, 128)
+    w13 = np.empty((E, 2 * I, H), np.uint8)
+    s13 = np.empty((E, 2 * I // 128, H // 128), np.float32)
+    w2 = np.empty((E, H, I), np.uint8)
+    s2 = np.empty((E, H // 128, I // 128), np.float32)
+    for e in range(E):
+        w13[e], s13[e] = quantize(rng.standard_normal((2 * I, H), dtype=np.float32), 128, 128)
+        w2[e], s2[e] = quantize(rng.standard_normal((H, I), dtype=np.float32), 128, 128)
+    return dict(a_q=a_q, a_s=a_s, topk_ids=ids, topk_weights=wts, w13=w13, s13=s13, w2=w2, s2=s2)
+
+
+def custom_w4a16_case(T, H, I, E, k, seed, kind="uniform") -> dict:
+    """A W4A16 case of any shape with the same recipe (for ragged and edge shapes)."""
+    return w4a16_case(MoEConfig("custom", T, H, I, E, k, "w4a16", kind, 0), seed=seed)
+
+
+def custom_fp8_case(T, H, I, E, k, seed, quantize, kind="uniform") -> dict:
+    return fp8_case(MoEConfig("custom", T, H, I, E, k, "fp8", kind, 0), quantize, seed=seed)
+
+
+def sample_rows(T: int, n: int, seed: int) -> np.ndarray:
+    """A sorted seeded subset of n token rows (all rows if n >= T)."""
+    if n >= T:
+        return np.arange(T, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(T, size=n, replace=False)).astype(np.int64)
