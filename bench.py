@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed, weight-quantized MoE expert FFN on one MI355X.
+
+One step = one full forward (align -> gate_up GEMM + SiLU*up -> down GEMM + weighted
+scatter-add -> bf16 output) on seeded synthetic inputs already resident in HBM.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|fp8|full384|tiny]
+
+Prints one JSON line. The default workload is the decode layer (32 tokens, hidden 7168,
+intermediate 2048, 48 local experts, top-8, INT4 group-32 weights); its value is the
+expert-weight bytes the forward must read divided by the step time (GB/s). Prefill-type
+workloads report TFLOP/s of the routed expert FLOPs. The "roofline" object covers the
+dominant kernel (the gate_up GEMM), timed with HIP events recorded on the stream it runs
+on, over the timed steps. "cpu_baseline" times the CPU oracle on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE FFN decode weight GB/s and prefill TFLOP/s, % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+# Kernel sources whose counters a traffic record covers (a change voids the record).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "fp8", "full384", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="token rows of the CPU-oracle sample (0 = workload default)")
+    return ap.parse_args()
+
+
+def weight_bytes_per_expert(cfg):
+    H, I = cfg.H, cfg.I
+    if cfg.fmt == "w4a16":
+        w13 = 2 * I * H // 2 + 2 * I * (H // 32) * 2
+        w2 = H * I // 2 + H * (I // 32) * 2
+    else:
+        w13 = 2 * I * H + (2 * I // 128) * (H // 128) * 4
+        w2 = H * I + (H // 128) * (I // 128) * 4
+    return w13, w2
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(kernel_key, launches_ok):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3 counters,
+    or None when there is no record or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE) or not launches_ok:
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_sha") != source_digest(rec["sources"]):
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the MoE "
+              "path has no multi-GPU mode here", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_mixture_experts_amd import binding, inputs
+
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    lib = binding.load()
+    import ctypes
+
+    cfg = inputs.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.time()
+
+    def to_dev(arrays):
+        return {k: torch.from_numpy(np.ascontiguousarray(v.view(np.int16) if v.dtype == np.uint16 else v)).to(dev)
+                for k, v in arrays.items()}
+
+    if cfg.fmt == "w4a16":
+        case = inputs.w4a16_case(cfg)
+    else:
+        def gpu_quant(v, br, bc):
+            q, s = binding.fp8_quantize_blocks(torch.from_numpy(v).to(dev), br, bc)
+            return q.cpu().numpy(), s.cpu().numpy()
+        case = inputs.fp8_case(cfg, gpu_quant)
+    d = to_dev(case)
+    gen_s = time.time() - t_gen
+
+    fmt = binding.FORMAT_W4A16 if cfg.fmt == "w4a16" else binding.FORMAT_FP8
+    chosen, block_m, ws_bytes = binding.plan(fmt, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+
+    if cfg.fmt == "w4a16":
+        def step():
+            binding.moe_w4a16_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
+                                      d["topk_weights"], out=out, workspace=workspace)
+    else:
+        def step():
+            binding.moe_fp8_block_forward(d["a_q"], d["a_s"], d["w13"], d["s13"], d["w2"], d["s2"],
+                                          d["topk_ids"], d["topk_weights"], out=out,
+                                          workspace=workspace)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if lib.qmoe_timing_begin(args.steps) != 0:
+        raise RuntimeError(lib.qmoe_last_error())
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_sum = (ctypes.c_float * 6)()
+    counts = (ctypes.c_int32 * 6)()
+    if lib.qmoe_timing_end(ms_sum, counts) != 0:
+        raise RuntimeError(lib.qmoe_last_error())
+    stage_names = ["zero", "align", "gate_up", "requant", "down", "cast"]
+    stage_ms = {n: (ms_sum[i] / counts[i] if counts[i] else None) for i, n in enumerate(stage_names)}
+
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ids = case["topk_ids"]
+    touched = int(np.unique(ids[(ids >= 0) & (ids < cfg.E)]).size)
+    w13_b, w2_b = weight_bytes_per_expert(cfg)
+    weight_bytes = touched * (w13_b + w2_b)
+    flops = cfg.P * (2 * cfg.H * 2 * cfg.I + 2 * cfg.I * cfg.H)
+    dtype = "bf16" if cfg.fmt == "w4a16" else "fp8"
+    hbm_bound = chosen == binding.SCHEDULE_DECODE
+    if hbm_bound:
+        value, unit = weight_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
+    else:
+        value, unit = flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+
+    # Dominant kernel: gate_up (two thirds of the weight bytes, deep K = hidden size).
+    gu_ms = stage_ms["gate_up"]
+    if hbm_bound:
+        per_launch = touched * w13_b
+        achieved = per_launch / (gu_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        per_launch = cfg.P * 2 * cfg.H * 2 * cfg.I
+        achieved = per_launch / (gu_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS[dtype]
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    kernel_key = f"{args.workload}/gate_up"
+    roof["kernel"] = kernel_key
+    roof["kernel_ms"] = round(gu_ms, 4)
+    roof["algorithmic_per_launch"] = per_launch
+    roof["traffic"] = traffic_record(kernel_key, counts[2] > 0)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nthreads = oracle.default_threads()
+        default_rows = {"tiny": cfg.T, "decode": cfg.T, "full384": 32, "prefill": 16, "fp8": 8}
+        nrows = args.cpu_rows or default_rows[args.workload]
+        rows = inputs.sample_rows(cfg.T, nrows, seed=cfg.seed)
+        tc = time.perf_counter()
+        if cfg.fmt == "w4a16":
+            oracle.w4a16_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
+                             case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
+        else:
+            oracle.fp8_moe(case["a_q"], case["a_s"], case["w13"], case["s13"], case["w2"],
+                           case["s2"], case["topk_ids"], case["topk_weights"], rows=rows,
+                           nthreads=nthreads)
+        cpu_s = time.perf_counter() - tc
+        # The oracle loops per (token, slot) and re-reads the expert's weights for each,
+        # so the full workload costs T / nrows times the sample.
+        full_s = cpu_s * cfg.T / len(rows)
+        cpu_value = (weight_bytes / full_s / 1e9) if hbm_bound else (flops / full_s / 1e12)
+        cpu = {"value": round(cpu_value, 6), "unit": unit, "cores": nthreads, "kind": "oracle",
+               "sample": f"{len(rows)} of {cfg.T} token rows (all {cfg.k} slots each), "
+                         f"{cpu_s:.1f} s on {nthreads} threads, scaled by {cfg.T}/{len(rows)}"}
+
+    names = {"decode": "decode W4A16", "prefill": "prefill W4A16 (Zipf routing)",
+             "fp8": "block-FP8 W8A8", "full384": "full 384-expert W4A16", "tiny": "tiny W4A16"}
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded; random-init quantized expert weights)",
+        "config": {"workload": f"{names[args.workload]}: {cfg.T} tokens, hidden {cfg.H}, "
+                               f"intermediate {cfg.I}, {cfg.E} experts, top-{cfg.k}",
+                   "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
+                   "top_k": cfg.k, "schedule": ["auto", "decode", "prefill"][chosen],
+                   "touched_experts": touched, "weight_bytes": weight_bytes, "flops": flops},
+        "stage_ms": {k: (round(v, 4) if v is not None else None) for k, v in stage_ms.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
+        "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

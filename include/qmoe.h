@@ -1,0 +1,217 @@
+/*
+ * qmoe.h - C ABI of the MI355X (gfx950) routed, weight-quantized MoE expert FFN.
+ *
+ * One routed MoE layer's expert FFN, on one GPU:
+ *   align (sort token slots to experts) -> gate_up grouped GEMM with INT4 group-32
+ *   dequantization (or block FP8) -> SiLU(gate) * up -> down grouped GEMM ->
+ *   top-k weighted combine (scatter-add) -> bf16 output.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [CHORD] "vLLM x Novita AI: Chord W4A16 INT4 MoE Kernel for Kimi K2.x" (Novita AI
+ *           blog): summary; "Two kernel families"; "vLLM integration"; "Kernel
+ *           optimizations" (indexed kernels; H200 and Blackwell indexed decode);
+ *           Figure 3 (where the padding lives).
+ *   [SGL]   "SGLang W8A8 Block FP8 quantization kernel config guide" (xdnf.cn):
+ *           background section (E4M3, [BLOCK_N, BLOCK_K] weight blocks, per-token-group
+ *           activation scales As, weight block scales Bs); kernel dispatch section
+ *           (cdiv(N, block_n) == Bs.shape[0], cdiv(K, block_k) == Bs.shape[1]).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library never
+ *     allocates or frees caller memory and never synchronizes the stream; all work is
+ *     enqueued on `stream` (a hipStream_t passed as void*, NULL = the null stream).
+ *   - Tensors are dense, row-major, contiguous. bf16 values travel as uint16_t bit
+ *     patterns; E4M3 values as uint8_t bit patterns of OCP E4M3FN (max 448).
+ *   - Pointers must be 16-byte aligned unless stated otherwise.
+ *   - Arguments are checked before anything touches the GPU; a failed check returns
+ *     QMOE_ERR_INVALID_ARG or QMOE_ERR_UNSUPPORTED and enqueues nothing. A failed
+ *     launch returns QMOE_ERR_HIP (the HIP error state is read and cleared).
+ *     qmoe_last_error() then returns a message for the calling thread.
+ *   - Entry points are thread-safe; calls that share output or workspace memory on
+ *     the same GPU must be ordered by the caller (same stream or events).
+ *   - Nothing reads a device value back to the host: every launch is sized for the
+ *     worst case and surplus work-groups exit on the device, so a forward can be
+ *     captured into a hipGraph ([CHORD] "vLLM integration": over-allocated align
+ *     buffers consumed without reading the routed count back).
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMOE_ABI_VERSION 1
+
+typedef enum qmoe_status {
+  QMOE_OK = 0,
+  QMOE_ERR_INVALID_ARG = 1, /* NULL or misaligned pointer, negative or inconsistent size */
+  QMOE_ERR_UNSUPPORTED = 2, /* well-formed but outside the supported shapes            */
+  QMOE_ERR_WORKSPACE = 3,   /* workspace smaller than the size the query returned       */
+  QMOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed               */
+} qmoe_status;
+
+/* Schedules of the forward passes. AUTO picks from routed tokens per expert,
+ * tok_e = T*k/E (a host-side quantity; no device readback): the bandwidth-bound
+ * decode profile below the crossover, the MFMA-bound prefill profile above it
+ * ([CHORD] "Kernel optimizations": the per-expert routed token count, not the total,
+ * decides which schedule wins; profiles tune on token counts). DECODE and PREFILL
+ * force one profile; both give results within the same tolerance. */
+typedef enum qmoe_schedule {
+  QMOE_SCHEDULE_AUTO = 0,
+  QMOE_SCHEDULE_DECODE = 1,
+  QMOE_SCHEDULE_PREFILL = 2
+} qmoe_schedule;
+
+/* Limits: 1 <= E <= QMOE_MAX_EXPERTS, 1 <= k <= E, T*k + E*(block_m-1) < 2^31. */
+#define QMOE_MAX_EXPERTS 4096
+
+/* ABI version of the loaded library (QMOE_ABI_VERSION it was built with). */
+int32_t qmoe_abi_version(void);
+
+/* Static English name of a status code. */
+const char* qmoe_status_string(int32_t status);
+
+/* Message describing the last non-OK status returned on the calling thread
+ * (empty string if none). Valid until the next call on that thread. */
+const char* qmoe_last_error(void);
+
+/*
+ * moe_align - sort routed (token, slot) pairs to experts and pad each expert's
+ * segment to a multiple of block_m ([CHORD] "Two kernel families": the indexed
+ * family consumes sorted_ids / expert_ids / num_tokens_padded; Figure 3: padding
+ * lives in the routing indices, -1 marks padding).
+ *
+ *   topk_ids          [T, k] int32: expert of slot s of token t. Flat pair index
+ *                     i = t*k + s. Ids outside [0, E) are dropped (never written).
+ *   block_m           power of two, 1 <= block_m <= 256.
+ *   sorted_ids        [L] int32, L = T*k + E*(block_m - 1). Expert e owns the segment
+ *                     [off[e], off[e+1]) with off[e+1] - off[e] = ceil(c_e / block_m) *
+ *                     block_m, c_e = number of pairs routed to e. The segment starts
+ *                     with e's pair indices in ascending order; its remaining slots,
+ *                     and every slot from off[E] to L, hold the sentinel T*k.
+ *   expert_ids        [ceil(L / block_m)] int32: expert of each block_m-row block;
+ *                     -1 for blocks at or past off[E].
+ *   num_tokens_padded [1] int32: off[E].
+ *   expert_offsets    [E + 1] int32: off, or NULL.
+ * All outputs are fully written on every call (no pre-clearing needed). The result is
+ * deterministic: bit-identical to a stable counting sort on the host. T = 0 is allowed.
+ * Pointers here need only 4-byte alignment.
+ */
+qmoe_status moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                      int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_tokens_padded,
+                      int32_t* expert_offsets, void* stream);
+
+/*
+ * moe_w4a16_forward - routed MoE expert FFN with BF16 activations and INT4 group-32
+ * weights with BF16 scales ([CHORD] summary: BF16 activations, INT4 weights, group-32
+ * scales; "vLLM integration": uint4 codes, group 32, BF16 scales; "H200 and Blackwell
+ * indexed decode": the weight is the code minus the zero point, then scaled).
+ *
+ *   x            [T, H] bf16.
+ *   w13, s13     [E, 2I, H/2] uint8 and [E, 2I, H/32] bf16: fused gate (rows [0, I))
+ *                and up (rows [I, 2I)) projections. Byte c/2 of a row holds code c in
+ *                its low nibble for even c, high nibble for odd c; weight(n, c) =
+ *                (code - 8) * s13[n, c/32].
+ *   w2, s2       [E, H, I/2] uint8 and [E, H, I/32] bf16: down projection, same format.
+ *   topk_ids     [T, k] int32 (see moe_align); topk_weights [T, k] fp32.
+ *   out          [T, H] bf16, overwritten:
+ *                out[t] = bf16(sum_s topk_weights[t,s] * FFN_{topk_ids[t,s]}(x[t])),
+ *                FFN_e(v) = W2_e (silu(W13_e[0:I] v) * W13_e[I:2I] v), fp32 accumulation.
+ *   schedule     a qmoe_schedule value.
+ *   workspace    device scratch, 256-byte aligned. If NULL, nothing is launched and the
+ *                required size is written to *workspace_bytes (same shapes and schedule).
+ *                Otherwise *workspace_bytes is the size provided; less than required ->
+ *                QMOE_ERR_WORKSPACE. Contents need no initialization and are clobbered.
+ * Requires H % 32 == 0 and I % 32 == 0 (QMOE_ERR_UNSUPPORTED otherwise; [CHORD] "vLLM
+ * integration": unsupported schemes fail instead of silently picking a wrong kernel).
+ * T = 0 writes nothing and returns QMOE_OK.
+ */
+qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                              const uint8_t* w2, const uint16_t* s2, const int32_t* topk_ids,
+                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
+                              void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * moe_fp8_block_forward - routed MoE expert FFN, W8A8 block FP8 ([SGL] background:
+ * E4M3 weights with one fp32 scale per [128, 128] block, activations E4M3 with one fp32
+ * scale per token and 128-column group; block scale = absmax / 448).
+ *
+ *   a_q, a_scale  [T, H] E4M3 and [T, H/128] fp32: x[t, c] = a_q[t, c] * a_scale[t, c/128].
+ *   w13, s13      [E, 2I, H] E4M3 and [E, 2I/128, H/128] fp32 (gate rows [0, I), up rows
+ *                 [I, 2I)); w2, s2  [E, H, I] E4M3 and [E, H/128, I/128] fp32.
+ *   The SiLU(gate) * up output h (fp32) is requantized to E4M3 per token and per 128
+ *   consecutive columns (scale = max(absmax, 1e-10) / 448, round to nearest even after
+ *   clamping to +-448) before the down projection; accumulation is fp32 throughout.
+ *   topk_ids, topk_weights, T, k, schedule, out, workspace: as moe_w4a16_forward.
+ * Requires H % 128 == 0 and I % 128 == 0 ([SGL] kernel dispatch: the scale grids must
+ * match cdiv(N, 128) x cdiv(K, 128) exactly).
+ */
+qmoe_status moe_fp8_block_forward(const uint8_t* a_q, const float* a_scale, const uint8_t* w13,
+                                  const float* s13, const uint8_t* w2, const float* s2,
+                                  const int32_t* topk_ids, const float* topk_weights, int32_t T,
+                                  int32_t H, int32_t I, int32_t E, int32_t k, int32_t schedule,
+                                  uint16_t* out, void* workspace, size_t* workspace_bytes,
+                                  void* stream);
+
+/*
+ * qmoe_fp8_quantize_blocks - block E4M3 quantizer ([SGL] background: each
+ * [BLOCK_N, BLOCK_K] block gets its own absmax-derived scale).
+ *   v      [R, C] fp32 (4-byte alignment suffices).
+ *   q      [R, C] E4M3 out; scale [ceil(R/br), ceil(C/bc)] fp32 out.
+ *   Per block: scale = max(absmax, 1e-10) / 448 and q = e4m3_rne(clamp(v / scale,
+ *   -448, 448)), computed in fp32 with IEEE division. br in [1, 128], bc in [1, 1024],
+ *   br * bc <= 16384. Per-token-group activations use br = 1, bc = 128; weights 128, 128.
+ */
+qmoe_status qmoe_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
+                                     uint8_t* q, float* scale, void* stream);
+
+/*
+ * qmoe_plan - the schedule and align block size a forward would use.
+ *   format      0 = W4A16, 1 = W8A8 block FP8.
+ *   schedule    requested qmoe_schedule (AUTO resolves here).
+ *   chosen      out: QMOE_SCHEDULE_DECODE or QMOE_SCHEDULE_PREFILL.
+ *   block_m     out: align block size of that schedule.
+ *   workspace_bytes out (may be NULL): workspace the forward needs.
+ * Pure host computation; touches no GPU.
+ */
+qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                      int32_t schedule, int32_t* chosen, int32_t* block_m,
+                      size_t* workspace_bytes);
+
+/*
+ * Stage timing (diagnostics and benchmarking). The stages of a forward, in launch
+ * order, are QMOE_STAGE_ZERO (clear the fp32 combine buffer), QMOE_STAGE_ALIGN,
+ * QMOE_STAGE_GATE_UP (gate_up GEMM + SiLU*up), QMOE_STAGE_REQUANT (block-FP8 only:
+ * E4M3 requantization of h), QMOE_STAGE_DOWN (down GEMM + weighted scatter-add) and
+ * QMOE_STAGE_CAST (fp32 -> bf16 output).
+ *
+ * qmoe_timing_begin(max_calls): the next max_calls forward calls in this process
+ *   record a HIP event pair around each stage's launch, on the forward's stream.
+ *   Event handles are created here (host-side objects; no device memory is touched).
+ * qmoe_timing_end(ms_sum, count): stops recording, waits for the recorded events and
+ *   writes, per stage, the summed event-to-event milliseconds and the number of
+ *   forwards recorded. Both arrays hold QMOE_NUM_STAGES entries.
+ * Not meant to be used from several threads at once.
+ */
+enum {
+  QMOE_STAGE_ZERO = 0,
+  QMOE_STAGE_ALIGN = 1,
+  QMOE_STAGE_GATE_UP = 2,
+  QMOE_STAGE_REQUANT = 3,
+  QMOE_STAGE_DOWN = 4,
+  QMOE_STAGE_CAST = 5,
+  QMOE_NUM_STAGES = 6
+};
+qmoe_status qmoe_timing_begin(int32_t max_calls);
+qmoe_status qmoe_timing_end(float* ms_sum, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

@@ -1,0 +1,194 @@
+"""Thin Python binding of libqmoe.so (the C ABI in include/qmoe.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their data pointers are handed to the library, and torch allocates the
+output and workspace buffers. Every step of the MoE path runs in the library's HIP
+kernels; there is no Python or CPU fallback. If the library is missing the first
+call raises.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qmoe.h")
+
+SCHEDULE_AUTO, SCHEDULE_DECODE, SCHEDULE_PREFILL = 0, 1, 2
+FORMAT_W4A16, FORMAT_FP8 = 0, 1
+STATUS = {0: "QMOE_OK", 1: "QMOE_ERR_INVALID_ARG", 2: "QMOE_ERR_UNSUPPORTED",
+          3: "QMOE_ERR_WORKSPACE", 4: "QMOE_ERR_HIP"}
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZP = ctypes.POINTER(ctypes.c_size_t)
+
+
+class QMoEError(RuntimeError):
+    def __init__(self, func, status, message):
+        self.status = status
+        super().__init__(f"{func}: {STATUS.get(status, status)}: {message}")
+
+
+def load():
+    """Load libqmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.qmoe_abi_version.restype = _I32
+    lib.qmoe_status_string.argtypes = [_I32]
+    lib.qmoe_status_string.restype = ctypes.c_char_p
+    lib.qmoe_last_error.restype = ctypes.c_char_p
+    lib.moe_align.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]
+    lib.moe_align.restype = _I32
+    lib.moe_w4a16_forward.argtypes = [_P] * 7 + [_I32] * 6 + [_P, _P, _SZP, _P]
+    lib.moe_w4a16_forward.restype = _I32
+    lib.moe_fp8_block_forward.argtypes = [_P] * 8 + [_I32] * 6 + [_P, _P, _SZP, _P]
+    lib.moe_fp8_block_forward.restype = _I32
+    lib.qmoe_fp8_quantize_blocks.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P, _P]
+    lib.qmoe_fp8_quantize_blocks.restype = _I32
+    lib.qmoe_plan.argtypes = [_I32] * 7 + [ctypes.POINTER(_I32), ctypes.POINTER(_I32), _SZP]
+    lib.qmoe_plan.restype = _I32
+    _lib = lib
+    return lib
+
+
+def declared_functions():
+    """Names of the functions include/qmoe.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                                 text, flags=re.M)))
+
+
+def _check(func, status):
+    if status != 0:
+        msg = load().qmoe_last_error().decode(errors="replace")
+        raise QMoEError(func, status, msg)
+
+
+def _stream_ptr(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtypes, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8,)
+_F8 = (torch.uint8, torch.float8_e4m3fn)
+
+
+def plan(fmt, T, H, I, E, k, schedule=SCHEDULE_AUTO):
+    """(chosen schedule, align block_m, workspace bytes) of a forward; host only."""
+    chosen, bm, ws = _I32(0), _I32(0), ctypes.c_size_t(0)
+    _check("qmoe_plan", load().qmoe_plan(fmt, T, H, I, E, k, schedule, ctypes.byref(chosen),
+                                         ctypes.byref(bm), ctypes.byref(ws)))
+    return chosen.value, bm.value, ws.value
+
+
+def moe_align(topk_ids, E, block_m, stream=None):
+    """Returns (sorted_ids [L], expert_ids [NB], num_tokens_padded [1], expert_offsets [E+1])."""
+    T, k = topk_ids.shape
+    ids = _dev(topk_ids, "topk_ids", (torch.int32,))
+    P = T * k
+    L = P + E * (block_m - 1)
+    NB = (L + block_m - 1) // block_m
+    dev = topk_ids.device
+    sorted_ids = torch.empty(L, dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(NB, dtype=torch.int32, device=dev)
+    ntp = torch.empty(1, dtype=torch.int32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    _check("moe_align", load().moe_align(ids, T, k, E, block_m, sorted_ids.data_ptr(),
+                                         expert_ids.data_ptr(), ntp.data_ptr(), offs.data_ptr(),
+                                         _stream_ptr(stream)))
+    return sorted_ids, expert_ids, ntp, offs
+
+
+def _workspace(fmt, T, H, I, E, k, schedule, workspace, device):
+    need = plan(fmt, T, H, I, E, k, schedule)[2]
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def moe_w4a16_forward(x, w13, s13, w2, s2, topk_ids, topk_weights, schedule=SCHEDULE_AUTO,
+                      out=None, workspace=None, stream=None):
+    T, H = x.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    k = topk_ids.shape[1]
+    args = [_dev(x, "x", _BF16, (T, H)),
+            _dev(w13, "w13", _U8, (E, 2 * I, H // 2)), _dev(s13, "s13", _BF16, (E, 2 * I, H // 32)),
+            _dev(w2, "w2", _U8, (E, H, I // 2)), _dev(s2, "s2", _BF16, (E, H, I // 32)),
+            _dev(topk_ids, "topk_ids", (torch.int32,), (T, k)),
+            _dev(topk_weights, "topk_weights", (torch.float32,), (T, k))]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    optr = _dev(out, "out", _BF16, (T, H))
+    workspace = _workspace(FORMAT_W4A16, T, H, I, E, k, schedule, workspace, x.device)
+    wptr = _dev(workspace, "workspace", (torch.uint8,))
+    size = ctypes.c_size_t(workspace.numel())
+    _check("moe_w4a16_forward",
+           load().moe_w4a16_forward(*args, T, H, I, E, k, schedule, optr, wptr, ctypes.byref(size),
+                                    _stream_ptr(stream)))
+    return out
+
+
+def moe_fp8_block_forward(a_q, a_scale, w13, s13, w2, s2, topk_ids, topk_weights,
+                          schedule=SCHEDULE_AUTO, out=None, workspace=None, stream=None):
+    T, H = a_q.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    k = topk_ids.shape[1]
+    args = [_dev(a_q, "a_q", _F8, (T, H)), _dev(a_scale, "a_scale", (torch.float32,), (T, H // 128)),
+            _dev(w13, "w13", _F8, (E, 2 * I, H)),
+            _dev(s13, "s13", (torch.float32,), (E, 2 * I // 128, H // 128)),
+            _dev(w2, "w2", _F8, (E, H, I)),
+            _dev(s2, "s2", (torch.float32,), (E, H // 128, I // 128)),
+            _dev(topk_ids, "topk_ids", (torch.int32,), (T, k)),
+            _dev(topk_weights, "topk_weights", (torch.float32,), (T, k))]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=a_q.device)
+    optr = _dev(out, "out", _BF16, (T, H))
+    workspace = _workspace(FORMAT_FP8, T, H, I, E, k, schedule, workspace, a_q.device)
+    wptr = _dev(workspace, "workspace", (torch.uint8,))
+    size = ctypes.c_size_t(workspace.numel())
+    _check("moe_fp8_block_forward",
+           load().moe_fp8_block_forward(*args, T, H, I, E, k, schedule, optr, wptr,
+                                        ctypes.byref(size), _stream_ptr(stream)))
+    return out
+
+
+def fp8_quantize_blocks(v, br, bc, stream=None):
+    """Block E4M3 quantizer on a 2-D fp32 GPU tensor: returns (codes uint8, scales fp32)."""
+    R, C = v.shape
+    vptr = _dev(v, "v", (torch.float32,))
+    q = torch.empty((R, C), dtype=torch.uint8, device=v.device)
+    s = torch.empty(((R + br - 1) // br, (C + bc - 1) // bc), dtype=torch.float32, device=v.device)
+    _check("qmoe_fp8_quantize_blocks",
+           load().qmoe_fp8_quantize_blocks(vptr, R, C, br, bc, q.data_ptr(), s.data_ptr(),
+                                           _stream_ptr(stream)))
+    return q, s

@@ -1,0 +1,413 @@
+// C ABI of the MoE expert FFN library: argument checks, schedule choice, workspace
+// layout and the launch sequence. Everything here is host code; no call reads a
+// device value back, allocates, frees or synchronizes.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/qmoe.h"
+#include "internal.h"
+
+namespace qmoe {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+qmoe_status fail(qmoe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+qmoe_status hip_fail(hipError_t err, const char* what) {
+  (void)hipGetLastError();  // clear the sticky launch error
+  return fail(QMOE_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kRegionAlign = 256;
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+enum Format { kW4A16 = 0, kFp8 = 1 };
+
+// Tokens-per-expert threshold of the decode profile, per pass size: the decode kernels
+// keep up to 16*mb rows of an expert per weight pass.
+int decode_mb_for(double tok_e) {
+  if (tok_e <= 10.0) return 1;
+  if (tok_e <= 20.0) return 2;
+  return 4;
+}
+
+struct Plan {
+  int fmt = 0;
+  int schedule = QMOE_SCHEDULE_DECODE;
+  int mb = 1;
+  int32_t block_m = kSegRows;
+  int64_t P = 0, L = 0, NB = 0;
+  size_t off_sorted = 0, off_expert_ids = 0, off_ntp = 0, off_offsets = 0, off_tiles = 0;
+  size_t off_h = 0, off_h32 = 0, off_hq = 0, off_hs = 0, off_out32 = 0;
+  size_t total = 0;
+};
+
+qmoe_status check_shape(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                        int32_t schedule) {
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0)
+    return fail(QMOE_ERR_INVALID_ARG, "sizes must be positive (T >= 0): T=%d H=%d I=%d E=%d k=%d",
+                T, H, I, E, k);
+  if (k > E) return fail(QMOE_ERR_INVALID_ARG, "top-k %d exceeds expert count %d", k, E);
+  if (E > QMOE_MAX_EXPERTS)
+    return fail(QMOE_ERR_UNSUPPORTED, "expert count %d exceeds %d", E, QMOE_MAX_EXPERTS);
+  if (schedule < QMOE_SCHEDULE_AUTO || schedule > QMOE_SCHEDULE_PREFILL)
+    return fail(QMOE_ERR_INVALID_ARG, "unknown schedule %d", schedule);
+  const int q = (fmt == kW4A16) ? 32 : 128;
+  if (H % q || I % q)
+    return fail(QMOE_ERR_UNSUPPORTED, "%s needs H and I multiples of %d (H=%d I=%d)",
+                fmt == kW4A16 ? "W4A16 group-32" : "block FP8 [128,128]", q, H, I);
+  const int64_t P = (int64_t)T * k;
+  const int64_t L = P + (int64_t)E * (kSegRows - 1);
+  if (L >= (int64_t(1) << 31) || (int64_t)L * (int64_t)I >= (int64_t(1) << 40))
+    return fail(QMOE_ERR_UNSUPPORTED, "too many routed pairs: T*k=%lld", (long long)P);
+  return QMOE_OK;
+}
+
+Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t schedule) {
+  Plan p;
+  p.fmt = fmt;
+  p.P = (int64_t)T * k;
+  const double tok_e = E > 0 ? (double)p.P / E : 0.0;
+  p.schedule = schedule;
+  if (schedule == QMOE_SCHEDULE_AUTO)
+    p.schedule = tok_e <= 40.0 ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
+  p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 4;
+  p.block_m = kSegRows;
+  p.L = p.P + (int64_t)E * (p.block_m - 1);
+  p.NB = (p.L + p.block_m - 1) / p.block_m;
+  size_t cur = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = cur;
+    cur = round_up(cur + bytes, kRegionAlign);
+    return at;
+  };
+  p.off_sorted = take(sizeof(int32_t) * p.L);
+  p.off_expert_ids = take(sizeof(int32_t) * p.NB);
+  p.off_ntp = take(sizeof(int32_t));
+  p.off_offsets = take(sizeof(int32_t) * (E + 1));
+  p.off_tiles = take(sizeof(int32_t) * (E + 1));
+  if (fmt == kW4A16) {
+    p.off_h = take(sizeof(uint16_t) * (size_t)p.L * I);
+  } else {
+    p.off_h32 = take(sizeof(float) * (size_t)p.L * I);
+    p.off_hq = take((size_t)p.L * I);
+    p.off_hs = take(sizeof(float) * (size_t)p.L * (I / 128));
+  }
+  p.off_out32 = take(sizeof(float) * (size_t)T * H);
+  p.total = cur;
+  return p;
+}
+
+// Optional event pairs around each stage launch (qmoe_timing_begin / _end).
+struct StageTimer {
+  std::mutex mu;
+  bool on = false;
+  int cap = 0;
+  int used[QMOE_NUM_STAGES] = {};
+  std::vector<hipEvent_t> ev[QMOE_NUM_STAGES];  // 2 per recorded forward
+
+  void clear() {
+    for (auto& v : ev) {
+      for (hipEvent_t e : v) (void)hipEventDestroy(e);
+      v.clear();
+    }
+    for (int& u : used) u = 0;
+    cap = 0;
+    on = false;
+  }
+};
+StageTimer g_timer;
+
+// Runs `launch` (returning hipError_t) bracketed by the stage's events if recording.
+template <typename F>
+hipError_t staged(int stage, hipStream_t s, F&& launch) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_timer.mu);
+    if (g_timer.on && g_timer.used[stage] < g_timer.cap) {
+      const int i = g_timer.used[stage]++;
+      e0 = g_timer.ev[stage][2 * i];
+      e1 = g_timer.ev[stage][2 * i + 1];
+    }
+  }
+  if (e0) {
+    hipError_t err = hipEventRecord(e0, s);
+    if (err != hipSuccess) return err;
+  }
+  hipError_t err = launch();
+  if (err == hipSuccess && e1) err = hipEventRecord(e1, s);
+  return err;
+}
+
+template <typename T>
+T* region(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+}  // namespace qmoe
+
+using namespace qmoe;
+
+extern "C" {
+
+int32_t qmoe_abi_version(void) { return QMOE_ABI_VERSION; }
+
+const char* qmoe_status_string(int32_t status) {
+  switch (status) {
+    case QMOE_OK: return "ok";
+    case QMOE_ERR_INVALID_ARG: return "invalid argument";
+    case QMOE_ERR_UNSUPPORTED: return "unsupported shape or format";
+    case QMOE_ERR_WORKSPACE: return "workspace too small";
+    case QMOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* qmoe_last_error(void) { return g_last_error; }
+
+qmoe_status moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, int32_t block_m,
+                      int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_tokens_padded,
+                      int32_t* expert_offsets, void* stream) {
+  g_last_error[0] = 0;
+  if (T < 0 || k <= 0 || E <= 0)
+    return fail(QMOE_ERR_INVALID_ARG, "bad sizes T=%d k=%d E=%d", T, k, E);
+  if (E > QMOE_MAX_EXPERTS)
+    return fail(QMOE_ERR_UNSUPPORTED, "expert count %d exceeds %d", E, QMOE_MAX_EXPERTS);
+  if (block_m < 1 || block_m > 256 || (block_m & (block_m - 1)))
+    return fail(QMOE_ERR_INVALID_ARG, "block_m %d must be a power of two in [1, 256]", block_m);
+  const int64_t P = (int64_t)T * k, L = P + (int64_t)E * (block_m - 1);
+  if (L >= (int64_t(1) << 31)) return fail(QMOE_ERR_UNSUPPORTED, "too many routed pairs");
+  if ((P > 0 && !topk_ids) || !sorted_ids || !expert_ids || !num_tokens_padded)
+    return fail(QMOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(topk_ids, 4) || !aligned(sorted_ids, 4) || !aligned(expert_ids, 4) ||
+      !aligned(num_tokens_padded, 4) || !aligned(expert_offsets, 4))
+    return fail(QMOE_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  const int64_t NB = (L + block_m - 1) / block_m;
+  hipError_t err = launch_align(topk_ids, (int32_t)P, E, block_m, (int32_t)L, (int32_t)NB,
+                                sorted_ids, expert_ids, num_tokens_padded, expert_offsets, 0,
+                                nullptr, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "align launch");
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                      int32_t schedule, int32_t* chosen, int32_t* block_m,
+                      size_t* workspace_bytes) {
+  g_last_error[0] = 0;
+  if (format != kW4A16 && format != kFp8)
+    return fail(QMOE_ERR_INVALID_ARG, "unknown format %d", format);
+  qmoe_status st = check_shape(format, T, H, I, E, k, schedule);
+  if (st != QMOE_OK) return st;
+  Plan p = make_plan(format, T, H, I, E, k, schedule);
+  if (chosen) *chosen = p.schedule;
+  if (block_m) *block_m = p.block_m;
+  if (workspace_bytes) *workspace_bytes = p.total;
+  return QMOE_OK;
+}
+
+qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                              const uint8_t* w2, const uint16_t* s2, const int32_t* topk_ids,
+                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
+                              void* workspace, size_t* workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  qmoe_status st = check_shape(kW4A16, T, H, I, E, k, schedule);
+  if (st != QMOE_OK) return st;
+  if (!workspace_bytes) return fail(QMOE_ERR_INVALID_ARG, "workspace_bytes is NULL");
+  const Plan p = make_plan(kW4A16, T, H, I, E, k, schedule);
+  if (!workspace) {
+    *workspace_bytes = p.total;
+    return QMOE_OK;
+  }
+  if (*workspace_bytes < p.total)
+    return fail(QMOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", *workspace_bytes, p.total);
+  if (T == 0) return QMOE_OK;
+  const void* ptrs[] = {x, w13, s13, w2, s2, topk_ids, topk_weights, out};
+  for (const void* q : ptrs)
+    if (!q) return fail(QMOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  for (const void* q : ptrs)
+    if (!aligned(q, 16)) return fail(QMOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!aligned(workspace, kRegionAlign))
+    return fail(QMOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Routing r{};
+  r.sorted_ids = region<int32_t>(workspace, p.off_sorted);
+  r.offsets = region<int32_t>(workspace, p.off_offsets);
+  r.tile_offsets = region<int32_t>(workspace, p.off_tiles);
+  r.topk_weights = topk_weights;
+  r.P = (int32_t)p.P;
+  r.k = k;
+  r.E = E;
+  r.L = (int32_t)p.L;
+  W4A16Problem prob{x, w13, s13, w2, s2, region<uint16_t>(workspace, p.off_h),
+                    region<float>(workspace, p.off_out32), T, H, I};
+
+  hipError_t err = staged(QMOE_STAGE_ZERO, s, [&] {
+    return launch_zero_f32(prob.out32, (int64_t)T * H, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "zero launch");
+  err = staged(QMOE_STAGE_ALIGN, s, [&] {
+    return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
+                        region<int32_t>(workspace, p.off_sorted),
+                        region<int32_t>(workspace, p.off_expert_ids),
+                        region<int32_t>(workspace, p.off_ntp),
+                        region<int32_t>(workspace, p.off_offsets), 0, nullptr, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "align launch");
+  err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_stream(prob, r, p.mb, s); });
+  if (err != hipSuccess) return hip_fail(err, "gate_up launch");
+  err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_stream(prob, r, p.mb, s); });
+  if (err != hipSuccess) return hip_fail(err, "down launch");
+  err = staged(QMOE_STAGE_CAST, s, [&] {
+    return launch_cast_f32_bf16(prob.out32, out, (int64_t)T * H, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "cast launch");
+  return QMOE_OK;
+}
+
+qmoe_status moe_fp8_block_forward(const uint8_t* a_q, const float* a_scale, const uint8_t* w13,
+                                  const float* s13, const uint8_t* w2, const float* s2,
+                                  const int32_t* topk_ids, const float* topk_weights, int32_t T,
+                                  int32_t H, int32_t I, int32_t E, int32_t k, int32_t schedule,
+                                  uint16_t* out, void* workspace, size_t* workspace_bytes,
+                                  void* stream) {
+  g_last_error[0] = 0;
+  qmoe_status st = check_shape(kFp8, T, H, I, E, k, schedule);
+  if (st != QMOE_OK) return st;
+  if (!workspace_bytes) return fail(QMOE_ERR_INVALID_ARG, "workspace_bytes is NULL");
+  const Plan p = make_plan(kFp8, T, H, I, E, k, schedule);
+  if (!workspace) {
+    *workspace_bytes = p.total;
+    return QMOE_OK;
+  }
+  if (*workspace_bytes < p.total)
+    return fail(QMOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", *workspace_bytes, p.total);
+  if (T == 0) return QMOE_OK;
+  const void* ptrs[] = {a_q, a_scale, w13, s13, w2, s2, topk_ids, topk_weights, out};
+  for (const void* q : ptrs)
+    if (!q) return fail(QMOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  for (const void* q : ptrs)
+    if (!aligned(q, 16)) return fail(QMOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!aligned(workspace, kRegionAlign))
+    return fail(QMOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Routing r{};
+  r.sorted_ids = region<int32_t>(workspace, p.off_sorted);
+  r.offsets = region<int32_t>(workspace, p.off_offsets);
+  r.tile_offsets = region<int32_t>(workspace, p.off_tiles);
+  r.topk_weights = topk_weights;
+  r.P = (int32_t)p.P;
+  r.k = k;
+  r.E = E;
+  r.L = (int32_t)p.L;
+  Fp8Problem prob{a_q, a_scale, w13, s13, w2, s2,
+                  region<float>(workspace, p.off_h32), region<uint8_t>(workspace, p.off_hq),
+                  region<float>(workspace, p.off_hs), region<float>(workspace, p.off_out32),
+                  T, H, I};
+
+  hipError_t err = staged(QMOE_STAGE_ZERO, s, [&] {
+    return launch_zero_f32(prob.out32, (int64_t)T * H, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "zero launch");
+  err = staged(QMOE_STAGE_ALIGN, s, [&] {
+    return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
+                        region<int32_t>(workspace, p.off_sorted),
+                        region<int32_t>(workspace, p.off_expert_ids),
+                        region<int32_t>(workspace, p.off_ntp),
+                        region<int32_t>(workspace, p.off_offsets), 0, nullptr, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "align launch");
+  err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_fp8_gateup_stream(prob, r, p.mb, s); });
+  if (err != hipSuccess) return hip_fail(err, "gate_up launch");
+  err = staged(QMOE_STAGE_REQUANT, s, [&] {
+    return launch_fp8_quantize_blocks(prob.h32, p.L, I, 1, 128, prob.hq, prob.hs, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "h requant launch");
+  err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_fp8_down_stream(prob, r, p.mb, s); });
+  if (err != hipSuccess) return hip_fail(err, "down launch");
+  err = staged(QMOE_STAGE_CAST, s, [&] {
+    return launch_cast_f32_bf16(prob.out32, out, (int64_t)T * H, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "cast launch");
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
+                                     uint8_t* q, float* scale, void* stream) {
+  g_last_error[0] = 0;
+  if (R < 0 || C < 0) return fail(QMOE_ERR_INVALID_ARG, "negative size");
+  if (br < 1 || br > 128 || bc < 1 || bc > 1024 || (int64_t)br * bc > 16384)
+    return fail(QMOE_ERR_UNSUPPORTED, "block [%d, %d] outside [1..128] x [1..1024]", br, bc);
+  if (R == 0 || C == 0) return QMOE_OK;
+  if (!v || !q || !scale) return fail(QMOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(v, 4) || !aligned(scale, 4))
+    return fail(QMOE_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  hipError_t err = launch_fp8_quantize_blocks(v, R, C, br, bc, q, scale,
+                                              static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "quantize launch");
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_timing_begin(int32_t max_calls) {
+  g_last_error[0] = 0;
+  if (max_calls < 1 || max_calls > 100000)
+    return fail(QMOE_ERR_INVALID_ARG, "max_calls %d outside [1, 100000]", max_calls);
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  g_timer.clear();
+  for (auto& v : g_timer.ev) {
+    v.resize(2 * (size_t)max_calls, nullptr);
+    for (hipEvent_t& e : v) {
+      hipError_t err = hipEventCreate(&e);
+      if (err != hipSuccess) {
+        g_timer.clear();
+        return hip_fail(err, "hipEventCreate");
+      }
+    }
+  }
+  g_timer.cap = max_calls;
+  g_timer.on = true;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_timing_end(float* ms_sum, int32_t* count) {
+  g_last_error[0] = 0;
+  if (!ms_sum || !count) return fail(QMOE_ERR_INVALID_ARG, "NULL output");
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  g_timer.on = false;
+  qmoe_status st = QMOE_OK;
+  for (int stg = 0; stg < QMOE_NUM_STAGES; ++stg) {
+    float sum = 0.f;
+    for (int i = 0; i < g_timer.used[stg]; ++i) {
+      hipEvent_t e0 = g_timer.ev[stg][2 * i], e1 = g_timer.ev[stg][2 * i + 1];
+      float ms = 0.f;
+      hipError_t err = hipEventSynchronize(e1);
+      if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+      if (err != hipSuccess) {
+        st = hip_fail(err, "stage event");
+        break;
+      }
+      sum += ms;
+    }
+    ms_sum[stg] = sum;
+    count[stg] = g_timer.used[stg];
+  }
+  g_timer.clear();
+  return st;
+}
+
+}  // extern "C"

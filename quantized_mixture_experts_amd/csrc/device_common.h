@@ -1,0 +1,109 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE expert FFN library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef int i32x8 __attribute__((__vector_size__(8 * sizeof(int))));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers (one wave, 16x16 output tile; lane l holds rows 4*(l/16)+r, r=0..3,
+// of column l%16). A operand: lane l supplies row l%16, k-slice (l/16); B operand:
+// lane l supplies column l%16, the same k-slice.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(const uint32_t (&a)[4], const uint32_t (&b)[4],
+                                                    f32x4 c) {
+  bf16x8 av, bv;
+  __builtin_memcpy(&av, a, 16);
+  __builtin_memcpy(&bv, b, 16);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
+}
+
+// E4M3 x E4M3, K = 128 per instruction (lane supplies 32 consecutive k values).
+// The block-scale operands are fixed at E8M0 127 (= 1.0): the block scales of this
+// format are general fp32 values and are applied to the fp32 accumulator instead.
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const u32x4 (&a)[2], const u32x4 (&b)[2],
+                                                    f32x4 c) {
+  i32x8 av, bv;
+  __builtin_memcpy(&av, a, 32);
+  __builtin_memcpy(&bv, b, 32);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane 4x4 transpose of 32-bit words among the four 16-lane rows of a wave:
+// on entry register j of row q holds M[q][j]; on exit register g of row q holds M[g][q].
+// Two permlane32 swaps exchange the off-diagonal 2x2 blocks of rows {0,1} x {2,3},
+// two permlane16 swaps finish inside each half.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void transpose4_rows(uint32_t (&m)[4]) {
+  auto s02 = __builtin_amdgcn_permlane32_swap(m[0], m[2], false, false);
+  auto s13 = __builtin_amdgcn_permlane32_swap(m[1], m[3], false, false);
+  m[0] = s02[0];
+  m[2] = s02[1];
+  m[1] = s13[0];
+  m[3] = s13[1];
+  auto s01 = __builtin_amdgcn_permlane16_swap(m[0], m[1], false, false);
+  auto s23 = __builtin_amdgcn_permlane16_swap(m[2], m[3], false, false);
+  m[0] = s01[0];
+  m[1] = s01[1];
+  m[2] = s23[0];
+  m[3] = s23[1];
+}
+
+// ---------------------------------------------------------------------------
+// INT4 codes -> bf16 operand registers.
+// A 32-bit word holds 8 codes n0..n7 (nibble j = bits 4j..4j+3). OR-ing a nibble into
+// the mantissa of bf16 128.0 (0x4300) gives exactly 128 + code, so
+//   b[0] = (n0, n4), b[1] = (n1, n5), b[2] = (n2, n6), b[3] = (n3, n7)
+// as bf16 pairs (low half first). The zero point (128 + 8) is removed on the fp32
+// accumulator (see the kernels), and the activation operand is permuted to the same
+// k order with perm_act8.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void int4_to_bf16_biased(uint32_t w, uint32_t (&b)[4]) {
+  constexpr uint32_t kMask = 0x000F000Fu, kOne28 = 0x43004300u;
+  b[0] = (w & kMask) | kOne28;
+  b[1] = ((w >> 4) & kMask) | kOne28;
+  b[2] = ((w >> 8) & kMask) | kOne28;
+  b[3] = ((w >> 12) & kMask) | kOne28;
+}
+
+// 8 consecutive bf16 activations x0..x7 (dwords d0..d3) -> operand order
+// (x0,x4), (x1,x5), (x2,x6), (x3,x7), matching int4_to_bf16_biased.
+__device__ __forceinline__ void perm_act8(const u32x4 d, uint32_t (&a)[4]) {
+  a[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
+  a[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
+  a[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
+  a[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+}  // namespace qmoe

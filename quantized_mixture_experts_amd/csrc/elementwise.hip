@@ -1,0 +1,110 @@
+// Elementwise kernels of the MoE FFN path: clearing the fp32 combine buffer, the final
+// fp32 -> bf16 rounding of the output, and the block E4M3 quantizer.
+//
+// The quantizer follows "SGLang W8A8 Block FP8 quantization kernel config guide",
+// background section: E4M3 (max 448), one scale per block from the block's absmax.
+// Per block: scale = max(absmax, 1e-10) / 448, q = e4m3(clamp(v / scale, -448, 448))
+// with IEEE fp32 division and round-to-nearest-even (gfx950's v_cvt_pk_fp8_f32 emits
+// OCP E4M3FN).
+#include "device_common.h"
+#include "internal.h"
+
+namespace qmoe {
+
+namespace {
+
+constexpr int kEwThreads = 256;
+
+__global__ void __launch_bounds__(kEwThreads) zero_f32_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kEwThreads * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * kEwThreads + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      *reinterpret_cast<f32x4*>(p + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      for (int64_t j = i; j < n; ++j) p[j] = 0.f;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kEwThreads)
+    cast_f32_bf16_kernel(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kEwThreads * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * kEwThreads + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(src + i);
+      uint32_t lo = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+      uint32_t hi = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+      *reinterpret_cast<uint2*>(dst + i) = make_uint2(lo, hi);
+    } else {
+      for (int64_t j = i; j < n; ++j) dst[j] = f32_to_bf16(src[j]);
+    }
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+  return v;
+}
+
+// One wave per [br, bc] block; four blocks per work-group.
+__global__ void __launch_bounds__(kEwThreads)
+    fp8_quantize_blocks_kernel(const float* __restrict__ v, int64_t R, int64_t C, int32_t br,
+                               int32_t bc, uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int64_t nbc = (C + bc - 1) / bc, nbr = (R + br - 1) / br;
+  const int64_t blk = (int64_t)blockIdx.x * (kEwThreads / kWave) + threadIdx.x / kWave;
+  if (blk >= nbr * nbc) return;
+  const int lane = lane_id();
+  const int64_t bi = blk / nbc, bj = blk % nbc;
+  const int64_t r0 = bi * br, c0 = bj * bc;
+  const int rows = (int)min<int64_t>(br, R - r0), cols = (int)min<int64_t>(bc, C - c0);
+  const int n = rows * cols;
+  float amax = 0.f;
+  for (int i = lane; i < n; i += kWave) {
+    const int64_t r = r0 + i / cols, c = c0 + i % cols;
+    amax = fmaxf(amax, fabsf(v[r * C + c]));
+  }
+  amax = wave_max(amax);
+  const float s = fmaxf(amax, 1e-10f) / 448.0f;
+  if (lane == 0) scale[blk] = s;
+  for (int i = lane; i < n; i += kWave) {
+    const int64_t r = r0 + i / cols, c = c0 + i % cols;
+    const float t = fminf(fmaxf(v[r * C + c] / s, -448.0f), 448.0f);
+    const uint32_t packed = __builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0u, false);
+    q[r * C + c] = (uint8_t)(packed & 0xFFu);
+  }
+}
+
+int grid_for(int64_t n) {
+  int64_t g = (n / 4 + kEwThreads - 1) / kEwThreads;
+  if (g < 1) g = 1;
+  if (g > 4096) g = 4096;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3(grid_for(n)), dim3(kEwThreads), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_f32_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_f32_bf16_kernel, dim3(grid_for(n)), dim3(kEwThreads), 0, stream, src,
+                     dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
+                                      uint8_t* q, float* scale, hipStream_t stream) {
+  const int64_t nblk = ((R + br - 1) / br) * ((C + bc - 1) / bc);
+  if (nblk <= 0) return hipSuccess;
+  const int64_t per = kEwThreads / kWave;
+  hipLaunchKernelGGL(fp8_quantize_blocks_kernel, dim3((unsigned)((nblk + per - 1) / per)),
+                     dim3(kEwThreads), 0, stream, v, R, C, br, bc, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,72 @@
+// Host-side declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// --- align (align.hip) -----------------------------------------------------
+size_t align_lds_bytes(int32_t E);
+hipError_t launch_align(const int32_t* ids, int32_t P, int32_t E, int32_t B, int32_t L, int32_t NB,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
+                        int32_t* expert_offsets, int32_t tile_m, int32_t* tile_offsets,
+                        hipStream_t stream);
+
+// --- elementwise helpers (elementwise.hip) --------------------------------
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
+hipError_t launch_cast_f32_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
+hipError_t launch_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
+                                      uint8_t* q, float* scale, hipStream_t stream);
+
+// --- grouped expert GEMMs ---------------------------------------------------
+// Routing view shared by the expert GEMMs: segments of the sorted pair list, each a
+// multiple of kSegRows rows, expert e owning [offsets[e], offsets[e+1]).
+constexpr int kSegRows = 16;
+
+struct Routing {
+  const int32_t* sorted_ids;    // [L]
+  const int32_t* offsets;       // [E + 1]
+  const int32_t* tile_offsets;  // [E + 1], tiles of the prefill GEMM's row-tile size
+  const float* topk_weights;    // [P]
+  int32_t P, k, E, L;
+};
+
+struct W4A16Problem {
+  const uint16_t* x;  // [T, H] bf16
+  const uint8_t* w13;
+  const uint16_t* s13;
+  const uint8_t* w2;
+  const uint16_t* s2;
+  uint16_t* h;    // [L, I] bf16
+  float* out32;   // [T, H]
+  int32_t T, H, I;
+};
+
+struct Fp8Problem {
+  const uint8_t* a_q;    // [T, H]
+  const float* a_scale;  // [T, H/128]
+  const uint8_t* w13;    // [E, 2I, H]
+  const float* s13;      // [E, 2I/128, H/128]
+  const uint8_t* w2;     // [E, H, I]
+  const float* s2;       // [E, H/128, I/128]
+  float* h32;            // [L, I]
+  uint8_t* hq;           // [L, I]
+  float* hs;             // [L, I/128]
+  float* out32;          // [T, H]
+  int32_t T, H, I;
+};
+
+// Decode profile: a work-group owns (expert, column chunk) and streams the weights
+// once per pass of up to 16*mb rows of that expert.
+hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, int mb,
+                                      hipStream_t stream);
+hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
+                                    hipStream_t stream);
+hipError_t launch_fp8_gateup_stream(const Fp8Problem& p, const Routing& r, int mb,
+                                    hipStream_t stream);
+hipError_t launch_fp8_down_stream(const Fp8Problem& p, const Routing& r, int mb,
+                                  hipStream_t stream);
+
+}  // namespace qmoe

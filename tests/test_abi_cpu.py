@@ -1,0 +1,96 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/qmoe.h
+declares, and rejects bad arguments with status codes before any GPU work."""
+import ctypes
+
+import pytest
+
+from quantized_mixture_experts_amd import binding
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000  # an aligned non-NULL address; never dereferenced by the checks
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = binding.declared_functions()
+    assert {"moe_align", "moe_w4a16_forward", "moe_fp8_block_forward", "qmoe_plan",
+            "qmoe_fp8_quantize_blocks", "qmoe_status_string", "qmoe_last_error",
+            "qmoe_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.qmoe_abi_version() == 1
+    assert lib.qmoe_status_string(3) == b"workspace too small"
+
+
+def _w4(lib, T=32, H=7168, I=2048, E=48, k=8, sched=0, ptr=FAKE, ws=None, size=1 << 40, out=FAKE):
+    sz = ctypes.c_size_t(size)
+    st = lib.moe_w4a16_forward(ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, k, sched, out, ws,
+                               ctypes.byref(sz), None)
+    return st, sz.value
+
+
+def test_workspace_query_and_plan(lib):
+    st, need = _w4(lib, ws=None)
+    assert st == OK and need > 0
+    chosen, bm, ws = binding.plan(binding.FORMAT_W4A16, 32, 7168, 2048, 48, 8)
+    assert chosen == binding.SCHEDULE_DECODE and ws == need and bm == 16
+    assert binding.plan(binding.FORMAT_W4A16, 8192, 7168, 2048, 48, 8)[0] == binding.SCHEDULE_PREFILL
+    # the workspace holds at least the combine buffer and h
+    assert need >= 32 * 7168 * 4 + 32 * 8 * 2048 * 2
+    assert binding.plan(binding.FORMAT_W4A16, 32, 7168, 2048, 48, 8, binding.SCHEDULE_PREFILL)[0] == 2
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=7169), UNSUPPORTED), (dict(H=7200 - 16), UNSUPPORTED), (dict(I=2040), UNSUPPORTED),
+    (dict(k=49), INVALID), (dict(E=0), INVALID), (dict(E=5000, k=8), UNSUPPORTED),
+    (dict(sched=7), INVALID), (dict(T=-1), INVALID),
+])
+def test_w4a16_rejects_bad_shapes(lib, kw, status):
+    st, _ = _w4(lib, ws=FAKE, **kw)
+    assert st == status, binding.load().qmoe_last_error()
+    assert lib.qmoe_last_error()
+
+
+def test_w4a16_rejects_small_workspace_null_and_misaligned(lib):
+    st, need = _w4(lib, ws=None)
+    assert _w4(lib, ws=FAKE, size=need - 1)[0] == WORKSPACE
+    assert _w4(lib, ws=FAKE, size=need, ptr=None)[0] == INVALID
+    assert _w4(lib, ws=FAKE, size=need, out=None)[0] == INVALID
+    assert _w4(lib, ws=FAKE, size=need, ptr=FAKE + 4)[0] == INVALID
+    assert _w4(lib, ws=FAKE + 16, size=need)[0] == INVALID  # workspace not 256-aligned
+    assert _w4(lib, T=0, ws=FAKE, size=need)[0] == OK  # nothing to do, nothing launched
+
+
+def test_fp8_rejects_bad_shapes(lib):
+    sz = ctypes.c_size_t(1 << 40)
+    f = lib.moe_fp8_block_forward
+    args = [FAKE] * 8
+    assert f(*args, 16, 7168 + 32, 2048, 32, 8, 0, FAKE, FAKE, ctypes.byref(sz), None) == UNSUPPORTED
+    assert f(*args, 16, 7168, 2048 + 64, 32, 8, 0, FAKE, FAKE, ctypes.byref(sz), None) == UNSUPPORTED
+    assert f(*args, 16, 7168, 2048, 32, 33, 0, FAKE, FAKE, ctypes.byref(sz), None) == INVALID
+    sz = ctypes.c_size_t(0)
+    assert f(*args, 16, 7168, 2048, 32, 8, 0, FAKE, None, ctypes.byref(sz), None) == OK
+    assert sz.value > 16 * 7168 * 4
+    need = sz.value
+    sz = ctypes.c_size_t(need - 1)
+    assert f(*args, 16, 7168, 2048, 32, 8, 0, FAKE, FAKE, ctypes.byref(sz), None) == WORKSPACE
+
+
+def test_align_and_quantizer_reject_bad_arguments(lib):
+    for bm in (0, 3, 512, -16):
+        assert lib.moe_align(FAKE, 4, 2, 8, bm, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_align(FAKE, 4, 2, 0, 16, FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_align(FAKE, 4, 2, 8, 16, None, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_align(FAKE, 4, 2, 8, 16, FAKE + 2, FAKE, FAKE, FAKE, None) == INVALID
+    assert lib.moe_align(FAKE, 4, 2, 9000, 16, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    q = lib.qmoe_fp8_quantize_blocks
+    assert q(FAKE, 4, 4, 0, 128, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, 4, 4, 129, 128, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, 4, 4, 128, 2048, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, -1, 4, 1, 128, FAKE, FAKE, None) == INVALID
+    assert q(None, 4, 4, 1, 128, FAKE, FAKE, None) == INVALID
+    assert q(FAKE, 0, 4, 1, 128, FAKE, FAKE, None) == OK  # empty: nothing launched

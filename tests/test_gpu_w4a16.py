@@ -1,0 +1,109 @@
+"""GPU W4A16 routed MoE forward (moe_w4a16_forward through the C ABI) against the CPU
+oracle, per token row within 1e-2 relative error: every workload at full size (all rows
+where the oracle is quick, a seeded sample of rows otherwise), both schedules, ragged
+and degenerate shapes, and exact special cases."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, bf16_out_to_f64, report, to_dev
+from quantized_mixture_experts_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+_CASES = {}
+
+
+def _case(name):
+    if name not in _CASES:
+        _CASES.clear()
+        _CASES[name] = inputs.w4a16_case(inputs.CONFIGS[name])
+    return _CASES[name]
+
+
+def _forward(case, schedule):
+    d = to_dev(case)
+    out = binding.moe_w4a16_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
+                                    d["topk_weights"], schedule=schedule)
+    torch.cuda.synchronize()
+    return bf16_out_to_f64(out)
+
+
+def _oracle(oracle_mod, case, rows):
+    return oracle_mod.w4a16_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
+                                case["topk_ids"], case["topk_weights"], rows=rows)
+
+
+# rows compared per workload (None = all rows)
+_ROWS = {"tiny": None, "decode": None, "prefill": 48, "full384": 32}
+
+
+_WORKLOADS = [(n, s) for n in ("tiny", "decode", "prefill", "full384")
+              for s in (binding.SCHEDULE_AUTO, binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL)
+              if not (n == "prefill" and s == binding.SCHEDULE_DECODE)]
+
+
+@pytest.mark.parametrize("name,schedule", _WORKLOADS)
+def test_w4a16_workloads(oracle_mod, name, schedule):
+    cfg = inputs.CONFIGS[name]
+    print(f"[w4a16] {name} schedule={schedule}", flush=True)
+    case = _case(name)
+    got = _forward(case, schedule)
+    n = _ROWS[name]
+    rows = inputs.sample_rows(cfg.T, n if n is not None else cfg.T, seed=cfg.seed)
+    ref = _oracle(oracle_mod, case, rows)
+    err = report(f"{name}/sched{schedule}", got[rows], ref)
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (50, 800, 352, 10, 3),   # ragged against the 256-deep k step and the column chunks
+    (1, 256, 128, 1, 1),     # one token, one expert: a dense SwiGLU FFN
+    (70, 288, 96, 4, 4),     # every expert active, > 16 rows per expert
+    (9, 32, 32, 3, 2),       # smallest group-aligned sizes
+])
+@pytest.mark.parametrize("schedule", [binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL])
+def test_w4a16_ragged_shapes(oracle_mod, T, H, I, E, k, schedule):
+    print(f"[w4a16] ragged T={T} H={H} I={I} E={E} k={k} schedule={schedule}", flush=True)
+    case = inputs.custom_w4a16_case(T, H, I, E, k, seed=T * 31 + H)
+    got = _forward(case, schedule)
+    ref = _oracle(oracle_mod, case, None)
+    assert report(f"ragged {T}x{H}x{I}", got, ref).max() <= TOL
+
+
+def test_w4a16_zero_routing_weights_give_exact_zero():
+    case = inputs.custom_w4a16_case(20, 256, 128, 8, 2, seed=5)
+    case["topk_weights"][:] = 0.0
+    assert np.all(_forward(case, binding.SCHEDULE_AUTO) == 0.0)
+
+
+def test_w4a16_zero_point_weights_give_zero():
+    case = inputs.custom_w4a16_case(20, 256, 128, 8, 2, seed=6)
+    case["w13"][:] = 0x88
+    got = _forward(case, binding.SCHEDULE_AUTO)
+    assert np.abs(got).max() <= 1e-6
+
+
+def test_w4a16_dropped_ids(oracle_mod):
+    case = inputs.custom_w4a16_case(12, 256, 128, 8, 3, seed=7)
+    case["topk_ids"][:, 2] = np.array([-1, 8, 100, -5] * 3, np.int32)
+    got = _forward(case, binding.SCHEDULE_AUTO)
+    ref = _oracle(oracle_mod, case, None)
+    assert report("dropped ids", got, ref).max() <= TOL
+
+
+def test_w4a16_empty_batch():
+    case = inputs.custom_w4a16_case(4, 256, 128, 8, 2, seed=8)
+    d = to_dev(case)
+    out = binding.moe_w4a16_forward(d["x"][:0], d["w13"], d["s13"], d["w2"], d["s2"],
+                                    d["topk_ids"][:0], d["topk_weights"][:0])
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
+
+
+def test_w4a16_repeat_calls_agree():
+    case = inputs.custom_w4a16_case(33, 512, 256, 6, 2, seed=10)
+    a = _forward(case, binding.SCHEDULE_AUTO)
+    b = _forward(case, binding.SCHEDULE_AUTO)
+    # fp32 atomics may add in a different order; the results stay within rounding
+    assert np.max(np.abs(a - b)) <= 1e-2 * np.max(np.abs(a))
