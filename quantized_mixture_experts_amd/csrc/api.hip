@@ -35,13 +35,10 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 enum Format { kW4A16 = 0, kFp8 = 1 };
 
-// Tokens-per-expert threshold of the decode profile, per pass size: the decode kernels
-// keep up to 16*mb rows of an expert per weight pass.
-int decode_mb_for(double tok_e) {
-  if (tok_e <= 10.0) return 1;
-  if (tok_e <= 20.0) return 2;
-  return 4;
-}
+// Rows per weight pass of the decode kernels, in 16-row blocks (1 or 2): one block
+// covers the usual decode load of a few rows per expert; two keep a pass register-resident
+// (larger passes spill).
+int decode_mb_for(double tok_e) { return tok_e <= 10.0 ? 1 : 2; }
 
 struct Plan {
   int fmt = 0;
@@ -83,7 +80,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   p.schedule = schedule;
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= 40.0 ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
-  p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 4;
+  p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 2;
   p.block_m = kSegRows;
   p.L = p.P + (int64_t)E * (p.block_m - 1);
   p.NB = (p.L + p.block_m - 1) / p.block_m;

@@ -244,11 +244,8 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
     case 1:
       hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), grid, dim3(kThreads), 0, stream, a);
       break;
-    case 2:
-      hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 2>), grid, dim3(kThreads), 0, stream, a);
-      break;
     default:
-      hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 4>), grid, dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 2>), grid, dim3(kThreads), 0, stream, a);
       break;
   }
   return hipGetLastError();
