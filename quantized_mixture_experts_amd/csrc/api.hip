@@ -47,7 +47,7 @@ struct Plan {
   int32_t block_m = kSegRows;
   int64_t P = 0, L = 0, NB = 0;
   size_t off_sorted = 0, off_expert_ids = 0, off_ntp = 0, off_offsets = 0, off_tiles = 0;
-  size_t off_h = 0, off_h32 = 0, off_hq = 0, off_hs = 0, off_out32 = 0;
+  size_t off_xs = 0, off_h = 0, off_h32 = 0, off_hq = 0, off_hs = 0, off_out32 = 0;
   size_t total = 0;
 };
 
@@ -96,6 +96,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   p.off_offsets = take(sizeof(int32_t) * (E + 1));
   p.off_tiles = take(sizeof(int32_t) * (E + 1));
   if (fmt == kW4A16) {
+    p.off_xs = take(sizeof(uint16_t) * (size_t)p.L * H);
     p.off_h = take(sizeof(uint16_t) * (size_t)p.L * I);
   } else {
     p.off_h32 = take(sizeof(float) * (size_t)p.L * I);
@@ -250,8 +251,9 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
   r.k = k;
   r.E = E;
   r.L = (int32_t)p.L;
-  W4A16Problem prob{x, w13, s13, w2, s2, region<uint16_t>(workspace, p.off_h),
-                    region<float>(workspace, p.off_out32), T, H, I};
+  W4A16Problem prob{x, region<uint16_t>(workspace, p.off_xs), w13, s13, w2, s2,
+                    region<uint16_t>(workspace, p.off_h), region<float>(workspace, p.off_out32),
+                    T, H, I};
 
   hipError_t err = staged(QMOE_STAGE_ZERO, s, [&] {
     return launch_zero_f32(prob.out32, (int64_t)T * H, s);
@@ -265,6 +267,11 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
                         region<int32_t>(workspace, p.off_offsets), 0, nullptr, s);
   });
   if (err != hipSuccess) return hip_fail(err, "align launch");
+  // The gathered activation rows belong to the align stage's timing.
+  err = staged(QMOE_STAGE_ALIGN, s, [&] {
+    return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "gather launch");
   err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_stream(prob, r, p.mb, s); });
   if (err != hipSuccess) return hip_fail(err, "gate_up launch");
   err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_stream(prob, r, p.mb, s); });

@@ -82,12 +82,31 @@ __device__ __forceinline__ void transpose4_rows(uint32_t (&m)[4]) {
 // accumulator (see the kernels), and the activation operand is permuted to the same
 // k order with perm_act8.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void int4_to_bf16_biased(uint32_t w, uint32_t (&b)[4]) {
-  constexpr uint32_t kMask = 0x000F000Fu, kOne28 = 0x43004300u;
-  b[0] = (w & kMask) | kOne28;
-  b[1] = ((w >> 4) & kMask) | kOne28;
-  b[2] = ((w >> 8) & kMask) | kOne28;
-  b[3] = ((w >> 12) & kMask) | kOne28;
+constexpr uint32_t kNibbleMask = 0x000F000Fu;
+constexpr uint32_t kBf16Bias128 = 0x43004300u;
+
+// `mask` must hold kNibbleMask (in an SGPR) and `one28` kBf16Bias128 (in a VGPR), see
+// opaque_sgpr / opaque_vgpr: with register operands the compiler selects one
+// v_and_or_b32 per pair (a VOP3 encoding reads at most one SGPR);
+// with two literal operands it would emit v_and_b32 + v_or_b32, since gfx9 VOP3
+// encodings take no literal.
+__device__ __forceinline__ void int4_to_bf16_biased(uint32_t w, uint32_t mask, uint32_t one28,
+                                                    uint32_t (&b)[4]) {
+  b[0] = (w & mask) | one28;
+  b[1] = ((w >> 4) & mask) | one28;
+  b[2] = ((w >> 8) & mask) | one28;
+  b[3] = ((w >> 12) & mask) | one28;
+}
+
+// Values the compiler must keep in a register and cannot fold (the empty asm emits no
+// instruction).
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t opaque_sgpr(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
 }
 
 // 8 consecutive bf16 activations x0..x7 (dwords d0..d3) -> operand order
@@ -97,6 +116,39 @@ __device__ __forceinline__ void perm_act8(const u32x4 d, uint32_t (&a)[4]) {
   a[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
   a[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
   a[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
+}
+
+// Position of element e (0..7) of an 8-element k slice in the operand k order
+// (0, 4, 1, 5, 2, 6, 3, 7): element e sits at ((e & 3) << 1) | (e >> 2).
+__device__ __forceinline__ int operand_pos8(int e) { return ((e & 3) << 1) | (e >> 2); }
+
+// Element offset of (row r, k index k) of an [rows, K] activation matrix in the tiled
+// operand layout used for the GEMMs' activation side: the operand of one (16-row block,
+// 32-deep k group) is 64 lanes x 16 B contiguous, lane (k slice q = (k % 32) / 8) * 16 +
+// (row r % 16) holding that slice's 8 values in operand k order. Rows must come in whole
+// 16-row blocks; the footprint equals the row-major one.
+__device__ __forceinline__ size_t tiled_offset(int r, int k, int K) {
+  const int m = r & 15, q = (k >> 3) & 3;
+  return (((size_t)(r >> 4) * (K >> 5) + (k >> 5)) * 64 + q * 16 + m) * 8 + operand_pos8(k & 7);
+}
+
+// ---------------------------------------------------------------------------
+// XCD-aware work distribution. MI355X has 8 XCDs, each with its own L2, and the
+// dispatcher deals work-groups to them round-robin by launch index. With a 1-D grid of
+// xcd_major_grid(items) work-groups, xcd_major_item() hands XCD x the contiguous item
+// range [x * per, (x + 1) * per): items that share data (the same expert) stay on one
+// L2. Returns -1 for the padding work-groups.
+// ---------------------------------------------------------------------------
+constexpr int kNumXcd = 8;
+
+__host__ __device__ inline int xcd_major_grid(int items) {
+  return (items + kNumXcd - 1) / kNumXcd * kNumXcd;
+}
+
+__device__ __forceinline__ int xcd_major_item(int block, int grid, int items) {
+  const int per = grid / kNumXcd;
+  const int item = (block % kNumXcd) * per + block / kNumXcd;
+  return item < items ? item : -1;
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

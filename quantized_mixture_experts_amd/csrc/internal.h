@@ -35,6 +35,7 @@ struct Routing {
 
 struct W4A16Problem {
   const uint16_t* x;  // [T, H] bf16
+  uint16_t* xs;       // [L, H] bf16: x gathered by sorted row, operand k order
   const uint8_t* w13;
   const uint16_t* s13;
   const uint8_t* w2;
@@ -57,6 +58,10 @@ struct Fp8Problem {
   float* out32;          // [T, H]
   int32_t T, H, I;
 };
+
+// xs[r] = x[token of sorted row r] in the GEMM operand k order.
+hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t* ntp, int32_t H,
+                              uint16_t* xs, hipStream_t stream);
 
 // Decode profile: a work-group owns (expert, column chunk) and streams the weights
 // once per pass of up to 16*mb rows of that expert.

@@ -5,20 +5,27 @@
 // "vLLM integration"). At a few routed rows per expert the work is a weight stream, so
 // the decode profile puts the dequantized weights on the MFMA column side and the
 // expert's rows (padded to 16) on the row side (the page's decode profile swaps the MMA
-// operands the same way, section "H200 and Blackwell indexed decode"), and one
-// work-group owns (expert, column chunk) so each weight byte is read once per pass.
+// operands the same way, section "H200 and Blackwell indexed decode"), and one wave owns
+// (expert, two column tiles) so each weight byte is read once per pass.
 //
 // gfx950 mapping, per wave and per 256-deep k step:
-//   * each lane loads 2 x 16 B of one weight row (128 B per row, full cache lines);
-//     lane quarter q holds whole groups q and 4+q; a 4x4 permlane transpose regroups
-//     them so that for every group the four quarters hold its four words, which is the
-//     k layout of one v_mfma_f32_16x16x32_bf16 (one MFMA = one scale group);
+//   * each lane loads 2 x 16 B of one weight row, so one step consumes a whole 128 B
+//     cache line per row; lane quarter q holds whole groups q and 4+q; a 4x4 permlane
+//     transpose regroups them so that for every group the four quarters hold its four
+//     words, the k layout of one v_mfma_f32_16x16x32_bf16 (one MFMA = one scale group);
 //   * codes become bf16 (128 + code) with one AND-OR per pair; the zero point is removed
-//     through the MFMA's C operand: C = x . (-136) for the group, computed by one extra
-//     MFMA per group shared by all column tiles;
+//     through the MFMA's C operand: C = x . (-136) for the group, from one extra MFMA per
+//     group shared by the wave's column tiles;
 //   * the group scale multiplies the fp32 MFMA result (one FMA per output element);
-//   * gate_up fuses SiLU(gate) * up and stores h (bf16, by sorted row); down scales by
-//     the routing weight and scatter-adds into the fp32 output with hardware atomics.
+//   * weights and scales are prefetched one k step ahead in registers; a small register
+//     footprint (4 waves per SIMD) is what hides HBM latency under load;
+//   * the activation operand (the expert's 16 rows) is shared by the work-group's four
+//     waves: 512-deep chunks are copied once into LDS (double-buffered, one barrier per
+//     chunk) and read with ds_read_b128, which keeps the per-CU vector-memory address
+//     path free for the weight stream. Activation rows live in a tiled layout in which
+//     the operand of one (16-row block, k group) is 1 KB contiguous.
+// gate_up fuses SiLU(gate) * up and stores h (bf16, tiled by sorted row); down scales by
+// the routing weight and scatter-adds into the fp32 output with hardware atomics.
 #include "device_common.h"
 #include "internal.h"
 
@@ -29,182 +36,217 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWavesPerGroup = kThreads / kWave;
 constexpr uint32_t kNeg136Pair = 0xC308C308u;  // bf16 -136, twice
+constexpr int kChunkGroups = 16;               // k groups per LDS activation chunk
 
 enum class Epi { GateUp, Down };
 
 struct StreamArgs {
-  const uint16_t* act;        // gate_up: x [T, K] (rows gathered by token); down: h [L, K]
+  const uint16_t* act;        // [L, K] activation rows, tiled layout (tiled_offset)
   const uint8_t* w;           // [E, N, K/2]
   const uint16_t* s;          // [E, N, K/32]
   const int32_t* sorted_ids;  // [L]
   const int32_t* offsets;     // [E + 1]
   const float* topk_weights;  // [P]
-  uint16_t* h;                // gate_up output [L, I]
+  uint16_t* h;                // gate_up output [L, I], tiled layout
   float* out32;               // down output [T, N]
   int32_t P, k, K, N, I;
+  int32_t chunks, items;      // column chunks per expert; E * chunks
 };
 
-struct WBuf {
-  u32x4 w[4][2];
-  u32x4 s[4];
+struct Stage {
+  u32x4 w[2][2];  // two 16 B chunks of each column tile's row (groups q and 4+q)
+  u32x4 s[2];     // eight bf16 group scales per tile
 };
 
 template <Epi EPI, int MB>
-__global__ void __launch_bounds__(kThreads) w4a16_stream_kernel(StreamArgs a) {
-  const int e = blockIdx.y;
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(MB == 1 ? 3 : 2)))
+    w4a16_stream_kernel(StreamArgs a) {
+  // Activation chunks: [buffer][M-block][group in chunk][lane], 16 B each.
+  __shared__ u32x4 a_lds[2][MB][kChunkGroups][kWave];
+
+  // Work-groups are dealt to the 8 XCDs round-robin by launch index; give each XCD a
+  // contiguous range of (expert, column chunk) items in expert-major order so that an
+  // expert's activation rows are read into one XCD's L2, not all eight.
+  const int item = xcd_major_item(blockIdx.x, gridDim.x, a.items);
+  if (item < 0) return;
+  const int e = item / a.chunks, chunk = item % a.chunks;
   const int seg0 = a.offsets[e], seg1 = a.offsets[e + 1];
   if (seg0 == seg1) return;
   const int wave = threadIdx.x / kWave, lane = lane_id();
   const int col = lane & 15, quad = lane >> 4;
 
-  // Column tiles of this wave (4 x 16 weight rows).
-  int row[4];
-  bool tile_ok[4];
+  // Two column tiles of 16 weight rows per wave: gate and up rows of the same 16 h
+  // columns for gate_up, 32 consecutive output columns for down. Waves past the end
+  // keep running (with a clamped tile) to take part in the work-group's barriers.
+  int row[2];
+  bool tile_ok[2];
   int j0 = 0;
   if constexpr (EPI == Epi::GateUp) {
-    j0 = (blockIdx.x * kWavesPerGroup + wave) * 32;
-    if (j0 >= a.I) return;
-    row[0] = j0 + col;
-    row[1] = j0 + 16 + col;
-    row[2] = a.I + j0 + col;
-    row[3] = a.I + j0 + 16 + col;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) tile_ok[t] = true;
+    j0 = (chunk * kWavesPerGroup + wave) * 16;
+    const bool ok = j0 < a.I;
+    const int jc = ok ? j0 : 0;
+    row[0] = jc + col;
+    row[1] = a.I + jc + col;
+    tile_ok[0] = tile_ok[1] = ok;
   } else {
-    j0 = (blockIdx.x * kWavesPerGroup + wave) * 64;
-    if (j0 >= a.N) return;
+    j0 = (chunk * kWavesPerGroup + wave) * 32;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
       tile_ok[t] = j0 + 16 * t < a.N;
       row[t] = tile_ok[t] ? j0 + 16 * t + col : col;
     }
   }
 
   const int K = a.K, G = K / 32, KB = K / 2;
-  const uint8_t* wrow[4];
-  const uint16_t* srow[4];
+  const uint8_t* wrow[2];
+  const uint16_t* srow[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < 2; ++t) {
     wrow[t] = a.w + ((size_t)e * a.N + row[t]) * KB;
     srow[t] = a.s + ((size_t)e * a.N + row[t]) * G;
   }
-  const int nfull = K / 256;
-  uint32_t neg136[4] = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
+  const int nstep = G / 8;  // full 256-deep steps
+  const int nchunk = (G + kChunkGroups - 1) / kChunkGroups;
+  const uint32_t neg136[4] = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
+  const uint32_t one28 = opaque_vgpr(kBf16Bias128), nib = opaque_sgpr(kNibbleMask);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   const int nmb_total = (seg1 - seg0) / kSegRows;
   for (int mb0 = 0; mb0 < nmb_total; mb0 += MB) {
     const int nmb = min(MB, nmb_total - mb0);
-    const uint16_t* arow[MB];
-    bool aok[MB];
+    // Tiled activation blocks of this pass. Blocks past the pass's last one re-read
+    // the first (results unused); padding rows inside a block hold zeros.
+    const u32x4* ablk[MB];
 #pragma unroll
     for (int b = 0; b < MB; ++b) {
-      const int r = seg0 + (mb0 + b) * kSegRows + col;
-      int sid = a.P;
-      if (b < nmb) sid = a.sorted_ids[r];
-      aok[b] = sid < a.P;
-      if constexpr (EPI == Epi::GateUp)
-        arow[b] = a.act + (size_t)(aok[b] ? sid / a.k : 0) * K + 8 * quad;
-      else
-        arow[b] = a.act + (size_t)(aok[b] ? r : 0) * K + 8 * quad;
+      const int blk = seg0 / kSegRows + (b < nmb ? mb0 + b : mb0);
+      ablk[b] = reinterpret_cast<const u32x4*>(a.act) + (size_t)blk * G * kWave;
     }
 
-    f32x4 acc[4][MB];
+    // Chunk c of every block: 16 groups x 64 lanes x 16 B, four 16 B pieces per thread
+    // and block. Loads are never predicated (chunks past the end re-read the last);
+    // a predicated load would make the compiler's wait-count insertion wait for every
+    // outstanding load.
+    u32x4 creg[MB][4];
+    auto chunk_load = [&](int c) {
+      c = min(c, nchunk - 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = threadIdx.x + kThreads * i;  // group-in-chunk * 64 + lane
+          const int g = min(c * kChunkGroups + idx / kWave, G - 1);
+          creg[b][i] = ablk[b][(size_t)g * kWave + (idx % kWave)];
+        }
+    };
+    auto chunk_store = [&](int buf) {
+#pragma unroll
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = threadIdx.x + kThreads * i;
+          a_lds[buf][b][idx / kWave][idx % kWave] = creg[b][i];
+        }
+    };
+
+    f32x4 acc[2][MB];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int b = 0; b < MB; ++b) acc[t][b] = zero4;
 
-    auto load = [&](WBuf& buf, int it) {
+    auto load = [&](Stage& st, int it) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 2; ++t) {
         const uint8_t* p = wrow[t] + it * 128 + 16 * quad;
-        buf.w[t][0] = ld16(p);
-        buf.w[t][1] = ld16(p + 64);
-        buf.s[t] = ld16(srow[t] + it * 8);
+        st.w[t][0] = ld16(p);
+        st.w[t][1] = ld16(p + 64);
+        st.s[t] = ld16(srow[t] + it * 8);
       }
+      // Keep the prefetch ahead of the compute that follows it.
+      __builtin_amdgcn_sched_barrier(0);
     };
 
-    auto compute = [&](const WBuf& buf, int it) {
-      uint32_t wt[4][8];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t lo[4] = {buf.w[t][0][0], buf.w[t][0][1], buf.w[t][0][2], buf.w[t][0][3]};
-        uint32_t hi[4] = {buf.w[t][1][0], buf.w[t][1][1], buf.w[t][1][2], buf.w[t][1][3]};
-        transpose4_rows(lo);
-        transpose4_rows(hi);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          wt[t][g] = lo[g];
-          wt[t][4 + g] = hi[g];
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        uint32_t av[MB][4];
-        f32x4 corr[MB];
-#pragma unroll
-        for (int b = 0; b < MB; ++b) {
-          u32x4 xv = {0u, 0u, 0u, 0u};
-          if (aok[b]) xv = ld16(arow[b] + it * 256 + 32 * g);
-          perm_act8(xv, av[b]);
-          corr[b] = mfma_bf16_16x16x32(av[b], neg136, zero4);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          uint32_t bw[4];
-          int4_to_bf16_biased(wt[t][g], bw);
-          const uint32_t sw = buf.s[t][g >> 1];
-          const float sc = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-#pragma unroll
-          for (int b = 0; b < MB; ++b) {
-            if (b < nmb) {
-              f32x4 d = mfma_bf16_16x16x32(av[b], bw, corr[b]);
-              acc[t][b] += sc * d;
-            }
-          }
-        }
-      }
-    };
-
-    if (nfull > 0) {
-      WBuf b0, b1;
-      load(b0, 0);
-      for (int it = 0; it < nfull; it += 2) {
-        if (it + 1 < nfull) load(b1, it + 1);
-        compute(b0, it);
-        if (it + 1 < nfull) {
-          if (it + 2 < nfull) load(b0, it + 2);
-          compute(b1, it + 1);
-        }
-      }
-    }
-    // Remaining groups (K not a multiple of 256): one group at a time, lane quarter q
-    // reads word q of the group directly.
-    for (int g = nfull * 8; g < G; ++g) {
+    // One group: activation operand from LDS, zero-point MFMA, then each tile.
+    auto group = [&](int buf, int gl, uint32_t w0, uint32_t w1, float sc0, float sc1) {
       uint32_t av[MB][4];
       f32x4 corr[MB];
 #pragma unroll
       for (int b = 0; b < MB; ++b) {
-        u32x4 xv = {0u, 0u, 0u, 0u};
-        if (aok[b]) xv = ld16(arow[b] + 32 * g);
-        perm_act8(xv, av[b]);
+        const u32x4 v = a_lds[buf][b][gl][lane];
+        av[b][0] = v[0];
+        av[b][1] = v[1];
+        av[b][2] = v[2];
+        av[b][3] = v[3];
         corr[b] = mfma_bf16_16x16x32(av[b], neg136, zero4);
       }
+      uint32_t bw0[4], bw1[4];
+      int4_to_bf16_biased(w0, nib, one28, bw0);
+      int4_to_bf16_biased(w1, nib, one28, bw1);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t word = *reinterpret_cast<const uint32_t*>(wrow[t] + g * 16 + 4 * quad);
-        uint32_t bw[4];
-        int4_to_bf16_biased(word, bw);
-        const float sc = bf16_to_f32(srow[t][g]);
-#pragma unroll
-        for (int b = 0; b < MB; ++b) {
-          if (b < nmb) {
-            f32x4 d = mfma_bf16_16x16x32(av[b], bw, corr[b]);
-            acc[t][b] += sc * d;
-          }
+      for (int b = 0; b < MB; ++b) {
+        if (b < nmb) {
+          const f32x4 d0 = mfma_bf16_16x16x32(av[b], bw0, corr[b]);
+          const f32x4 d1 = mfma_bf16_16x16x32(av[b], bw1, corr[b]);
+          acc[0][b] += sc0 * d0;
+          acc[1][b] += sc1 * d1;
         }
       }
+    };
+
+    // A full step (eight groups) from the staged weights; gl0 = first group in chunk.
+    auto compute = [&](Stage& st, int buf, int gl0) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t wt[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) wt[t][i] = st.w[t][half][i];
+          transpose4_rows(wt[t]);
+        }
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int g = 4 * half + g4;
+          const uint32_t s0w = st.s[0][g >> 1], s1w = st.s[1][g >> 1];
+          const float sc0 = (g & 1) ? bf16_hi(s0w) : bf16_lo(s0w);
+          const float sc1 = (g & 1) ? bf16_hi(s1w) : bf16_lo(s1w);
+          group(buf, gl0 + g, wt[0][g4], wt[1][g4], sc0, sc1);
+        }
+      }
+    };
+
+    chunk_load(0);
+    chunk_store(0);
+    chunk_load(1);
+    __syncthreads();
+    if (nstep > 0) {
+      // Steps 2c and 2c+1 use chunk c. Weight loads run one step ahead and are never
+      // predicated (a step past the end re-reads the last, served by the cache).
+      const int last = nstep - 1;
+      Stage s0, s1;
+      load(s0, 0);
+      for (int it = 0; it < nstep; it += 2) {
+        const int c = it / 2, buf = c & 1;
+        load(s1, min(it + 1, last));
+        compute(s0, buf, 0);
+        load(s0, min(it + 2, last));
+        if (it + 1 < nstep) compute(s1, buf, 8);
+        // Chunk boundary: chunk c+1 goes to the other buffer (whose readers, chunk
+        // c-1, all passed the previous barrier), then the next chunk is requested.
+        chunk_store(buf ^ 1);
+        chunk_load(c + 2);
+        __syncthreads();
+      }
+    }
+    // Groups past the last full step (K not a multiple of 256): lane quarter q reads word
+    // q of the group directly; the activation comes from the chunk holding the group.
+    for (int g = nstep * 8; g < G; ++g) {
+      const int c = g / kChunkGroups;
+      const uint32_t w0 = *reinterpret_cast<const uint32_t*>(wrow[0] + g * 16 + 4 * quad);
+      const uint32_t w1 = *reinterpret_cast<const uint32_t*>(wrow[1] + g * 16 + 4 * quad);
+      group(c & 1, g % kChunkGroups, w0, w1, bf16_to_f32(srow[0][g]), bf16_to_f32(srow[1][g]));
     }
 
     // Epilogue.
@@ -213,11 +255,11 @@ __global__ void __launch_bounds__(kThreads) w4a16_stream_kernel(StreamArgs a) {
       if (b >= nmb) continue;
       const int rbase = seg0 + (mb0 + b) * kSegRows + 4 * quad;
       if constexpr (EPI == Epi::GateUp) {
+        if (tile_ok[0]) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          uint16_t* hrow = a.h + (size_t)(rbase + r) * a.I + j0 + col;
-          hrow[0] = f32_to_bf16(silu_f32(acc[0][b][r]) * acc[2][b][r]);
-          hrow[16] = f32_to_bf16(silu_f32(acc[1][b][r]) * acc[3][b][r]);
+          for (int r = 0; r < 4; ++r)
+            a.h[tiled_offset(rbase + r, j0 + col, a.I)] =
+                f32_to_bf16(silu_f32(acc[0][b][r]) * acc[1][b][r]);
         }
       } else {
 #pragma unroll
@@ -227,43 +269,74 @@ __global__ void __launch_bounds__(kThreads) w4a16_stream_kernel(StreamArgs a) {
           const float wt = a.topk_weights[sid];
           float* orow = a.out32 + (size_t)(sid / a.k) * a.N + j0 + col;
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
+          for (int t = 0; t < 2; ++t)
             if (tile_ok[t]) unsafeAtomicAdd(orow + 16 * t, wt * acc[t][b][r]);
         }
       }
     }
+    if (mb0 + MB < nmb_total) __syncthreads();  // LDS chunks are reused by the next pass
+  }
+}
+
+// xs = x gathered by sorted row, in the tiled operand layout, for every row below
+// num_tokens_padded; padding rows are zero so the GEMM loads them unmasked.
+// One work-group per row; each thread moves 8 consecutive k values (16 B).
+__global__ void __launch_bounds__(kThreads)
+    gather_rows_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
+                       const int32_t* __restrict__ ntp, int32_t P, int32_t k, int32_t H,
+                       uint16_t* __restrict__ xs) {
+  const int r = blockIdx.x;
+  if (r >= ntp[0]) return;
+  const int sid = sorted_ids[r];
+  const uint16_t* src = x + (size_t)(sid < P ? sid / k : 0) * H;
+  for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (sid < P) {
+      uint32_t p[4];
+      perm_act8(ld16(src + c), p);
+      out = u32x4{p[0], p[1], p[2], p[3]};
+    }
+    // tiled_offset(r, c, H) is the start of a 16 B operand piece (c is a multiple of 8)
+    *reinterpret_cast<u32x4*>(xs + tiled_offset(r, c, H)) = out;
   }
 }
 
 template <Epi EPI>
 hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream) {
-  const int cols_per_group = (EPI == Epi::GateUp) ? 32 * kWavesPerGroup : 64 * kWavesPerGroup;
+  const int cols_per_group = (EPI == Epi::GateUp) ? 16 * kWavesPerGroup : 32 * kWavesPerGroup;
   const int extent = (EPI == Epi::GateUp) ? a.I : a.N;
-  dim3 grid((extent + cols_per_group - 1) / cols_per_group, E);
-  switch (mb) {
-    case 1:
-      hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), grid, dim3(kThreads), 0, stream, a);
-      break;
-    default:
-      hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 2>), grid, dim3(kThreads), 0, stream, a);
-      break;
-  }
+  StreamArgs args = a;
+  args.chunks = (extent + cols_per_group - 1) / cols_per_group;
+  args.items = E * args.chunks;
+  dim3 grid(xcd_major_grid(args.items));
+  if (mb == 1)
+    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), grid, dim3(kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 2>), grid, dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t* ntp, int32_t H,
+                              uint16_t* xs, hipStream_t stream) {
+  if (r.L <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(r.L), dim3(kThreads), 0, stream, x, r.sorted_ids,
+                     ntp, r.P, r.k, H, xs);
+  return hipGetLastError();
+}
+
 hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, int mb,
                                       hipStream_t stream) {
-  StreamArgs a{p.x, p.w13, p.s13, r.sorted_ids, r.offsets, r.topk_weights, p.h, nullptr,
-               r.P, r.k, p.H, 2 * p.I, p.I};
+  StreamArgs a{p.xs, p.w13, p.s13, r.sorted_ids, r.offsets, r.topk_weights, p.h, nullptr,
+               r.P, r.k, p.H, 2 * p.I, p.I, 0, 0};
   return launch_stream<Epi::GateUp>(a, r.E, mb, stream);
 }
 
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
                                     hipStream_t stream) {
   StreamArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.topk_weights, nullptr, p.out32,
-               r.P, r.k, p.I, p.H, p.I};
+               r.P, r.k, p.I, p.H, p.I, 0, 0};
   return launch_stream<Epi::Down>(a, r.E, mb, stream);
 }
 
