@@ -35,10 +35,8 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 enum Format { kW4A16 = 0, kFp8 = 1 };
 
-// Rows per weight pass of the decode kernels, in 16-row blocks (1 or 2): one block
-// covers the usual decode load of a few rows per expert; two keep a pass register-resident
-// (larger passes spill).
-int decode_mb_for(double tok_e) { return tok_e <= 10.0 ? 1 : 2; }
+// Rows per weight pass of the decode kernels, in 16-row blocks.
+int decode_mb_for(double) { return 1; }
 
 struct Plan {
   int fmt = 0;

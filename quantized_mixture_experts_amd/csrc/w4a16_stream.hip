@@ -14,16 +14,21 @@
 //     transpose regroups them so that for every group the four quarters hold its four
 //     words, the k layout of one v_mfma_f32_16x16x32_bf16 (one MFMA = one scale group);
 //   * codes become bf16 (128 + code) with one AND-OR per pair; the zero point is removed
-//     through the MFMA's C operand: C = x . (-136) for the group, from one extra MFMA per
-//     group shared by the wave's column tiles;
+//     through the MFMA's C operand: C = x . (-136) for the group, computed once per
+//     work-group and group (one MFMA on the activation operand) and kept in LDS beside
+//     the operand, so the weight MFMAs of a group do not wait on each other;
 //   * the group scale multiplies the fp32 MFMA result (one FMA per output element);
-//   * weights and scales are prefetched one k step ahead in registers; a small register
-//     footprint (4 waves per SIMD) is what hides HBM latency under load;
-//   * the activation operand (the expert's 16 rows) is shared by the work-group's four
+//   * weights are prefetched three k steps ahead through a ring of four register
+//     stages: under full load HBM latency is a few microseconds, so each wave keeps
+//     ~12 KB in flight; scales (one 128 B line per row covers 8 steps) are loaded once
+//     per 8 steps into the wave's LDS slice, since per-step reads would re-fetch lines
+//     the weight stream has already evicted from L2;
+//   * the activation operand (the expert's 16 rows) is shared by the work-group's eight
 //     waves: 512-deep chunks are copied once into LDS (double-buffered, one barrier per
-//     chunk) and read with ds_read_b128, which keeps the per-CU vector-memory address
-//     path free for the weight stream. Activation rows live in a tiled layout in which
-//     the operand of one (16-row block, k group) is 1 KB contiguous.
+//     chunk) and read with ds_read_b128. Every byte loaded besides the weight stream
+//     costs the stream bandwidth, so the eight waves share one copy. Activation rows live
+//     in a tiled layout in which the operand of one (16-row block, k group) is 1 KB
+//     contiguous.
 // gate_up fuses SiLU(gate) * up and stores h (bf16, tiled by sorted row); down scales by
 // the routing weight and scatter-adds into the fp32 output with hardware atomics.
 #include "device_common.h"
@@ -33,8 +38,9 @@ namespace qmoe {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWavesPerGroup = kThreads / kWave;
+constexpr int kChunkPieces = 1024 / kThreads;  // 16 B chunk pieces per thread and block
 constexpr uint32_t kNeg136Pair = 0xC308C308u;  // bf16 -136, twice
 constexpr int kChunkGroups = 16;               // k groups per LDS activation chunk
 
@@ -55,15 +61,22 @@ struct StreamArgs {
 
 struct Stage {
   u32x4 w[2][2];  // two 16 B chunks of each column tile's row (groups q and 4+q)
-  u32x4 s[2];     // eight bf16 group scales per tile
 };
+
+constexpr int kScaleBlockSteps = 8;  // one 128 B line of bf16 scales = 64 groups = 8 steps
+constexpr int kStages = 4;           // weight register stages (loads run kStages-1 ahead)
 
 template <Epi EPI, int MB>
 __global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(MB == 1 ? 3 : 2)))
+    __attribute__((amdgpu_waves_per_eu(2)))
     w4a16_stream_kernel(StreamArgs a) {
-  // Activation chunks: [buffer][M-block][group in chunk][lane], 16 B each.
+  // Activation chunks: [buffer][M-block][group in chunk][lane], 16 B each, and the
+  // zero-point term of each group in the MFMA result layout (4 fp32 per lane).
   __shared__ u32x4 a_lds[2][MB][kChunkGroups][kWave];
+  __shared__ f32x4 c_lds[2][MB][kChunkGroups][kWave];
+  // Group scales of each wave's tiles for one 8-step block: [wave][tile][row][piece],
+  // piece p = the 8 scales of step p.
+  __shared__ u32x4 s_lds[kWavesPerGroup][2][16][kScaleBlockSteps];
 
   // Work-groups are dealt to the 8 XCDs round-robin by launch index; give each XCD a
   // contiguous range of (expert, column chunk) items in expert-major order so that an
@@ -128,25 +141,31 @@ __global__ void __launch_bounds__(kThreads)
     // and block. Loads are never predicated (chunks past the end re-read the last);
     // a predicated load would make the compiler's wait-count insertion wait for every
     // outstanding load.
-    u32x4 creg[MB][4];
+    u32x4 creg[MB][kChunkPieces];
     auto chunk_load = [&](int c) {
       c = min(c, nchunk - 1);
 #pragma unroll
       for (int b = 0; b < MB; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < kChunkPieces; ++i) {
           const int idx = threadIdx.x + kThreads * i;  // group-in-chunk * 64 + lane
           const int g = min(c * kChunkGroups + idx / kWave, G - 1);
           creg[b][i] = ablk[b][(size_t)g * kWave + (idx % kWave)];
         }
     };
+    // Piece i of this thread is the MFMA activation operand of group wave + 8i for this
+    // lane, so each wave also derives the zero-point term x . (-136) of those groups (one
+    // MFMA each) and parks it next to the operands: the weight MFMAs then take it as
+    // their accumulator input without waiting on another MFMA.
     auto chunk_store = [&](int buf) {
 #pragma unroll
       for (int b = 0; b < MB; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int idx = threadIdx.x + kThreads * i;
-          a_lds[buf][b][idx / kWave][idx % kWave] = creg[b][i];
+        for (int i = 0; i < kChunkPieces; ++i) {
+          const int g = wave + kWavesPerGroup * i;
+          a_lds[buf][b][g][lane] = creg[b][i];
+          const uint32_t av[4] = {creg[b][i][0], creg[b][i][1], creg[b][i][2], creg[b][i][3]};
+          c_lds[buf][b][g][lane] = mfma_bf16_16x16x32(av, neg136, zero4);
         }
     };
 
@@ -162,13 +181,35 @@ __global__ void __launch_bounds__(kThreads)
         const uint8_t* p = wrow[t] + it * 128 + 16 * quad;
         st.w[t][0] = ld16(p);
         st.w[t][1] = ld16(p + 64);
-        st.s[t] = ld16(srow[t] + it * 8);
       }
       // Keep the prefetch ahead of the compute that follows it.
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // One group: activation operand from LDS, zero-point MFMA, then each tile.
+    // Scales: one 128 B line per weight row covers 8 steps. Reading them per step from
+    // global memory re-fetches the line up to eight times (the weight stream evicts it
+    // from L2 between steps), so each block of 8 steps is loaded once (lane quarter q
+    // takes pieces 2q and 2q+1 of its row), parked in this wave's LDS slice, and read
+    // back per step. Pieces past the end of a row are clamped into it (never used).
+    u32x4 sreg[2][2];
+    const int row_bytes = G * 2;
+    auto scale_load = [&](int blk) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int off = min(blk * 128 + 16 * (2 * quad + i), row_bytes - 16);
+          sreg[t][i] = ld16(reinterpret_cast<const uint8_t*>(srow[t]) + max(off, 0));
+        }
+    };
+    auto scale_store = [&]() {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) s_lds[wave][t][col][2 * quad + i] = sreg[t][i];
+    };
+
+    // One group: activation operand and zero-point term from LDS, then each tile.
     auto group = [&](int buf, int gl, uint32_t w0, uint32_t w1, float sc0, float sc1) {
       uint32_t av[MB][4];
       f32x4 corr[MB];
@@ -179,7 +220,7 @@ __global__ void __launch_bounds__(kThreads)
         av[b][1] = v[1];
         av[b][2] = v[2];
         av[b][3] = v[3];
-        corr[b] = mfma_bf16_16x16x32(av[b], neg136, zero4);
+        corr[b] = c_lds[buf][b][gl][lane];
       }
       uint32_t bw0[4], bw1[4];
       int4_to_bf16_biased(w0, nib, one28, bw0);
@@ -195,8 +236,10 @@ __global__ void __launch_bounds__(kThreads)
       }
     };
 
-    // A full step (eight groups) from the staged weights; gl0 = first group in chunk.
-    auto compute = [&](Stage& st, int buf, int gl0) {
+    // A full step (eight groups) from the staged weights; gl0 = first group in chunk,
+    // sp = the step's scale piece within the current scale block.
+    auto compute = [&](Stage& st, int buf, int gl0, int sp) {
+      const u32x4 sv[2] = {s_lds[wave][0][col][sp], s_lds[wave][1][col][sp]};
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         uint32_t wt[2][4];
@@ -209,7 +252,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int g = 4 * half + g4;
-          const uint32_t s0w = st.s[0][g >> 1], s1w = st.s[1][g >> 1];
+          const uint32_t s0w = sv[0][g >> 1], s1w = sv[1][g >> 1];
           const float sc0 = (g & 1) ? bf16_hi(s0w) : bf16_lo(s0w);
           const float sc1 = (g & 1) ? bf16_hi(s1w) : bf16_lo(s1w);
           group(buf, gl0 + g, wt[0][g4], wt[1][g4], sc0, sc1);
@@ -222,22 +265,35 @@ __global__ void __launch_bounds__(kThreads)
     chunk_load(1);
     __syncthreads();
     if (nstep > 0) {
-      // Steps 2c and 2c+1 use chunk c. Weight loads run one step ahead and are never
-      // predicated (a step past the end re-reads the last, served by the cache).
+      // Steps 2c and 2c+1 use chunk c; steps 8b..8b+7 use scale block b. Loads are
+      // never predicated (a step or block past the end re-reads the last one, which the
+      // cache serves): a predicated load would make the compiler's wait-count insertion
+      // wait for every outstanding load. Scales run one block ahead.
       const int last = nstep - 1;
-      Stage s0, s1;
-      load(s0, 0);
-      for (int it = 0; it < nstep; it += 2) {
-        const int c = it / 2, buf = c & 1;
-        load(s1, min(it + 1, last));
-        compute(s0, buf, 0);
-        load(s0, min(it + 2, last));
-        if (it + 1 < nstep) compute(s1, buf, 8);
-        // Chunk boundary: chunk c+1 goes to the other buffer (whose readers, chunk
-        // c-1, all passed the previous barrier), then the next chunk is requested.
-        chunk_store(buf ^ 1);
-        chunk_load(c + 2);
-        __syncthreads();
+      const int nblk = (nstep + kScaleBlockSteps - 1) / kScaleBlockSteps;
+      const int nscale_blk = (G + 63) / 64;
+      // Four register stages in a ring, weights loaded three steps ahead.
+      Stage st[kStages];
+      scale_load(0);
+#pragma unroll
+      for (int i = 0; i < kStages - 1; ++i) load(st[i], min(i, last));
+      for (int blk = 0; blk < nblk; ++blk) {
+        scale_store();
+        scale_load(min(blk + 1, nscale_blk - 1));
+#pragma unroll
+        for (int j = 0; j < kScaleBlockSteps; ++j) {
+          const int it = blk * kScaleBlockSteps + j;
+          const int c = it / 2, buf = c & 1;
+          load(st[(j + kStages - 1) % kStages], min(it + kStages - 1, last));
+          if (it < nstep) compute(st[j % kStages], buf, 8 * (j & 1), j);
+          if (j & 1) {
+            // Chunk boundary: chunk c+1 goes to the other buffer (whose readers, chunk
+            // c-1, all passed the previous barrier), then the next chunk is requested.
+            chunk_store(buf ^ 1);
+            chunk_load(c + 2);
+            __syncthreads();
+          }
+        }
       }
     }
     // Groups past the last full step (K not a multiple of 256): lane quarter q reads word
@@ -309,10 +365,8 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
   args.chunks = (extent + cols_per_group - 1) / cols_per_group;
   args.items = E * args.chunks;
   dim3 grid(xcd_major_grid(args.items));
-  if (mb == 1)
-    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), grid, dim3(kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 2>), grid, dim3(kThreads), 0, stream, args);
+  (void)mb;  // one 16-row block per weight pass (larger passes do not fit the registers)
+  hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), grid, dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 
