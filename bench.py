@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="token rows of the CPU-oracle sample (0 = workload default)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the MoE step, run a plain device-to-device copy of MIB "
+                         "MiB (the known-size reference for HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -83,6 +86,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
+        return
 
     from quantized_mixture_experts_amd import binding, inputs
 
