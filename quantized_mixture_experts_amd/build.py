@@ -11,7 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqmoe.so")
-SOURCES = ["api.hip", "align.hip", "elementwise.hip", "w4a16_stream.hip", "fp8_stream.hip"]
+SOURCES = ["api.hip", "align.hip", "elementwise.hip", "w4a16_stream.hip", "w4a16_tiled.hip",
+           "fp8_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -1,6 +1,7 @@
 // C ABI of the MoE expert FFN library: argument checks, schedule choice, workspace
 // layout and the launch sequence. Everything here is host code; no call reads a
 // device value back, allocates, frees or synchronizes.
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -42,10 +43,11 @@ struct Plan {
   int fmt = 0;
   int schedule = QMOE_SCHEDULE_DECODE;
   int mb = 1;
+  bool tiled = false;  // W4A16 prefill on the 256-row tile kernels
   int32_t block_m = kSegRows;
   int64_t P = 0, L = 0, NB = 0;
   size_t off_sorted = 0, off_expert_ids = 0, off_ntp = 0, off_offsets = 0, off_tiles = 0;
-  size_t off_xs = 0, off_h = 0, off_h32 = 0, off_hq = 0, off_hs = 0, off_out32 = 0;
+  size_t off_xs = 0, off_h = 0, off_h32 = 0, off_hq = 0, off_hs = 0, off_out32 = 0, off_y = 0;
   size_t total = 0;
 };
 
@@ -72,6 +74,7 @@ qmoe_status check_shape(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int
 
 Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t schedule) {
   Plan p;
+  (void)k;
   p.fmt = fmt;
   p.P = (int64_t)T * k;
   const double tok_e = E > 0 ? (double)p.P / E : 0.0;
@@ -79,9 +82,13 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= 40.0 ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
   p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 2;
+  p.tiled = fmt == kW4A16 && p.schedule == QMOE_SCHEDULE_PREFILL && w4a16_tiled_supported(H, I);
   p.block_m = kSegRows;
   p.L = p.P + (int64_t)E * (p.block_m - 1);
   p.NB = (p.L + p.block_m - 1) / p.block_m;
+  // The tile kernels address activation rows with 32-bit byte offsets.
+  if (p.tiled && (uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32))
+    p.tiled = false;
   size_t cur = 0;
   auto take = [&](size_t bytes) {
     size_t at = cur;
@@ -101,7 +108,10 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     p.off_hq = take((size_t)p.L * I);
     p.off_hs = take(sizeof(float) * (size_t)p.L * (I / 128));
   }
-  p.off_out32 = take(sizeof(float) * (size_t)T * H);
+  if (p.tiled)
+    p.off_y = take(sizeof(float) * (size_t)p.P * H);
+  else
+    p.off_out32 = take(sizeof(float) * (size_t)T * H);
   p.total = cur;
   return p;
 }
@@ -252,6 +262,33 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
   W4A16Problem prob{x, region<uint16_t>(workspace, p.off_xs), w13, s13, w2, s2,
                     region<uint16_t>(workspace, p.off_h), region<float>(workspace, p.off_out32),
                     T, H, I};
+
+  if (p.tiled) {
+    const int32_t tm = w4a16_tiled_rows();
+    hipError_t err = staged(QMOE_STAGE_ALIGN, s, [&] {
+      return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
+                          region<int32_t>(workspace, p.off_sorted),
+                          region<int32_t>(workspace, p.off_expert_ids),
+                          region<int32_t>(workspace, p.off_ntp),
+                          region<int32_t>(workspace, p.off_offsets), tm,
+                          region<int32_t>(workspace, p.off_tiles), s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "align launch");
+    err = staged(QMOE_STAGE_ALIGN, s, [&] {
+      return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "gather launch");
+    err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_tiled(prob, r, s); });
+    if (err != hipSuccess) return hip_fail(err, "gate_up launch");
+    float* y = region<float>(workspace, p.off_y);
+    err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_tiled(prob, r, y, s); });
+    if (err != hipSuccess) return hip_fail(err, "down launch");
+    err = staged(QMOE_STAGE_CAST, s, [&] {
+      return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return QMOE_OK;
+  }
 
   hipError_t err = staged(QMOE_STAGE_ZERO, s, [&] {
     return launch_zero_f32(prob.out32, (int64_t)T * H, s);
