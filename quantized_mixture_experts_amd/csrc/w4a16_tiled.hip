@@ -3,9 +3,10 @@
 // Method: BF16 activations times INT4 group-32 weights with BF16 scales, fp32
 // accumulation ("vLLM x Novita AI: Chord W4A16 INT4 MoE Kernel for Kimi K2.x": summary;
 // "vLLM integration"). With hundreds of routed rows per expert the product is a grouped
-// GEMM over the expert segments of the sorted row list ("SGLang fused_moe_triton":
-// moe_align_block_size and the fused kernel's expert blocks), so the cost is the
-// contraction and the kernel is laid out for the matrix cores.
+// GEMM over the expert segments of the sorted row list (same page, "Two kernel
+// families": the indexed path consumes sorted ids, expert ids and the padded count), and
+// prefill is bound by the matrix units (same page, "Kernel optimizations"), so the
+// kernel is laid out for the matrix cores.
 //
 // gfx950 mapping. A work-group owns one (256-row tile of an expert segment, 256 weight
 // rows) output tile; its four waves each own all 256 rows and 64 weight rows (four
@@ -29,6 +30,7 @@
 // weighted rows per (token, slot) pair in fp32 and a combine kernel sums the top-k rows
 // of every token, so the prefill output does not depend on atomic ordering.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -42,10 +44,13 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kRowBlocks = kTileRows / 16;        // 16-row MFMA tiles per wave
 constexpr int kColTiles = 4;                      // 16-column MFMA tiles per wave
-constexpr int kStages = 4;                        // LDS ring of activation k groups
-constexpr int kAhead = kStages - 1;               // groups copied ahead of use
+constexpr int kStages = 7;                        // LDS ring of activation k groups
 constexpr int kCopiesPerWave = kRowBlocks / kWaves;  // 1 KB copies per wave and group
 constexpr int kGroupsPerBlock = 8;                // k groups per 256-deep weight block
+// LDS layout in 16 B units (see the kernel).
+constexpr int kWBase = kStages * kRowBlocks * kWave;
+constexpr int kSBase = kWBase + kWaves * 2 * kColTiles * kWave;
+constexpr int kSmemUnits = kSBase + kWaves * kColTiles * 16;
 
 enum class TEpi { GateUp, Down };
 
@@ -86,20 +91,13 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Four MFMAs of one row block (A operand `a`) against the wave's four column tiles,
-// accumulating in place. Written as assembly so that the 256 accumulator values stay
-// pinned in AGPRs (the register allocator otherwise shuffles them through VGPRs);
-// `s_nop 1` gives the two wait states a VALU write of an operand register needs before
-// an MFMA reads it.
-__device__ __forceinline__ void mfma4_acc(f32x4 (&acc)[4], const u32x4& a, const u32x4 (&b)[4]) {
-  asm volatile(
-      "s_nop 1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %0, %4, %5, %0\n\t"
-      "v_mfma_f32_16x16x32_bf16 %1, %4, %6, %1\n\t"
-      "v_mfma_f32_16x16x32_bf16 %2, %4, %7, %2\n\t"
-      "v_mfma_f32_16x16x32_bf16 %3, %4, %8, %3"
-      : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3])
-      : "v"(a), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]));
+// One MFMA accumulating in place. Written as assembly so that the 256 accumulator values
+// stay pinned in AGPRs (the register allocator otherwise shuffles them through VGPRs).
+// The compiler does not see the operand reads, so the code around it keeps VALU writes
+// of MFMA operands at least two instructions away: operands come from LDS reads or
+// from VALU work of the previous step, and each step opens with `s_nop 1`.
+__device__ __forceinline__ void mfma_acc(f32x4& acc, const u32x4& a, const u32x4& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Orders every later read of the accumulators after at least 24 wait states following
@@ -114,7 +112,18 @@ __device__ __forceinline__ void drain_acc(f32x4 (&acc)[kRowBlocks][kColTiles]) {
 
 template <TEpi EPI>
 __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
-  __shared__ u32x4 a_lds[kStages][kRowBlocks][kWave];  // 64 KB
+  // One LDS array (148 KB), in 16 B units:
+  //   activation ring [stage][row block][lane], 16 KB per k group;
+  //   per wave, the two half blocks of weight words [half][tile][lane];
+  //   per wave, the block's scales [tile][row] (16 B = eight groups per weight row).
+  // A single object also keeps the compiler from adding conservative waits between the
+  // asynchronous copies and the reads of other staging areas.
+  __shared__ u32x4 smem[kSmemUnits];
+  auto a_at = [&](int st, int rb) { return &smem[(st * kRowBlocks + rb) * kWave]; };
+  auto w_at = [&](int wv, int hf, int t) {
+    return &smem[kWBase + ((wv * 2 + hf) * kColTiles + t) * kWave];
+  };
+  auto s_at = [&](int wv, int t) { return &smem[kSBase + (wv * kColTiles + t) * 16]; };
 
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
@@ -135,25 +144,25 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   const int K = a.K, KG = K >> 5;
   const int nsteps = KG, nblocks = K >> 8;
 
-  // Weight rows of this wave's four column tiles; per-lane byte offsets stay 32-bit
-  // (host-checked) on top of the expert's uniform base.
-  int wrow[kColTiles];
-#pragma unroll
-  for (int t = 0; t < kColTiles; ++t) {
+  // Weight row of tile t for column c of this wave.
+  auto weight_row = [&](int t, int c) {
     if constexpr (EPI == TEpi::GateUp) {
-      const int j = ctile * 128 + wave * 32 + (t & 1) * 16 + col;
-      wrow[t] = (t < 2) ? j : a.I + j;
+      const int j = ctile * 128 + wave * 32 + (t & 1) * 16 + c;
+      return (t < 2) ? j : a.I + j;
     } else {
-      wrow[t] = ctile * 256 + wave * 64 + t * 16 + col;
+      return ctile * 256 + wave * 64 + t * 16 + c;
     }
-  }
+  };
+  // Per-lane byte offsets stay 32-bit (host-checked) on top of uniform bases. Weight
+  // words: lane (col, quad) takes 16 B of row col at quarter `quad` of a 64 B half line.
+  // Scales: lane l takes word l % 4 of the 16 B (eight groups) of row l / 4.
   const uint8_t* wbase = a.w + (size_t)e * a.N * (size_t)(K >> 1);
   const uint8_t* sbase = reinterpret_cast<const uint8_t*>(a.s + (size_t)e * a.N * (size_t)KG);
   uint32_t woff[kColTiles], soff[kColTiles];
 #pragma unroll
   for (int t = 0; t < kColTiles; ++t) {
-    woff[t] = (uint32_t)wrow[t] * (uint32_t)(K >> 1) + 16u * quad;
-    soff[t] = (uint32_t)wrow[t] * (uint32_t)(KG * 2);
+    woff[t] = (uint32_t)weight_row(t, col) * (uint32_t)(K >> 1) + 16u * quad;
+    soff[t] = (uint32_t)weight_row(t, lane >> 2) * (uint32_t)(KG * 2) + 4u * (lane & 3);
   }
 
   // Activation copies of this wave: row blocks wave*4 .. wave*4+3 of the tile.
@@ -164,31 +173,36 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
     const int rb = min(rb0 + wave * kCopiesPerWave + i, rb_last);
     aoff[i] = (uint32_t)rb * (uint32_t)(KG * 1024) + lane * 16u;
   }
-  // Copies group min(g, last) into stage g % kStages. Past the end the copy repeats the
-  // last group into a free stage, so that every k step issues the same number of vector
-  // memory instructions and the vmcnt thresholds below hold at the tail too.
-  auto copy_group = [&](int g) {
-    const int st = g & (kStages - 1);
+
+  // All global reads of the loop are asynchronous LDS copies whose completion this code
+  // tracks itself with vmcnt (the compiler does not count them). They are issued in a
+  // fixed order and never skipped: past the end they repeat the last group or block, so
+  // the counts below hold at the tail as well. Per 8-group block and wave: four
+  // activation copies every step, the next block's first half of weight words and its
+  // scales at j = 1 (8), its second half at j = 5 (4).
+  auto copy_group = [&](int g, int st) {
     const uint32_t src = (uint32_t)min(g, nsteps - 1) * 1024u;
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i)
       __builtin_amdgcn_global_load_lds(
           (const void*)(abase + (aoff[i] + src)),
-          (__attribute__((address_space(3))) void*)&a_lds[st][wave * kCopiesPerWave + i][0], 16,
-          0, 0);
+          (__attribute__((address_space(3))) void*)a_at(st, wave * kCopiesPerWave + i), 16, 0, 0);
   };
-  // Weight words of half `hf` (groups 4*hf .. 4*hf+3) of block min(kb, last): 16 B per
-  // tile; the scales of a block are one 16 B load per tile. Clamped, never skipped, for
-  // the same reason as copy_group.
-  auto load_half = [&](int kb, int hf, u32x4 (&dst)[kColTiles]) {
+  auto copy_half = [&](int kb, int hf) {
     const uint32_t o = (uint32_t)min(kb, nblocks - 1) * 128u + 64u * hf;
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t) dst[t] = ld16(wbase + (woff[t] + o));
+    for (int t = 0; t < kColTiles; ++t)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(wbase + (woff[t] + o)),
+          (__attribute__((address_space(3))) void*)w_at(wave, hf, t), 16, 0, 0);
   };
-  auto load_scales = [&](int kb, u32x4 (&dst)[kColTiles]) {
+  auto copy_scales = [&](int kb) {
     const uint32_t o = (uint32_t)min(kb, nblocks - 1) * 16u;
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t) dst[t] = ld16(sbase + (soff[t] + o));
+    for (int t = 0; t < kColTiles; ++t)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(sbase + (soff[t] + o)),
+          (__attribute__((address_space(3))) void*)s_at(wave, t), 4, 0, 0);
   };
 
   f32x4 acc[kRowBlocks][kColTiles];
@@ -200,95 +214,208 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   const uint32_t mask = opaque_sgpr(0x000F000Fu);
   const uint32_t magic = opaque_vgpr(0x64006400u);
 
-  // Weight words of the next half block (`pend`) are loaded four groups ahead of their
-  // first use; `spend` holds the next block's scales. Step g runs the MFMAs of group g
-  // on operands dequantized during step g-1 (buffer g % 2) and dequantizes group g+1
-  // into the other buffer, one (tile, pair) piece after each row block's MFMAs, so the
-  // VALU work overlaps the matrix core.
-  u32x4 pend[kColTiles], spend[kColTiles], scur[kColTiles];
+  // tw: the current half block's words, transposed so that word g of lane quarter q is
+  // slice q of group g. scur: the current block's scales. Step g runs the MFMAs of group
+  // g on operands dequantized during step g-1 (buffer g % 2) and dequantizes group g+1
+  // into the other buffer, spread between the MFMAs so the VALU work overlaps them.
+  // wnext / snext: staged words or scales read from LDS one step before they are used.
   uint32_t tw[kColTiles][4];
+  u32x4 scur[kColTiles];
   u32x4 bq[2][kColTiles];
-  auto transpose_pend = [&]() {
+  u32x4 wnext[kColTiles], snext[kColTiles];
+  auto read_staged_half = [&](int hf) {
+#pragma unroll
+    for (int t = 0; t < kColTiles; ++t) wnext[t] = w_at(wave, hf, t)[lane];
+  };
+  auto read_staged_scales = [&]() {
+#pragma unroll
+    for (int t = 0; t < kColTiles; ++t) snext[t] = s_at(wave, t)[col];
+  };
+  auto take_half = [&]() {
 #pragma unroll
     for (int t = 0; t < kColTiles; ++t) {
-      tw[t][0] = pend[t].x;
-      tw[t][1] = pend[t].y;
-      tw[t][2] = pend[t].z;
-      tw[t][3] = pend[t].w;
+      tw[t][0] = wnext[t].x;
+      tw[t][1] = wnext[t].y;
+      tw[t][2] = wnext[t].z;
+      tw[t][3] = wnext[t].w;
       transpose4_rows(tw[t]);
     }
   };
-  // Piece p (0..15) of group j's operands: tile p / 4, bf16 pair p % 4.
-  auto dequant_piece = [&](int j, int p, u32x4 (&dst)[kColTiles]) {
-    const int t = p >> 2, i = p & 3;
-    const uint32_t sw = scur[t][j >> 1];
-    const float sc = (j & 1) ? bf16_hi(sw) : bf16_lo(sw);
-    const uint32_t pr = ((tw[t][j & 3] >> (4 * i)) & mask) | magic;
-    const f16x2 hv = __builtin_bit_cast(f16x2, pr);
-    const float c = -1032.0f * sc;
-    const f32x2 f = {__builtin_fmaf((float)hv.x, sc, c), __builtin_fmaf((float)hv.y, sc, c)};
-    dst[t][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  auto wait_lds_reads = [] {
+    // lgkmcnt(0), other counters left alone
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
   };
+  auto next_stage = [](int s_) { return s_ == kStages - 1 ? 0 : s_ + 1; };
 
-  // Prologue: block 0's first half and scales, the first kAhead activation groups, then
-  // (as at the end of a block) the operands of group 0 and the load of the second half.
-  load_half(0, 0, pend);
-  load_scales(0, spend);
+  // Issue schedule (per wave). Step g issues, right after its barrier, the copy of
+  // activation group g + kStages into the stage group g has just released; at block
+  // position j = 1 the next block's first half of weight words and its scales (8), at
+  // j = 5 its second half (4). The staged words are read into registers one step
+  // before use (j = 2: second half of this block; j = 6: first half and scales of the
+  // next block). The prologue issues the same sequence for the steps before group 0.
+  copy_group(0, 0);  // step -7 (j = 1)
+  copy_half(0, 0);
+  copy_scales(0);
+  copy_group(1, 1);  // step -6
+  copy_group(2, 2);  // step -5
+  copy_group(3, 3);  // step -4
+  copy_group(4, 4);  // step -3 (j = 5)
+  copy_half(0, 1);
+  copy_group(5, 5);  // step -2 (j = 6): younger than the scales are copies 1..5 and a half
+  wait_vmcnt<5 * kCopiesPerWave + kColTiles>();
+  read_staged_half(0);
+  read_staged_scales();
+  // step -1 (j = 7): group 0's copies; younger are 8 weight copies and copies 1..5 and
+  // the second half
+  wait_vmcnt<2 * kColTiles + 5 * kCopiesPerWave + kColTiles>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  copy_group(6, 6);
+  __builtin_amdgcn_sched_barrier(0);
+  // Activation operands are read from LDS in groups of four row blocks, a whole group
+  // ahead, into two register sets: the compiler waits for all outstanding LDS reads
+  // (lgkmcnt(0)) before the first use of each group, and by then they have landed.
+  u32x4 ra[2][4];
+  {
+    const u32x4* as0 = a_at(0, 0) + lane;
 #pragma unroll
-  for (int g = 0; g < kAhead; ++g) copy_group(g);
-  transpose_pend();
+    for (int r = 0; r < 4; ++r) ra[0][r] = as0[r * kWave];
+  }
+  take_half();
 #pragma unroll
-  for (int t = 0; t < kColTiles; ++t) scur[t] = spend[t];
+  for (int t = 0; t < kColTiles; ++t) scur[t] = snext[t];
 #pragma unroll
-  for (int p = 0; p < 16; ++p) dequant_piece(0, p, bq[0]);
-  load_half(0, 1, pend);
+  for (int p = 0; p < 16; ++p) {
+    const int t = p >> 2, i = p & 3;
+    const float sc = bf16_lo(scur[t][0]);
+    const uint32_t pr = ((tw[t][0] >> (4 * i)) & mask) | magic;
+    const f16x2 hv = __builtin_bit_cast(f16x2, pr);
+    const f32x2 f = {__builtin_fmaf((float)hv.x, sc, -1032.0f * sc),
+                     __builtin_fmaf((float)hv.y, sc, -1032.0f * sc)};
+    bq[0][t][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  }
 
+  int st = 0;  // stage of group g
   for (int kb = 0; kb < nblocks; ++kb) {
-#pragma unroll
-    for (int j = 0; j < kGroupsPerBlock; ++j) {
+    auto step = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
       const int g = kb * kGroupsPerBlock + j;
-      // This wave's copies of group g are complete once no more than what it issued
-      // after them is pending: the copies of groups g+1 and g+2 plus the weight loads
-      // of the three previous steps (8 issued at j = 3, 4 at j = 7). Vector memory
-      // loads complete in issue order.
-      if (j == 3 || j == 7) wait_vmcnt<2 * kCopiesPerWave>();
-      else if (j < 3) wait_vmcnt<2 * kCopiesPerWave + kColTiles>();
-      else wait_vmcnt<2 * kCopiesPerWave + 2 * kColTiles>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      copy_group(g + kAhead);
-      // The vmcnt thresholds assume the weight loads below issue after this step's
-      // copies; keep the scheduler from swapping them.
-      __builtin_amdgcn_sched_barrier(0);
-      // The next half's words are transposed at j = 3 and 7 (the current half is no
-      // longer needed: group j's operands already exist), then the following half is
-      // requested.
-      if (j == 3 || j == 7) {
-        transpose_pend();
-        if (j == 7) {
-#pragma unroll
-          for (int t = 0; t < kColTiles; ++t) scur[t] = spend[t];
-          load_half(kb + 1, 1, pend);
-        } else {
-          load_half(kb + 1, 0, pend);
-          load_scales(kb + 1, spend);
-        }
-      }
-      const int st = g & (kStages - 1);
       const int jn = (j + 1) & 7;
-      u32x4 a0 = a_lds[st][0][lane];
-      u32x4 a1 = a_lds[st][1][lane];
+      // Operand registers written by VALU instructions at the end of the last step.
+      asm volatile("s_nop 1");
+      if (j == 3) {
+        take_half();
+      } else if (j == 7) {
+        take_half();
+#pragma unroll
+        for (int t = 0; t < kColTiles; ++t) scur[t] = snext[t];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4* as = a_at(st, 0) + lane;
+      const int stn = next_stage(st);
+      const u32x4* asn = a_at(stn, 0) + lane;
+      const u32x4 (&bc)[kColTiles] = bq[j & 1];
+      u32x4 (&bn)[kColTiles] = bq[(j + 1) & 1];
+      float sc = 0.f, cc = 0.f;
+      uint32_t pr = 0;
+      float flo = 0.f, fhi = 0.f;
+      // Row block m: its four MFMAs, each followed by about a quarter of piece m of the
+      // next group's operands (fenced, so the VALU work issues while the matrix pipe is
+      // busy); the next four row blocks' operands are requested after each group's
+      // first MFMA.
 #pragma unroll
       for (int m = 0; m < kRowBlocks; ++m) {
-        u32x4 a2 = a1;
-        if (m + 2 < kRowBlocks) a2 = a_lds[st][m + 2][lane];
-        mfma4_acc(acc[m], a0, bq[j & 1]);
-        dequant_piece(jn, m, bq[(j + 1) & 1]);
-        a0 = a1;
-        a1 = a2;
+        const int t = m >> 2, i = m & 3;
+        const int q = m >> 2, r = m & 3;
+        const u32x4& a0 = ra[q & 1][r];
+        mfma_acc(acc[m][0], a0, bc[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        // After the group's first MFMA, so that the wait before it does not cover them.
+        if (r == 0 && q < 3) {
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) ra[(q + 1) & 1][rr] = as[(4 * (q + 1) + rr) * kWave];
+        }
+        if (i == 0) {
+          const uint32_t sw = scur[t][jn >> 1];
+          sc = (jn & 1) ? bf16_hi(sw) : bf16_lo(sw);
+          cc = -1032.0f * sc;
+        }
+        pr = ((tw[t][jn & 3] >> (4 * i)) & mask) | magic;
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_acc(acc[m][1], a0, bc[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          const f16x2 hv = __builtin_bit_cast(f16x2, pr);
+          flo = __builtin_fmaf((float)hv.x, sc, cc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_acc(acc[m][2], a0, bc[2]);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          const f16x2 hv = __builtin_bit_cast(f16x2, pr);
+          fhi = __builtin_fmaf((float)hv.y, sc, cc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_acc(acc[m][3], a0, bc[3]);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          const f32x2 f = {flo, fhi};
+          bn[t][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (m == kRowBlocks - 4) {
+          // Every read of this stage has been issued. Once they have completed and
+          // group g+1's copies have landed (vmcnt: at most the younger copies of groups
+          // g+2 .. g+6 and the weight copies of the last six steps, positions j+2 .. j+7
+          // of the block, are pending; loads complete in issue order), the barrier lets
+          // group g + kStages reuse this stage, and the next step's first reads go out
+          // while the last row blocks' MFMAs run (register set 0 is free again).
+          wait_lds_reads();
+          constexpr int kLater = (kStages - 2) * kCopiesPerWave;
+          constexpr int w1 = 2 * kColTiles, w5 = kColTiles;
+          constexpr int kPrev = w1 + w5 - ((j == 1 || j == 0) ? w1 : 0) -
+                                ((j == 5 || j == 4) ? w5 : 0);
+          wait_vmcnt<kLater + kPrev>();
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          copy_group(g + kStages, st);
+          if (j == 1) {
+            copy_half(kb + 1, 0);
+            copy_scales(kb + 1);
+          } else if (j == 5) {
+            copy_half(kb + 1, 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (j == 2) {
+            // Second half of this block (copied at j = 5 of the last block): younger
+            // are five steps of activation copies and the next first half and scales.
+            wait_vmcnt<5 * kCopiesPerWave + 2 * kColTiles>();
+            read_staged_half(1);
+          } else if (j == 6) {
+            // Next block's first half and scales (copied at j = 1): younger are five
+            // steps of activation copies and the next second half.
+            wait_vmcnt<5 * kCopiesPerWave + kColTiles>();
+            read_staged_half(0);
+            read_staged_scales();
+          }
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) ra[0][rr] = asn[rr * kWave];
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
+      st = stn;
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 5>{});
+    step(std::integral_constant<int, 6>{});
+    step(std::integral_constant<int, 7>{});
   }
+  // No copy may still be landing in LDS when the work-group's LDS is released.
+  wait_vmcnt<0>();
   // The matrix-core results must be settled before ordinary instructions read them.
   drain_acc(acc);
 
@@ -322,7 +449,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
         const float wt = a.topk_weights[pair];
         float* yrow = a.y + (size_t)pair * a.N;
 #pragma unroll
-        for (int t = 0; t < kColTiles; ++t) yrow[wrow[t]] = wt * acc[m][t][r];
+        for (int t = 0; t < kColTiles; ++t) yrow[weight_row(t, col)] = wt * acc[m][t][r];
       }
     }
   }
