@@ -334,26 +334,44 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-// xs = x gathered by sorted row, in the tiled operand layout, for every row below
-// num_tokens_padded; padding rows are zero so the GEMM loads them unmasked.
-// One work-group per row; each thread moves 8 consecutive k values (16 B).
-__global__ void __launch_bounds__(kThreads)
+// xs = x gathered by sorted row in the tiled operand layout, for rows below
+// num_tokens_padded; padding rows are zero so the GEMMs load them unmasked.
+// One work-group per 16-row block; each wave writes whole 1 KB operands (one k group of
+// the block): lane (q, m) reads 16 B of row m at k slice q and stores them, permuted to
+// the operand k order, at its place in the operand, so every store is a full line.
+constexpr int kGatherThreads = 256;
+constexpr int kGatherWaves = kGatherThreads / kWave;
+
+__global__ void __launch_bounds__(kGatherThreads)
     gather_rows_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
                        const int32_t* __restrict__ ntp, int32_t P, int32_t k, int32_t H,
                        uint16_t* __restrict__ xs) {
-  const int r = blockIdx.x;
-  if (r >= ntp[0]) return;
-  const int sid = sorted_ids[r];
-  const uint16_t* src = x + (size_t)(sid < P ? sid / k : 0) * H;
-  for (int c = threadIdx.x * 8; c < H; c += kThreads * 8) {
-    u32x4 out = {0u, 0u, 0u, 0u};
-    if (sid < P) {
-      uint32_t p[4];
-      perm_act8(ld16(src + c), p);
-      out = u32x4{p[0], p[1], p[2], p[3]};
-    }
-    // tiled_offset(r, c, H) is the start of a 16 B operand piece (c is a multiple of 8)
-    *reinterpret_cast<u32x4*>(xs + tiled_offset(r, c, H)) = out;
+  const int rb = blockIdx.x;
+  if (rb * 16 >= ntp[0]) return;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int q = lane >> 4, m = lane & 15;
+  const int sid = sorted_ids[rb * 16 + m];
+  const bool real = sid < P;
+  const uint16_t* src = x + (size_t)(real ? sid / k : 0) * H + 8 * q;
+  const int KG = H >> 5;
+  uint16_t* dst = xs + ((size_t)rb * KG * 64 + lane) * 8;
+  int kg = wave;
+  for (; kg + kGatherWaves < KG; kg += 2 * kGatherWaves) {
+    const u32x4 v0 = ld16(src + kg * 32);
+    const u32x4 v1 = ld16(src + (kg + kGatherWaves) * 32);
+    uint32_t p0[4], p1[4];
+    perm_act8(v0, p0);
+    perm_act8(v1, p1);
+    *reinterpret_cast<u32x4*>(dst + (size_t)kg * 512) =
+        real ? u32x4{p0[0], p0[1], p0[2], p0[3]} : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(dst + (size_t)(kg + kGatherWaves) * 512) =
+        real ? u32x4{p1[0], p1[1], p1[2], p1[3]} : u32x4{0u, 0u, 0u, 0u};
+  }
+  for (; kg < KG; kg += kGatherWaves) {
+    uint32_t p0[4];
+    perm_act8(ld16(src + kg * 32), p0);
+    *reinterpret_cast<u32x4*>(dst + (size_t)kg * 512) =
+        real ? u32x4{p0[0], p0[1], p0[2], p0[3]} : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -375,8 +393,9 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
 hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t* ntp, int32_t H,
                               uint16_t* xs, hipStream_t stream) {
   if (r.L <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(r.L), dim3(kThreads), 0, stream, x, r.sorted_ids,
-                     ntp, r.P, r.k, H, xs);
+  // L is at least num_tokens_padded, a multiple of 16
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((r.L + 15) / 16), dim3(kGatherThreads), 0, stream,
+                     x, r.sorted_ids, ntp, r.P, r.k, H, xs);
   return hipGetLastError();
 }
 

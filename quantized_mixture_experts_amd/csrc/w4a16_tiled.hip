@@ -455,27 +455,48 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   }
 }
 
-// out[t, :] = bf16(sum of y[t*k + s, :] over the valid slots s of token t).
+// out[t, :] = bf16(sum of y[t*k + s, :] over the valid slots s of token t, in slot
+// order). A thread owns 8 columns of one token; the rows of up to kSlotBatch slots are
+// requested before any is summed.
 constexpr int kCombineThreads = 256;
+constexpr int kSlotBatch = 8;
 
 __global__ void __launch_bounds__(kCombineThreads)
     combine_rows_kernel(const float* __restrict__ y, const int32_t* __restrict__ ids,
                         int32_t T, int32_t k, int32_t E, int32_t H, uint16_t* __restrict__ out) {
-  const int64_t quads = (int64_t)T * (H >> 2);
-  for (int64_t i = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x; i < quads;
+  const int chunks = H >> 3;
+  const int64_t items = (int64_t)T * chunks;
+  for (int64_t i = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x; i < items;
        i += (int64_t)gridDim.x * kCombineThreads) {
-    const int64_t t = i / (H >> 2);
-    const int c = (int)(i - t * (H >> 2)) * 4;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < k; ++s) {
-      const int64_t pair = t * k + s;
-      const int id = ids[pair];
-      if (id < 0 || id >= E) continue;
-      sum += *reinterpret_cast<const f32x4*>(y + pair * H + c);
+    const int64_t t = i / chunks;
+    const int c = (int)(i - t * chunks) * 8;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < k; s0 += kSlotBatch) {
+      f32x4 vl[kSlotBatch], vh[kSlotBatch];
+      bool ok[kSlotBatch];
+#pragma unroll
+      for (int s = 0; s < kSlotBatch; ++s) {
+        const int64_t pair = t * k + s0 + s;
+        const int id = (s0 + s < k) ? ids[pair] : -1;
+        ok[s] = id >= 0 && id < E;
+        const float* row = y + (ok[s] ? pair : 0) * H + c;
+        vl[s] = *reinterpret_cast<const f32x4*>(row);
+        vh[s] = *reinterpret_cast<const f32x4*>(row + 4);
+      }
+#pragma unroll
+      for (int s = 0; s < kSlotBatch; ++s) {
+        if (ok[s]) {
+          lo += vl[s];
+          hi += vh[s];
+        }
+      }
     }
-    const uint32_t lo = (uint32_t)f32_to_bf16(sum.x) | ((uint32_t)f32_to_bf16(sum.y) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16(sum.z) | ((uint32_t)f32_to_bf16(sum.w) << 16);
-    *reinterpret_cast<uint2*>(out + t * H + c) = make_uint2(lo, hi);
+    u32x4 o;
+    o.x = (uint32_t)f32_to_bf16(lo.x) | ((uint32_t)f32_to_bf16(lo.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(lo.z) | ((uint32_t)f32_to_bf16(lo.w) << 16);
+    o.z = (uint32_t)f32_to_bf16(hi.x) | ((uint32_t)f32_to_bf16(hi.y) << 16);
+    o.w = (uint32_t)f32_to_bf16(hi.z) | ((uint32_t)f32_to_bf16(hi.w) << 16);
+    *reinterpret_cast<u32x4*>(out + t * H + c) = o;
   }
 }
 
@@ -510,9 +531,9 @@ hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, floa
 
 hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,
                                int32_t E, int32_t H, uint16_t* out, hipStream_t stream) {
-  const int64_t quads = (int64_t)T * (H / 4);
-  if (quads <= 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((quads + kCombineThreads - 1) / kCombineThreads, 8192);
+  const int64_t items = (int64_t)T * (H / 8);
+  if (items <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((items + kCombineThreads - 1) / kCombineThreads, 16384);
   hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
                      stream, y, topk_ids, T, k, E, H, out);
   return hipGetLastError();
