@@ -12,7 +12,11 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqmoe.so")
 SOURCES = ["api.hip", "align.hip", "elementwise.hip", "w4a16_stream.hip", "w4a16_tiled.hip",
-           "fp8_stream.hip"]
+           "fp8_stream.hip", "fp8_tiled.hip"]
+# Per-source extra flags. The FP8 tile kernel promotes every MFMA result with VALU
+# multiply-adds, so its MFMAs must write VGPRs (the default heuristics pick AGPRs and then
+# copy every result back).
+EXTRA_FLAGS = {"fp8_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -26,7 +30,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     objs, procs = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -82,12 +82,14 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= 40.0 ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
   p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 2;
-  p.tiled = fmt == kW4A16 && p.schedule == QMOE_SCHEDULE_PREFILL && w4a16_tiled_supported(H, I);
+  p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&
+            (fmt == kW4A16 ? w4a16_tiled_supported(H, I) : fp8_tiled_supported(H, I));
   p.block_m = kSegRows;
   p.L = p.P + (int64_t)E * (p.block_m - 1);
   p.NB = (p.L + p.block_m - 1) / p.block_m;
   // The tile kernels address activation rows with 32-bit byte offsets.
-  if (p.tiled && (uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32))
+  if (p.tiled && fmt == kW4A16 &&
+      (uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32))
     p.tiled = false;
   size_t cur = 0;
   auto take = [&](size_t bytes) {
@@ -358,6 +360,32 @@ qmoe_status moe_fp8_block_forward(const uint8_t* a_q, const float* a_scale, cons
                   region<float>(workspace, p.off_h32), region<uint8_t>(workspace, p.off_hq),
                   region<float>(workspace, p.off_hs), region<float>(workspace, p.off_out32),
                   T, H, I};
+
+  if (p.tiled) {
+    hipError_t err = staged(QMOE_STAGE_ALIGN, s, [&] {
+      return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
+                          region<int32_t>(workspace, p.off_sorted),
+                          region<int32_t>(workspace, p.off_expert_ids),
+                          region<int32_t>(workspace, p.off_ntp),
+                          region<int32_t>(workspace, p.off_offsets), fp8_tiled_rows(),
+                          region<int32_t>(workspace, p.off_tiles), s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "align launch");
+    err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_fp8_gateup_tiled(prob, r, s); });
+    if (err != hipSuccess) return hip_fail(err, "gate_up launch");
+    err = staged(QMOE_STAGE_REQUANT, s, [&] {
+      return launch_fp8_quantize_blocks(prob.h32, p.L, I, 1, 128, prob.hq, prob.hs, s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "h requant launch");
+    float* y = region<float>(workspace, p.off_y);
+    err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_fp8_down_tiled(prob, r, y, s); });
+    if (err != hipSuccess) return hip_fail(err, "down launch");
+    err = staged(QMOE_STAGE_CAST, s, [&] {
+      return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return QMOE_OK;
+  }
 
   hipError_t err = staged(QMOE_STAGE_ZERO, s, [&] {
     return launch_zero_f32(prob.out32, (int64_t)T * H, s);

@@ -152,6 +152,9 @@ __device__ __forceinline__ int xcd_major_item(int block, int grid, int items) {
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// With the accurate exponential: for h that is requantized to E4M3 (a step function),
+// where the fast exponential's ~1e-6 relative error flips codes measurably often.
+__device__ __forceinline__ float silu_f32_accurate(float z) { return z / (1.0f + expf(-z)); }
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));

@@ -153,8 +153,8 @@ __global__ void __launch_bounds__(kThreads) fp8_stream_kernel(Fp8StreamArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float* hrow = a.h32 + (size_t)(rbase + r) * a.I + j0 + col;
-          hrow[0] = silu_f32(acc[0][b][r]) * acc[2][b][r];
-          hrow[16] = silu_f32(acc[1][b][r]) * acc[3][b][r];
+          hrow[0] = silu_f32_accurate(acc[0][b][r]) * acc[2][b][r];
+          hrow[16] = silu_f32_accurate(acc[1][b][r]) * acc[3][b][r];
         }
       } else {
 #pragma unroll

@@ -1,0 +1,348 @@
+// W8A8 block-FP8 grouped expert GEMMs, prefill profile (row tiles of 128, MFMA-bound).
+//
+// Method ("SGLang W8A8 Block FP8 quantization kernel config guide", background
+// section): E4M3 activations with one fp32 scale per token and 128-column group (As),
+// E4M3 weights with one fp32 scale per [128, 128] block (Bs); the per-expert product is
+// C = sum over 128-deep k blocks of (A_q B_q^T)_block * As * Bs. With hundreds of rows
+// per expert it is a grouped GEMM over the expert segments of the sorted row list
+// ("vLLM x Novita AI: Chord W4A16 INT4 MoE Kernel for Kimi K2.x", "Two kernel
+// families").
+//
+// gfx950 mapping. A work-group owns one (128-row tile of an expert segment, 256 weight
+// rows) output tile; its four waves each own the 128 rows and 64 weight rows: 8 x 4
+// MFMA tiles, 128 fp32 accumulators per lane, kept in VGPRs because every 128-deep block
+// is promoted with a VALU multiply-add:
+//   * one v_mfma_scale_f32_16x16x128_f8f6f4 (block scales pinned to 1.0) is one k block;
+//     its fp32 result d is added as acc += d * (As[row] * Bs), the scales being general
+//     fp32 values (a power-of-two block scale cannot carry them);
+//   * activation rows (gathered by token for gate_up, sorted rows of h for down), their
+//     scales and the weights of each k block go global -> LDS by global_load_lds into a
+//     ring of three stages; every wave waits on its own copies with vmcnt (the compiler
+//     does not count these) before the stage's barrier, which sits in the middle of the
+//     step so the last MFMAs cover it;
+// gate_up stores SiLU(gate) * up in fp32 by sorted row (the block quantizer turns it into
+// E4M3 per 128 columns); down stores the routing-weighted rows per (token, slot) pair,
+// summed per token by the combine kernel.
+#include <algorithm>
+#include <type_traits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace qmoe {
+
+namespace {
+
+constexpr int kTileRows = 128;
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kRowBlocks = kTileRows / 16;  // 8
+constexpr int kColTiles = 4;
+constexpr int kStages = 3;
+constexpr int kBlocksPerWave = kRowBlocks / kWaves;  // activation row blocks copied per wave
+constexpr int kScaleRowsPerWave = kTileRows / kWaves;  // activation scale rows per wave
+// Vector memory instructions per wave and step: activation planes, activation scales,
+// weight planes.
+constexpr int kCopiesPerStep = kBlocksPerWave * 2 + 1 + kColTiles * 2;
+constexpr int kMaxKBlocks = 64;  // per-wave weight-scale rows held in LDS (K <= 8192)
+
+// LDS layout in 16 B units: per stage the activation planes [block][plane][lane], the
+// activation scales (128 floats), and per wave the weight planes [tile][plane][lane];
+// then per wave the weight block scales for the whole K (two rows for gate/up).
+constexpr int kAUnits = kRowBlocks * 2 * kWave;       // 1024
+// activation scales: per wave 64 floats, rows wave*32 .. +32 then a copy of them (every
+// lane of the copy is active, so the loop body stays one basic block)
+constexpr int kAsUnits = kWaves * 64 / 4;             // 64
+constexpr int kBUnits = kWaves * kColTiles * 2 * kWave;  // 2048
+constexpr int kStageUnits = kAUnits + kAsUnits + kBUnits;
+constexpr int kBsBase = kStages * kStageUnits;
+constexpr int kSmemUnits = kBsBase + kWaves * 2 * (kMaxKBlocks / 4);
+
+enum class FEpi { GateUp, Down };
+
+struct Fp8TiledArgs {
+  const uint8_t* act;           // gate_up: a_q [T, K]; down: hq [L, K]
+  const float* act_scale;       // gate_up: a_scale [T, K/128]; down: hs [L, K/128]
+  const uint8_t* w;             // [E, N, K]
+  const float* ws;              // [E, N/128, K/128]
+  const int32_t* sorted_ids;    // [L]
+  const int32_t* offsets;       // [E + 1]
+  const int32_t* tile_offsets;  // [E + 1], 128-row tiles
+  const float* topk_weights;    // [P]
+  float* h32;                   // gate_up output [L, I]
+  float* y;                     // down output [P, N]
+  int32_t P, k, E, K, N, I;
+  int32_t col_tiles;
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ int expert_of_tile(const int32_t* toff, int E, int m) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (toff[mid] <= m) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// LDS destination operand of global_load_lds.
+#define QMOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <FEpi EPI>
+__global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
+  __shared__ u32x4 smem[kSmemUnits];
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int col = lane & 15, quad = lane >> 4;
+
+  const int total = a.tile_offsets[a.E] * a.col_tiles;
+  const int per = (total + kNumXcd - 1) / kNumXcd;
+  const int xi = blockIdx.x / kNumXcd;
+  const int item = (blockIdx.x % kNumXcd) * per + xi;
+  if (xi >= per || item >= total) return;
+  // Items are ordered expert-major, then column tile, then row tile: the row tiles of
+  // one (expert, column tile) are neighbours, run together on one XCD and share the
+  // weight tile (the larger of the two operand streams here) in its L2.
+  const int e = expert_of_tile(a.tile_offsets, a.E, item / a.col_tiles);
+  const int ntile_e = a.tile_offsets[e + 1] - a.tile_offsets[e];
+  const int local = item - a.tile_offsets[e] * a.col_tiles;
+  const int ctile = local / ntile_e, rt = local - ctile * ntile_e;
+  const int seg1 = a.offsets[e + 1];
+  const int row0 = a.offsets[e] + rt * kTileRows;
+  const int rb0 = row0 >> 4;
+  const int rb_last = (seg1 >> 4) - 1;
+  const int K = a.K, KB = K >> 7;
+
+  auto weight_row = [&](int t, int c) {
+    if constexpr (EPI == FEpi::GateUp) {
+      const int j = ctile * 128 + wave * 32 + (t & 1) * 16 + c;
+      return (t < 2) ? j : a.I + j;
+    } else {
+      return ctile * 256 + wave * 64 + t * 16 + c;
+    }
+  };
+  // Activation row (of the act matrix) for tile row r; padding rows read row 0.
+  auto act_row = [&](int r) {
+    if constexpr (EPI == FEpi::GateUp) {
+      const int sid = a.sorted_ids[r];
+      return sid < a.P ? sid / a.k : 0;
+    } else {
+      return r;
+    }
+  };
+
+  // Per-lane source offsets (bytes, 64-bit: the activation and weight matrices can pass
+  // 4 GB).
+  const uint8_t* abase[kBlocksPerWave];
+#pragma unroll
+  for (int i = 0; i < kBlocksPerWave; ++i) {
+    const int rb = min(rb0 + wave * kBlocksPerWave + i, rb_last);
+    abase[i] = a.act + (size_t)act_row(rb * 16 + col) * K + 32 * quad;
+  }
+  const float* sbase;
+  {
+    const int r = min(row0 + wave * kScaleRowsPerWave + (lane & (kScaleRowsPerWave - 1)),
+                      rb_last * 16 + 15);  // lanes 32..63 repeat lanes 0..31
+    sbase = a.act_scale + (size_t)act_row(r) * KB;
+  }
+  const uint8_t* wbase[kColTiles];
+#pragma unroll
+  for (int t = 0; t < kColTiles; ++t)
+    wbase[t] = a.w + ((size_t)e * a.N + weight_row(t, col)) * (size_t)K + 32 * quad;
+
+  auto stage_at = [&](int st) { return &smem[st * kStageUnits]; };
+  auto copy_step = [&](int g, int st) {
+    const int kb = min(g, KB - 1);
+    u32x4* s = stage_at(st);
+#pragma unroll
+    for (int i = 0; i < kBlocksPerWave; ++i)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(abase[i] + kb * 128 + 16 * p),
+            QMOE_LDS(s + ((wave * kBlocksPerWave + i) * 2 + p) * kWave), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(sbase + kb), QMOE_LDS(s + kAUnits + wave * 16), 4,
+                                     0, 0);
+#pragma unroll
+    for (int t = 0; t < kColTiles; ++t)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(wbase[t] + kb * 128 + 16 * p),
+            QMOE_LDS(s + kAUnits + kAsUnits + ((wave * kColTiles + t) * 2 + p) * kWave), 16, 0, 0);
+  };
+
+  // Weight block scales of this wave for the whole K: row 0 for tiles 0-1, row 1 for
+  // tiles 2-3 (gate / up for gate_up; the same block for down).
+  u32x4* bs_lds = &smem[kBsBase + wave * 2 * (kMaxKBlocks / 4)];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int nb = weight_row(2 * h, 0) >> 7;
+    const float* src = a.ws + ((size_t)e * (a.N >> 7) + nb) * KB + min(lane, KB - 1);
+    __builtin_amdgcn_global_load_lds((const void*)src, QMOE_LDS(bs_lds + h * (kMaxKBlocks / 4)), 4, 0,
+                                     0);
+  }
+
+  f32x4 acc[kRowBlocks][kColTiles];
+#pragma unroll
+  for (int m = 0; m < kRowBlocks; ++m)
+#pragma unroll
+    for (int t = 0; t < kColTiles; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // Prologue: the two block-scale copies, then steps 0 .. kStages-1.
+#pragma unroll
+  for (int g = 0; g < kStages; ++g) copy_step(g, g);
+  wait_vmcnt<(kStages - 1) * kCopiesPerStep>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  int st = 0;
+  for (int g = 0; g < KB; ++g) {
+    const u32x4* s = stage_at(st);
+    const float* as_f = reinterpret_cast<const float*>(s + kAUnits);
+    const float bs0 = reinterpret_cast<const float*>(bs_lds)[g];
+    const float bs1 = reinterpret_cast<const float*>(bs_lds + kMaxKBlocks / 4)[g];
+    u32x4 bv[kColTiles][2];
+#pragma unroll
+    for (int t = 0; t < kColTiles; ++t)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        bv[t][p] = s[kAUnits + kAsUnits + ((wave * kColTiles + t) * 2 + p) * kWave + lane];
+    // Row block m's operands are read one block ahead; the stage's last reads (block 7)
+    // are issued before block 6's MFMAs, so the barrier can follow those and the last
+    // block's MFMAs cover it. The four MFMA results of block m are promoted into the
+    // accumulators while block m+1's MFMAs run (no VALU waits on a fresh MFMA result).
+    u32x4 av[2] = {s[lane], s[kWave + lane]};
+    auto as_row = [&](int r) { return as_f + (r >> 5) * 64 + (r & 31); };
+    f32x4 as4 = *reinterpret_cast<const f32x4*>(as_row(4 * quad));
+    f32x4 dprev[kColTiles];
+    f32x4 scprev0 = zero4, scprev1 = zero4;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m <= kRowBlocks; ++m) {
+      f32x4 dcur[kColTiles];
+      u32x4 avn[2] = {av[0], av[1]};
+      f32x4 as4n = as4;
+      if (m < kRowBlocks) {
+        if (m + 1 < kRowBlocks) {
+          avn[0] = s[((m + 1) * 2) * kWave + lane];
+          avn[1] = s[((m + 1) * 2 + 1) * kWave + lane];
+          as4n = *reinterpret_cast<const f32x4*>(as_row((m + 1) * 16 + 4 * quad));
+        }
+#pragma unroll
+        for (int t = 0; t < kColTiles; ++t) {
+          const u32x4 bb[2] = {bv[t][0], bv[t][1]};
+          dcur[t] = mfma_fp8_16x16x128(av, bb, zero4);
+        }
+      }
+      if (m > 0) {
+#pragma unroll
+        for (int t = 0; t < kColTiles; ++t) {
+          const f32x4 sc = (t < 2) ? scprev0 : scprev1;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            acc[m - 1][t][r] = __builtin_fmaf(dprev[t][r], sc[r], acc[m - 1][t][r]);
+        }
+      }
+      if (m < kRowBlocks) {
+#pragma unroll
+        for (int t = 0; t < kColTiles; ++t) dprev[t] = dcur[t];
+        scprev0 = as4 * bs0;
+        scprev1 = as4 * bs1;
+      }
+      if (m == kRowBlocks - 2) {
+        // All reads of this stage were issued; once they and the copies of step g+1
+        // (younger: the copies of step g+2) have completed, the barrier frees the stage
+        // for step g + kStages.
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+        wait_vmcnt<(kStages - 2) * kCopiesPerStep>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        copy_step(g + kStages, st);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      av[0] = avn[0];
+      av[1] = avn[1];
+      as4 = as4n;
+      // Keep each block's LDS reads in its own iteration (hoisting them all would take
+      // 128 more registers): a compiler-level memory fence, no instruction.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st = (st == kStages - 1) ? 0 : st + 1;
+  }
+  wait_vmcnt<0>();
+
+  if constexpr (EPI == FEpi::GateUp) {
+#pragma unroll
+    for (int m = 0; m < kRowBlocks; ++m) {
+      const int rb = rb0 + m;
+      if (rb > rb_last) break;
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp) {
+        const int j = ctile * 128 + wave * 32 + tp * 16 + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float gv = acc[m][tp][r], uv = acc[m][tp + 2][r];
+          a.h32[(size_t)(rb * 16 + 4 * quad + r) * a.I + j] = silu_f32_accurate(gv) * uv;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < kRowBlocks; ++m) {
+      const int rb = rb0 + m;
+      if (rb > rb_last) break;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pair = a.sorted_ids[rb * 16 + 4 * quad + r];
+        if (pair >= a.P) continue;
+        const float wt = a.topk_weights[pair];
+        float* yrow = a.y + (size_t)pair * a.N;
+#pragma unroll
+        for (int t = 0; t < kColTiles; ++t) yrow[weight_row(t, col)] = wt * acc[m][t][r];
+      }
+    }
+  }
+}
+
+template <FEpi EPI>
+hipError_t launch_fp8_tiled(const Fp8TiledArgs& a, int64_t max_row_tiles, hipStream_t stream) {
+  const int64_t items = max_row_tiles * a.col_tiles;
+  if (items <= 0) return hipSuccess;
+  if (items > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fp8_tiled_kernel<EPI>), dim3(xcd_major_grid((int)items)), dim3(kThreads),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool fp8_tiled_supported(int32_t H, int32_t I) {
+  return H % 256 == 0 && I % 128 == 0 && H / 128 <= kMaxKBlocks && I / 128 <= kMaxKBlocks;
+}
+
+int32_t fp8_tiled_rows() { return kTileRows; }
+
+hipError_t launch_fp8_gateup_tiled(const Fp8Problem& p, const Routing& r, hipStream_t stream) {
+  Fp8TiledArgs a{p.a_q, p.a_scale, p.w13, p.s13, r.sorted_ids, r.offsets, r.tile_offsets,
+                 r.topk_weights, p.h32, nullptr, r.P, r.k, r.E, p.H, 2 * p.I, p.I, p.I / 128};
+  return launch_fp8_tiled<FEpi::GateUp>(a, (int64_t)r.P / kTileRows + r.E, stream);
+}
+
+hipError_t launch_fp8_down_tiled(const Fp8Problem& p, const Routing& r, float* y,
+                                 hipStream_t stream) {
+  Fp8TiledArgs a{p.hq, p.hs, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets,
+                 r.topk_weights, nullptr, y, r.P, r.k, r.E, p.I, p.H, p.I, p.H / 256};
+  return launch_fp8_tiled<FEpi::Down>(a, (int64_t)r.P / kTileRows + r.E, stream);
+}
+
+}  // namespace qmoe
