@@ -2,7 +2,10 @@
 """Benchmark of the routed, weight-quantized MoE expert FFN on one MI355X.
 
 One step = one full forward (align -> gate_up GEMM + SiLU*up -> down GEMM + weighted
-scatter-add -> bf16 output) on seeded synthetic inputs already resident in HBM.
+scatter-add -> bf16 output) on seeded synthetic inputs already resident in HBM. The timed
+steps are plain calls without instrumentation (--launch graph: replays of one captured HIP
+graph); the per-kernel times come from a separate pass of K steps with HIP events recorded
+around every kernel on its launch stream.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|fp8|full384|tiny]
 
@@ -38,6 +41,10 @@ def parse():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "fp8", "full384", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
+                    help="how the timed steps are issued: eager library calls (default), or "
+                         "replays of one captured HIP graph of the forward (slower on this "
+                         "ROCm for these few-kernel forwards)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="token rows of the CPU-oracle sample (0 = workload default)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -142,21 +149,50 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # Instrumented pass: K eager steps with HIP events recorded by the library around every
+    # stage launch on the launch stream; the per-kernel times (and the roofline) come from
+    # these events.
     if lib.qmoe_timing_begin(args.steps) != 0:
         raise RuntimeError(lib.qmoe_last_error())
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    te0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    te1 = time.perf_counter()
     ms_sum = (ctypes.c_float * 6)()
     counts = (ctypes.c_int32 * 6)()
     if lib.qmoe_timing_end(ms_sum, counts) != 0:
         raise RuntimeError(lib.qmoe_last_error())
     stage_names = ["zero", "align", "gate_up", "requant", "down", "cast"]
     stage_ms = {n: (ms_sum[i] / counts[i] if counts[i] else None) for i, n in enumerate(stage_names)}
+    instrumented_ms = (te1 - te0) * 1e3 / args.steps
 
+    # Timed pass: K steps without instrumentation, as one captured graph replayed K times
+    # (the forward's kernels are launched on the capturing stream; nothing in it allocates
+    # or synchronizes) or as eager calls.
+    if args.launch == "graph":
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        run = graph.replay
+    else:
+        run = step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ids = case["topk_ids"]
     touched = int(np.unique(ids[(ids >= 0) & (ids < cfg.E)]).size)
@@ -225,6 +261,8 @@ def main():
                    "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
                    "top_k": cfg.k, "schedule": ["auto", "decode", "prefill"][chosen],
                    "touched_experts": touched, "weight_bytes": weight_bytes, "flops": flops},
+        "launch": args.launch,
+        "instrumented_ms_per_step": round(instrumented_ms, 4),
         "stage_ms": {k: (round(v, 4) if v is not None else None) for k, v in stage_ms.items()},
         "roofline": roof,
         "cpu_baseline": cpu,

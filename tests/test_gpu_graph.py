@@ -1,0 +1,99 @@
+"""The forward captured once into a HIP graph (through torch.cuda.CUDAGraph on the
+binding's launch stream) and replayed several times, with unrelated eager forwards and
+synchronizations between the replays: every replay must reproduce the eager result. The
+tile paths (prefill W4A16 and block FP8) are deterministic and must match bit for bit; the
+decode path adds its rows with fp32 atomics, whose order may change between runs."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import bf16_out_to_f64, row_rel_err, to_dev
+from quantized_mixture_experts_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _w4a16_runner(case, schedule):
+    d = to_dev(case)
+    T, H = case["x"].shape
+    E, twoI, _ = case["w13"].shape
+    k = case["topk_ids"].shape[1]
+    _, _, ws = binding.plan(binding.FORMAT_W4A16, T, H, twoI // 2, E, k, schedule)
+    work = torch.empty(ws, dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        binding.moe_w4a16_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
+                                  d["topk_weights"], schedule=schedule, out=out, workspace=work)
+    return run, out
+
+
+def _fp8_runner(case, schedule):
+    d = to_dev(case)
+    T, H = case["a_q"].shape
+    E, twoI, _ = case["w13"].shape
+    k = case["topk_ids"].shape[1]
+    _, _, ws = binding.plan(binding.FORMAT_FP8, T, H, twoI // 2, E, k, schedule)
+    work = torch.empty(ws, dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        binding.moe_fp8_block_forward(d["a_q"], d["a_s"], d["w13"], d["s13"], d["w2"], d["s2"],
+                                      d["topk_ids"], d["topk_weights"], schedule=schedule,
+                                      out=out, workspace=work)
+    return run, out
+
+
+def _capture(run):
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run()
+    return graph
+
+
+def _check_replays(run, out, other, exact):
+    run()
+    torch.cuda.synchronize()
+    eager = bf16_out_to_f64(out)
+    graph = _capture(run)
+    for i in range(3):
+        out.zero_()
+        other()  # unrelated eager work between the replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = bf16_out_to_f64(out)
+        if exact:
+            assert np.array_equal(got, eager), f"replay {i} differs"
+        else:
+            assert row_rel_err(got, eager).max() <= 1e-3, f"replay {i} differs"
+
+
+@pytest.mark.parametrize("schedule,shape", [
+    (binding.SCHEDULE_DECODE, (24, 512, 256, 8, 4)),
+    (binding.SCHEDULE_PREFILL, (600, 512, 256, 4, 2)),
+])
+def test_w4a16_graph_replays(schedule, shape):
+    print(f"[graph] w4a16 schedule={schedule} shape={shape}", flush=True)
+    run, out = _w4a16_runner(inputs.custom_w4a16_case(*shape, seed=31), schedule)
+    other, _ = _w4a16_runner(inputs.custom_w4a16_case(*shape, seed=32), schedule)
+    _check_replays(run, out, other, exact=schedule == binding.SCHEDULE_PREFILL)
+
+
+def test_fp8_graph_replays():
+    import oracle
+    print("[graph] fp8 prefill", flush=True)
+    shape = (400, 512, 256, 4, 2)
+    run, out = _fp8_runner(inputs.custom_fp8_case(*shape, seed=33,
+                                                  quantize=oracle.fp8_quantize_blocks),
+                           binding.SCHEDULE_PREFILL)
+    other, _ = _fp8_runner(inputs.custom_fp8_case(*shape, seed=34,
+                                                  quantize=oracle.fp8_quantize_blocks),
+                           binding.SCHEDULE_PREFILL)
+    _check_replays(run, out, other, exact=True)
