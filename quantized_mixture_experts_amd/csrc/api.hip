@@ -256,6 +256,8 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
   r.sorted_ids = region<int32_t>(workspace, p.off_sorted);
   r.offsets = region<int32_t>(workspace, p.off_offsets);
   r.tile_offsets = region<int32_t>(workspace, p.off_tiles);
+  r.expert_ids = region<int32_t>(workspace, p.off_expert_ids);
+  r.ntp = region<int32_t>(workspace, p.off_ntp);
   r.topk_weights = topk_weights;
   r.P = (int32_t)p.P;
   r.k = k;
@@ -351,6 +353,8 @@ qmoe_status moe_fp8_block_forward(const uint8_t* a_q, const float* a_scale, cons
   r.sorted_ids = region<int32_t>(workspace, p.off_sorted);
   r.offsets = region<int32_t>(workspace, p.off_offsets);
   r.tile_offsets = region<int32_t>(workspace, p.off_tiles);
+  r.expert_ids = region<int32_t>(workspace, p.off_expert_ids);
+  r.ntp = region<int32_t>(workspace, p.off_ntp);
   r.topk_weights = topk_weights;
   r.P = (int32_t)p.P;
   r.k = k;

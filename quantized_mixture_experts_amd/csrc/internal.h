@@ -29,6 +29,8 @@ struct Routing {
   const int32_t* sorted_ids;    // [L]
   const int32_t* offsets;       // [E + 1]
   const int32_t* tile_offsets;  // [E + 1], tiles of the prefill GEMM's row-tile size
+  const int32_t* expert_ids;    // [L / kSegRows], expert of each kSegRows-row block
+  const int32_t* ntp;           // rows in use (offsets[E]), on the device
   const float* topk_weights;    // [P]
   int32_t P, k, E, L;
 };

@@ -31,6 +31,10 @@
 //     contiguous.
 // gate_up fuses SiLU(gate) * up and stores h (bf16, tiled by sorted row); down scales by
 // the routing weight and scatter-adds into the fp32 output with hardware atomics.
+#include <algorithm>
+#include <atomic>
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -52,6 +56,8 @@ struct StreamArgs {
   const uint16_t* s;          // [E, N, K/32]
   const int32_t* sorted_ids;  // [L]
   const int32_t* offsets;     // [E + 1]
+  const int32_t* expert_ids;  // [L / 16], expert of each 16-row block
+  const int32_t* ntp;         // rows in use (a multiple of 16)
   const float* topk_weights;  // [P]
   uint16_t* h;                // gate_up output [L, I], tiled layout
   float* out32;               // down output [T, N]
@@ -334,6 +340,252 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// Persistent variant for K a multiple of 512. The grid is one work-group per compute
+// unit; work-group w takes a contiguous range of units, a unit being 512 of one item's K
+// (two 256-deep steps, i.e. one activation chunk), in (16-row block, column chunk, k)
+// order. The weight ring, the activation chunk double buffer and the scale pieces run on
+// across item boundaries, so a work-group never waits for a pipeline refill after the
+// first, and every work-group gets the same number of units up to one. down ranges may
+// start or end inside an item: each piece adds its partial sum into the fp32 output with
+// the same atomics as whole items. gate_up ranges hold whole items, since SiLU needs the
+// complete sums.
+constexpr int kUnitGroups = 16;  // k groups per unit (= kChunkGroups)
+
+struct Unit {
+  int rb, cc, kc, e;  // 16-row block, column chunk, unit within the item's K, expert
+};
+
+// A read of data that no launch in flight writes, through the constant address space so
+// that a uniform index becomes a scalar load: a vector load would enter the in-order
+// vector memory counter, and waiting for it would also wait for the weight prefetches.
+__device__ __forceinline__ int32_t ld_invariant(const int32_t* p, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+template <Epi EPI>
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(2)))
+    w4a16_persist_kernel(StreamArgs a) {
+  __shared__ u32x4 a_lds[2][kChunkGroups][kWave];
+  __shared__ f32x4 c_lds[2][kChunkGroups][kWave];
+  // Scale pieces of the current unit: [wave][tile][row][step], 8 bf16 scales each.
+  __shared__ u32x4 s_lds[kWavesPerGroup][2][16][2];
+
+  const int K = a.K, G = K / 32, KB = K / 2, N = a.N;
+  const int upi = K / 512;  // units per item
+  const int items = (ld_invariant(a.ntp, 0) / kSegRows) * a.chunks;
+  const int nwg = gridDim.x;  // a multiple of the XCD count
+  // XCD-major numbering: the work-groups of one XCD hold consecutive ranges, so the
+  // column chunks of one expert (which share its activation rows) meet in one L2.
+  const int wg = (blockIdx.x % kNumXcd) * (nwg / kNumXcd) + blockIdx.x / kNumXcd;
+  int u0, u1;
+  if constexpr (EPI == Epi::GateUp) {
+    const int per = (items + nwg - 1) / nwg;
+    u0 = min(items, wg * per) * upi;
+    u1 = min(items, wg * per + per) * upi;
+  } else {
+    const int total = items * upi;
+    const int per = (total + nwg - 1) / nwg;
+    u0 = min(total, wg * per);
+    u1 = min(total, wg * per + per);
+  }
+  if (u0 >= u1) return;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = lane_id();
+  const int col = lane & 15, quad = lane >> 4;
+  const uint32_t neg136[4] = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
+  const uint32_t one28 = opaque_vgpr(kBf16Bias128), nib = opaque_sgpr(kNibbleMask);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  auto desc = [&](int u) {
+    Unit d;
+    const int item = u / upi;
+    d.kc = u - item * upi;
+    d.rb = item / a.chunks;
+    d.cc = item - d.rb * a.chunks;
+    d.e = ld_invariant(a.expert_ids, d.rb);
+    return d;
+  };
+  // First weight row of tile t of this wave in column chunk cc, and whether the tile
+  // exists (tiles past the end read rows 0..15 of the expert; results unused).
+  auto tile_row0 = [&](int cc, int t) {
+    if constexpr (EPI == Epi::GateUp) {
+      const int j0 = (cc * kWavesPerGroup + wave) * 16;
+      return (j0 < a.I ? j0 : 0) + (t ? a.I : 0);
+    } else {
+      const int j0 = (cc * kWavesPerGroup + wave) * 32 + 16 * t;
+      return j0 < N ? j0 : 0;
+    }
+  };
+  // Per-lane parts of the weight and scale addresses, the same for every unit.
+  const uint32_t lane_w = col * KB + 16 * quad;
+  const int st_t = quad >> 1, st_p = quad & 1;  // the scale piece this lane stages
+  const uint32_t lane_s = (col * G + 8 * st_p) * 2;
+
+  Stage st[kStages];
+  auto load = [&](Stage& s, const Unit& d, int p) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint8_t* base = a.w + ((size_t)d.e * N + tile_row0(d.cc, t)) * KB + d.kc * 256;
+      const uint8_t* q = base + lane_w + p * 128;
+      s.w[t][0] = ld16(q);
+      s.w[t][1] = ld16(q + 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  u32x4 sreg[2];
+  auto scale_load = [&](u32x4& r, const Unit& d) {
+    const int row0 = st_t ? tile_row0(d.cc, 1) : tile_row0(d.cc, 0);
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.s) +
+                          (((size_t)d.e * N + row0) * G + d.kc * kUnitGroups) * 2;
+    r = ld16(base + lane_s);
+  };
+  auto scale_store = [&](const u32x4& r) { s_lds[wave][st_t][col][st_p] = r; };
+
+  u32x4 creg[kChunkPieces];
+  auto chunk_load = [&](const Unit& d) {
+    const u32x4* ablk = reinterpret_cast<const u32x4*>(a.act) + (size_t)d.rb * G * kWave;
+#pragma unroll
+    for (int i = 0; i < kChunkPieces; ++i) {
+      const int idx = threadIdx.x + kThreads * i;  // group-in-chunk * 64 + lane
+      creg[i] = ablk[(size_t)(d.kc * kUnitGroups + idx / kWave) * kWave + idx % kWave];
+    }
+  };
+  auto chunk_store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kChunkPieces; ++i) {
+      const int g = wave + kWavesPerGroup * i;
+      a_lds[buf][g][lane] = creg[i];
+      const uint32_t av[4] = {creg[i][0], creg[i][1], creg[i][2], creg[i][3]};
+      c_lds[buf][g][lane] = mfma_bf16_16x16x32(av, neg136, zero4);
+    }
+  };
+
+  f32x4 acc[2] = {zero4, zero4};
+  auto group = [&](int buf, int gl, uint32_t w0, uint32_t w1, float sc0, float sc1) {
+    const u32x4 v = a_lds[buf][gl][lane];
+    const uint32_t av[4] = {v[0], v[1], v[2], v[3]};
+    const f32x4 corr = c_lds[buf][gl][lane];
+    uint32_t bw0[4], bw1[4];
+    int4_to_bf16_biased(w0, nib, one28, bw0);
+    int4_to_bf16_biased(w1, nib, one28, bw1);
+    const f32x4 d0 = mfma_bf16_16x16x32(av, bw0, corr);
+    const f32x4 d1 = mfma_bf16_16x16x32(av, bw1, corr);
+    acc[0] += sc0 * d0;
+    acc[1] += sc1 * d1;
+  };
+  // One 256-deep step: groups 8p..8p+7 of the unit's chunk, scale piece p.
+  auto compute = [&](Stage& s, int buf, int p) {
+    const u32x4 sv[2] = {s_lds[wave][0][col][p], s_lds[wave][1][col][p]};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t wt[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wt[t][i] = s.w[t][half][i];
+        transpose4_rows(wt[t]);
+      }
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int g = 4 * half + g4;
+        const uint32_t s0w = sv[0][g >> 1], s1w = sv[1][g >> 1];
+        const float sc0 = (g & 1) ? bf16_hi(s0w) : bf16_lo(s0w);
+        const float sc1 = (g & 1) ? bf16_hi(s1w) : bf16_lo(s1w);
+        group(buf, 8 * p + g, wt[0][g4], wt[1][g4], sc0, sc1);
+      }
+    }
+  };
+  // down: pair ids of this lane's four rows for the current and the next unit, and the
+  // routing weights of the current unit's rows, loaded a unit ahead of their use.
+  int sid_c[4], sid_n[4];
+  float wt_c[4];
+  auto sid_load = [&](int (&sid)[4], const Unit& d) {
+    if constexpr (EPI == Epi::Down) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sid[r] = a.sorted_ids[d.rb * kSegRows + 4 * quad + r];
+    }
+  };
+  auto wt_load = [&]() {
+    if constexpr (EPI == Epi::Down) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wt_c[r] = a.topk_weights[min(sid_c[r], a.P - 1)];
+    }
+  };
+  auto epilogue = [&](const Unit& d) {
+    const int rbase = d.rb * kSegRows + 4 * quad;
+    if constexpr (EPI == Epi::GateUp) {
+      const int j0 = (d.cc * kWavesPerGroup + wave) * 16;
+      if (j0 < a.I) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          a.h[tiled_offset(rbase + r, j0 + col, a.I)] =
+              f32_to_bf16(silu_f32(acc[0][r]) * acc[1][r]);
+      }
+    } else {
+      const int j0 = (d.cc * kWavesPerGroup + wave) * 32;
+      (void)rbase;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int sid = sid_c[r];
+        if (sid >= a.P) continue;
+        float* orow = a.out32 + (size_t)(sid / a.k) * N + j0 + col;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          if (j0 + 16 * t < N) unsafeAtomicAdd(orow + 16 * t, wt_c[r] * acc[t][r]);
+      }
+    }
+    acc[0] = zero4;
+    acc[1] = zero4;
+  };
+
+  // Descriptors of units u, u+1, u+2 (clamped to the range: loads past its end re-read
+  // the last unit, which the cache serves, and are never used).
+  const int ulast = u1 - 1;
+  Unit d0 = desc(u0), d1 = desc(min(u0 + 1, ulast)), d2 = desc(min(u0 + 2, ulast));
+  sid_load(sid_c, d0);
+  scale_load(sreg[0], d0);
+  scale_load(sreg[1], d1);
+  chunk_load(d0);
+  load(st[0], d0, 0);
+  load(st[1], d0, 1);
+  load(st[2], d1, 0);
+  chunk_store(0);
+  chunk_load(d1);
+  __syncthreads();
+
+  // Unit u with local parity P uses activation buffer P, scale registers P and ring
+  // slots 2P (step 0) and 2P+1 (step 1); the loads of step s+3 are issued at step s.
+  auto unit = [&](auto P_, int u) {
+    constexpr int P = decltype(P_)::value;
+    const bool live = u < u1;
+    wt_load();
+    sid_load(sid_n, d1);
+    scale_store(sreg[P]);
+    scale_load(sreg[P], d2);
+    load(st[(2 * P + 3) % kStages], d1, 1);
+    if (live) compute(st[2 * P], P, 0);
+    load(st[(2 * P + 4) % kStages], d2, 0);
+    if (live) compute(st[2 * P + 1], P, 1);
+    if (live && (d0.kc == upi - 1 || u == ulast)) epilogue(d0);
+    chunk_store(P ^ 1);
+    chunk_load(d2);
+    __syncthreads();
+    d0 = d1;
+    d1 = d2;
+    d2 = desc(min(u + 3, ulast));
+    if constexpr (EPI == Epi::Down) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sid_c[r] = sid_n[r];
+    }
+  };
+  for (int u = u0; u < u1; u += 2) {
+    unit(std::integral_constant<int, 0>{}, u);
+    unit(std::integral_constant<int, 1>{}, u + 1);
+  }
+}
+
 // xs = x gathered by sorted row in the tiled operand layout, for rows below
 // num_tokens_padded; padding rows are zero so the GEMMs load them unmasked.
 // One work-group per 16-row block; each wave writes whole 1 KB operands (one k group of
@@ -375,6 +627,23 @@ __global__ void __launch_bounds__(kGatherThreads)
   }
 }
 
+// One work-group per compute unit (the persistent kernel's resources allow no second),
+// rounded down to a multiple of the XCD count; queried once per device.
+int persistent_grid() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cu = 0;
+    n = std::max(kNumXcd, cu / kNumXcd * kNumXcd);
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <Epi EPI>
 hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream) {
   const int cols_per_group = (EPI == Epi::GateUp) ? 16 * kWavesPerGroup : 32 * kWavesPerGroup;
@@ -382,9 +651,14 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
   StreamArgs args = a;
   args.chunks = (extent + cols_per_group - 1) / cols_per_group;
   args.items = E * args.chunks;
-  dim3 grid(xcd_major_grid(args.items));
   (void)mb;  // one 16-row block per weight pass (larger passes do not fit the registers)
-  hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), grid, dim3(kThreads), 0, stream, args);
+  if (a.K % 512 == 0) {
+    hipLaunchKernelGGL((w4a16_persist_kernel<EPI>), dim3(persistent_grid()), dim3(kThreads), 0,
+                       stream, args);
+  } else {
+    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), dim3(xcd_major_grid(args.items)),
+                       dim3(kThreads), 0, stream, args);
+  }
   return hipGetLastError();
 }
 
@@ -401,14 +675,16 @@ hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t
 
 hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, int mb,
                                       hipStream_t stream) {
-  StreamArgs a{p.xs, p.w13, p.s13, r.sorted_ids, r.offsets, r.topk_weights, p.h, nullptr,
+  StreamArgs a{p.xs, p.w13, p.s13, r.sorted_ids, r.offsets, r.expert_ids, r.ntp, r.topk_weights,
+               p.h, nullptr,
                r.P, r.k, p.H, 2 * p.I, p.I, 0, 0};
   return launch_stream<Epi::GateUp>(a, r.E, mb, stream);
 }
 
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
                                     hipStream_t stream) {
-  StreamArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.topk_weights, nullptr, p.out32,
+  StreamArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.expert_ids, r.ntp, r.topk_weights,
+               nullptr, p.out32,
                r.P, r.k, p.I, p.H, p.I, 0, 0};
   return launch_stream<Epi::Down>(a, r.E, mb, stream);
 }

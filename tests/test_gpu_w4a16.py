@@ -71,6 +71,26 @@ def test_w4a16_ragged_shapes(oracle_mod, T, H, I, E, k, schedule):
     assert report(f"ragged {T}x{H}x{I}", got, ref).max() <= TOL
 
 
+# Decode profile shapes with K a multiple of 512 in one or both GEMMs, which run the
+# persistent stream kernels: down ranges that split items between work-groups, several
+# 16-row blocks per expert (zipf routing), fewer units than work-groups, and column tiles
+# past the end of h (I = 96) or of the output (H = 800).
+@pytest.mark.parametrize("T,H,I,E,k,kind", [
+    (40, 1024, 512, 8, 4, "uniform"),
+    (300, 1536, 1536, 16, 4, "zipf"),
+    (3, 2560, 1024, 64, 2, "uniform"),
+    (60, 800, 512, 12, 3, "uniform"),
+    (25, 1024, 96, 5, 2, "uniform"),
+    (200, 512, 512, 64, 8, "zipf"),
+])
+def test_w4a16_decode_persistent_shapes(oracle_mod, T, H, I, E, k, kind):
+    print(f"[w4a16] persistent T={T} H={H} I={I} E={E} k={k} {kind}", flush=True)
+    case = inputs.custom_w4a16_case(T, H, I, E, k, seed=T * 17 + I, kind=kind)
+    got = _forward(case, binding.SCHEDULE_DECODE)
+    ref = _oracle(oracle_mod, case, None)
+    assert report(f"persistent {T}x{H}x{I}x{E}", got, ref).max() <= TOL
+
+
 def test_w4a16_zero_routing_weights_give_exact_zero():
     case = inputs.custom_w4a16_case(20, 256, 128, 8, 2, seed=5)
     case["topk_weights"][:] = 0.0
