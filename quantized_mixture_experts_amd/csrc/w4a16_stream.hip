@@ -350,6 +350,20 @@ __global__ void __launch_bounds__(kThreads)
 // the same atomics as whole items. gate_up ranges hold whole items, since SiLU needs the
 // complete sums.
 constexpr int kUnitGroups = 16;  // k groups per unit (= kChunkGroups)
+// Weight ring depth in 256-deep steps (loads run kRing - 1 steps ahead). Under full load
+// HBM latency is a few microseconds; each step holds 4 KB per wave.
+constexpr int kRing = 4;
+static_assert(kRing % 2 == 0 && kRing >= 4, "ring of whole units, at least two");
+// Group scales are staged per block of kScaleUnits units: 128 B (one cache line) of
+// each weight row, loaded a block ahead with whole lines per row.
+constexpr int kScaleUnits = 4;
+constexpr int kBodyUnits = (kRing / 2) % 2 == 0 ? kRing / 2 : kRing;
+constexpr int kWin = kRing / 2 + 1;  // unit descriptors kept ahead (the farthest load)
+
+template <typename F, int... U>
+__device__ __forceinline__ void unroll_units(F& f, int u, std::integer_sequence<int, U...>) {
+  (f(std::integral_constant<int, U>{}, u + U), ...);
+}
 
 struct Unit {
   int rb, cc, kc, e;  // 16-row block, column chunk, unit within the item's K, expert
@@ -368,8 +382,9 @@ __global__ void __launch_bounds__(kThreads)
     w4a16_persist_kernel(StreamArgs a) {
   __shared__ u32x4 a_lds[2][kChunkGroups][kWave];
   __shared__ f32x4 c_lds[2][kChunkGroups][kWave];
-  // Scale pieces of the current unit: [wave][tile][row][step], 8 bf16 scales each.
-  __shared__ u32x4 s_lds[kWavesPerGroup][2][16][2];
+  // Scales of the current block: [wave][tile][step in block][row], 8 bf16 scales each
+  // (rows innermost, so the sixteen rows a wave reads at once are 16 B apart).
+  __shared__ u32x4 s_lds[kWavesPerGroup][2][2 * kScaleUnits][16];
 
   const int K = a.K, G = K / 32, KB = K / 2, N = a.N;
   const int upi = K / 512;  // units per item
@@ -390,6 +405,7 @@ __global__ void __launch_bounds__(kThreads)
     u1 = min(total, wg * per + per);
   }
   if (u0 >= u1) return;
+  const int ulast = u1 - 1;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = lane_id();
@@ -420,10 +436,7 @@ __global__ void __launch_bounds__(kThreads)
   };
   // Per-lane parts of the weight and scale addresses, the same for every unit.
   const uint32_t lane_w = col * KB + 16 * quad;
-  const int st_t = quad >> 1, st_p = quad & 1;  // the scale piece this lane stages
-  const uint32_t lane_s = (col * G + 8 * st_p) * 2;
 
-  Stage st[kStages];
   auto load = [&](Stage& s, const Unit& d, int p) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -434,14 +447,27 @@ __global__ void __launch_bounds__(kThreads)
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  u32x4 sreg[2];
-  auto scale_load = [&](u32x4& r, const Unit& d) {
-    const int row0 = st_t ? tile_row0(d.cc, 1) : tile_row0(d.cc, 0);
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.s) +
-                          (((size_t)d.e * N + row0) * G + d.kc * kUnitGroups) * 2;
-    r = ld16(base + lane_s);
+  // A block's scales: load i covers tile i / 2, rows 8 (i % 2) .. + 7, one 128 B line
+  // per row (lane l: row + l / 8, 16 B piece l % 8, i.e. step l % 8 of the block). Pieces
+  // past the end of a row are clamped into it (never used).
+  u32x4 snext[4];
+  const int s_row = lane >> 3, s_piece = lane & 7;
+  auto scale_block_load = [&](const Unit& d) {
+    const int off = min((d.kc & ~(kScaleUnits - 1)) * 32 + s_piece * 16, G * 2 - 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile_row0(d.cc, i >> 1) + 8 * (i & 1) + s_row;
+      snext[i] = ld16(reinterpret_cast<const uint8_t*>(a.s) + ((size_t)d.e * N + row) * G * 2 + off);
+    }
   };
-  auto scale_store = [&](const u32x4& r) { s_lds[wave][st_t][col][st_p] = r; };
+  auto scale_block_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_lds[wave][i >> 1][s_piece][8 * (i & 1) + s_row] = snext[i];
+  };
+  // First unit of the block after unit u's (the next item's first unit at an item end).
+  auto next_block = [&](int u, int kc) {
+    return min(u + min(kScaleUnits - (kc & (kScaleUnits - 1)), upi - kc), ulast);
+  };
 
   u32x4 creg[kChunkPieces];
   auto chunk_load = [&](const Unit& d) {
@@ -463,23 +489,21 @@ __global__ void __launch_bounds__(kThreads)
   };
 
   f32x4 acc[2] = {zero4, zero4};
-  auto group = [&](int buf, int gl, uint32_t w0, uint32_t w1, float sc0, float sc1) {
-    const u32x4 v = a_lds[buf][gl][lane];
-    const uint32_t av[4] = {v[0], v[1], v[2], v[3]};
-    const f32x4 corr = c_lds[buf][gl][lane];
-    uint32_t bw0[4], bw1[4];
-    int4_to_bf16_biased(w0, nib, one28, bw0);
-    int4_to_bf16_biased(w1, nib, one28, bw1);
-    const f32x4 d0 = mfma_bf16_16x16x32(av, bw0, corr);
-    const f32x4 d1 = mfma_bf16_16x16x32(av, bw1, corr);
-    acc[0] += sc0 * d0;
-    acc[1] += sc1 * d1;
-  };
-  // One 256-deep step: groups 8p..8p+7 of the unit's chunk, scale piece p.
-  auto compute = [&](Stage& s, int buf, int p) {
-    const u32x4 sv[2] = {s_lds[wave][0][col][p], s_lds[wave][1][col][p]};
+  // One 256-deep step: groups 8p..8p+7 of the unit's chunk, scale piece p, in two halves
+  // of four groups. Each half reads its four activation operands and zero-point terms
+  // from LDS at once and issues its eight MFMAs back to back before the scale FMAs, so
+  // neither the LDS latency nor the MFMA latency is paid once per group.
+  auto compute = [&](Stage& s, int buf, int p, int sp) {
+    const u32x4 sv[2] = {s_lds[wave][0][sp][col], s_lds[wave][1][sp][col]};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+      u32x4 av[4];
+      f32x4 cv[4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        av[g4] = a_lds[buf][8 * p + 4 * half + g4][lane];
+        cv[g4] = c_lds[buf][8 * p + 4 * half + g4][lane];
+      }
       uint32_t wt[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -487,13 +511,25 @@ __global__ void __launch_bounds__(kThreads)
         for (int i = 0; i < 4; ++i) wt[t][i] = s.w[t][half][i];
         transpose4_rows(wt[t]);
       }
+      f32x4 d[2][4];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const uint32_t a4[4] = {av[g4][0], av[g4][1], av[g4][2], av[g4][3]};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          uint32_t bw[4];
+          int4_to_bf16_biased(wt[t][g4], nib, one28, bw);
+          d[t][g4] = mfma_bf16_16x16x32(a4, bw, cv[g4]);
+        }
+      }
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int g = 4 * half + g4;
-        const uint32_t s0w = sv[0][g >> 1], s1w = sv[1][g >> 1];
-        const float sc0 = (g & 1) ? bf16_hi(s0w) : bf16_lo(s0w);
-        const float sc1 = (g & 1) ? bf16_hi(s1w) : bf16_lo(s1w);
-        group(buf, 8 * p + g, wt[0][g4], wt[1][g4], sc0, sc1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t sw = sv[t][g >> 1];
+          acc[t] += ((g & 1) ? bf16_hi(sw) : bf16_lo(sw)) * d[t][g4];
+        }
       }
     }
   };
@@ -542,48 +578,57 @@ __global__ void __launch_bounds__(kThreads)
 
   // Descriptors of units u, u+1, u+2 (clamped to the range: loads past its end re-read
   // the last unit, which the cache serves, and are never used).
-  const int ulast = u1 - 1;
-  Unit d0 = desc(u0), d1 = desc(min(u0 + 1, ulast)), d2 = desc(min(u0 + 2, ulast));
-  sid_load(sid_c, d0);
-  scale_load(sreg[0], d0);
-  scale_load(sreg[1], d1);
-  chunk_load(d0);
-  load(st[0], d0, 0);
-  load(st[1], d0, 1);
-  load(st[2], d1, 0);
+  // Descriptors of units u .. u + kWin - 1, clamped to the range (loads past its end
+  // re-read the last unit, which the cache serves, and are never used).
+  Unit dq[kWin];
+#pragma unroll
+  for (int i = 0; i < kWin; ++i) dq[i] = desc(min(u0 + i, ulast));
+  sid_load(sid_c, dq[0]);
+  scale_block_load(dq[0]);
+  chunk_load(dq[0]);
+  Stage st[kRing];
+#pragma unroll
+  for (int j = 0; j < kRing - 1; ++j) load(st[j], dq[j / 2], j & 1);
   chunk_store(0);
-  chunk_load(d1);
+  chunk_load(dq[1]);
+  scale_block_store();
+  scale_block_load(desc(next_block(u0, dq[0].kc)));
   __syncthreads();
 
-  // Unit u with local parity P uses activation buffer P, scale registers P and ring
-  // slots 2P (step 0) and 2P+1 (step 1); the loads of step s+3 are issued at step s.
-  auto unit = [&](auto P_, int u) {
-    constexpr int P = decltype(P_)::value;
+  // Unit u at position U of the unrolled body uses activation buffer and scale registers
+  // U & 1 and ring slots (2U + p) % kRing for its steps p = 0, 1; the loads of local step
+  // s + kRing - 1 are issued at step s.
+  auto unit = [&](auto U_, int u) {
+    constexpr int U = decltype(U_)::value;
+    constexpr int P = U & 1;
+    constexpr int a0 = kRing - 1, a1 = kRing;  // steps ahead of the loads, from step 0
     const bool live = u < u1;
     wt_load();
-    sid_load(sid_n, d1);
-    scale_store(sreg[P]);
-    scale_load(sreg[P], d2);
-    load(st[(2 * P + 3) % kStages], d1, 1);
-    if (live) compute(st[2 * P], P, 0);
-    load(st[(2 * P + 4) % kStages], d2, 0);
-    if (live) compute(st[2 * P + 1], P, 1);
-    if (live && (d0.kc == upi - 1 || u == ulast)) epilogue(d0);
+    sid_load(sid_n, dq[1]);
+    const int kc = dq[0].kc;
+    if (live && u != u0 && (kc & (kScaleUnits - 1)) == 0) {
+      scale_block_store();
+      scale_block_load(desc(next_block(u, kc)));
+    }
+    const int sp = 2 * (kc & (kScaleUnits - 1));
+    load(st[(2 * U + a0) % kRing], dq[a0 / 2], a0 & 1);
+    if (live) compute(st[(2 * U) % kRing], P, 0, sp);
+    load(st[(2 * U + 1 + a0) % kRing], dq[a1 / 2], a1 & 1);
+    if (live) compute(st[(2 * U + 1) % kRing], P, 1, sp + 1);
+    if (live && (dq[0].kc == upi - 1 || u == ulast)) epilogue(dq[0]);
     chunk_store(P ^ 1);
-    chunk_load(d2);
+    chunk_load(dq[2]);
     __syncthreads();
-    d0 = d1;
-    d1 = d2;
-    d2 = desc(min(u + 3, ulast));
+#pragma unroll
+    for (int i = 0; i + 1 < kWin; ++i) dq[i] = dq[i + 1];
+    dq[kWin - 1] = desc(min(u + kWin, ulast));
     if constexpr (EPI == Epi::Down) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sid_c[r] = sid_n[r];
     }
   };
-  for (int u = u0; u < u1; u += 2) {
-    unit(std::integral_constant<int, 0>{}, u);
-    unit(std::integral_constant<int, 1>{}, u + 1);
-  }
+  for (int u = u0; u < u1; u += kBodyUnits)
+    unroll_units(unit, u, std::make_integer_sequence<int, kBodyUnits>{});
 }
 
 // xs = x gathered by sorted row in the tiled operand layout, for rows below
