@@ -381,7 +381,9 @@ __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(2)))
     w4a16_persist_kernel(StreamArgs a) {
   __shared__ u32x4 a_lds[2][kChunkGroups][kWave];
-  __shared__ f32x4 c_lds[2][kChunkGroups][kWave];
+  // Zero-point term of each group per activation row: the same for every column, so one
+  // float per row (read by the four lanes of a row quarter at once).
+  __shared__ float c_lds[2][kChunkGroups][16];
   // Scales of the current block: [wave][tile][step in block][row], 8 bf16 scales each
   // (rows innermost, so the sixteen rows a wave reads at once are 16 B apart).
   __shared__ u32x4 s_lds[kWavesPerGroup][2][2 * kScaleUnits][16];
@@ -484,7 +486,8 @@ __global__ void __launch_bounds__(kThreads)
       const int g = wave + kWavesPerGroup * i;
       a_lds[buf][g][lane] = creg[i];
       const uint32_t av[4] = {creg[i][0], creg[i][1], creg[i][2], creg[i][3]};
-      c_lds[buf][g][lane] = mfma_bf16_16x16x32(av, neg136, zero4);
+      const f32x4 c = mfma_bf16_16x16x32(av, neg136, zero4);
+      if (col == 0) *reinterpret_cast<f32x4*>(&c_lds[buf][g][4 * quad]) = c;
     }
   };
 
@@ -502,7 +505,7 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         av[g4] = a_lds[buf][8 * p + 4 * half + g4][lane];
-        cv[g4] = c_lds[buf][8 * p + 4 * half + g4][lane];
+        cv[g4] = *reinterpret_cast<const f32x4*>(&c_lds[buf][8 * p + 4 * half + g4][4 * quad]);
       }
       uint32_t wt[2][4];
 #pragma unroll
