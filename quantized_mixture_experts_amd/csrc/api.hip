@@ -294,10 +294,11 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
     return QMOE_OK;
   }
 
-  hipError_t err = staged(QMOE_STAGE_ZERO, s, [&] {
-    return launch_zero_f32(prob.out32, (int64_t)T * H, s);
-  });
-  if (err != hipSuccess) return hip_fail(err, "zero launch");
+  hipError_t err = hipSuccess;
+  if (!w4a16_stream_zeroes_output(H)) {
+    err = staged(QMOE_STAGE_ZERO, s, [&] { return launch_zero_f32(prob.out32, (int64_t)T * H, s); });
+    if (err != hipSuccess) return hip_fail(err, "zero launch");
+  }
   err = staged(QMOE_STAGE_ALIGN, s, [&] {
     return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
                         region<int32_t>(workspace, p.off_sorted),

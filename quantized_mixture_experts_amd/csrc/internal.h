@@ -69,6 +69,9 @@ hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t
 // once per pass of up to 16*mb rows of that expert.
 hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, int mb,
                                       hipStream_t stream);
+// Whether the decode gate_up launch also clears out32 (then no separate clearing launch
+// is needed before down).
+bool w4a16_stream_zeroes_output(int32_t H);
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
                                     hipStream_t stream);
 // Prefill profile (W4A16): 256-row tiles of each expert segment on the matrix cores.

@@ -63,6 +63,8 @@ struct StreamArgs {
   float* out32;               // down output [T, N]
   int32_t P, k, K, N, I;
   int32_t chunks, items;      // column chunks per expert; E * chunks
+  float* zero_out;            // persistent gate_up: fp32 buffer it clears first (or null)
+  int64_t zero_n;             // its length in floats, a multiple of 4
 };
 
 struct Stage {
@@ -388,6 +390,16 @@ __global__ void __launch_bounds__(kThreads)
   // (rows innermost, so the sixteen rows a wave reads at once are 16 B apart).
   __shared__ u32x4 s_lds[kWavesPerGroup][2][2 * kScaleUnits][16];
 
+  // gate_up clears the fp32 output that down accumulates into (down starts after the
+  // last gate_up work-group has ended).
+  if constexpr (EPI == Epi::GateUp) {
+    if (a.zero_out) {
+      const int64_t n4 = a.zero_n / 4;
+      for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
+           i += (int64_t)gridDim.x * kThreads)
+        reinterpret_cast<f32x4*>(a.zero_out)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
   const int K = a.K, G = K / 32, KB = K / 2, N = a.N;
   const int upi = K / 512;  // units per item
   const int items = (ld_invariant(a.ntp, 0) / kSegRows) * a.chunks;
@@ -636,11 +648,13 @@ __global__ void __launch_bounds__(kThreads)
 
 // xs = x gathered by sorted row in the tiled operand layout, for rows below
 // num_tokens_padded; padding rows are zero so the GEMMs load them unmasked.
-// One work-group per 16-row block; each wave writes whole 1 KB operands (one k group of
+// One work-group per (16-row block, range of kGatherGroups k groups), so that a few
+// hundred rows still fill the chip; each wave writes whole 1 KB operands (one k group of
 // the block): lane (q, m) reads 16 B of row m at k slice q and stores them, permuted to
 // the operand k order, at its place in the operand, so every store is a full line.
 constexpr int kGatherThreads = 256;
 constexpr int kGatherWaves = kGatherThreads / kWave;
+constexpr int kGatherGroups = 32;  // 1024 columns per work-group
 
 __global__ void __launch_bounds__(kGatherThreads)
     gather_rows_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
@@ -654,9 +668,10 @@ __global__ void __launch_bounds__(kGatherThreads)
   const bool real = sid < P;
   const uint16_t* src = x + (size_t)(real ? sid / k : 0) * H + 8 * q;
   const int KG = H >> 5;
+  const int kg_end = min(KG, (int)(blockIdx.y + 1) * kGatherGroups);
   uint16_t* dst = xs + ((size_t)rb * KG * 64 + lane) * 8;
-  int kg = wave;
-  for (; kg + kGatherWaves < KG; kg += 2 * kGatherWaves) {
+  int kg = blockIdx.y * kGatherGroups + wave;
+  for (; kg + kGatherWaves < kg_end; kg += 2 * kGatherWaves) {
     const u32x4 v0 = ld16(src + kg * 32);
     const u32x4 v1 = ld16(src + (kg + kGatherWaves) * 32);
     uint32_t p0[4], p1[4];
@@ -667,7 +682,7 @@ __global__ void __launch_bounds__(kGatherThreads)
     *reinterpret_cast<u32x4*>(dst + (size_t)(kg + kGatherWaves) * 512) =
         real ? u32x4{p1[0], p1[1], p1[2], p1[3]} : u32x4{0u, 0u, 0u, 0u};
   }
-  for (; kg < KG; kg += kGatherWaves) {
+  for (; kg < kg_end; kg += kGatherWaves) {
     uint32_t p0[4];
     perm_act8(ld16(src + kg * 32), p0);
     *reinterpret_cast<u32x4*>(dst + (size_t)kg * 512) =
@@ -716,16 +731,21 @@ hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t
                               uint16_t* xs, hipStream_t stream) {
   if (r.L <= 0) return hipSuccess;
   // L is at least num_tokens_padded, a multiple of 16
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((r.L + 15) / 16), dim3(kGatherThreads), 0, stream,
-                     x, r.sorted_ids, ntp, r.P, r.k, H, xs);
+  const int kchunks = (H / 32 + kGatherGroups - 1) / kGatherGroups;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((r.L + 15) / 16, kchunks), dim3(kGatherThreads), 0,
+                     stream, x, r.sorted_ids, ntp, r.P, r.k, H, xs);
   return hipGetLastError();
 }
 
+bool w4a16_stream_zeroes_output(int32_t H) { return H % 512 == 0; }
+
 hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, int mb,
                                       hipStream_t stream) {
+  const bool zero = w4a16_stream_zeroes_output(p.H);
   StreamArgs a{p.xs, p.w13, p.s13, r.sorted_ids, r.offsets, r.expert_ids, r.ntp, r.topk_weights,
                p.h, nullptr,
-               r.P, r.k, p.H, 2 * p.I, p.I, 0, 0};
+               r.P, r.k, p.H, 2 * p.I, p.I, 0, 0,
+               zero ? p.out32 : nullptr, zero ? (int64_t)p.T * p.H : 0};
   return launch_stream<Epi::GateUp>(a, r.E, mb, stream);
 }
 
@@ -733,7 +753,7 @@ hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int
                                     hipStream_t stream) {
   StreamArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.expert_ids, r.ntp, r.topk_weights,
                nullptr, p.out32,
-               r.P, r.k, p.I, p.H, p.I, 0, 0};
+               r.P, r.k, p.I, p.H, p.I, 0, 0, nullptr, 0};
   return launch_stream<Epi::Down>(a, r.E, mb, stream);
 }
 
