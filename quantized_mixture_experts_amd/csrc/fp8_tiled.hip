@@ -34,29 +34,35 @@ namespace qmoe {
 namespace {
 
 constexpr int kTileRows = 128;
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * kWave;
 constexpr int kRowBlocks = kTileRows / 16;  // 8
-constexpr int kColTiles = 4;
+// Eight waves: wave (wr, wc) owns row half wr (four 16-row blocks) and column quarter wc
+// (four 16-column MFMA tiles) of the 128 x 256 tile, two waves per SIMD so that one
+// wave's LDS and barrier waits are covered by the other's MFMAs.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kRowHalves = 2;
+constexpr int kMyBlocks = kRowBlocks / kRowHalves;  // 4 row blocks per wave
+constexpr int kColTiles = 4;                        // MFMA column tiles per wave
+constexpr int kTileCols = 16;                       // column tiles per work-group tile
 constexpr int kStages = 3;
-constexpr int kBlocksPerWave = kRowBlocks / kWaves;  // activation row blocks copied per wave
-constexpr int kScaleRowsPerWave = kTileRows / kWaves;  // activation scale rows per wave
-// Vector memory instructions per wave and step: activation planes, activation scales,
-// weight planes.
-constexpr int kCopiesPerStep = kBlocksPerWave * 2 + 1 + kColTiles * 2;
+constexpr int kScaleRowsPerWave = kTileRows / kWaves;  // 16 activation scale rows per wave
+// Vector memory instructions per wave and step: one activation row block (two planes),
+// the activation scales, two of the sixteen weight column tiles (two planes each).
+constexpr int kCopiesPerStep = 2 + 1 + 2 * 2;
 constexpr int kMaxKBlocks = 64;  // per-wave weight-scale rows held in LDS (K <= 8192)
 
 // LDS layout in 16 B units: per stage the activation planes [block][plane][lane], the
-// activation scales (128 floats), and per wave the weight planes [tile][plane][lane];
-// then per wave the weight block scales for the whole K (two rows for gate/up).
+// activation scales (per wave 64 floats: its 16 rows, then three copies of them, so that
+// every lane of the copy is active and the loop body stays one basic block), and the
+// weight planes [column tile][plane][lane]; then per wave the weight block scales for the
+// whole K (two rows: gate and up for gate_up, the same block twice for down).
 constexpr int kAUnits = kRowBlocks * 2 * kWave;       // 1024
-// activation scales: per wave 64 floats, rows wave*32 .. +32 then a copy of them (every
-// lane of the copy is active, so the loop body stays one basic block)
-constexpr int kAsUnits = kWaves * 64 / 4;             // 64
-constexpr int kBUnits = kWaves * kColTiles * 2 * kWave;  // 2048
+constexpr int kAsUnits = kWaves * 64 / 4;             // 128
+constexpr int kBUnits = kTileCols * 2 * kWave;        // 2048
 constexpr int kStageUnits = kAUnits + kAsUnits + kBUnits;
 constexpr int kBsBase = kStages * kStageUnits;
 constexpr int kSmemUnits = kBsBase + kWaves * 2 * (kMaxKBlocks / 4);
+static_assert(kSmemUnits * 16 <= 160 * 1024, "LDS budget");
 
 enum class FEpi { GateUp, Down };
 
@@ -99,7 +105,8 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
   __shared__ u32x4 smem[kSmemUnits];
 
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wr = wave / (kWaves / kRowHalves), wc = wave % (kWaves / kRowHalves);
   const int col = lane & 15, quad = lane >> 4;
 
   const int total = a.tile_offsets[a.E] * a.col_tiles;
@@ -120,12 +127,15 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
   const int rb_last = (seg1 >> 4) - 1;
   const int K = a.K, KB = K >> 7;
 
-  auto weight_row = [&](int t, int c) {
+  // Weight row of column tile tt (0..15) of the work-group tile, column c: for gate_up,
+  // quarter tt / 4 covers 32 h columns, its tiles 0-1 the gate rows and 2-3 the up rows.
+  auto weight_row = [&](int tt, int c) {
     if constexpr (EPI == FEpi::GateUp) {
-      const int j = ctile * 128 + wave * 32 + (t & 1) * 16 + c;
+      const int t = tt & 3;
+      const int j = ctile * 128 + (tt >> 2) * 32 + (t & 1) * 16 + c;
       return (t < 2) ? j : a.I + j;
     } else {
-      return ctile * 256 + wave * 64 + t * 16 + c;
+      return ctile * 256 + tt * 16 + c;
     }
   };
   // Activation row (of the act matrix) for tile row r; padding rows read row 0.
@@ -138,45 +148,43 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
     }
   };
 
-  // Per-lane source offsets (bytes, 64-bit: the activation and weight matrices can pass
-  // 4 GB).
-  const uint8_t* abase[kBlocksPerWave];
-#pragma unroll
-  for (int i = 0; i < kBlocksPerWave; ++i) {
-    const int rb = min(rb0 + wave * kBlocksPerWave + i, rb_last);
-    abase[i] = a.act + (size_t)act_row(rb * 16 + col) * K + 32 * quad;
+  // Per-lane source pointers (64-bit: the activation and weight matrices can pass 4 GB).
+  // Wave w copies activation row block w, the scales of rows 16w .. 16w+15 and weight
+  // column tiles 4 wc + 2 wr and 4 wc + 2 wr + 1.
+  const uint8_t* abase;
+  {
+    const int rb = min(rb0 + wave, rb_last);
+    abase = a.act + (size_t)act_row(rb * 16 + col) * K + 32 * quad;
   }
   const float* sbase;
   {
     const int r = min(row0 + wave * kScaleRowsPerWave + (lane & (kScaleRowsPerWave - 1)),
-                      rb_last * 16 + 15);  // lanes 32..63 repeat lanes 0..31
+                      rb_last * 16 + 15);  // lanes 16..63 repeat lanes 0..15
     sbase = a.act_scale + (size_t)act_row(r) * KB;
   }
-  const uint8_t* wbase[kColTiles];
+  const int my_tile0 = wc * kColTiles + 2 * wr;
+  const uint8_t* wbase[2];
 #pragma unroll
-  for (int t = 0; t < kColTiles; ++t)
-    wbase[t] = a.w + ((size_t)e * a.N + weight_row(t, col)) * (size_t)K + 32 * quad;
+  for (int i = 0; i < 2; ++i)
+    wbase[i] = a.w + ((size_t)e * a.N + weight_row(my_tile0 + i, col)) * (size_t)K + 32 * quad;
 
   auto stage_at = [&](int st) { return &smem[st * kStageUnits]; };
   auto copy_step = [&](int g, int st) {
     const int kb = min(g, KB - 1);
     u32x4* s = stage_at(st);
 #pragma unroll
-    for (int i = 0; i < kBlocksPerWave; ++i)
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(abase[i] + kb * 128 + 16 * p),
-            QMOE_LDS(s + ((wave * kBlocksPerWave + i) * 2 + p) * kWave), 16, 0, 0);
+    for (int p = 0; p < 2; ++p)
+      __builtin_amdgcn_global_load_lds((const void*)(abase + kb * 128 + 16 * p),
+                                       QMOE_LDS(s + (wave * 2 + p) * kWave), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(sbase + kb), QMOE_LDS(s + kAUnits + wave * 16), 4,
                                      0, 0);
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
         __builtin_amdgcn_global_load_lds(
-            (const void*)(wbase[t] + kb * 128 + 16 * p),
-            QMOE_LDS(s + kAUnits + kAsUnits + ((wave * kColTiles + t) * 2 + p) * kWave), 16, 0, 0);
+            (const void*)(wbase[i] + kb * 128 + 16 * p),
+            QMOE_LDS(s + kAUnits + kAsUnits + ((my_tile0 + i) * 2 + p) * kWave), 16, 0, 0);
   };
 
   // Weight block scales of this wave for the whole K: row 0 for tiles 0-1, row 1 for
@@ -184,15 +192,15 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
   u32x4* bs_lds = &smem[kBsBase + wave * 2 * (kMaxKBlocks / 4)];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int nb = weight_row(2 * h, 0) >> 7;
+    const int nb = weight_row(wc * kColTiles + 2 * h, 0) >> 7;
     const float* src = a.ws + ((size_t)e * (a.N >> 7) + nb) * KB + min(lane, KB - 1);
     __builtin_amdgcn_global_load_lds((const void*)src, QMOE_LDS(bs_lds + h * (kMaxKBlocks / 4)), 4, 0,
                                      0);
   }
 
-  f32x4 acc[kRowBlocks][kColTiles];
+  f32x4 acc[kMyBlocks][kColTiles];
 #pragma unroll
-  for (int m = 0; m < kRowBlocks; ++m)
+  for (int m = 0; m < kMyBlocks; ++m)
 #pragma unroll
     for (int t = 0; t < kColTiles; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -204,6 +212,7 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 
+  const int rbt0 = wr * kMyBlocks;  // first row block of this wave within the tile
   int st = 0;
   for (int g = 0; g < KB; ++g) {
     const u32x4* s = stage_at(st);
@@ -215,27 +224,30 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
     for (int t = 0; t < kColTiles; ++t)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
-        bv[t][p] = s[kAUnits + kAsUnits + ((wave * kColTiles + t) * 2 + p) * kWave + lane];
-    // Row block m's operands are read one block ahead; the stage's last reads (block 7)
-    // are issued before block 6's MFMAs, so the barrier can follow those and the last
+        bv[t][p] = s[kAUnits + kAsUnits + ((wc * kColTiles + t) * 2 + p) * kWave + lane];
+    // Row block m's operands are read one block ahead; the stage's last reads are issued
+    // before the next-to-last block's MFMAs, so the barrier can follow those and the last
     // block's MFMAs cover it. The four MFMA results of block m are promoted into the
     // accumulators while block m+1's MFMAs run (no VALU waits on a fresh MFMA result).
-    u32x4 av[2] = {s[lane], s[kWave + lane]};
-    auto as_row = [&](int r) { return as_f + (r >> 5) * 64 + (r & 31); };
-    f32x4 as4 = *reinterpret_cast<const f32x4*>(as_row(4 * quad));
+    // Scales of tile row r were copied by wave r / 16, to its 64-float slice.
+    auto as_blk = [&](int rbt) {
+      return *reinterpret_cast<const f32x4*>(as_f + rbt * 64 + 4 * quad);
+    };
+    u32x4 av[2] = {s[(rbt0 * 2) * kWave + lane], s[(rbt0 * 2 + 1) * kWave + lane]};
+    f32x4 as4 = as_blk(rbt0);
     f32x4 dprev[kColTiles];
     f32x4 scprev0 = zero4, scprev1 = zero4;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m <= kRowBlocks; ++m) {
+    for (int m = 0; m <= kMyBlocks; ++m) {
       f32x4 dcur[kColTiles];
       u32x4 avn[2] = {av[0], av[1]};
       f32x4 as4n = as4;
-      if (m < kRowBlocks) {
-        if (m + 1 < kRowBlocks) {
-          avn[0] = s[((m + 1) * 2) * kWave + lane];
-          avn[1] = s[((m + 1) * 2 + 1) * kWave + lane];
-          as4n = *reinterpret_cast<const f32x4*>(as_row((m + 1) * 16 + 4 * quad));
+      if (m < kMyBlocks) {
+        if (m + 1 < kMyBlocks) {
+          avn[0] = s[((rbt0 + m + 1) * 2) * kWave + lane];
+          avn[1] = s[((rbt0 + m + 1) * 2 + 1) * kWave + lane];
+          as4n = as_blk(rbt0 + m + 1);
         }
 #pragma unroll
         for (int t = 0; t < kColTiles; ++t) {
@@ -252,13 +264,13 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
             acc[m - 1][t][r] = __builtin_fmaf(dprev[t][r], sc[r], acc[m - 1][t][r]);
         }
       }
-      if (m < kRowBlocks) {
+      if (m < kMyBlocks) {
 #pragma unroll
         for (int t = 0; t < kColTiles; ++t) dprev[t] = dcur[t];
         scprev0 = as4 * bs0;
         scprev1 = as4 * bs1;
       }
-      if (m == kRowBlocks - 2) {
+      if (m == kMyBlocks - 2) {
         // All reads of this stage were issued; once they and the copies of step g+1
         // (younger: the copies of step g+2) have completed, the barrier frees the stage
         // for step g + kStages.
@@ -272,8 +284,8 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
       av[0] = avn[0];
       av[1] = avn[1];
       as4 = as4n;
-      // Keep each block's LDS reads in its own iteration (hoisting them all would take
-      // 128 more registers): a compiler-level memory fence, no instruction.
+      // Keep each block's LDS reads in its own iteration: a compiler-level memory fence,
+      // no instruction.
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -283,12 +295,12 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
 
   if constexpr (EPI == FEpi::GateUp) {
 #pragma unroll
-    for (int m = 0; m < kRowBlocks; ++m) {
-      const int rb = rb0 + m;
+    for (int m = 0; m < kMyBlocks; ++m) {
+      const int rb = rb0 + rbt0 + m;
       if (rb > rb_last) break;
 #pragma unroll
       for (int tp = 0; tp < 2; ++tp) {
-        const int j = ctile * 128 + wave * 32 + tp * 16 + col;
+        const int j = ctile * 128 + wc * 32 + tp * 16 + col;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float gv = acc[m][tp][r], uv = acc[m][tp + 2][r];
@@ -298,8 +310,8 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
     }
   } else {
 #pragma unroll
-    for (int m = 0; m < kRowBlocks; ++m) {
-      const int rb = rb0 + m;
+    for (int m = 0; m < kMyBlocks; ++m) {
+      const int rb = rb0 + rbt0 + m;
       if (rb > rb_last) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -308,7 +320,8 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
         const float wt = a.topk_weights[pair];
         float* yrow = a.y + (size_t)pair * a.N;
 #pragma unroll
-        for (int t = 0; t < kColTiles; ++t) yrow[weight_row(t, col)] = wt * acc[m][t][r];
+        for (int t = 0; t < kColTiles; ++t)
+          yrow[weight_row(wc * kColTiles + t, col)] = wt * acc[m][t][r];
       }
     }
   }
