@@ -10,8 +10,9 @@
 //   1. every work-group builds the full per-expert histogram in LDS (LDS atomics only
 //      count; the order they land in does not matter);
 //   2. an exclusive scan of the padded counts gives every segment offset;
-//   3. work-group e compacts the indices of expert e in ascending order with wave
-//      ballots and a per-iteration prefix over the four waves (deterministic);
+//   3. work-group e compacts the indices of expert e in ascending order: per pass each
+//      thread counts the matches in its run of consecutive indices and a work-group
+//      scan orders the runs (deterministic);
 //   4. it writes its segment's sentinel padding and expert_ids, and a strided share
 //      of the tail past off[E].
 // The result is bit-identical to a stable counting sort on the host.
@@ -24,6 +25,9 @@ namespace {
 
 constexpr int kAlignThreads = 256;
 constexpr int kAlignWaves = kAlignThreads / kWave;
+// Pair ids per thread and pass: all of a pass's loads are in flight at once, so a pass
+// costs one memory latency instead of kRun.
+constexpr int kRun = 16;
 
 // Exclusive scan of v over the work-group; returns this thread's prefix, writes the
 // total to *total. Uses kAlignWaves ints of LDS at `tmp`.
@@ -59,16 +63,22 @@ __global__ void __launch_bounds__(kAlignThreads)
   int32_t* off = lds + E;      // [E + 1]
   int32_t* toff = off + E + 1; // [E + 1] (tiles of tile_m rows per expert)
   int32_t* tmp = toff + E + 1; // [kAlignWaves]
-  __shared__ int32_t wave_cnt[kAlignWaves];
 
   const int tid = threadIdx.x;
   const int me = blockIdx.x;
 
   for (int e = tid; e < E; e += kAlignThreads) cnt[e] = 0;
   __syncthreads();
-  for (int i = tid; i < P; i += kAlignThreads) {
-    int e = ids[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  for (int base = 0; base < P; base += kAlignThreads * kRun) {
+    int v[kRun];
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      const int i = base + j * kAlignThreads + tid;
+      v[j] = i < P ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < kRun; ++j)
+      if ((unsigned)v[j] < (unsigned)E) atomicAdd(&cnt[v[j]], 1);
   }
   __syncthreads();
 
@@ -111,29 +121,33 @@ __global__ void __launch_bounds__(kAlignThreads)
   for (int b = ntp / B + me * kAlignThreads + tid; b < NB; b += E * kAlignThreads)
     expert_ids[b] = -1;
 
-  // Stable compaction of this expert's pair indices.
+  // Stable compaction of this expert's pair indices: per pass each thread takes a run
+  // of kRun consecutive indices, counts its matches, and an exclusive scan over the
+  // work-group places the runs in order. The next pass's ids are loaded before this
+  // pass's scan.
   if (c == 0) return;
-  const int lane = lane_id(), wave = tid / kWave;
-  int running = 0;
-  for (int base = 0; base < P; base += kAlignThreads) {
-    const int i = base + tid;
-    const bool hit = (i < P) && (ids[i] == me);
-    const uint64_t mask = __ballot(hit);
-    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                               __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-    if (lane == 0) wave_cnt[wave] = __popcll(mask);
-    __syncthreads();
-    int before = 0, all = 0;
+  auto load_run = [&](int base, int (&v)[kRun]) {
+    const int i0 = base + tid * kRun;
 #pragma unroll
-    for (int w = 0; w < kAlignWaves; ++w) {
-      int n = wave_cnt[w];
-      if (w < wave) before += n;
-      all += n;
-    }
-    if (hit) sorted_ids[seg0 + running + before + rank] = i;
-    running += all;
-    __syncthreads();
-    if (running == c) break;  // uniform: every thread sees the same running count
+    for (int j = 0; j < kRun; ++j) v[j] = (i0 + j < P) ? ids[i0 + j] : -1;
+  };
+  int cur[kRun], nxt[kRun];
+  load_run(0, cur);
+  int running = 0;
+  for (int base = 0; base < P && running < c; base += kAlignThreads * kRun) {
+    load_run(base + kAlignThreads * kRun, nxt);
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) n += (cur[j] == me);
+    int all;
+    int pos = seg0 + running + block_exclusive_scan(n, tmp, &all);
+    const int i0 = base + tid * kRun;
+#pragma unroll
+    for (int j = 0; j < kRun; ++j)
+      if (cur[j] == me) sorted_ids[pos++] = i0 + j;
+    running += all;  // the same in every thread: the loop condition is uniform
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) cur[j] = nxt[j];
   }
 }
 
