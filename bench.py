@@ -166,7 +166,9 @@ def main():
     if lib.qmoe_timing_end(ms_sum, counts) != 0:
         raise RuntimeError(lib.qmoe_last_error())
     stage_names = ["zero", "align", "gate_up", "requant", "down", "cast"]
-    stage_ms = {n: (ms_sum[i] / counts[i] if counts[i] else None) for i, n in enumerate(stage_names)}
+    # Per forward: a stage can hold more than one launch (align = sort + row gather).
+    stage_ms = {n: (ms_sum[i] / args.steps if counts[i] else None)
+                for i, n in enumerate(stage_names)}
     instrumented_ms = (te1 - te0) * 1e3 / args.steps
 
     # Timed pass: K steps without instrumentation, as one captured graph replayed K times
@@ -207,7 +209,7 @@ def main():
         value, unit = flops / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
 
     # Dominant kernel: gate_up (two thirds of the weight bytes, deep K = hidden size).
-    gu_ms = stage_ms["gate_up"]
+    gu_ms = ms_sum[2] / counts[2]  # per launch (one per forward)
     if hbm_bound:
         per_launch = touched * w13_b
         achieved = per_launch / (gu_ms * 1e-3) / 1e9
