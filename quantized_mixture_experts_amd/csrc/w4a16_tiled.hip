@@ -50,7 +50,11 @@ constexpr int kGroupsPerBlock = 8;                // k groups per 256-deep weigh
 // LDS layout in 16 B units (see the kernel).
 constexpr int kWBase = kStages * kRowBlocks * kWave;
 constexpr int kSBase = kWBase + kWaves * 2 * kColTiles * kWave;
-constexpr int kSmemUnits = kSBase + kWaves * kColTiles * 16;
+constexpr int kEBase = kSBase + kWaves * kColTiles * 16;
+// down: the pair id of each of the tile's rows (256 ints), copied at the start of the
+// item so the epilogue needs one round trip (the routing weights) instead of two per
+// row block.
+constexpr int kSmemUnits = kEBase + kTileRows / 4;
 
 enum class TEpi { GateUp, Down };
 
@@ -112,10 +116,11 @@ __device__ __forceinline__ void drain_acc(f32x4 (&acc)[kRowBlocks][kColTiles]) {
 
 template <TEpi EPI>
 __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
-  // One LDS array (148 KB), in 16 B units:
+  // One LDS array (150 KB), in 16 B units:
   //   activation ring [stage][row block][lane], 16 KB per k group;
   //   per wave, the two half blocks of weight words [half][tile][lane];
   //   per wave, the block's scales [tile][row] (16 B = eight groups per weight row).
+  //   down: the tile rows' pair ids (1 KB).
   // A single object also keeps the compiler from adding conservative waits between the
   // asynchronous copies and the reads of other staging areas.
   __shared__ u32x4 smem[kSmemUnits];
@@ -253,6 +258,14 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // j = 5 its second half (4). The staged words are read into registers one step
   // before use (j = 2: second half of this block; j = 6: first half and scales of the
   // next block). The prologue issues the same sequence for the steps before group 0.
+  if constexpr (EPI == TEpi::Down) {
+    // Pair ids of rows row0 + 64 wave + lane (clamped into the segment; rows past it
+    // are not stored). Older than every copy below, so the waits below cover it.
+    const int r = min(row0 + wave * kWave + lane, rb_last * 16 + 15);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(a.sorted_ids + r),
+        (__attribute__((address_space(3))) void*)&smem[kEBase + wave * (kWave / 4)], 4, 0, 0);
+  }
   copy_group(0, 0);  // step -7 (j = 1)
   copy_half(0, 0);
   copy_scales(0);
@@ -437,19 +450,39 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
       }
     }
   } else {
+    // Pair ids from LDS, then the routing weights of eight row blocks requested before
+    // any is used (two round trips per tile instead of one per row block).
+    const int* ep = reinterpret_cast<const int*>(&smem[kEBase]);
 #pragma unroll
-    for (int m = 0; m < kRowBlocks; ++m) {
-      const int rb = rb0 + m;
-      if (rb > rb_last) break;
-      __builtin_amdgcn_sched_barrier(0);
+    for (int h = 0; h < 2; ++h) {
+      int pair[kRowBlocks / 2][4];
+      float wt[kRowBlocks / 2][4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pair = a.sorted_ids[rb * 16 + 4 * quad + r];
-        if (pair >= a.P) continue;
-        const float wt = a.topk_weights[pair];
-        float* yrow = a.y + (size_t)pair * a.N;
+      for (int mm = 0; mm < kRowBlocks / 2; ++mm) {
+        const u32x4 v =
+            *reinterpret_cast<const u32x4*>(ep + (h * (kRowBlocks / 2) + mm) * 16 + 4 * quad);
 #pragma unroll
-        for (int t = 0; t < kColTiles; ++t) yrow[weight_row(t, col)] = wt * acc[m][t][r];
+        for (int r = 0; r < 4; ++r) pair[mm][r] = (int)v[r];
+      }
+#pragma unroll
+      for (int mm = 0; mm < kRowBlocks / 2; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wt[mm][r] = a.topk_weights[min(pair[mm][r], a.P - 1)];
+#pragma unroll
+      for (int mm = 0; mm < kRowBlocks / 2; ++mm) {
+        const int m = h * (kRowBlocks / 2) + mm;
+        if (rb0 + m <= rb_last) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (pair[mm][r] < a.P) {
+              float* yrow = a.y + (size_t)pair[mm][r] * a.N;
+#pragma unroll
+              for (int t = 0; t < kColTiles; ++t)
+                yrow[weight_row(t, col)] = wt[mm][r] * acc[m][t][r];
+            }
+          }
+        }
       }
     }
   }
