@@ -352,6 +352,17 @@ __global__ void __launch_bounds__(kThreads)
 // the same atomics as whole items. gate_up ranges hold whole items, since SiLU needs the
 // complete sums.
 constexpr int kUnitGroups = 16;  // k groups per unit (= kChunkGroups)
+// Work-group shape of the persistent kernel: kPWaves waves, kPGroupsPerCu work-groups
+// per compute unit (kPWavesPerEu waves per SIMD).
+constexpr int kPWaves = 8;
+constexpr int kPGroupsPerCu = 1;
+constexpr int kPThreads = kPWaves * kWave;
+constexpr int kPWavesPerEu = kPWaves * kPGroupsPerCu / 4;
+constexpr int kPPieces = 1024 / kPThreads;  // 16 B chunk pieces per thread
+static_assert(1024 % kPThreads == 0, "chunk pieces per thread");
+// Groups per batch of a half step: their activation operands and zero-point terms are
+// read from LDS at once and their MFMAs issued back to back before the scale FMAs.
+constexpr int kPBatch = 4;
 // Weight ring depth in 256-deep steps (loads run kRing - 1 steps ahead). Under full load
 // HBM latency is a few microseconds; each step holds 4 KB per wave.
 constexpr int kRing = 4;
@@ -379,8 +390,8 @@ __device__ __forceinline__ int32_t ld_invariant(const int32_t* p, int i) {
 }
 
 template <Epi EPI>
-__global__ void __launch_bounds__(kThreads)
-    __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(kPThreads)
+    __attribute__((amdgpu_waves_per_eu(kPWavesPerEu)))
     w4a16_persist_kernel(StreamArgs a) {
   __shared__ u32x4 a_lds[2][kChunkGroups][kWave];
   // Zero-point term of each group per activation row: the same for every column, so one
@@ -388,15 +399,15 @@ __global__ void __launch_bounds__(kThreads)
   __shared__ float c_lds[2][kChunkGroups][16];
   // Scales of the current block: [wave][tile][step in block][row], 8 bf16 scales each
   // (rows innermost, so the sixteen rows a wave reads at once are 16 B apart).
-  __shared__ u32x4 s_lds[kWavesPerGroup][2][2 * kScaleUnits][16];
+  __shared__ u32x4 s_lds[kPWaves][2][2 * kScaleUnits][16];
 
   // gate_up clears the fp32 output that down accumulates into (down starts after the
   // last gate_up work-group has ended).
   if constexpr (EPI == Epi::GateUp) {
     if (a.zero_out) {
       const int64_t n4 = a.zero_n / 4;
-      for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4;
-           i += (int64_t)gridDim.x * kThreads)
+      for (int64_t i = (int64_t)blockIdx.x * kPThreads + threadIdx.x; i < n4;
+           i += (int64_t)gridDim.x * kPThreads)
         reinterpret_cast<f32x4*>(a.zero_out)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
@@ -441,10 +452,10 @@ __global__ void __launch_bounds__(kThreads)
   // exists (tiles past the end read rows 0..15 of the expert; results unused).
   auto tile_row0 = [&](int cc, int t) {
     if constexpr (EPI == Epi::GateUp) {
-      const int j0 = (cc * kWavesPerGroup + wave) * 16;
+      const int j0 = (cc * kPWaves + wave) * 16;
       return (j0 < a.I ? j0 : 0) + (t ? a.I : 0);
     } else {
-      const int j0 = (cc * kWavesPerGroup + wave) * 32 + 16 * t;
+      const int j0 = (cc * kPWaves + wave) * 32 + 16 * t;
       return j0 < N ? j0 : 0;
     }
   };
@@ -483,19 +494,19 @@ __global__ void __launch_bounds__(kThreads)
     return min(u + min(kScaleUnits - (kc & (kScaleUnits - 1)), upi - kc), ulast);
   };
 
-  u32x4 creg[kChunkPieces];
+  u32x4 creg[kPPieces];
   auto chunk_load = [&](const Unit& d) {
     const u32x4* ablk = reinterpret_cast<const u32x4*>(a.act) + (size_t)d.rb * G * kWave;
 #pragma unroll
-    for (int i = 0; i < kChunkPieces; ++i) {
-      const int idx = threadIdx.x + kThreads * i;  // group-in-chunk * 64 + lane
+    for (int i = 0; i < kPPieces; ++i) {
+      const int idx = threadIdx.x + kPThreads * i;  // group-in-chunk * 64 + lane
       creg[i] = ablk[(size_t)(d.kc * kUnitGroups + idx / kWave) * kWave + idx % kWave];
     }
   };
   auto chunk_store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < kChunkPieces; ++i) {
-      const int g = wave + kWavesPerGroup * i;
+    for (int i = 0; i < kPPieces; ++i) {
+      const int g = wave + kPWaves * i;
       a_lds[buf][g][lane] = creg[i];
       const uint32_t av[4] = {creg[i][0], creg[i][1], creg[i][2], creg[i][3]};
       const f32x4 c = mfma_bf16_16x16x32(av, neg136, zero4);
@@ -504,21 +515,13 @@ __global__ void __launch_bounds__(kThreads)
   };
 
   f32x4 acc[2] = {zero4, zero4};
-  // One 256-deep step: groups 8p..8p+7 of the unit's chunk, scale piece p, in two halves
-  // of four groups. Each half reads its four activation operands and zero-point terms
-  // from LDS at once and issues its eight MFMAs back to back before the scale FMAs, so
-  // neither the LDS latency nor the MFMA latency is paid once per group.
+  // One 256-deep step: groups 8p..8p+7 of the unit's chunk, scale piece p, in batches of
+  // kPBatch groups whose LDS reads and MFMAs are issued together, so neither the LDS
+  // latency nor the MFMA latency is paid once per group.
   auto compute = [&](Stage& s, int buf, int p, int sp) {
     const u32x4 sv[2] = {s_lds[wave][0][sp][col], s_lds[wave][1][sp][col]};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      u32x4 av[4];
-      f32x4 cv[4];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        av[g4] = a_lds[buf][8 * p + 4 * half + g4][lane];
-        cv[g4] = *reinterpret_cast<const f32x4*>(&c_lds[buf][8 * p + 4 * half + g4][4 * quad]);
-      }
       uint32_t wt[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -526,24 +529,35 @@ __global__ void __launch_bounds__(kThreads)
         for (int i = 0; i < 4; ++i) wt[t][i] = s.w[t][half][i];
         transpose4_rows(wt[t]);
       }
-      f32x4 d[2][4];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const uint32_t a4[4] = {av[g4][0], av[g4][1], av[g4][2], av[g4][3]};
+      for (int b0 = 0; b0 < 4; b0 += kPBatch) {
+        u32x4 av[kPBatch];
+        f32x4 cv[kPBatch];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          uint32_t bw[4];
-          int4_to_bf16_biased(wt[t][g4], nib, one28, bw);
-          d[t][g4] = mfma_bf16_16x16x32(a4, bw, cv[g4]);
+        for (int gb = 0; gb < kPBatch; ++gb) {
+          const int gl = 8 * p + 4 * half + b0 + gb;
+          av[gb] = a_lds[buf][gl][lane];
+          cv[gb] = *reinterpret_cast<const f32x4*>(&c_lds[buf][gl][4 * quad]);
         }
-      }
+        f32x4 d[2][kPBatch];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int g = 4 * half + g4;
+        for (int gb = 0; gb < kPBatch; ++gb) {
+          const uint32_t a4[4] = {av[gb][0], av[gb][1], av[gb][2], av[gb][3]};
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint32_t sw = sv[t][g >> 1];
-          acc[t] += ((g & 1) ? bf16_hi(sw) : bf16_lo(sw)) * d[t][g4];
+          for (int t = 0; t < 2; ++t) {
+            uint32_t bw[4];
+            int4_to_bf16_biased(wt[t][b0 + gb], nib, one28, bw);
+            d[t][gb] = mfma_bf16_16x16x32(a4, bw, cv[gb]);
+          }
+        }
+#pragma unroll
+        for (int gb = 0; gb < kPBatch; ++gb) {
+          const int g = 4 * half + b0 + gb;
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const uint32_t sw = sv[t][g >> 1];
+            acc[t] += ((g & 1) ? bf16_hi(sw) : bf16_lo(sw)) * d[t][gb];
+          }
         }
       }
     }
@@ -567,7 +581,7 @@ __global__ void __launch_bounds__(kThreads)
   auto epilogue = [&](const Unit& d) {
     const int rbase = d.rb * kSegRows + 4 * quad;
     if constexpr (EPI == Epi::GateUp) {
-      const int j0 = (d.cc * kWavesPerGroup + wave) * 16;
+      const int j0 = (d.cc * kPWaves + wave) * 16;
       if (j0 < a.I) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -575,7 +589,7 @@ __global__ void __launch_bounds__(kThreads)
               f32_to_bf16(silu_f32(acc[0][r]) * acc[1][r]);
       }
     } else {
-      const int j0 = (d.cc * kWavesPerGroup + wave) * 32;
+      const int j0 = (d.cc * kPWaves + wave) * 32;
       (void)rbase;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -709,14 +723,17 @@ int persistent_grid() {
 
 template <Epi EPI>
 hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream) {
-  const int cols_per_group = (EPI == Epi::GateUp) ? 16 * kWavesPerGroup : 32 * kWavesPerGroup;
+  const bool persist = a.K % 512 == 0;
+  const int waves = persist ? kPWaves : kWavesPerGroup;
+  const int cols_per_group = (EPI == Epi::GateUp) ? 16 * waves : 32 * waves;
   const int extent = (EPI == Epi::GateUp) ? a.I : a.N;
   StreamArgs args = a;
   args.chunks = (extent + cols_per_group - 1) / cols_per_group;
   args.items = E * args.chunks;
   (void)mb;  // one 16-row block per weight pass (larger passes do not fit the registers)
-  if (a.K % 512 == 0) {
-    hipLaunchKernelGGL((w4a16_persist_kernel<EPI>), dim3(persistent_grid()), dim3(kThreads), 0,
+  if (persist) {
+    hipLaunchKernelGGL((w4a16_persist_kernel<EPI>), dim3(persistent_grid() * kPGroupsPerCu),
+                       dim3(kPThreads), 0,
                        stream, args);
   } else {
     hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), dim3(xcd_major_grid(args.items)),
