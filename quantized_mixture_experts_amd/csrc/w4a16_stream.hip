@@ -418,11 +418,24 @@ __global__ void __launch_bounds__(kPThreads)
   // XCD-major numbering: the work-groups of one XCD hold consecutive ranges, so the
   // column chunks of one expert (which share its activation rows) meet in one L2.
   const int wg = (blockIdx.x % kNumXcd) * (nwg / kNumXcd) + blockIdx.x / kNumXcd;
+  // gate_up: work-group k of an XCD (of wpx) takes items xbase + k, xbase + k + wpx,
+  // xbase + k + 2 wpx, ... of its XCD's range: at any time the XCD's work-groups work on
+  // the column chunks of the same one or two row blocks, so each activation chunk is
+  // read once into the XCD's L2 and shared, instead of being read again by one
+  // work-group item after item (by then the weight stream has evicted it). Its units are
+  // numbered locally: unit u is unit u % upi of its item u / upi. down: a contiguous
+  // range of global units.
+  const int wpx = nwg / kNumXcd, kk = wg % wpx;
+  int per_items = 0, xbase = 0;
   int u0, u1;
   if constexpr (EPI == Epi::GateUp) {
-    const int per = (items + nwg - 1) / nwg;
-    u0 = min(items, wg * per) * upi;
-    u1 = min(items, wg * per + per) * upi;
+    per_items = (items + nwg - 1) / nwg;
+    xbase = (wg / wpx) * wpx * per_items;
+    // items of this work-group: the j with xbase + j * wpx + kk < items (a prefix)
+    const int left = items - xbase - kk;
+    const int mine = left <= 0 ? 0 : min(per_items, (left + wpx - 1) / wpx);
+    u0 = 0;
+    u1 = mine * upi;
   } else {
     const int total = items * upi;
     const int per = (total + nwg - 1) / nwg;
@@ -441,8 +454,15 @@ __global__ void __launch_bounds__(kPThreads)
 
   auto desc = [&](int u) {
     Unit d;
-    const int item = u / upi;
-    d.kc = u - item * upi;
+    int item;
+    if constexpr (EPI == Epi::GateUp) {
+      const int j = u / upi;
+      d.kc = u - j * upi;
+      item = xbase + j * wpx + kk;
+    } else {
+      item = u / upi;
+      d.kc = u - item * upi;
+    }
     d.rb = item / a.chunks;
     d.cc = item - d.rb * a.chunks;
     d.e = ld_invariant(a.expert_ids, d.rb);
