@@ -106,7 +106,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     p.off_xs = take(sizeof(uint16_t) * (size_t)p.L * H);
     p.off_h = take(sizeof(uint16_t) * (size_t)p.L * I);
   } else {
-    p.off_h32 = take(sizeof(float) * (size_t)p.L * I);
+    if (!p.tiled) p.off_h32 = take(sizeof(float) * (size_t)p.L * I);  // quantized afterwards
     p.off_hq = take((size_t)p.L * I);
     p.off_hs = take(sizeof(float) * (size_t)p.L * (I / 128));
   }
@@ -376,12 +376,9 @@ qmoe_status moe_fp8_block_forward(const uint8_t* a_q, const float* a_scale, cons
                           region<int32_t>(workspace, p.off_tiles), s);
     });
     if (err != hipSuccess) return hip_fail(err, "align launch");
+    // gate_up writes h already quantized (E4M3 per row and 128 columns).
     err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_fp8_gateup_tiled(prob, r, s); });
     if (err != hipSuccess) return hip_fail(err, "gate_up launch");
-    err = staged(QMOE_STAGE_REQUANT, s, [&] {
-      return launch_fp8_quantize_blocks(prob.h32, p.L, I, 1, 128, prob.hq, prob.hs, s);
-    });
-    if (err != hipSuccess) return hip_fail(err, "h requant launch");
     float* y = region<float>(workspace, p.off_y);
     err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_fp8_down_tiled(prob, r, y, s); });
     if (err != hipSuccess) return hip_fail(err, "down launch");

@@ -20,9 +20,10 @@
 //     ring of three stages; every wave waits on its own copies with vmcnt (the compiler
 //     does not count these) before the stage's barrier, which sits in the middle of the
 //     step so the last MFMAs cover it;
-// gate_up stores SiLU(gate) * up in fp32 by sorted row (the block quantizer turns it into
-// E4M3 per 128 columns); down stores the routing-weighted rows per (token, slot) pair,
-// summed per token by the combine kernel.
+// gate_up quantizes SiLU(gate) * up to E4M3 per row and 128 columns in its epilogue (the
+// tile's 128 h columns are one block; the rows' maxima meet through LDS); down stores
+// the routing-weighted rows per (token, slot) pair, summed per token by the combine
+// kernel.
 #include <algorithm>
 #include <type_traits>
 
@@ -61,7 +62,9 @@ constexpr int kAsUnits = kWaves * 64 / 4;             // 128
 constexpr int kBUnits = kTileCols * 2 * kWave;        // 2048
 constexpr int kStageUnits = kAUnits + kAsUnits + kBUnits;
 constexpr int kBsBase = kStages * kStageUnits;
-constexpr int kSmemUnits = kBsBase + kWaves * 2 * (kMaxKBlocks / 4);
+// gate_up epilogue: per tile row, the four column quarters' partial absolute maxima of h.
+constexpr int kAmaxBase = kBsBase + kWaves * 2 * (kMaxKBlocks / 4);
+constexpr int kSmemUnits = kAmaxBase + kTileRows * 4 / 4;
 static_assert(kSmemUnits * 16 <= 160 * 1024, "LDS budget");
 
 enum class FEpi { GateUp, Down };
@@ -75,7 +78,8 @@ struct Fp8TiledArgs {
   const int32_t* offsets;       // [E + 1]
   const int32_t* tile_offsets;  // [E + 1], 128-row tiles
   const float* topk_weights;    // [P]
-  float* h32;                   // gate_up output [L, I]
+  uint8_t* hq;                  // gate_up output [L, I], E4M3
+  float* hs;                    // gate_up output scales [L, I/128]
   float* y;                     // down output [P, N]
   int32_t P, k, E, K, N, I;
   int32_t col_tiles;
@@ -294,17 +298,49 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
   wait_vmcnt<0>();
 
   if constexpr (EPI == FEpi::GateUp) {
+    // h = SiLU(gate) * up in fp32, then the E4M3 quantization of every row's block of
+    // 128 h columns (the tile's columns are exactly one such block) with the block
+    // quantizer's arithmetic: s = max(absmax, 1e-10) / 448, q = e4m3(clamp(h / s)).
+    float hv[kMyBlocks][2][4];
+#pragma unroll
+    for (int m = 0; m < kMyBlocks; ++m)
+#pragma unroll
+      for (int tp = 0; tp < 2; ++tp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          hv[m][tp][r] = silu_f32_accurate(acc[m][tp][r]) * acc[m][tp + 2][r];
+    // Row maxima: over this lane's two columns, the 16 lanes of its row quarter, then the
+    // four column quarters (waves) through LDS.
+    float* amax_lds = reinterpret_cast<float*>(&smem[kAmaxBase]);
+#pragma unroll
+    for (int m = 0; m < kMyBlocks; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = fmaxf(fabsf(hv[m][0][r]), fabsf(hv[m][1][r]));
+#pragma unroll
+        for (int d = 8; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+        if (col == 0) amax_lds[((rbt0 + m) * 16 + 4 * quad + r) * 4 + wc] = v;
+      }
+    __syncthreads();
+    const int nblk = a.I >> 7;
 #pragma unroll
     for (int m = 0; m < kMyBlocks; ++m) {
       const int rb = rb0 + rbt0 + m;
       if (rb > rb_last) break;
 #pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        const int j = ctile * 128 + wc * 32 + tp * 16 + col;
+      for (int r = 0; r < 4; ++r) {
+        const int row = rb * 16 + 4 * quad + r;
+        const f32x4 am =
+            *reinterpret_cast<const f32x4*>(&amax_lds[((rbt0 + m) * 16 + 4 * quad + r) * 4]);
+        const float amax = fmaxf(fmaxf(am[0], am[1]), fmaxf(am[2], am[3]));
+        const float sc = fmaxf(amax, 1e-10f) / 448.0f;
+        if (wc == 0 && col == 0) a.hs[(size_t)row * nblk + ctile] = sc;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float gv = acc[m][tp][r], uv = acc[m][tp + 2][r];
-          a.h32[(size_t)(rb * 16 + 4 * quad + r) * a.I + j] = silu_f32_accurate(gv) * uv;
+        for (int tp = 0; tp < 2; ++tp) {
+          const int j = ctile * 128 + wc * 32 + tp * 16 + col;
+          const float t = fminf(fmaxf(hv[m][tp][r] / sc, -448.0f), 448.0f);
+          a.hq[(size_t)row * a.I + j] =
+              (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0u, false) & 0xFFu);
         }
       }
     }
@@ -347,14 +383,14 @@ int32_t fp8_tiled_rows() { return kTileRows; }
 
 hipError_t launch_fp8_gateup_tiled(const Fp8Problem& p, const Routing& r, hipStream_t stream) {
   Fp8TiledArgs a{p.a_q, p.a_scale, p.w13, p.s13, r.sorted_ids, r.offsets, r.tile_offsets,
-                 r.topk_weights, p.h32, nullptr, r.P, r.k, r.E, p.H, 2 * p.I, p.I, p.I / 128};
+                 r.topk_weights, p.hq, p.hs, nullptr, r.P, r.k, r.E, p.H, 2 * p.I, p.I, p.I / 128};
   return launch_fp8_tiled<FEpi::GateUp>(a, (int64_t)r.P / kTileRows + r.E, stream);
 }
 
 hipError_t launch_fp8_down_tiled(const Fp8Problem& p, const Routing& r, float* y,
                                  hipStream_t stream) {
   Fp8TiledArgs a{p.hq, p.hs, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets,
-                 r.topk_weights, nullptr, y, r.P, r.k, r.E, p.I, p.H, p.I, p.H / 256};
+                 r.topk_weights, nullptr, nullptr, y, r.P, r.k, r.E, p.I, p.H, p.I, p.H / 256};
   return launch_fp8_tiled<FEpi::Down>(a, (int64_t)r.P / kTileRows + r.E, stream);
 }
 

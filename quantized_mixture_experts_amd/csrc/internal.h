@@ -88,7 +88,8 @@ hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t 
 
 // Prefill profile (block FP8): 128-row tiles; needs H % 256 == 0 and I % 128 == 0 and
 // at most 64 k blocks; align must have produced tile_offsets for fp8_tiled_rows() rows.
-// gate_up writes h32 (quantized by launch_fp8_quantize_blocks), down writes y[P, H].
+// gate_up writes hq and hs (h quantized to E4M3 per row and 128 columns), down writes
+// y[P, H].
 bool fp8_tiled_supported(int32_t H, int32_t I);
 int32_t fp8_tiled_rows();
 hipError_t launch_fp8_gateup_tiled(const Fp8Problem& p, const Routing& r, hipStream_t stream);
