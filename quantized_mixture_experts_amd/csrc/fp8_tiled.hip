@@ -345,19 +345,29 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
       }
     }
   } else {
+    // Every pair id of this wave's rows, then every routing weight, requested before any
+    // is used (two round trips per tile instead of two per row block).
+    int pair[kMyBlocks][4];
+    float wt[kMyBlocks][4];
+#pragma unroll
+    for (int m = 0; m < kMyBlocks; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        pair[m][r] = a.sorted_ids[min(rb0 + rbt0 + m, rb_last) * 16 + 4 * quad + r];
+#pragma unroll
+    for (int m = 0; m < kMyBlocks; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wt[m][r] = a.topk_weights[min(pair[m][r], a.P - 1)];
 #pragma unroll
     for (int m = 0; m < kMyBlocks; ++m) {
-      const int rb = rb0 + rbt0 + m;
-      if (rb > rb_last) break;
+      if (rb0 + rbt0 + m > rb_last) break;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int pair = a.sorted_ids[rb * 16 + 4 * quad + r];
-        if (pair >= a.P) continue;
-        const float wt = a.topk_weights[pair];
-        float* yrow = a.y + (size_t)pair * a.N;
+        if (pair[m][r] >= a.P) continue;
+        float* yrow = a.y + (size_t)pair[m][r] * a.N;
 #pragma unroll
         for (int t = 0; t < kColTiles; ++t)
-          yrow[weight_row(wc * kColTiles + t, col)] = wt * acc[m][t][r];
+          yrow[weight_row(wc * kColTiles + t, col)] = wt[m][r] * acc[m][t][r];
       }
     }
   }
