@@ -9,23 +9,23 @@
 // kernel is laid out for the matrix cores.
 //
 // gfx950 mapping. A work-group owns one (256-row tile of an expert segment, 256 weight
-// rows) output tile; its four waves each own all 256 rows and 64 weight rows (four
-// 16-column MFMA tiles), so every weight element is dequantized exactly once per tile
-// and reused for 16 row blocks:
+// rows) output tile over eight waves, two per SIMD; each wave owns all 256 rows and 32
+// weight rows (two 16-column MFMA tiles), so every weight element is dequantized exactly
+// once per tile and reused for 16 row blocks:
 //   * activation rows (bf16, tiled layout: the operand of one 16-row block and k group
-//     is 1 KB contiguous) go global -> LDS through global_load_lds_dwordx4 into a ring of
-//     four 16 KB stages, three k groups ahead; each wave copies four of the sixteen
-//     blocks of a stage and waits on its own copies with vmcnt before the stage's
-//     barrier (the compiler does not track these asynchronous LDS writes);
-//   * each lane loads 2 x 16 B of its weight row per 256 k (a whole 128 B line per row)
-//     plus the 16 B of that row's eight group scales, one block ahead in registers; a
-//     4x4 permlane transpose regroups the words so that every lane quarter holds its
-//     k slice of each group (the B operand layout of v_mfma_f32_16x16x32_bf16);
+//     is 1 KB contiguous), weight words and block scales move global -> LDS by buffer
+//     loads into LDS: activations through a ring of seven 16 KB stages, six k groups
+//     ahead; weight words and scales through per-wave staging one 256-deep block ahead.
+//     Completion is tracked with counted vmcnt waits (the compiler does not track these
+//     asynchronous LDS writes), and one barrier per k group publishes a stage;
+//   * staged weight words are read into registers, and a 4x4 permlane transpose
+//     regroups them so that every lane quarter holds its k slice of each group (the B
+//     operand layout of v_mfma_f32_16x16x32_bf16);
 //   * dequantization folds the scale into the operand: OR-ing a code into fp16 1024.0
 //     gives 1024 + code exactly, v_fma_mix_f32 forms (1024 + code) * s - 1032 * s =
 //     (code - 8) * s exactly in fp32 (1032 * s is exact for a bf16 s), and
-//     v_cvt_pk_bf16_f32 rounds it to the bf16 operand; 16 M tiles share each operand;
-//   * 64 accumulator tiles (256 fp32 per lane) per wave.
+//     v_cvt_pk_bf16_f32 rounds it to the bf16 operand; 16 row blocks share each operand;
+//   * 32 accumulator tiles (128 fp32 per lane) per wave.
 // gate_up stores h = SiLU(gate) * up (bf16, tiled layout); down stores the routing-
 // weighted rows per (token, slot) pair in fp32 and a combine kernel sums the top-k rows
 // of every token, so the prefill output does not depend on atomic ordering.
@@ -40,10 +40,11 @@ namespace qmoe {
 namespace {
 
 constexpr int kTileRows = 256;                    // rows per work-group tile
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kRowBlocks = kTileRows / 16;        // 16-row MFMA tiles per wave
-constexpr int kColTiles = 4;                      // 16-column MFMA tiles per wave
+constexpr int kColTiles = 2;                      // 16-column MFMA tiles per wave
+constexpr int kPieces = kColTiles * 4;            // dequantized operand words per lane and group
 constexpr int kStages = 7;                        // LDS ring of activation k groups
 constexpr int kCopiesPerWave = kRowBlocks / kWaves;  // 1 KB copies per wave and group
 constexpr int kGroupsPerBlock = 8;                // k groups per 256-deep weight block
@@ -55,6 +56,8 @@ constexpr int kEBase = kSBase + kWaves * kColTiles * 16;
 // item so the epilogue needs one round trip (the routing weights) instead of two per
 // row block.
 constexpr int kSmemUnits = kEBase + kTileRows / 4;
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle, no index).
+constexpr int kRsrcWord3 = 0x00020000;
 
 enum class TEpi { GateUp, Down };
 
@@ -70,6 +73,7 @@ struct TiledArgs {
   float* y;                     // down output [P, N] per routed pair
   int32_t P, E, K, N, I;
   int32_t col_tiles;            // output column tiles per row tile
+  uint32_t act_bytes;           // size of act (L * K * 2 < 2^32, host-checked)
 };
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -111,7 +115,8 @@ __device__ __forceinline__ void drain_acc(f32x4 (&acc)[kRowBlocks][kColTiles]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
   for (int m = 0; m < kRowBlocks; ++m)
-    asm volatile("" : "+a"(acc[m][0]), "+a"(acc[m][1]), "+a"(acc[m][2]), "+a"(acc[m][3]));
+#pragma unroll
+    for (int t = 0; t < kColTiles; ++t) asm volatile("" : "+a"(acc[m][t]));
 }
 
 template <TEpi EPI>
@@ -131,7 +136,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   auto s_at = [&](int wv, int t) { return &smem[kSBase + (wv * kColTiles + t) * 16]; };
 
   const int lane = lane_id();
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = lane & 15, quad = lane >> 4;
 
   // XCD-aware item order over the real tile count: XCD x takes a contiguous range.
@@ -152,10 +157,10 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // Weight row of tile t for column c of this wave.
   auto weight_row = [&](int t, int c) {
     if constexpr (EPI == TEpi::GateUp) {
-      const int j = ctile * 128 + wave * 32 + (t & 1) * 16 + c;
-      return (t < 2) ? j : a.I + j;
+      const int j = ctile * 128 + wave * (kColTiles * 8) + (t % (kColTiles / 2)) * 16 + c;
+      return (t < kColTiles / 2) ? j : a.I + j;
     } else {
-      return ctile * 256 + wave * 64 + t * 16 + c;
+      return ctile * 256 + wave * (kColTiles * 16) + t * 16 + c;
     }
   };
   // Per-lane byte offsets stay 32-bit (host-checked) on top of uniform bases. Weight
@@ -170,8 +175,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
     soff[t] = (uint32_t)weight_row(t, lane >> 2) * (uint32_t)(KG * 2) + 4u * (lane & 3);
   }
 
-  // Activation copies of this wave: row blocks wave*4 .. wave*4+3 of the tile.
-  const uint8_t* abase = reinterpret_cast<const uint8_t*>(a.act);
+  // Activation copies of this wave: row blocks wave*kCopiesPerWave + i of the tile.
   uint32_t aoff[kCopiesPerWave];
 #pragma unroll
   for (int i = 0; i < kCopiesPerWave; ++i) {
@@ -182,32 +186,44 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // All global reads of the loop are asynchronous LDS copies whose completion this code
   // tracks itself with vmcnt (the compiler does not count them). They are issued in a
   // fixed order and never skipped: past the end they repeat the last group or block, so
-  // the counts below hold at the tail as well. Per 8-group block and wave: four
+  // the counts below hold at the tail as well. Per 8-group block and wave: kCopiesPerWave
   // activation copies every step, the next block's first half of weight words and its
-  // scales at j = 1 (8), its second half at j = 5 (4).
+  // scales at j = 1 (2 kColTiles), its second half at j = 5 (kColTiles).
+  // Copies are buffer loads into LDS: the loop-invariant per-lane offset is the vector
+  // offset and the step's byte offset the scalar one, so a copy needs no vector address
+  // arithmetic. Reads past a buffer's size return zeros.
+  const __amdgpu_buffer_rsrc_t ars =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)wbase, (short)0, (int)((uint32_t)a.N * (uint32_t)(K >> 1)), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)sbase, (short)0, (int)((uint32_t)a.N * (uint32_t)(KG * 2)), kRsrcWord3);
+  auto copy_act = [&](int g, int st, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        ars, (__attribute__((address_space(3))) void*)a_at(st, wave * kCopiesPerWave + i), 16,
+        (int)aoff[i], min(g, nsteps - 1) * 1024, 0, 0);
+  };
+  auto copy_words = [&](int kb, int hf, int t) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        wrs, (__attribute__((address_space(3))) void*)w_at(wave, hf, t), 16, (int)woff[t],
+        min(kb, nblocks - 1) * 128 + 64 * hf, 0, 0);
+  };
+  auto copy_scale = [&](int kb, int t) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        srs, (__attribute__((address_space(3))) void*)s_at(wave, t), 4, (int)soff[t],
+        min(kb, nblocks - 1) * 16, 0, 0);
+  };
   auto copy_group = [&](int g, int st) {
-    const uint32_t src = (uint32_t)min(g, nsteps - 1) * 1024u;
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(abase + (aoff[i] + src)),
-          (__attribute__((address_space(3))) void*)a_at(st, wave * kCopiesPerWave + i), 16, 0, 0);
+    for (int i = 0; i < kCopiesPerWave; ++i) copy_act(g, st, i);
   };
   auto copy_half = [&](int kb, int hf) {
-    const uint32_t o = (uint32_t)min(kb, nblocks - 1) * 128u + 64u * hf;
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(wbase + (woff[t] + o)),
-          (__attribute__((address_space(3))) void*)w_at(wave, hf, t), 16, 0, 0);
+    for (int t = 0; t < kColTiles; ++t) copy_words(kb, hf, t);
   };
   auto copy_scales = [&](int kb) {
-    const uint32_t o = (uint32_t)min(kb, nblocks - 1) * 16u;
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t)
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(sbase + (soff[t] + o)),
-          (__attribute__((address_space(3))) void*)s_at(wave, t), 4, 0, 0);
+    for (int t = 0; t < kColTiles; ++t) copy_scale(kb, t);
   };
 
   f32x4 acc[kRowBlocks][kColTiles];
@@ -252,15 +268,17 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   };
   auto next_stage = [](int s_) { return s_ == kStages - 1 ? 0 : s_ + 1; };
 
-  // Issue schedule (per wave). Step g issues, right after its barrier, the copy of
-  // activation group g + kStages into the stage group g has just released; at block
-  // position j = 1 the next block's first half of weight words and its scales (8), at
-  // j = 5 its second half (4). The staged words are read into registers one step
-  // before use (j = 2: second half of this block; j = 6: first half and scales of the
-  // next block). The prologue issues the same sequence for the steps before group 0.
-  if constexpr (EPI == TEpi::Down) {
+  // Issue schedule (per wave). Step g issues, after its barrier (one copy per MFMA of the
+  // last three row blocks), the copies of activation group g + kStages into the stage
+  // group g has just released (kCopiesPerWave); at block position j = 1 the next block's
+  // first half of weight words and its scales (2 kColTiles), at j = 5 its second half
+  // (kColTiles). The staged words are read into registers one step before use (j = 2:
+  // second half of this block; j = 6: first half and scales of the next block). The
+  // prologue issues the same sequence for the steps before group 0.
+  if (EPI == TEpi::Down && wave < kTileRows / kWave) {
     // Pair ids of rows row0 + 64 wave + lane (clamped into the segment; rows past it
-    // are not stored). Older than every copy below, so the waits below cover it.
+    // are not stored), by the first four waves. Older than every copy below, so the
+    // waits below cover it.
     const int r = min(row0 + wave * kWave + lane, rb_last * 16 + 15);
     __builtin_amdgcn_global_load_lds(
         (const void*)(a.sorted_ids + r),
@@ -289,6 +307,12 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // ahead, into two register sets: the compiler waits for all outstanding LDS reads
   // (lgkmcnt(0)) before the first use of each group, and by then they have landed.
   u32x4 ra[2][4];
+  // An operand set stays allocated until it is refilled: otherwise the register allocator
+  // hands a just-read operand register to the next dequantized weights, and every such
+  // write needs a wait state after the MFMA that read it.
+  auto keep_live = [](const u32x4 (&v)[4]) {
+    asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]));
+  };
   {
     const u32x4* as0 = a_at(0, 0) + lane;
 #pragma unroll
@@ -298,7 +322,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
 #pragma unroll
   for (int t = 0; t < kColTiles; ++t) scur[t] = snext[t];
 #pragma unroll
-  for (int p = 0; p < 16; ++p) {
+  for (int p = 0; p < kPieces; ++p) {
     const int t = p >> 2, i = p & 3;
     const float sc = bf16_lo(scur[t][0]);
     const uint32_t pr = ((tw[t][0] >> (4 * i)) & mask) | magic;
@@ -338,40 +362,59 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
       // first MFMA.
 #pragma unroll
       for (int m = 0; m < kRowBlocks; ++m) {
-        const int t = m >> 2, i = m & 3;
         const int q = m >> 2, r = m & 3;
+        // Row blocks 2p and 2p + 1 carry piece p of the next group's operands: its scale
+        // and codes, the two products, then the conversion (behind the next piece's mask,
+        // since a bf16 conversion right behind an MFMA needs a wait state).
+        const int p = m >> 1, odd = m & 1;
+        const int t = p >> 2, i = p & 3;
         const u32x4& a0 = ra[q & 1][r];
+        // This step's copies, issued after the barrier one per MFMA of row blocks
+        // kRowBlocks-3 .. kRowBlocks-1 (a run of copies stalls the wave), in a fixed
+        // order: activation group g + kStages, then at j = 1 the next block's first half
+        // of weight words and its scales, at j = 5 its second half.
+        auto copy_slot = [&](int k) {
+          if (m < kRowBlocks - 3) return;
+          const int c = (m - (kRowBlocks - 3)) * kColTiles + k;
+          if (c < kCopiesPerWave) {
+            copy_act(g + kStages, st, c);
+          } else if (c < kCopiesPerWave + kColTiles) {
+            if (j == 1) copy_words(kb + 1, 0, c - kCopiesPerWave);
+            else if (j == 5) copy_words(kb + 1, 1, c - kCopiesPerWave);
+          } else if (c < kCopiesPerWave + 2 * kColTiles) {
+            if (j == 1) copy_scale(kb + 1, c - kCopiesPerWave - kColTiles);
+          }
+        };
         mfma_acc(acc[m][0], a0, bc[0]);
         __builtin_amdgcn_sched_barrier(0);
+        copy_slot(0);
         // After the group's first MFMA, so that the wait before it does not cover them.
         if (r == 0 && q < 3) {
+          keep_live(ra[(q + 1) & 1]);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) ra[(q + 1) & 1][rr] = as[(4 * (q + 1) + rr) * kWave];
         }
-        if (i == 0) {
-          const uint32_t sw = scur[t][jn >> 1];
-          sc = (jn & 1) ? bf16_hi(sw) : bf16_lo(sw);
-          cc = -1032.0f * sc;
+        uint32_t shv = 0;
+        if (!odd) {
+          if (i == 0) {
+            const uint32_t sw = scur[t][jn >> 1];
+            sc = (jn & 1) ? bf16_hi(sw) : bf16_lo(sw);
+            cc = -1032.0f * sc;
+          }
+          if (m == 0) pr = (tw[0][jn & 3] & mask) | magic;
+        } else if (p + 1 < kPieces) {
+          shv = tw[(p + 1) >> 2][jn & 3] >> (4 * ((p + 1) & 3));
         }
-        pr = ((tw[t][jn & 3] >> (4 * i)) & mask) | magic;
         __builtin_amdgcn_sched_barrier(0);
         mfma_acc(acc[m][1], a0, bc[1]);
         __builtin_amdgcn_sched_barrier(0);
-        {
+        copy_slot(1);
+        if (!odd) {
           const f16x2 hv = __builtin_bit_cast(f16x2, pr);
           flo = __builtin_fmaf((float)hv.x, sc, cc);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_acc(acc[m][2], a0, bc[2]);
-        __builtin_amdgcn_sched_barrier(0);
-        {
-          const f16x2 hv = __builtin_bit_cast(f16x2, pr);
           fhi = __builtin_fmaf((float)hv.y, sc, cc);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_acc(acc[m][3], a0, bc[3]);
-        __builtin_amdgcn_sched_barrier(0);
-        {
+        } else {
+          if (p + 1 < kPieces) pr = (shv & mask) | magic;
           const f32x2 f = {flo, fhi};
           bn[t][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
         }
@@ -391,26 +434,20 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
           wait_vmcnt<kLater + kPrev>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
-          copy_group(g + kStages, st);
-          if (j == 1) {
-            copy_half(kb + 1, 0);
-            copy_scales(kb + 1);
-          } else if (j == 5) {
-            copy_half(kb + 1, 1);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          // (This step's copies follow, spread over the next MFMAs.)
           if (j == 2) {
             // Second half of this block (copied at j = 5 of the last block): younger
-            // are five steps of activation copies and the next first half and scales.
-            wait_vmcnt<5 * kCopiesPerWave + 2 * kColTiles>();
+            // are four steps of activation copies and the next first half and scales.
+            wait_vmcnt<4 * kCopiesPerWave + 2 * kColTiles>();
             read_staged_half(1);
           } else if (j == 6) {
-            // Next block's first half and scales (copied at j = 1): younger are five
+            // Next block's first half and scales (copied at j = 1): younger are four
             // steps of activation copies and the next second half.
-            wait_vmcnt<5 * kCopiesPerWave + kColTiles>();
+            wait_vmcnt<4 * kCopiesPerWave + kColTiles>();
             read_staged_half(0);
             read_staged_scales();
           }
+          keep_live(ra[0]);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) ra[0][rr] = asn[rr * kWave];
           __builtin_amdgcn_sched_barrier(0);
@@ -440,11 +477,11 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
       if (rb > rb_last) break;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int tp = 0; tp < 2; ++tp) {
-        const int j = ctile * 128 + wave * 32 + tp * 16 + col;
+      for (int tp = 0; tp < kColTiles / 2; ++tp) {
+        const int j = ctile * 128 + wave * (kColTiles * 8) + tp * 16 + col;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float gv = acc[m][tp][r], uv = acc[m][tp + 2][r];
+          const float gv = acc[m][tp][r], uv = acc[m][tp + kColTiles / 2][r];
           a.h[tiled_offset(rb * 16 + 4 * quad + r, j, a.I)] = f32_to_bf16(silu_f32(gv) * uv);
         }
       }
@@ -551,14 +588,16 @@ int32_t w4a16_tiled_rows() { return kTileRows; }
 
 hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, hipStream_t stream) {
   TiledArgs a{p.xs, p.w13, p.s13, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
-              p.h, nullptr, r.P, r.E, p.H, 2 * p.I, p.I, p.I / 128};
+              p.h, nullptr, r.P, r.E, p.H, 2 * p.I, p.I, p.I / 128,
+              (uint32_t)((uint64_t)r.L * p.H * 2u)};
   return launch_tiled<TEpi::GateUp>(a, (int64_t)r.P / kTileRows + r.E, stream);
 }
 
 hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, float* y,
                                    hipStream_t stream) {
   TiledArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
-              nullptr, y, r.P, r.E, p.I, p.H, p.I, p.H / 256};
+              nullptr, y, r.P, r.E, p.I, p.H, p.I, p.H / 256,
+              (uint32_t)((uint64_t)r.L * p.I * 2u)};
   return launch_tiled<TEpi::Down>(a, (int64_t)r.P / kTileRows + r.E, stream);
 }
 
