@@ -397,9 +397,10 @@ __global__ void __launch_bounds__(kPThreads)
   // Zero-point term of each group per activation row: the same for every column, so one
   // float per row (read by the four lanes of a row quarter at once).
   __shared__ float c_lds[2][kChunkGroups][16];
-  // Scales of the current block: [wave][tile][step in block][row], 8 bf16 scales each
-  // (rows innermost, so the sixteen rows a wave reads at once are 16 B apart).
-  __shared__ u32x4 s_lds[kPWaves][2][2 * kScaleUnits][16];
+  // Scales of the current block as fp32, converted once when the block is staged:
+  // [wave][tile][step in block][half step][row], four groups each (rows innermost, so
+  // the sixteen rows a wave reads at once are 16 B apart).
+  __shared__ f32x4 s_lds[kPWaves][2][2 * kScaleUnits][2][16];
 
   // gate_up clears the fp32 output that down accumulates into (down starts after the
   // last gate_up work-group has ended).
@@ -507,7 +508,13 @@ __global__ void __launch_bounds__(kPThreads)
   };
   auto scale_block_store = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_lds[wave][i >> 1][s_piece][8 * (i & 1) + s_row] = snext[i];
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = snext[i];
+      s_lds[wave][i >> 1][s_piece][0][8 * (i & 1) + s_row] =
+          f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+      s_lds[wave][i >> 1][s_piece][1][8 * (i & 1) + s_row] =
+          f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+    }
   };
   // First unit of the block after unit u's (the next item's first unit at an item end).
   auto next_block = [&](int u, int kc) {
@@ -539,9 +546,11 @@ __global__ void __launch_bounds__(kPThreads)
   // kPBatch groups whose LDS reads and MFMAs are issued together, so neither the LDS
   // latency nor the MFMA latency is paid once per group.
   auto compute = [&](Stage& s, int buf, int p, int sp) {
-    const u32x4 sv[2] = {s_lds[wave][0][sp][col], s_lds[wave][1][sp][col]};
+    f32x4 sv[2][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
+      sv[0][half] = s_lds[wave][0][sp][half][col];
+      sv[1][half] = s_lds[wave][1][sp][half][col];
       uint32_t wt[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -575,8 +584,7 @@ __global__ void __launch_bounds__(kPThreads)
           const int g = 4 * half + b0 + gb;
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const uint32_t sw = sv[t][g >> 1];
-            acc[t] += ((g & 1) ? bf16_hi(sw) : bf16_lo(sw)) * d[t][gb];
+            acc[t] += sv[t][half][g & 3] * d[t][gb];
           }
         }
       }
