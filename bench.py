@@ -7,7 +7,7 @@ steps are plain calls without instrumentation (--launch graph: replays of one ca
 graph); the per-kernel times come from a separate pass of K steps with HIP events recorded
 around every kernel on its launch stream.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|fp8|full384|tiny]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|fp8|full384|tiny|router]
 
 Prints one JSON line. The default workload is the decode layer (32 tokens, hidden 7168,
 intermediate 2048, 48 local experts, top-8, INT4 group-32 weights); its value is the
@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "fp8", "full384", "tiny"])
+                    choices=["decode", "prefill", "fp8", "full384", "tiny", "router"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
                     help="how the timed steps are issued: eager library calls (default), or "
@@ -111,6 +111,10 @@ def main():
         __graft_entry__.build()
     lib = binding.load()
     import ctypes
+
+    if args.workload == "router":
+        bench_router(args, np, torch, binding, inputs)
+        return
 
     cfg = inputs.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
@@ -270,6 +274,71 @@ def main():
         "cpu_baseline": cpu,
         "device": torch.cuda.get_device_name(0),
         "input_gen_s": round(gen_s, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_router(args, np, torch, binding, inputs):
+    """Router step before align: softmax -> top-8 -> renormalization over the 384 experts of
+    the full layer for a prefill batch of 8192 tokens, ids mapped to one GPU's share of
+    48 experts (expert parallelism over 8). Bound: HBM (logits read, ids and weights
+    written once); timed with HIP events on the launch stream."""
+    T, E, k, share = 8192, 384, 8, 48
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rng = np.random.default_rng(97)
+    logits_h = inputs.router_logits(rng, T, E, "zipf")
+    emap_h = np.full(E, -1, np.int32)
+    emap_h[share:2 * share] = np.arange(share, dtype=np.int32)
+    logits = torch.from_numpy(logits_h).to(dev)
+    emap = torch.from_numpy(emap_h).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return binding.moe_topk_softmax(logits, k, True, emap, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    nbytes = T * E * 4 + T * k * 8
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 512
+        tc = time.perf_counter()
+        oracle.topk_softmax(logits_h[:rows], k, True, emap_h)
+        cpu_s = time.perf_counter() - tc
+        full_s = cpu_s * T / rows
+        cpu = {"value": round(nbytes / full_s / 1e9, 6), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{rows} of {T} token rows, {cpu_s:.3f} s on 1 thread, scaled by "
+                         f"{T}/{rows}"}
+    line = {
+        "metric": "router GB/s (logits read, ids and weights written), % of HBM roofline",
+        "value": round(achieved, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "wall_ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Zipf router logits)",
+        "config": {"workload": f"router: {T} tokens, {E} experts, top-{k}, renormalized, "
+                               f"ids mapped to {share} local experts",
+                   "tokens": T, "experts": E, "top_k": k, "local_experts": share},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "kernel": "router/topk_softmax", "kernel_ms": round(ms, 5),
+                     "algorithmic_per_launch": nbytes, "traffic": None},
+        "cpu_baseline": cpu,
+        "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(line), flush=True)
 

@@ -80,6 +80,34 @@ const char* qmoe_status_string(int32_t status);
 const char* qmoe_last_error(void);
 
 /*
+ * moe_topk_softmax - the router step before align: for each token, the k experts with
+ * the largest router logits and their softmax weights ([CHORD] "Two kernel families":
+ * the indexed kernels consume the framework's routing, these ids and weights; "vLLM
+ * integration": under expert parallelism, the EP8 profiles, a GPU holds a share of the
+ * experts).
+ *
+ *   logits        [T, E] fp32, finite.
+ *   k             1 <= k <= E <= QMOE_MAX_EXPERTS.
+ *   renormalize   nonzero: the k weights sum to 1; zero: they are the selected experts'
+ *                 full softmax probabilities.
+ *   expert_map    [E] int32 or NULL. Local id of each (global) expert, or -1 for an
+ *                 expert held by another GPU; moe_align and the forwards drop slots whose
+ *                 id is outside [0, E_local), so the outputs pass to them unchanged.
+ *                 NULL: ids stay global.
+ *   topk_ids      [T, k] int32 out: slot s holds the expert with the (s+1)-th largest
+ *                 logit (equal logits: the lower expert id first; -0 equals +0), mapped.
+ *   topk_weights  [T, k] fp32 out: exp(l - m) / S, m the token's largest logit and S the
+ *                 sum of exp(l - m) over the k selected experts (renormalize) or over all
+ *                 E experts. Weights of unmapped (-1) slots are kept: they belong to the
+ *                 GPU holding that expert.
+ * Selection compares logits, which orders the experts as their softmax probabilities do
+ * (exp is increasing) without exp's rounding. T = 0 is allowed. 4-byte alignment.
+ */
+qmoe_status moe_topk_softmax(const float* logits, int32_t T, int32_t E, int32_t k,
+                             int32_t renormalize, const int32_t* expert_map, int32_t* topk_ids,
+                             float* topk_weights, void* stream);
+
+/*
  * moe_align - sort routed (token, slot) pairs to experts and pad each expert's
  * segment to a multiple of block_m ([CHORD] "Two kernel families": the indexed
  * family consumes sorted_ids / expert_ids / num_tokens_padded; Figure 3: padding

@@ -30,6 +30,8 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     lib.oracle_moe_align.argtypes = [_P, _I64, _I32, _I32, _P, _I64, _P, _I64, _P, _P]
     lib.oracle_moe_align.restype = ctypes.c_int
+    lib.oracle_topk_softmax.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P]
+    lib.oracle_topk_softmax.restype = ctypes.c_int
     lib.oracle_w4a16_moe.argtypes = [_P] * 7 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
     lib.oracle_w4a16_moe.restype = ctypes.c_int
     lib.oracle_fp8_moe.argtypes = [_P] * 8 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
@@ -62,6 +64,22 @@ def align_capacity(P: int, E: int, B: int):
     """Sorted-id capacity L = P + E*(B-1) and block capacity NB = ceil(L/B)."""
     L = P + E * (B - 1)
     return L, (L + B - 1) // B
+
+
+def topk_softmax(logits, k: int, renormalize: bool = True, expert_map=None):
+    """Router: softmax over each token's fp32 logits [T,E], its k largest (equal logits:
+    lower id first), weights renormalized over the k or not; ids mapped through
+    expert_map [E] when given. Returns (ids int32 [T,k], weights float64 [T,k])."""
+    lg = _c(logits, np.float32)
+    T, E = lg.shape
+    mp = None if expert_map is None else _c(expert_map, np.int32)
+    ids = np.empty((T, k), np.int32)
+    wts = np.empty((T, k), np.float64)
+    rc = _load().oracle_topk_softmax(_ptr(lg), T, E, k, 1 if renormalize else 0,
+                                     None if mp is None else _ptr(mp), _ptr(ids), _ptr(wts))
+    if rc != 0:
+        raise ValueError("oracle_topk_softmax: bad arguments")
+    return ids, wts
 
 
 def moe_align(topk_ids, E: int, B: int):

@@ -36,7 +36,12 @@
  *  - E4M3 is OCP E4M3FN, round-to-nearest-even after clamping to +-448;
  *    block scale = max(absmax, 1e-10) / 448;
  *  - in the W8A8 variant the SiLU*up output is requantized per token and per
- *    128-column group before the down projection.
+ *    128-column group before the down projection;
+ *  - the router that feeds the path (the pages give the kernels top-k ids and
+ *    weights, [CHORD] "Two kernel families") is softmax over the token's logits,
+ *    the k largest, optionally renormalized over the k; equal logits keep the lower
+ *    expert id first; an expert-parallel map sends global ids to local ones (-1: held
+ *    by another GPU, [CHORD] "vLLM integration", EP8 profiles).
  *
  * Parity pins for every function live in tests/test_oracle_*.py.
  */
@@ -157,6 +162,57 @@ int oracle_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int64_t br,
         }
     }
   }
+  return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Router (softmax over a token's logits, its top k, optional renormalization) */
+/* ------------------------------------------------------------------------- */
+
+/* logits [T, E] fp32. For each token t, in order of decreasing probability:
+ *   p_e = exp(l_e) / sum_j exp(l_j)   (softmax),
+ *   the k experts with the largest p (= the largest logits; equal logits: lower id),
+ *   weight_s = p_s / sum over the k selected p   (renormalize != 0), else p_s.
+ * ids[t*k + s] = map ? map[id] : id. Probabilities in fp64 (max-subtracted exponents,
+ * which leaves each ratio unchanged). */
+int oracle_topk_softmax(const float* logits, int64_t T, int32_t E, int32_t k, int32_t renormalize,
+                        const int32_t* map, int32_t* ids, double* weights) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E || (T > 0 && (!logits || !ids || !weights)))
+    return ORACLE_BAD_ARG;
+  double* p = (double*)malloc((size_t)E * sizeof(double));
+  unsigned char* used = (unsigned char*)malloc((size_t)E);
+  if (!p || !used) {
+    free(p);
+    free(used);
+    return ORACLE_BAD_ARG;
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    const float* l = logits + t * E;
+    double m = (double)l[0];
+    for (int32_t e = 1; e < E; ++e)
+      if ((double)l[e] > m) m = (double)l[e];
+    double total = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+      p[e] = exp((double)l[e] - m);
+      total += p[e];
+    }
+    for (int32_t e = 0; e < E; ++e) p[e] /= total;
+    memset(used, 0, (size_t)E);
+    double sel = 0.0;
+    for (int32_t s = 0; s < k; ++s) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e) /* strict '>' keeps the lower id among equals */
+        if (!used[e] && (best < 0 || (double)l[e] > (double)l[best])) best = e;
+      used[best] = 1;
+      ids[t * k + s] = map ? map[best] : best;
+      weights[t * k + s] = p[best];
+      sel += p[best];
+    }
+    if (renormalize)
+      for (int32_t s = 0; s < k; ++s) weights[t * k + s] /= sel;
+  }
+  free(p);
+  free(used);
   return ORACLE_OK;
 }
 

@@ -49,6 +49,8 @@ def load():
     lib.qmoe_last_error.restype = ctypes.c_char_p
     lib.moe_align.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P]
     lib.moe_align.restype = _I32
+    lib.moe_topk_softmax.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
+    lib.moe_topk_softmax.restype = _I32
     lib.moe_w4a16_forward.argtypes = [_P] * 7 + [_I32] * 6 + [_P, _P, _SZP, _P]
     lib.moe_w4a16_forward.restype = _I32
     lib.moe_fp8_block_forward.argtypes = [_P] * 8 + [_I32] * 6 + [_P, _P, _SZP, _P]
@@ -107,6 +109,24 @@ def plan(fmt, T, H, I, E, k, schedule=SCHEDULE_AUTO):
     _check("qmoe_plan", load().qmoe_plan(fmt, T, H, I, E, k, schedule, ctypes.byref(chosen),
                                          ctypes.byref(bm), ctypes.byref(ws)))
     return chosen.value, bm.value, ws.value
+
+
+def moe_topk_softmax(logits, k, renormalize=True, expert_map=None, stream=None):
+    """Router: (topk_ids int32 [T,k], topk_weights fp32 [T,k]) from fp32 logits [T,E].
+
+    expert_map: optional int32 [E] GPU tensor of local ids (-1: expert held elsewhere).
+    """
+    if logits.dim() != 2:
+        raise ValueError("logits must be [T, E]")
+    T, E = logits.shape
+    lp = _dev(logits, "logits", (torch.float32,))
+    mp = None if expert_map is None else _dev(expert_map, "expert_map", (torch.int32,), (E,))
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    wts = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("moe_topk_softmax",
+           load().moe_topk_softmax(lp, T, E, k, 1 if renormalize else 0, mp, ids.data_ptr(),
+                                   wts.data_ptr(), _stream_ptr(stream)))
+    return ids, wts
 
 
 def moe_align(topk_ids, E, block_m, stream=None):

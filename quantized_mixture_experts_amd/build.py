@@ -11,8 +11,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqmoe.so")
-SOURCES = ["api.hip", "align.hip", "elementwise.hip", "w4a16_stream.hip", "w4a16_tiled.hip",
-           "fp8_stream.hip", "fp8_tiled.hip"]
+SOURCES = ["api.hip", "router.hip", "align.hip", "elementwise.hip", "w4a16_stream.hip",
+           "w4a16_tiled.hip", "fp8_stream.hip", "fp8_tiled.hip"]
 # Per-source extra flags. The FP8 tile kernel promotes every MFMA result with VALU
 # multiply-adds, so its MFMAs must write VGPRs (the default heuristics pick AGPRs and then
 # copy every result back).

@@ -211,6 +211,25 @@ qmoe_status moe_align(const int32_t* topk_ids, int32_t T, int32_t k, int32_t E, 
   return QMOE_OK;
 }
 
+qmoe_status moe_topk_softmax(const float* logits, int32_t T, int32_t E, int32_t k,
+                             int32_t renormalize, const int32_t* expert_map, int32_t* topk_ids,
+                             float* topk_weights, void* stream) {
+  g_last_error[0] = 0;
+  if (T < 0 || E <= 0 || k <= 0 || k > E)
+    return fail(QMOE_ERR_INVALID_ARG, "bad sizes T=%d E=%d k=%d", T, E, k);
+  if (E > QMOE_MAX_EXPERTS)
+    return fail(QMOE_ERR_UNSUPPORTED, "expert count %d exceeds %d", E, QMOE_MAX_EXPERTS);
+  if (T > 0 && (!logits || !topk_ids || !topk_weights))
+    return fail(QMOE_ERR_INVALID_ARG, "NULL pointer");
+  if (!aligned(logits, 4) || !aligned(expert_map, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_weights, 4))
+    return fail(QMOE_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  hipError_t err = launch_topk_softmax(logits, T, E, k, renormalize ? 1 : 0, expert_map, topk_ids,
+                                       topk_weights, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "router launch");
+  return QMOE_OK;
+}
+
 qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                       int32_t schedule, int32_t* chosen, int32_t* block_m,
                       size_t* workspace_bytes) {

@@ -7,6 +7,13 @@
 
 namespace qmoe {
 
+// --- router (router.hip) ---------------------------------------------------
+// Top-k experts by router logit with softmax weights (renormalized over the k or not),
+// ids mapped through expert_map when it is not null. E <= QMOE_MAX_EXPERTS, 1 <= k <= E.
+hipError_t launch_topk_softmax(const float* logits, int32_t T, int32_t E, int32_t k,
+                               int32_t renormalize, const int32_t* expert_map, int32_t* ids,
+                               float* weights, hipStream_t stream);
+
 // --- align (align.hip) -----------------------------------------------------
 size_t align_lds_bytes(int32_t E);
 hipError_t launch_align(const int32_t* ids, int32_t P, int32_t E, int32_t B, int32_t L, int32_t NB,

@@ -76,23 +76,30 @@ def bf16_value(b) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def routing(rng: np.random.Generator, T: int, E: int, k: int, kind: str = "uniform"):
-    """Router output: topk_ids int32 [T,k] (descending probability), topk_weights fp32 [T,k].
+def router_logits(rng: np.random.Generator, T: int, E: int, kind: str = "uniform"):
+    """Router logits fp32 [T,E].
 
-    uniform: i.i.d. N(0,1) logits, so every k-subset is equally likely.
-    zipf: logits log(p_e) + Gumbel(0,1) with p_e proportional to 1/(e+1); the top-k of
+    uniform: i.i.d. N(0,1), so every k-subset of experts is equally likely to be the top k.
+    zipf: log(p_e) + Gumbel(0,1) with p_e proportional to 1/(e+1); the top-k of
     Gumbel-perturbed log-probabilities samples k distinct experts without replacement
     in proportion to p (expert 0 the most popular).
     """
     if kind == "uniform":
-        logits = rng.standard_normal((T, E), dtype=np.float32)
-    elif kind == "zipf":
+        return rng.standard_normal((T, E), dtype=np.float32)
+    if kind == "zipf":
         logp = -np.log(np.arange(1, E + 1, dtype=np.float64))
         logp -= np.log(np.exp(logp).sum())
         g = rng.gumbel(0.0, 1.0, size=(T, E))
-        logits = (logp[None, :] + g).astype(np.float32)
-    else:
-        raise ValueError(kind)
+        return (logp[None, :] + g).astype(np.float32)
+    raise ValueError(kind)
+
+
+def routing(rng: np.random.Generator, T: int, E: int, k: int, kind: str = "uniform"):
+    """Routed FFN inputs: topk_ids int32 [T,k] (descending probability), topk_weights fp32
+    [T,k], from router_logits by a host softmax (fp32) -> top-k -> renormalization. This
+    only draws inputs for the expert FFN; the router step itself is tested separately
+    against the oracle on the logits alone."""
+    logits = router_logits(rng, T, E, kind)
     z = logits - logits.max(axis=1, keepdims=True)
     ez = np.exp(z, dtype=np.float32)
     p = ez / ez.sum(axis=1, keepdims=True, dtype=np.float32)

@@ -17,8 +17,8 @@ def lib():
 
 def test_exports_every_declared_function(lib):
     names = binding.declared_functions()
-    assert {"moe_align", "moe_w4a16_forward", "moe_fp8_block_forward", "qmoe_plan",
-            "qmoe_fp8_quantize_blocks", "qmoe_status_string", "qmoe_last_error",
+    assert {"moe_topk_softmax", "moe_align", "moe_w4a16_forward", "moe_fp8_block_forward",
+            "qmoe_plan", "qmoe_fp8_quantize_blocks", "qmoe_status_string", "qmoe_last_error",
             "qmoe_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -94,3 +94,17 @@ def test_align_and_quantizer_reject_bad_arguments(lib):
     assert q(FAKE, -1, 4, 1, 128, FAKE, FAKE, None) == INVALID
     assert q(None, 4, 4, 1, 128, FAKE, FAKE, None) == INVALID
     assert q(FAKE, 0, 4, 1, 128, FAKE, FAKE, None) == OK  # empty: nothing launched
+
+
+def test_router_rejects_bad_arguments(lib):
+    r = lib.moe_topk_softmax
+    assert r(FAKE, 4, 8, 0, 1, None, FAKE, FAKE, None) == INVALID   # k = 0
+    assert r(FAKE, 4, 8, 9, 1, None, FAKE, FAKE, None) == INVALID   # k > E
+    assert r(FAKE, -1, 8, 2, 1, None, FAKE, FAKE, None) == INVALID  # T < 0
+    assert r(FAKE, 4, 0, 1, 1, None, FAKE, FAKE, None) == INVALID   # E = 0
+    assert r(FAKE, 4, 5000, 2, 1, None, FAKE, FAKE, None) == UNSUPPORTED
+    assert r(None, 4, 8, 2, 1, None, FAKE, FAKE, None) == INVALID
+    assert r(FAKE, 4, 8, 2, 1, None, None, FAKE, None) == INVALID
+    assert r(FAKE + 2, 4, 8, 2, 1, None, FAKE, FAKE, None) == INVALID
+    assert r(FAKE, 4, 8, 2, 1, FAKE + 1, FAKE, FAKE, None) == INVALID  # misaligned map
+    assert r(None, 0, 8, 2, 1, None, None, None, None) == OK  # empty: nothing launched
