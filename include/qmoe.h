@@ -199,6 +199,16 @@ qmoe_status qmoe_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32
                                      uint8_t* q, float* scale, void* stream);
 
 /*
+ * qmoe_fp8_quantize_blocks_bf16 - the same quantizer on bf16 values (bit patterns, 2-byte
+ * alignment), widened exactly to fp32 first, so the codes and scales equal those of
+ * qmoe_fp8_quantize_blocks on the widened values. With br = 1, bc = 128 it turns a
+ * model's bf16 activations [T, H] into the W8A8 path's a_q and a_s ([SGL] background:
+ * per-token-group activation scales As).
+ */
+qmoe_status qmoe_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t C, int32_t br,
+                                          int32_t bc, uint8_t* q, float* scale, void* stream);
+
+/*
  * qmoe_plan - the schedule and align block size a forward would use.
  *   format      0 = W4A16, 1 = W8A8 block FP8.
  *   schedule    requested qmoe_schedule (AUTO resolves here).

@@ -57,6 +57,8 @@ def load():
     lib.moe_fp8_block_forward.restype = _I32
     lib.qmoe_fp8_quantize_blocks.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P, _P]
     lib.qmoe_fp8_quantize_blocks.restype = _I32
+    lib.qmoe_fp8_quantize_blocks_bf16.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P, _P]
+    lib.qmoe_fp8_quantize_blocks_bf16.restype = _I32
     lib.qmoe_plan.argtypes = [_I32] * 7 + [ctypes.POINTER(_I32), ctypes.POINTER(_I32), _SZP]
     lib.qmoe_plan.restype = _I32
     _lib = lib
@@ -203,12 +205,14 @@ def moe_fp8_block_forward(a_q, a_scale, w13, s13, w2, s2, topk_ids, topk_weights
 
 
 def fp8_quantize_blocks(v, br, bc, stream=None):
-    """Block E4M3 quantizer on a 2-D fp32 GPU tensor: returns (codes uint8, scales fp32)."""
+    """Block E4M3 quantizer on a 2-D fp32 or bf16 GPU tensor: returns (codes uint8, scales
+    fp32). bf16 values are widened exactly, so they quantize like their fp32 values."""
     R, C = v.shape
-    vptr = _dev(v, "v", (torch.float32,))
+    bf16 = v.dtype in _BF16
+    vptr = _dev(v, "v", _BF16 if bf16 else (torch.float32,))
     q = torch.empty((R, C), dtype=torch.uint8, device=v.device)
     s = torch.empty(((R + br - 1) // br, (C + bc - 1) // bc), dtype=torch.float32, device=v.device)
-    _check("qmoe_fp8_quantize_blocks",
-           load().qmoe_fp8_quantize_blocks(vptr, R, C, br, bc, q.data_ptr(), s.data_ptr(),
-                                           _stream_ptr(stream)))
+    name = "qmoe_fp8_quantize_blocks_bf16" if bf16 else "qmoe_fp8_quantize_blocks"
+    _check(name, getattr(load(), name)(vptr, R, C, br, bc, q.data_ptr(), s.data_ptr(),
+                                       _stream_ptr(stream)))
     return q, s

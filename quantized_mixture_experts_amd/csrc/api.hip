@@ -435,18 +435,39 @@ qmoe_status moe_fp8_block_forward(const uint8_t* a_q, const float* a_scale, cons
   return QMOE_OK;
 }
 
-qmoe_status qmoe_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
-                                     uint8_t* q, float* scale, void* stream) {
-  g_last_error[0] = 0;
+namespace {
+qmoe_status check_quantize_args(const void* v, int64_t R, int64_t C, int32_t br, int32_t bc,
+                                const uint8_t* q, const float* scale, size_t v_align) {
   if (R < 0 || C < 0) return fail(QMOE_ERR_INVALID_ARG, "negative size");
   if (br < 1 || br > 128 || bc < 1 || bc > 1024 || (int64_t)br * bc > 16384)
     return fail(QMOE_ERR_UNSUPPORTED, "block [%d, %d] outside [1..128] x [1..1024]", br, bc);
   if (R == 0 || C == 0) return QMOE_OK;
   if (!v || !q || !scale) return fail(QMOE_ERR_INVALID_ARG, "NULL pointer");
-  if (!aligned(v, 4) || !aligned(scale, 4))
-    return fail(QMOE_ERR_INVALID_ARG, "pointers must be 4-byte aligned");
+  if (!aligned(v, v_align) || !aligned(scale, 4))
+    return fail(QMOE_ERR_INVALID_ARG, "pointers must be aligned (values %zu bytes, scales 4)",
+                v_align);
+  return QMOE_OK;
+}
+}  // namespace
+
+qmoe_status qmoe_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
+                                     uint8_t* q, float* scale, void* stream) {
+  g_last_error[0] = 0;
+  const qmoe_status st = check_quantize_args(v, R, C, br, bc, q, scale, 4);
+  if (st != QMOE_OK || R == 0 || C == 0) return st;
   hipError_t err = launch_fp8_quantize_blocks(v, R, C, br, bc, q, scale,
                                               static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err, "quantize launch");
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t C, int32_t br,
+                                          int32_t bc, uint8_t* q, float* scale, void* stream) {
+  g_last_error[0] = 0;
+  const qmoe_status st = check_quantize_args(v, R, C, br, bc, q, scale, 2);
+  if (st != QMOE_OK || R == 0 || C == 0) return st;
+  hipError_t err = launch_fp8_quantize_blocks_bf16(v, R, C, br, bc, q, scale,
+                                                   static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err, "quantize launch");
   return QMOE_OK;
 }

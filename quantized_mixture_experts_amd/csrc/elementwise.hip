@@ -47,9 +47,17 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// One wave per [br, bc] block; four blocks per work-group.
+__device__ __forceinline__ float load_value(const float* p) { return *p; }
+// bf16 bit pattern: the top half of the fp32 value (exact).
+__device__ __forceinline__ float load_value(const uint16_t* p) {
+  return __builtin_bit_cast(float, (uint32_t)*p << 16);
+}
+
+// One wave per [br, bc] block; four blocks per work-group. In: fp32 values or bf16 bit
+// patterns (widened exactly, so both give the same codes for the same values).
+template <typename In>
 __global__ void __launch_bounds__(kEwThreads)
-    fp8_quantize_blocks_kernel(const float* __restrict__ v, int64_t R, int64_t C, int32_t br,
+    fp8_quantize_blocks_kernel(const In* __restrict__ v, int64_t R, int64_t C, int32_t br,
                                int32_t bc, uint8_t* __restrict__ q, float* __restrict__ scale) {
   const int64_t nbc = (C + bc - 1) / bc, nbr = (R + br - 1) / br;
   const int64_t blk = (int64_t)blockIdx.x * (kEwThreads / kWave) + threadIdx.x / kWave;
@@ -62,14 +70,14 @@ __global__ void __launch_bounds__(kEwThreads)
   float amax = 0.f;
   for (int i = lane; i < n; i += kWave) {
     const int64_t r = r0 + i / cols, c = c0 + i % cols;
-    amax = fmaxf(amax, fabsf(v[r * C + c]));
+    amax = fmaxf(amax, fabsf(load_value(v + r * C + c)));
   }
   amax = wave_max(amax);
   const float s = fmaxf(amax, 1e-10f) / 448.0f;
   if (lane == 0) scale[blk] = s;
   for (int i = lane; i < n; i += kWave) {
     const int64_t r = r0 + i / cols, c = c0 + i % cols;
-    const float t = fminf(fmaxf(v[r * C + c] / s, -448.0f), 448.0f);
+    const float t = fminf(fmaxf(load_value(v + r * C + c) / s, -448.0f), 448.0f);
     const uint32_t packed = __builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0u, false);
     q[r * C + c] = (uint8_t)(packed & 0xFFu);
   }
@@ -97,14 +105,28 @@ hipError_t launch_cast_f32_bf16(const float* src, uint16_t* dst, int64_t n, hipS
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
-                                      uint8_t* q, float* scale, hipStream_t stream) {
+namespace {
+template <typename In>
+hipError_t launch_quantize(const In* v, int64_t R, int64_t C, int32_t br, int32_t bc, uint8_t* q,
+                           float* scale, hipStream_t stream) {
   const int64_t nblk = ((R + br - 1) / br) * ((C + bc - 1) / bc);
   if (nblk <= 0) return hipSuccess;
   const int64_t per = kEwThreads / kWave;
-  hipLaunchKernelGGL(fp8_quantize_blocks_kernel, dim3((unsigned)((nblk + per - 1) / per)),
+  hipLaunchKernelGGL(fp8_quantize_blocks_kernel<In>, dim3((unsigned)((nblk + per - 1) / per)),
                      dim3(kEwThreads), 0, stream, v, R, C, br, bc, q, scale);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
+                                      uint8_t* q, float* scale, hipStream_t stream) {
+  return launch_quantize(v, R, C, br, bc, q, scale, stream);
+}
+
+hipError_t launch_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t C, int32_t br,
+                                           int32_t bc, uint8_t* q, float* scale,
+                                           hipStream_t stream) {
+  return launch_quantize(v, R, C, br, bc, q, scale, stream);
 }
 
 }  // namespace qmoe

@@ -26,6 +26,9 @@ hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_cast_f32_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
 hipError_t launch_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int32_t br, int32_t bc,
                                       uint8_t* q, float* scale, hipStream_t stream);
+hipError_t launch_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t C, int32_t br,
+                                           int32_t bc, uint8_t* q, float* scale,
+                                           hipStream_t stream);
 
 // --- grouped expert GEMMs ---------------------------------------------------
 // Routing view shared by the expert GEMMs: segments of the sorted pair list, each a

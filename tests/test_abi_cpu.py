@@ -18,8 +18,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = binding.declared_functions()
     assert {"moe_topk_softmax", "moe_align", "moe_w4a16_forward", "moe_fp8_block_forward",
-            "qmoe_plan", "qmoe_fp8_quantize_blocks", "qmoe_status_string", "qmoe_last_error",
-            "qmoe_abi_version"} <= set(names)
+            "qmoe_plan", "qmoe_fp8_quantize_blocks", "qmoe_fp8_quantize_blocks_bf16",
+            "qmoe_status_string", "qmoe_last_error", "qmoe_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert lib.qmoe_abi_version() == 1
@@ -94,6 +94,10 @@ def test_align_and_quantizer_reject_bad_arguments(lib):
     assert q(FAKE, -1, 4, 1, 128, FAKE, FAKE, None) == INVALID
     assert q(None, 4, 4, 1, 128, FAKE, FAKE, None) == INVALID
     assert q(FAKE, 0, 4, 1, 128, FAKE, FAKE, None) == OK  # empty: nothing launched
+    qb = lib.qmoe_fp8_quantize_blocks_bf16
+    assert qb(FAKE + 1, 4, 4, 1, 128, FAKE, FAKE, None) == INVALID
+    assert qb(FAKE, 4, 4, 0, 128, FAKE, FAKE, None) == UNSUPPORTED
+    assert qb(None, 4, 4, 1, 128, FAKE, FAKE, None) == INVALID
 
 
 def test_router_rejects_bad_arguments(lib):

@@ -42,6 +42,21 @@ def test_quantizer_bit_exact(oracle_mod, R, C, br, bc):
     assert np.array_equal(q.cpu().numpy(), rq)
 
 
+@pytest.mark.parametrize("T,H", [(32, 7168), (1024, 7168), (7, 384), (3, 200)])
+def test_bf16_activation_quantizer_bit_exact(oracle_mod, T, H):
+    # bf16 activations -> E4M3 per token and 128 columns (the W8A8 path's a_q, a_s): the
+    # same codes and scales as the oracle's quantizer on the exactly widened values.
+    print(f"[quant bf16] T={T} H={H}", flush=True)
+    rng = np.random.default_rng(T * 3 + H)
+    x = inputs.bf16_bits(rng.standard_normal((T, H), dtype=np.float32) *
+                         np.exp(rng.uniform(-6, 6, (T, 1))).astype(np.float32))
+    q, s = binding.fp8_quantize_blocks(torch.from_numpy(x.view(np.int16)).cuda(), 1, 128)
+    torch.cuda.synchronize()
+    rq, rs = oracle_mod.fp8_quantize_blocks(inputs.bf16_value(x), 1, 128)
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
 def _forward(case, schedule):
     d = to_dev(case)
     out = binding.moe_fp8_block_forward(d["a_q"], d["a_s"], d["w13"], d["s13"], d["w2"],

@@ -74,3 +74,61 @@ def test_router_is_deterministic():
     a = binding.moe_topk_softmax(lg, 8)
     b = binding.moe_topk_softmax(lg, 8)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("schedule", [binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL])
+def test_router_to_w4a16_forward_under_expert_parallelism(oracle_mod, schedule):
+    # The GPU's share: global experts 4..11 of 16 as local experts 0..7. Router on the
+    # GPU (global top-4, renormalized, ids mapped, remote slots -1), then the forward on
+    # the local experts; the oracle takes the same path from the same logits.
+    from gpu_util import TOL, bf16_out_to_f64, report, to_dev
+    T, H, I, E_glob, E_loc, k = 300, 512, 256, 16, 8, 4
+    print(f"[route->w4a16] schedule={schedule}", flush=True)
+    case = inputs.custom_w4a16_case(T, H, I, E_loc, k, seed=77)
+    emap = np.full(E_glob, -1, np.int32)
+    emap[4:12] = np.arange(E_loc, dtype=np.int32)
+    logits = inputs.router_logits(np.random.default_rng(78), T, E_glob, "zipf")
+    ids, wts = binding.moe_topk_softmax(torch.from_numpy(logits).cuda(), k, True,
+                                        torch.from_numpy(emap).cuda())
+    d = to_dev(case)
+    out = binding.moe_w4a16_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], ids, wts,
+                                    schedule=schedule)
+    torch.cuda.synchronize()
+    rids, rw = oracle_mod.topk_softmax(logits, k, True, emap)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rids)
+    ref = oracle_mod.w4a16_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"], rids,
+                               rw.astype(np.float32))
+    e = report(f"router->w4a16 EP share sched={schedule}", bf16_out_to_f64(out), ref)
+    assert e.max() <= TOL
+    remote = np.all(rids < 0, axis=1)  # tokens whose top-4 are all held elsewhere
+    assert np.all(bf16_out_to_f64(out)[remote] == 0.0)
+
+
+def test_router_and_bf16_quantizer_to_fp8_forward(oracle_mod):
+    # bf16 activations quantized on the GPU (E4M3 per token and 128 columns) and routed
+    # on the GPU, then the block-FP8 forward; the oracle quantizes and routes the same way.
+    from gpu_util import TOL, bf16_out_to_f64, report
+    T, H, I, E, k = 400, 512, 256, 8, 2
+    print("[route+quant->fp8]", flush=True)
+    case = inputs.custom_fp8_case(T, H, I, E, k, seed=55, quantize=oracle_mod.fp8_quantize_blocks)
+    x = inputs.bf16_bits(np.random.default_rng(56).standard_normal((T, H), dtype=np.float32))
+    logits = inputs.router_logits(np.random.default_rng(57), T, E, "uniform")
+    a_q, a_s = binding.fp8_quantize_blocks(torch.from_numpy(x.view(np.int16)).cuda(), 1, 128)
+    ids, wts = binding.moe_topk_softmax(torch.from_numpy(logits).cuda(), k)
+    dev = {n: torch.from_numpy(case[n]).cuda() for n in ("w13", "s13", "w2", "s2")}
+    out = binding.moe_fp8_block_forward(a_q, a_s, dev["w13"], dev["s13"], dev["w2"], dev["s2"],
+                                        ids, wts)
+    torch.cuda.synchronize()
+    rq, rs = oracle_mod.fp8_quantize_blocks(inputs.bf16_value(x), 1, 128)
+    rids, rw = oracle_mod.topk_softmax(logits, k)
+    assert np.array_equal(a_q.cpu().numpy(), rq) and np.array_equal(a_s.cpu().numpy(), rs)
+    ref = oracle_mod.fp8_moe(rq, rs, case["w13"], case["s13"], case["w2"], case["s2"], rids,
+                             rw.astype(np.float32))
+    # The W8A8 small-shape criterion (the fp8 matrix cores' block sums flip single E4M3
+    # codes of h; a flip moves one row, a fault the whole output): normwise <= 5e-3, at
+    # least 99% of the rows within TOL, none beyond 5e-2.
+    got = bf16_out_to_f64(out)
+    e = report("router+quantizer->fp8", got, ref)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 5e-3
+    assert np.mean(e <= TOL) >= 0.99
+    assert e.max() <= 5e-2
