@@ -79,8 +79,14 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   p.P = (int64_t)T * k;
   const double tok_e = E > 0 ? (double)p.P / E : 0.0;
   p.schedule = schedule;
+  // Crossover of the two profiles, measured on MI355X for hidden 7168, intermediate 2048
+  // (quantized_mixture_experts_amd.tune_schedule): the decode profile streams the
+  // weights once per 16-row block, so it loses to the tile kernels past about 56 routed
+  // rows per expert for W4A16 (48: 0.94 vs 1.08 ms; 64: 1.19 vs 1.08 ms) and past about
+  // 12 for block FP8 (8: 0.30 vs 0.38 ms; 16: 0.52 vs 0.38 ms).
+  const double crossover = fmt == kW4A16 ? 56.0 : 12.0;
   if (schedule == QMOE_SCHEDULE_AUTO)
-    p.schedule = tok_e <= 40.0 ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
+    p.schedule = tok_e <= crossover ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
   p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 2;
   p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&
             (fmt == kW4A16 ? w4a16_tiled_supported(H, I) : fp8_tiled_supported(H, I));
