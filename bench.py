@@ -7,12 +7,15 @@ steps are plain calls without instrumentation (--launch graph: replays of one ca
 graph); the per-kernel times come from a separate pass of K steps with HIP events recorded
 around every kernel on its launch stream.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|fp8|full384|tiny|router]
+  python bench.py [--gpus 1] [--steps K] [--warmup W]
+                  [--workload decode|prefill|fp8|full384|tiny|router|grouped_prefill|grouped_decode]
 
 Prints one JSON line. The default workload is the decode layer (32 tokens, hidden 7168,
 intermediate 2048, 48 local experts, top-8, INT4 group-32 weights); its value is the
 expert-weight bytes the forward must read divided by the step time (GB/s). Prefill-type
-workloads report TFLOP/s of the routed expert FLOPs. The "roofline" object covers the
+workloads report TFLOP/s of the routed expert FLOPs. The grouped workloads take rows
+already grouped by expert (contiguous: 48 experts x 128 rows; masked: 48 experts x 32
+valid rows in a budget of 64), one pair of weight 1 per row. The "roofline" object covers the
 dominant kernel (the gate_up GEMM), timed with HIP events recorded on the stream it runs
 on, over the timed steps. "cpu_baseline" times the CPU oracle on a bounded sample.
 """
@@ -39,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "fp8", "full384", "tiny", "router"])
+                    choices=["decode", "prefill", "fp8", "full384", "tiny", "router",
+                             "grouped_prefill", "grouped_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
                     help="how the timed steps are issued: eager library calls (default), or "
@@ -116,7 +120,7 @@ def main():
         bench_router(args, np, torch, binding, inputs)
         return
 
-    cfg = inputs.CONFIGS[args.workload]
+    grouped = inputs.GROUPED.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.time()
@@ -125,22 +129,60 @@ def main():
         return {k: torch.from_numpy(np.ascontiguousarray(v.view(np.int16) if v.dtype == np.uint16 else v)).to(dev)
                 for k, v in arrays.items()}
 
-    if cfg.fmt == "w4a16":
+    if grouped:
+        g = grouped
+        case = inputs.grouped_case(args.workload)
+        masked = g["layout"] == "masked"
+        if masked:
+            counts = np.clip(case["masked_m"], 0, g["max_m"])
+            rows_total = g["E"] * g["max_m"]
+            ids = np.where(np.arange(g["max_m"])[None, :] < counts[:, None],
+                           np.arange(g["E"])[:, None], -1).reshape(-1, 1)
+        else:
+            rows_total = case["a"].shape[0]
+            ids = case["m_indices"].reshape(-1, 1)
+        # k = 1: every row is one pair of weight 1
+        cfg = inputs.MoEConfig(args.workload, rows_total, g["H"], g["I"], g["E"], 1, "w4a16",
+                               "grouped", 0)
+    elif inputs.CONFIGS[args.workload].fmt == "w4a16":
+        cfg = inputs.CONFIGS[args.workload]
         case = inputs.w4a16_case(cfg)
+        ids = case["topk_ids"]
     else:
+        cfg = inputs.CONFIGS[args.workload]
+
         def gpu_quant(v, br, bc):
             q, s = binding.fp8_quantize_blocks(torch.from_numpy(v).to(dev), br, bc)
             return q.cpu().numpy(), s.cpu().numpy()
         case = inputs.fp8_case(cfg, gpu_quant)
+        ids = case["topk_ids"]
     d = to_dev(case)
     gen_s = time.time() - t_gen
 
     fmt = binding.FORMAT_W4A16 if cfg.fmt == "w4a16" else binding.FORMAT_FP8
-    chosen, block_m, ws_bytes = binding.plan(fmt, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
-    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
+    if grouped:
+        # The schedule AUTO picks from the expected rows per expert (k = 1).
+        chosen = binding.plan(fmt, g["rows"] * cfg.E, cfg.H, cfg.I, cfg.E, 1)[0]
+        ws_bytes = binding.grouped_workspace_bytes(masked, g["max_m"] if masked else cfg.T, cfg.H,
+                                                   cfg.I, cfg.E, g["rows"])
+    else:
+        chosen, block_m, ws_bytes = binding.plan(fmt, cfg.T, cfg.H, cfg.I, cfg.E, cfg.k)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
-    if cfg.fmt == "w4a16":
+    if grouped and masked:
+        a3 = d["a"]
+
+        def step():
+            binding.moe_w4a16_grouped_masked(a3, d["w13"], d["s13"], d["w2"], d["s2"],
+                                             d["masked_m"], g["rows"], out=out,
+                                             workspace=workspace)
+    elif grouped:
+        def step():
+            binding.moe_w4a16_grouped_contiguous(d["a"], d["w13"], d["s13"], d["w2"], d["s2"],
+                                                 d["m_indices"], g["rows"], out=out,
+                                                 workspace=workspace)
+    elif cfg.fmt == "w4a16":
         def step():
             binding.moe_w4a16_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
                                       d["topk_weights"], out=out, workspace=workspace)
@@ -157,7 +199,9 @@ def main():
     # Instrumented pass: K eager steps with HIP events recorded by the library around every
     # stage launch on the launch stream; the per-kernel times (and the roofline) come from
     # these events.
-    if lib.qmoe_timing_begin(args.steps) != 0:
+    # Room for every launch of a stage: align holds up to three per forward (the grouped
+    # layouts' per-row routing, the sort, the row gather).
+    if lib.qmoe_timing_begin(args.steps * 3) != 0:
         raise RuntimeError(lib.qmoe_last_error())
     torch.cuda.synchronize()
     te0 = time.perf_counter()
@@ -200,11 +244,12 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    ids = case["topk_ids"]
-    touched = int(np.unique(ids[(ids >= 0) & (ids < cfg.E)]).size)
+    valid = (ids >= 0) & (ids < cfg.E)
+    touched = int(np.unique(ids[valid]).size)
+    pairs = int(valid.sum())  # routed (row, expert) pairs
     w13_b, w2_b = weight_bytes_per_expert(cfg)
     weight_bytes = touched * (w13_b + w2_b)
-    flops = cfg.P * (2 * cfg.H * 2 * cfg.I + 2 * cfg.I * cfg.H)
+    flops = pairs * (2 * cfg.H * 2 * cfg.I + 2 * cfg.I * cfg.H)
     dtype = "bf16" if cfg.fmt == "w4a16" else "fp8"
     hbm_bound = chosen == binding.SCHEDULE_DECODE
     if hbm_bound:
@@ -220,7 +265,7 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
     else:
-        per_launch = cfg.P * 2 * cfg.H * 2 * cfg.I
+        per_launch = pairs * 2 * cfg.H * 2 * cfg.I
         achieved = per_launch / (gu_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
@@ -235,11 +280,20 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         nthreads = oracle.default_threads()
-        default_rows = {"tiny": cfg.T, "decode": cfg.T, "full384": 32, "prefill": 16, "fp8": 8}
+        default_rows = {"tiny": cfg.T, "decode": cfg.T, "full384": 32, "prefill": 16, "fp8": 8,
+                        "grouped_prefill": 1536, "grouped_decode": 1536}
         nrows = args.cpu_rows or default_rows[args.workload]
-        rows = inputs.sample_rows(cfg.T, nrows, seed=cfg.seed)
+        valid_rows = np.flatnonzero(valid.any(axis=1))
+        rows = valid_rows[inputs.sample_rows(valid_rows.size, nrows, seed=cfg.seed)]
         tc = time.perf_counter()
-        if cfg.fmt == "w4a16":
+        if grouped and masked:
+            oracle.w4a16_grouped_masked(case["a"], case["w13"], case["s13"], case["w2"], case["s2"],
+                                        case["masked_m"], rows=rows, nthreads=nthreads)
+        elif grouped:
+            oracle.w4a16_grouped_contiguous(case["a"], case["w13"], case["s13"], case["w2"],
+                                            case["s2"], case["m_indices"], rows=rows,
+                                            nthreads=nthreads)
+        elif cfg.fmt == "w4a16":
             oracle.w4a16_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
                              case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
         else:
@@ -247,26 +301,35 @@ def main():
                            case["s2"], case["topk_ids"], case["topk_weights"], rows=rows,
                            nthreads=nthreads)
         cpu_s = time.perf_counter() - tc
-        # The oracle loops per (token, slot) and re-reads the expert's weights for each,
-        # so the full workload costs T / nrows times the sample.
-        full_s = cpu_s * cfg.T / len(rows)
+        # The oracle loops per (row, slot) and re-reads the expert's weights for each, so
+        # the full workload costs (rows holding a pair) / nrows times the sample.
+        full_s = cpu_s * valid_rows.size / len(rows)
         cpu_value = (weight_bytes / full_s / 1e9) if hbm_bound else (flops / full_s / 1e12)
         cpu = {"value": round(cpu_value, 6), "unit": unit, "cores": nthreads, "kind": "oracle",
-               "sample": f"{len(rows)} of {cfg.T} token rows (all {cfg.k} slots each), "
-                         f"{cpu_s:.1f} s on {nthreads} threads, scaled by {cfg.T}/{len(rows)}"}
+               "sample": f"{len(rows)} of {valid_rows.size} rows (all {cfg.k} slots each), "
+                         f"{cpu_s:.1f} s on {nthreads} threads, scaled by "
+                         f"{valid_rows.size}/{len(rows)}"}
 
     names = {"decode": "decode W4A16", "prefill": "prefill W4A16 (Zipf routing)",
              "fp8": "block-FP8 W8A8", "full384": "full 384-expert W4A16", "tiny": "tiny W4A16"}
+    if grouped:
+        layout = (f"masked, {g['rows']} valid rows per expert in a budget of {g['max_m']}"
+                  if masked else f"contiguous, {g['rows']} rows per expert")
+        workload = (f"grouped W4A16 ({layout}): {cfg.T} rows, hidden {cfg.H}, intermediate "
+                    f"{cfg.I}, {cfg.E} experts, one pair of weight 1 per row")
+    else:
+        workload = (f"{names[args.workload]}: {cfg.T} tokens, hidden {cfg.H}, intermediate "
+                    f"{cfg.I}, {cfg.E} experts, top-{cfg.k}")
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic (seeded; random-init quantized expert weights)",
-        "config": {"workload": f"{names[args.workload]}: {cfg.T} tokens, hidden {cfg.H}, "
-                               f"intermediate {cfg.I}, {cfg.E} experts, top-{cfg.k}",
+        "config": {"workload": workload,
                    "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
                    "top_k": cfg.k, "schedule": ["auto", "decode", "prefill"][chosen],
-                   "touched_experts": touched, "weight_bytes": weight_bytes, "flops": flops},
+                   "routed_pairs": pairs, "touched_experts": touched,
+                   "weight_bytes": weight_bytes, "flops": flops},
         "launch": args.launch,
         "instrumented_ms_per_step": round(instrumented_ms, 4),
         "stage_ms": {k: (round(v, 4) if v is not None else None) for k, v in stage_ms.items()},

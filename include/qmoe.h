@@ -9,8 +9,9 @@
  * Sources (web pages, cited by title and section):
  *   [CHORD] "vLLM x Novita AI: Chord W4A16 INT4 MoE Kernel for Kimi K2.x" (Novita AI
  *           blog): summary; "Two kernel families"; "vLLM integration"; "Kernel
- *           optimizations" (indexed kernels; H200 and Blackwell indexed decode);
- *           Figure 3 (where the padding lives).
+ *           optimizations" (indexed kernels; H200 and Blackwell indexed decode;
+ *           SM90 grouped kernels); Figure 3 (where the padding lives); "Measurements"
+ *           (the grouped prefill and decode rows).
  *   [SGL]   "SGLang W8A8 Block FP8 quantization kernel config guide" (xdnf.cn):
  *           background section (E4M3, [BLOCK_N, BLOCK_K] weight blocks, per-token-group
  *           activation scales As, weight block scales Bs); kernel dispatch section
@@ -163,6 +164,53 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
                               const float* topk_weights, int32_t T, int32_t H, int32_t I,
                               int32_t E, int32_t k, int32_t schedule, uint16_t* out,
                               void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * moe_w4a16_grouped_contiguous - the W4A16 expert FFN on the contiguous grouped layout
+ * ([CHORD] "Kernel optimizations", SM90 grouped kernels, and Figure 3: the rows are
+ * concatenated expert by expert, each expert's run padded, with an int32 expert index
+ * per row and -1 on padding rows). Each row is one (row, expert) pair of weight 1:
+ *
+ *   a            [M, H] bf16 rows.
+ *   m_indices    [M] int32 (4-byte alignment suffices): the row's expert; -1 (any value
+ *                outside [0, E)) marks a padding row. Rows need not be sorted.
+ *   out          [M, H] bf16, overwritten: out[r] = bf16(FFN_{m_indices[r]}(a[r])) with
+ *                FFN_e as in moe_w4a16_forward, and 0 on padding rows.
+ *   expected_m   rows per expert the caller expects (a host-side hint that picks the
+ *                AUTO schedule); 0 = M / E.
+ *   w13, s13, w2, s2, H, I, E, schedule, workspace: as moe_w4a16_forward (the weights
+ *   are the same canonical tensors: no separate packing per layout). The workspace
+ *   size differs from moe_w4a16_forward's; query it with workspace = NULL.
+ * Equal to moe_w4a16_forward with topk_ids = m_indices as [M, 1] and weights 1.
+ */
+qmoe_status moe_w4a16_grouped_contiguous(const uint16_t* a, const uint8_t* w13,
+                                         const uint16_t* s13, const uint8_t* w2,
+                                         const uint16_t* s2, const int32_t* m_indices, int32_t M,
+                                         int32_t H, int32_t I, int32_t E, int32_t expected_m,
+                                         int32_t schedule, uint16_t* out, void* workspace,
+                                         size_t* workspace_bytes, void* stream);
+
+/*
+ * moe_w4a16_grouped_masked - the W4A16 expert FFN on the masked grouped layout ([CHORD]
+ * "Kernel optimizations", SM90 grouped kernels: a fixed budget of max_m rows per expert,
+ * a device-side count of the valid rows, a host-side expected count that picks the
+ * launch, and a flat output whose rows past the count are not part of the result).
+ *
+ *   a            [E, max_m, H] bf16 (or [E * max_m, H]): row r of expert g at g*max_m + r.
+ *   masked_m     [E] int32 on the device (4-byte alignment suffices): valid rows of each
+ *                expert; a count above max_m means max_m, a negative count 0. Read only
+ *                on the device, so a forward can be captured into a hipGraph.
+ *   out          [E * max_m, H] bf16, overwritten: out[g*max_m + r] = bf16(FFN_g(a[g, r]))
+ *                for r < masked_m[g], and 0 on the rows past the count.
+ *   expected_m   host-side hint of the valid rows per expert (0 = max_m).
+ *   w13, s13, w2, s2, H, I, E, schedule, workspace: as moe_w4a16_grouped_contiguous.
+ */
+qmoe_status moe_w4a16_grouped_masked(const uint16_t* a, const uint8_t* w13, const uint16_t* s13,
+                                     const uint8_t* w2, const uint16_t* s2,
+                                     const int32_t* masked_m, int32_t max_m, int32_t H, int32_t I,
+                                     int32_t E, int32_t expected_m, int32_t schedule,
+                                     uint16_t* out, void* workspace, size_t* workspace_bytes,
+                                     void* stream);
 
 /*
  * moe_fp8_block_forward - routed MoE expert FFN, W8A8 block FP8 ([SGL] background:

@@ -133,6 +133,28 @@ def w4a16_moe(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=N
     return out
 
 
+def w4a16_grouped_contiguous(a, w13, s13, w2, s2, m_indices, rows=None, nthreads=None):
+    """The W4A16 expert FFN on the contiguous grouped layout ("vLLM x Novita AI: Chord W4A16
+    INT4 MoE Kernel for Kimi K2.x", SM90 grouped kernels and Figure 3): row r is the single
+    pair (r, m_indices[r]) of weight 1; an index outside [0, E) marks padding, whose output
+    row is 0. a [M,H] bf16 bits, m_indices int32 [M]. Returns float64 [nrows, H]."""
+    ids = np.ascontiguousarray(np.asarray(m_indices, dtype=np.int32).reshape(-1, 1))
+    return w4a16_moe(a, w13, s13, w2, s2, ids, np.ones(ids.shape, np.float32), rows, nthreads)
+
+
+def w4a16_grouped_masked(a, w13, s13, w2, s2, masked_m, rows=None, nthreads=None):
+    """The W4A16 expert FFN on the masked grouped layout (same page and section): a
+    [E, max_m, H] bf16 bits; row r of expert g (flat row g * max_m + r) is the pair (row,
+    g) of weight 1 when r < masked_m[g] (counts taken within [0, max_m]) and 0 otherwise.
+    Returns float64 [nrows, H] over the flat rows."""
+    E, max_m, H = a.shape
+    counts = np.clip(np.asarray(masked_m, dtype=np.int64), 0, max_m)
+    valid = np.arange(max_m)[None, :] < counts[:, None]
+    ids = np.where(valid, np.arange(E)[:, None], -1).astype(np.int32).reshape(-1, 1)
+    return w4a16_moe(np.ascontiguousarray(a).reshape(E * max_m, H), w13, s13, w2, s2, ids,
+                     np.ones(ids.shape, np.float32), rows, nthreads)
+
+
 def fp8_moe(a_q, a_s, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=None):
     """Routed W8A8 block-FP8 MoE FFN in fp64 (h requantized per 128 in fp32)."""
     a_q = _c(a_q, np.uint8)

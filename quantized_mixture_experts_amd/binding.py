@@ -53,6 +53,10 @@ def load():
     lib.moe_topk_softmax.restype = _I32
     lib.moe_w4a16_forward.argtypes = [_P] * 7 + [_I32] * 6 + [_P, _P, _SZP, _P]
     lib.moe_w4a16_forward.restype = _I32
+    for name in ("moe_w4a16_grouped_contiguous", "moe_w4a16_grouped_masked"):
+        fn = getattr(lib, name)
+        fn.argtypes = [_P] * 6 + [_I32] * 6 + [_P, _P, _SZP, _P]
+        fn.restype = _I32
     lib.moe_fp8_block_forward.argtypes = [_P] * 8 + [_I32] * 6 + [_P, _P, _SZP, _P]
     lib.moe_fp8_block_forward.restype = _I32
     lib.qmoe_fp8_quantize_blocks.argtypes = [_P, _I64, _I64, _I32, _I32, _P, _P, _P]
@@ -177,6 +181,63 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, topk_ids, topk_weights, schedule=SCHE
            load().moe_w4a16_forward(*args, T, H, I, E, k, schedule, optr, wptr, ctypes.byref(size),
                                     _stream_ptr(stream)))
     return out
+
+
+def _grouped(name, a2, w13, s13, w2, s2, route, M, rows, expected_m, schedule, out, workspace,
+             stream):
+    H = a2.shape[1]
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    args = [_dev(a2, "a", _BF16, (rows, H)),
+            _dev(w13, "w13", _U8, (E, 2 * I, H // 2)), _dev(s13, "s13", _BF16, (E, 2 * I, H // 32)),
+            _dev(w2, "w2", _U8, (E, H, I // 2)), _dev(s2, "s2", _BF16, (E, H, I // 32)), route]
+    if out is None:
+        out = torch.empty((rows, H), dtype=torch.bfloat16, device=a2.device)
+    optr = _dev(out, "out", _BF16, (rows, H))
+    fn = getattr(load(), name)
+    tail = (M, H, I, E, expected_m, schedule, optr)
+    if workspace is None:
+        need = ctypes.c_size_t(0)
+        _check(name, fn(*args, *tail, None, ctypes.byref(need), _stream_ptr(stream)))
+        workspace = torch.empty(max(need.value, 256), dtype=torch.uint8, device=a2.device)
+    wptr = _dev(workspace, "workspace", (torch.uint8,))
+    size = ctypes.c_size_t(workspace.numel())
+    _check(name, fn(*args, *tail, wptr, ctypes.byref(size), _stream_ptr(stream)))
+    return out
+
+
+def grouped_workspace_bytes(masked, M, H, I, E, expected_m=0, schedule=SCHEDULE_AUTO):
+    """Workspace bytes of a grouped forward (M = rows, or max_m when masked); host only."""
+    name = "moe_w4a16_grouped_masked" if masked else "moe_w4a16_grouped_contiguous"
+    need = ctypes.c_size_t(0)
+    _check(name, getattr(load(), name)(*([None] * 6), M, H, I, E, expected_m, schedule, None, None,
+                                       ctypes.byref(need), None))
+    return need.value
+
+
+def moe_w4a16_grouped_contiguous(a, w13, s13, w2, s2, m_indices, expected_m=0,
+                                 schedule=SCHEDULE_AUTO, out=None, workspace=None, stream=None):
+    """W4A16 expert FFN on rows grouped by expert: a [M, H] bf16, m_indices int32 [M] (the
+    row's expert, -1 on padding rows). Returns [M, H] bf16, zero on padding rows."""
+    M = a.shape[0]
+    route = _dev(m_indices, "m_indices", (torch.int32,), (M,))
+    return _grouped("moe_w4a16_grouped_contiguous", a, w13, s13, w2, s2, route, M, M, expected_m,
+                    schedule, out, workspace, stream)
+
+
+def moe_w4a16_grouped_masked(a, w13, s13, w2, s2, masked_m, expected_m=0,
+                             schedule=SCHEDULE_AUTO, out=None, workspace=None, stream=None):
+    """W4A16 expert FFN on a fixed row budget per expert: a [E, max_m, H] bf16, masked_m
+    int32 [E] valid rows per expert (on the GPU). Returns [E * max_m, H] bf16, zero past
+    each expert's count."""
+    if a.dim() != 3:
+        raise ValueError("a must be [E, max_m, H]")
+    E, max_m, H = a.shape
+    route = _dev(masked_m, "masked_m", (torch.int32,), (E,))
+    if w13.shape[0] != E:
+        raise ValueError(f"a holds {E} experts, w13 {w13.shape[0]}")
+    return _grouped("moe_w4a16_grouped_masked", a.view(E * max_m, H), w13, s13, w2, s2, route,
+                    max_m, E * max_m, expected_m, schedule, out, workspace, stream)
 
 
 def moe_fp8_block_forward(a_q, a_scale, w13, s13, w2, s2, topk_ids, topk_weights,

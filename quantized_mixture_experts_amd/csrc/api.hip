@@ -72,12 +72,14 @@ qmoe_status check_shape(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int
   return QMOE_OK;
 }
 
-Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t schedule) {
+// tok_e_hint > 0 replaces the routed-rows-per-expert estimate T * k / E that picks the
+// schedule (the grouped layouts pass the caller's expected rows per expert).
+Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t schedule,
+               double tok_e_hint = -1.0) {
   Plan p;
-  (void)k;
   p.fmt = fmt;
   p.P = (int64_t)T * k;
-  const double tok_e = E > 0 ? (double)p.P / E : 0.0;
+  const double tok_e = tok_e_hint > 0 ? tok_e_hint : E > 0 ? (double)p.P / E : 0.0;
   p.schedule = schedule;
   // Crossover of the two profiles, measured on MI355X for hidden 7168, intermediate 2048
   // (quantized_mixture_experts_amd.tune_schedule): the decode profile streams the
@@ -168,6 +170,137 @@ hipError_t staged(int stage, hipStream_t s, F&& launch) {
 template <typename T>
 T* region(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// The W4A16 forward after argument checks: align, gather, gate_up, down, combine.
+qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                      const uint8_t* w2, const uint16_t* s2, const int32_t* topk_ids,
+                      const float* topk_weights, int32_t T, int32_t H, int32_t I, int32_t E,
+                      int32_t k, uint16_t* out, void* workspace, hipStream_t s) {
+  Routing r{};
+  r.sorted_ids = region<int32_t>(workspace, p.off_sorted);
+  r.offsets = region<int32_t>(workspace, p.off_offsets);
+  r.tile_offsets = region<int32_t>(workspace, p.off_tiles);
+  r.expert_ids = region<int32_t>(workspace, p.off_expert_ids);
+  r.ntp = region<int32_t>(workspace, p.off_ntp);
+  r.topk_weights = topk_weights;
+  r.P = (int32_t)p.P;
+  r.k = k;
+  r.E = E;
+  r.L = (int32_t)p.L;
+  W4A16Problem prob{x, region<uint16_t>(workspace, p.off_xs), w13, s13, w2, s2,
+                    region<uint16_t>(workspace, p.off_h), region<float>(workspace, p.off_out32),
+                    T, H, I};
+
+  if (p.tiled) {
+    const int32_t tm = w4a16_tiled_rows();
+    hipError_t err = staged(QMOE_STAGE_ALIGN, s, [&] {
+      return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
+                          region<int32_t>(workspace, p.off_sorted),
+                          region<int32_t>(workspace, p.off_expert_ids),
+                          region<int32_t>(workspace, p.off_ntp),
+                          region<int32_t>(workspace, p.off_offsets), tm,
+                          region<int32_t>(workspace, p.off_tiles), s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "align launch");
+    err = staged(QMOE_STAGE_ALIGN, s, [&] {
+      return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "gather launch");
+    err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_tiled(prob, r, s); });
+    if (err != hipSuccess) return hip_fail(err, "gate_up launch");
+    float* y = region<float>(workspace, p.off_y);
+    err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_tiled(prob, r, y, s); });
+    if (err != hipSuccess) return hip_fail(err, "down launch");
+    err = staged(QMOE_STAGE_CAST, s, [&] {
+      return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    return QMOE_OK;
+  }
+
+  hipError_t err = hipSuccess;
+  if (!w4a16_stream_zeroes_output(H)) {
+    err = staged(QMOE_STAGE_ZERO, s, [&] { return launch_zero_f32(prob.out32, (int64_t)T * H, s); });
+    if (err != hipSuccess) return hip_fail(err, "zero launch");
+  }
+  err = staged(QMOE_STAGE_ALIGN, s, [&] {
+    return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
+                        region<int32_t>(workspace, p.off_sorted),
+                        region<int32_t>(workspace, p.off_expert_ids),
+                        region<int32_t>(workspace, p.off_ntp),
+                        region<int32_t>(workspace, p.off_offsets), 0, nullptr, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "align launch");
+  // The gathered activation rows belong to the align stage's timing.
+  err = staged(QMOE_STAGE_ALIGN, s, [&] {
+    return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "gather launch");
+  err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_stream(prob, r, p.mb, s); });
+  if (err != hipSuccess) return hip_fail(err, "gate_up launch");
+  err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_stream(prob, r, p.mb, s); });
+  if (err != hipSuccess) return hip_fail(err, "down launch");
+  err = staged(QMOE_STAGE_CAST, s, [&] {
+    return launch_cast_f32_bf16(prob.out32, out, (int64_t)T * H, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "cast launch");
+  return QMOE_OK;
+}
+
+// Grouped layouts: the rows arrive grouped by expert (the layout an expert-parallel
+// dispatch hands over), each row one pair of routing weight 1, so the forward is the
+// indexed one with k = 1 and the row's expert as its only id. `route` is m_indices
+// (contiguous) or masked_m (masked, then M is max_m and there are E * M rows).
+qmoe_status w4a16_grouped(bool masked, const uint16_t* a, const uint8_t* w13, const uint16_t* s13,
+                          const uint8_t* w2, const uint16_t* s2, const int32_t* route,
+                          int32_t M, int32_t H, int32_t I, int32_t E, int32_t expected_m,
+                          int32_t schedule, uint16_t* out, void* workspace,
+                          size_t* workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  if (M < 0)
+    return fail(QMOE_ERR_INVALID_ARG, "%s must be >= 0 (got %d)", masked ? "max_m" : "row count",
+                M);
+  if (expected_m < 0)
+    return fail(QMOE_ERR_INVALID_ARG, "expected_m must be >= 0 (got %d)", expected_m);
+  const int64_t rows = masked ? (int64_t)std::max(E, 0) * M : M;
+  if (rows > INT32_MAX)
+    return fail(QMOE_ERR_UNSUPPORTED, "too many rows: %lld", (long long)rows);
+  const int32_t T = (int32_t)rows;
+  qmoe_status st = check_shape(kW4A16, T, H, I, E, 1, schedule);
+  if (st != QMOE_OK) return st;
+  if (!workspace_bytes) return fail(QMOE_ERR_INVALID_ARG, "workspace_bytes is NULL");
+  const Plan p = make_plan(kW4A16, T, H, I, E, 1, schedule, expected_m > 0 ? expected_m : -1.0);
+  const size_t off_ones = p.total;
+  const size_t off_ids = off_ones + round_up(sizeof(float) * (size_t)T, kRegionAlign);
+  const size_t total = off_ids + (masked ? round_up(sizeof(int32_t) * (size_t)T, kRegionAlign) : 0);
+  if (!workspace) {
+    *workspace_bytes = total;
+    return QMOE_OK;
+  }
+  if (*workspace_bytes < total)
+    return fail(QMOE_ERR_WORKSPACE, "workspace %zu bytes, need %zu", *workspace_bytes, total);
+  if (T == 0) return QMOE_OK;
+  const void* ptrs[] = {a, w13, s13, w2, s2, out};
+  for (const void* q : ptrs)
+    if (!q) return fail(QMOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  for (const void* q : ptrs)
+    if (!aligned(q, 16)) return fail(QMOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!route || !aligned(route, 4))
+    return fail(QMOE_ERR_INVALID_ARG, "%s must be a 4-byte aligned device pointer",
+                masked ? "masked_m" : "m_indices");
+  if (!aligned(workspace, kRegionAlign))
+    return fail(QMOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ones = region<float>(workspace, off_ones);
+  int32_t* ids = masked ? region<int32_t>(workspace, off_ids) : nullptr;
+  hipError_t err = staged(QMOE_STAGE_ALIGN, s, [&] {
+    return launch_grouped_routing(masked ? route : nullptr, M, T, ids, ones, s);
+  });
+  if (err != hipSuccess) return hip_fail(err, "grouped routing launch");
+  return w4a16_run(p, a, w13, s13, w2, s2, masked ? ids : route, ones, T, H, I, E, 1, out,
+                   workspace, s);
 }
 
 }  // namespace
@@ -276,76 +409,28 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
   if (!aligned(workspace, kRegionAlign))
     return fail(QMOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  Routing r{};
-  r.sorted_ids = region<int32_t>(workspace, p.off_sorted);
-  r.offsets = region<int32_t>(workspace, p.off_offsets);
-  r.tile_offsets = region<int32_t>(workspace, p.off_tiles);
-  r.expert_ids = region<int32_t>(workspace, p.off_expert_ids);
-  r.ntp = region<int32_t>(workspace, p.off_ntp);
-  r.topk_weights = topk_weights;
-  r.P = (int32_t)p.P;
-  r.k = k;
-  r.E = E;
-  r.L = (int32_t)p.L;
-  W4A16Problem prob{x, region<uint16_t>(workspace, p.off_xs), w13, s13, w2, s2,
-                    region<uint16_t>(workspace, p.off_h), region<float>(workspace, p.off_out32),
-                    T, H, I};
+  return w4a16_run(p, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k, out,
+                   workspace, static_cast<hipStream_t>(stream));
+}
 
-  if (p.tiled) {
-    const int32_t tm = w4a16_tiled_rows();
-    hipError_t err = staged(QMOE_STAGE_ALIGN, s, [&] {
-      return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
-                          region<int32_t>(workspace, p.off_sorted),
-                          region<int32_t>(workspace, p.off_expert_ids),
-                          region<int32_t>(workspace, p.off_ntp),
-                          region<int32_t>(workspace, p.off_offsets), tm,
-                          region<int32_t>(workspace, p.off_tiles), s);
-    });
-    if (err != hipSuccess) return hip_fail(err, "align launch");
-    err = staged(QMOE_STAGE_ALIGN, s, [&] {
-      return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s);
-    });
-    if (err != hipSuccess) return hip_fail(err, "gather launch");
-    err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_tiled(prob, r, s); });
-    if (err != hipSuccess) return hip_fail(err, "gate_up launch");
-    float* y = region<float>(workspace, p.off_y);
-    err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_tiled(prob, r, y, s); });
-    if (err != hipSuccess) return hip_fail(err, "down launch");
-    err = staged(QMOE_STAGE_CAST, s, [&] {
-      return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);
-    });
-    if (err != hipSuccess) return hip_fail(err, "combine launch");
-    return QMOE_OK;
-  }
+qmoe_status moe_w4a16_grouped_contiguous(const uint16_t* a, const uint8_t* w13,
+                                         const uint16_t* s13, const uint8_t* w2,
+                                         const uint16_t* s2, const int32_t* m_indices, int32_t M,
+                                         int32_t H, int32_t I, int32_t E, int32_t expected_m,
+                                         int32_t schedule, uint16_t* out, void* workspace,
+                                         size_t* workspace_bytes, void* stream) {
+  return w4a16_grouped(false, a, w13, s13, w2, s2, m_indices, M, H, I, E, expected_m, schedule,
+                       out, workspace, workspace_bytes, stream);
+}
 
-  hipError_t err = hipSuccess;
-  if (!w4a16_stream_zeroes_output(H)) {
-    err = staged(QMOE_STAGE_ZERO, s, [&] { return launch_zero_f32(prob.out32, (int64_t)T * H, s); });
-    if (err != hipSuccess) return hip_fail(err, "zero launch");
-  }
-  err = staged(QMOE_STAGE_ALIGN, s, [&] {
-    return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
-                        region<int32_t>(workspace, p.off_sorted),
-                        region<int32_t>(workspace, p.off_expert_ids),
-                        region<int32_t>(workspace, p.off_ntp),
-                        region<int32_t>(workspace, p.off_offsets), 0, nullptr, s);
-  });
-  if (err != hipSuccess) return hip_fail(err, "align launch");
-  // The gathered activation rows belong to the align stage's timing.
-  err = staged(QMOE_STAGE_ALIGN, s, [&] {
-    return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s);
-  });
-  if (err != hipSuccess) return hip_fail(err, "gather launch");
-  err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_stream(prob, r, p.mb, s); });
-  if (err != hipSuccess) return hip_fail(err, "gate_up launch");
-  err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_stream(prob, r, p.mb, s); });
-  if (err != hipSuccess) return hip_fail(err, "down launch");
-  err = staged(QMOE_STAGE_CAST, s, [&] {
-    return launch_cast_f32_bf16(prob.out32, out, (int64_t)T * H, s);
-  });
-  if (err != hipSuccess) return hip_fail(err, "cast launch");
-  return QMOE_OK;
+qmoe_status moe_w4a16_grouped_masked(const uint16_t* a, const uint8_t* w13, const uint16_t* s13,
+                                     const uint8_t* w2, const uint16_t* s2,
+                                     const int32_t* masked_m, int32_t max_m, int32_t H, int32_t I,
+                                     int32_t E, int32_t expected_m, int32_t schedule,
+                                     uint16_t* out, void* workspace, size_t* workspace_bytes,
+                                     void* stream) {
+  return w4a16_grouped(true, a, w13, s13, w2, s2, masked_m, max_m, H, I, E, expected_m, schedule,
+                       out, workspace, workspace_bytes, stream);
 }
 
 qmoe_status moe_fp8_block_forward(const uint8_t* a_q, const float* a_scale, const uint8_t* w13,

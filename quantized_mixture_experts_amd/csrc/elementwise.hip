@@ -1,11 +1,14 @@
 // Elementwise kernels of the MoE FFN path: clearing the fp32 combine buffer, the final
-// fp32 -> bf16 rounding of the output, and the block E4M3 quantizer.
+// fp32 -> bf16 rounding of the output, the block E4M3 quantizer, and the per-row routing
+// of the grouped layouts.
 //
 // The quantizer follows "SGLang W8A8 Block FP8 quantization kernel config guide",
 // background section: E4M3 (max 448), one scale per block from the block's absmax.
 // Per block: scale = max(absmax, 1e-10) / 448, q = e4m3(clamp(v / scale, -448, 448))
 // with IEEE fp32 division and round-to-nearest-even (gfx950's v_cvt_pk_fp8_f32 emits
 // OCP E4M3FN).
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -83,6 +86,23 @@ __global__ void __launch_bounds__(kEwThreads)
   }
 }
 
+// Per-row routing of the grouped layouts: every row is one pair of routing weight 1.
+// With masked_m, row g * max_m + r belongs to expert g when r < masked_m[g] and is
+// padding (-1, dropped by align) otherwise, so a count above max_m means all max_m rows
+// and a negative count none.
+__global__ void __launch_bounds__(kEwThreads)
+    grouped_routing_kernel(const int32_t* __restrict__ masked_m, int32_t max_m, int32_t n,
+                           int32_t* __restrict__ ids, float* __restrict__ ones) {
+  const int32_t stride = (int32_t)gridDim.x * kEwThreads;
+  for (int32_t i = (int32_t)blockIdx.x * kEwThreads + threadIdx.x; i < n; i += stride) {
+    ones[i] = 1.f;
+    if (masked_m) {
+      const int32_t g = i / max_m;
+      ids[i] = i - g * max_m < masked_m[g] ? g : -1;
+    }
+  }
+}
+
 int grid_for(int64_t n) {
   int64_t g = (n / 4 + kEwThreads - 1) / kEwThreads;
   if (g < 1) g = 1;
@@ -127,6 +147,16 @@ hipError_t launch_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t
                                            int32_t bc, uint8_t* q, float* scale,
                                            hipStream_t stream) {
   return launch_quantize(v, R, C, br, bc, q, scale, stream);
+}
+
+hipError_t launch_grouped_routing(const int32_t* masked_m, int32_t max_m, int32_t n, int32_t* ids,
+                                  float* ones, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (masked_m && (max_m <= 0 || !ids)) return hipErrorInvalidValue;
+  const int32_t blocks = std::min<int32_t>((n + kEwThreads - 1) / kEwThreads, 1024);
+  hipLaunchKernelGGL(grouped_routing_kernel, dim3(blocks), dim3(kEwThreads), 0, stream, masked_m,
+                     max_m, n, ids, ones);
+  return hipGetLastError();
 }
 
 }  // namespace qmoe

@@ -29,6 +29,10 @@ hipError_t launch_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int3
 hipError_t launch_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t C, int32_t br,
                                            int32_t bc, uint8_t* q, float* scale,
                                            hipStream_t stream);
+// Grouped layouts: ones[0, n) = 1 and, when masked_m is not null, ids[g * max_m + r] = g
+// for r < masked_m[g], else -1.
+hipError_t launch_grouped_routing(const int32_t* masked_m, int32_t max_m, int32_t n, int32_t* ids,
+                                  float* ones, hipStream_t stream);
 
 // --- grouped expert GEMMs ---------------------------------------------------
 // Routing view shared by the expert GEMMs: segments of the sorted pair list, each a

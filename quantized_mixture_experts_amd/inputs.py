@@ -15,6 +15,12 @@ Block FP8 quantization kernel config guide", background section):
   fp8       1024 tokens, H 7168, I 2048, 32 experts, top-8, W8A8 block FP8
   full384   256 tokens, H 7168, I 2048, 384 experts, top-8, W4A16, uniform routing
 
+Grouped layouts (same page, SM90 grouped kernels, Figure 3 and the grouped rows of the
+measurements; rows already grouped by expert, one pair of weight 1 per row):
+
+  grouped_prefill  contiguous, 48 experts x 128 rows (no padding), H 7168, I 2048
+  grouped_decode   masked, 48 experts x 32 valid rows in a budget of max_m = 64
+
 Recipe (per case, numpy default_rng(seed), draws in this order):
   x       bf16(N(0,1)) [T,H]                      (FP8: fp32 N(0,1) source)
   router  logits N(0,1) [T,E]; Zipf: log(1/(e+1)) + Gumbel(0,1)
@@ -164,6 +170,57 @@ def custom_w4a16_case(T, H, I, E, k, seed, kind="uniform") -> dict:
 
 def custom_fp8_case(T, H, I, E, k, seed, quantize, kind="uniform") -> dict:
     return fp8_case(MoEConfig("custom", T, H, I, E, k, "fp8", kind, 0), quantize, seed=seed)
+
+
+def _w4a16_weights(rng, H, I, E):
+    w13 = _bytes(rng, (E, 2 * I, H // 2))
+    s13 = _scales(rng, (E, 2 * I, H // 32))
+    w2 = _bytes(rng, (E, H, I // 2))
+    s2 = _scales(rng, (E, H, I // 32))
+    return dict(w13=w13, s13=s13, w2=w2, s2=s2)
+
+
+def grouped_contiguous_case(counts, H, I, pad, seed) -> dict:
+    """Contiguous grouped layout: expert g's counts[g] rows, then padding rows (index -1)
+    up to a multiple of `pad` rows, expert after expert. Draws: a bf16(N(0,1)) [M,H]
+    (padding rows too), then the W4A16 weights of len(counts) experts."""
+    rng = np.random.default_rng(seed)
+    counts = [int(c) for c in counts]
+    padded = [-(-c // pad) * pad for c in counts]
+    M = sum(padded)
+    a = bf16_bits(rng.standard_normal((M, H), dtype=np.float32))
+    m_indices = np.full(M, -1, np.int32)
+    at = 0
+    for g, (c, p) in enumerate(zip(counts, padded)):
+        m_indices[at:at + c] = g
+        at += p
+    return dict(a=a, m_indices=m_indices, **_w4a16_weights(rng, H, I, len(counts)))
+
+
+def grouped_masked_case(counts, max_m, H, I, seed) -> dict:
+    """Masked grouped layout: a [E, max_m, H] bf16(N(0,1)) (every budget row drawn),
+    masked_m = counts as int32, then the W4A16 weights of len(counts) experts."""
+    rng = np.random.default_rng(seed)
+    E = len(counts)
+    a = bf16_bits(rng.standard_normal((E, max_m, H), dtype=np.float32))
+    masked_m = np.asarray(counts, dtype=np.int32)
+    return dict(a=a, masked_m=masked_m, **_w4a16_weights(rng, H, I, E))
+
+
+GROUPED = {
+    "grouped_prefill": dict(layout="contiguous", E=48, rows=128, H=7168, I=2048, seed=SEED_BASE + 6),
+    "grouped_decode": dict(layout="masked", E=48, rows=32, max_m=64, H=7168, I=2048,
+                           seed=SEED_BASE + 7),
+}
+
+
+def grouped_case(name: str) -> dict:
+    """One of the GROUPED workloads: every expert holds the same number of valid rows."""
+    g = GROUPED[name]
+    counts = [g["rows"]] * g["E"]
+    if g["layout"] == "contiguous":
+        return grouped_contiguous_case(counts, g["H"], g["I"], 128, g["seed"])
+    return grouped_masked_case(counts, g["max_m"], g["H"], g["I"], g["seed"])
 
 
 def sample_rows(T: int, n: int, seed: int) -> np.ndarray:

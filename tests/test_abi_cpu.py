@@ -18,6 +18,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = binding.declared_functions()
     assert {"moe_topk_softmax", "moe_align", "moe_w4a16_forward", "moe_fp8_block_forward",
+            "moe_w4a16_grouped_contiguous", "moe_w4a16_grouped_masked",
             "qmoe_plan", "qmoe_fp8_quantize_blocks", "qmoe_fp8_quantize_blocks_bf16",
             "qmoe_status_string", "qmoe_last_error", "qmoe_abi_version"} <= set(names)
     for n in names:
@@ -112,3 +113,32 @@ def test_router_rejects_bad_arguments(lib):
     assert r(FAKE + 2, 4, 8, 2, 1, None, FAKE, FAKE, None) == INVALID
     assert r(FAKE, 4, 8, 2, 1, FAKE + 1, FAKE, FAKE, None) == INVALID  # misaligned map
     assert r(None, 0, 8, 2, 1, None, None, None, None) == OK  # empty: nothing launched
+
+
+def _grouped(lib, masked, M=128, H=7168, I=2048, E=48, em=0, sched=0, ptr=FAKE, route=FAKE,
+             ws=None, size=1 << 40, out=FAKE):
+    fn = lib.moe_w4a16_grouped_masked if masked else lib.moe_w4a16_grouped_contiguous
+    sz = ctypes.c_size_t(size)
+    st = fn(ptr, ptr, ptr, ptr, ptr, route, M, H, I, E, em, sched, out, ws, ctypes.byref(sz), None)
+    return st, sz.value
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_grouped_layouts_check_arguments(lib, masked):
+    st, need = _grouped(lib, masked)
+    assert st == OK
+    rows = 48 * 128 if masked else 128
+    # the indexed forward's workspace at k = 1, plus the weights of 1 (and the masked ids)
+    base = _w4(lib, T=rows, k=1, ws=None)[1]
+    assert need >= base + 4 * rows and need <= base + 8 * rows + 512
+    assert _grouped(lib, masked, ws=FAKE, size=need - 1)[0] == WORKSPACE
+    assert _grouped(lib, masked, ws=FAKE, size=need, route=None)[0] == INVALID
+    assert _grouped(lib, masked, ws=FAKE, size=need, route=FAKE + 2)[0] == INVALID
+    assert _grouped(lib, masked, ws=FAKE, size=need, ptr=FAKE + 8)[0] == INVALID
+    assert _grouped(lib, masked, ws=FAKE, size=need, out=None)[0] == INVALID
+    assert _grouped(lib, masked, M=-1, ws=FAKE)[0] == INVALID
+    assert _grouped(lib, masked, em=-1, ws=FAKE)[0] == INVALID
+    assert _grouped(lib, masked, H=7168 + 16, ws=FAKE)[0] == UNSUPPORTED
+    assert _grouped(lib, masked, E=0, ws=FAKE)[0] == INVALID
+    assert _grouped(lib, masked, sched=9, ws=FAKE)[0] == INVALID
+    assert _grouped(lib, masked, M=0, ws=FAKE, size=need)[0] == OK  # no rows: nothing launched
