@@ -34,12 +34,16 @@ def _load():
     lib.oracle_topk_softmax.restype = ctypes.c_int
     lib.oracle_w4a16_moe.argtypes = [_P] * 7 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
     lib.oracle_w4a16_moe.restype = ctypes.c_int
+    lib.oracle_mxfp4_moe.argtypes = [_P] * 7 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
+    lib.oracle_mxfp4_moe.restype = ctypes.c_int
     lib.oracle_fp8_moe.argtypes = [_P] * 8 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
     lib.oracle_fp8_moe.restype = ctypes.c_int
     lib.oracle_fp8_quantize_blocks.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P]
     lib.oracle_fp8_quantize_blocks.restype = ctypes.c_int
     lib.oracle_f64_to_bf16_array.argtypes = [_P, _I64, _P]
     lib.oracle_e4m3_to_f64_array.argtypes = [_P, _I64, _P]
+    lib.oracle_e2m1_to_f64_array.argtypes = [_P, _I64, _P]
+    lib.oracle_e8m0_to_f64_array.argtypes = [_P, _I64, _P]
     lib.oracle_f32_to_e4m3_array.argtypes = [_P, _I64, _P]
     _lib = lib
     return lib
@@ -101,18 +105,12 @@ def moe_align(topk_ids, E: int, B: int):
     return sorted_ids, expert_ids, int(ntp[0]), offs
 
 
-def w4a16_moe(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=None):
-    """Routed W4A16 MoE FFN in fp64 for the given token rows (all rows if None).
-
-    x [T,H] uint16 (bf16 bits); w13 [E,2I,H/2] uint8; s13 [E,2I,H/32] uint16;
-    w2 [E,H,I/2] uint8; s2 [E,H,I/32] uint16; topk_ids int32 [T,k];
-    topk_weights float32 [T,k]. Returns float64 [nrows, H] (before bf16 rounding).
-    """
+def _w4_moe(fn, sdtype, x, w13, s13, w2, s2, topk_ids, topk_weights, rows, nthreads):
     x = _c(x, np.uint16)
     w13 = _c(w13, np.uint8)
-    s13 = _c(s13, np.uint16)
+    s13 = _c(s13, sdtype)
     w2 = _c(w2, np.uint8)
-    s2 = _c(s2, np.uint16)
+    s2 = _c(s2, sdtype)
     ids = _c(topk_ids, np.int32)
     wts = _c(topk_weights, np.float32)
     T, H = x.shape
@@ -125,13 +123,31 @@ def w4a16_moe(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=N
         rows_arr = _c(np.asarray(rows, dtype=np.int64), np.int64)
         nrows, rp = rows_arr.size, _ptr(rows_arr)
     out = np.zeros((nrows, H), np.float64)
-    rc = _load().oracle_w4a16_moe(_ptr(x), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), _ptr(ids),
-                                  _ptr(wts), T, H, I, E, k, rp, nrows, _ptr(out),
-                                  nthreads or default_threads())
+    rc = getattr(_load(), fn)(_ptr(x), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), _ptr(ids),
+                              _ptr(wts), T, H, I, E, k, rp, nrows, _ptr(out),
+                              nthreads or default_threads())
     if rc != 0:
-        raise ValueError("oracle_w4a16_moe: bad arguments")
+        raise ValueError(f"{fn}: bad arguments")
     return out
 
+
+def w4a16_moe(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=None):
+    """Routed W4A16 MoE FFN in fp64 for the given token rows (all rows if None).
+
+    x [T,H] uint16 (bf16 bits); w13 [E,2I,H/2] uint8; s13 [E,2I,H/32] uint16;
+    w2 [E,H,I/2] uint8; s2 [E,H,I/32] uint16; topk_ids int32 [T,k];
+    topk_weights float32 [T,k]. Returns float64 [nrows, H] (before bf16 rounding).
+    """
+    return _w4_moe("oracle_w4a16_moe", np.uint16, x, w13, s13, w2, s2, topk_ids, topk_weights,
+                   rows, nthreads)
+
+
+def mxfp4_moe(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=None):
+    """Routed MoE FFN with MXFP4 weights (E2M1 codes packed like the INT4 codes, E8M0
+    scales per row and 32 columns: s13 [E,2I,H/32] uint8, s2 [E,H,I/32] uint8) and bf16
+    activations, in fp64. Returns float64 [nrows, H] (before bf16 rounding)."""
+    return _w4_moe("oracle_mxfp4_moe", np.uint8, x, w13, s13, w2, s2, topk_ids, topk_weights,
+                   rows, nthreads)
 
 def w4a16_grouped_contiguous(a, w13, s13, w2, s2, m_indices, rows=None, nthreads=None):
     """The W4A16 expert FFN on the contiguous grouped layout ("vLLM x Novita AI: Chord W4A16
@@ -193,6 +209,22 @@ def fp8_quantize_blocks(v, br: int, bc: int):
     if rc != 0:
         raise ValueError("oracle_fp8_quantize_blocks: bad arguments")
     return q, s
+
+
+def e2m1_to_f64(codes):
+    """E2M1 codes (low 4 bits of each uint8) -> float64."""
+    c = _c(np.asarray(codes, dtype=np.uint8), np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e2m1_to_f64_array(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def e8m0_to_f64(codes):
+    """E8M0 scale codes (uint8) -> float64 2^(code - 127); 255 -> NaN."""
+    c = _c(np.asarray(codes, dtype=np.uint8), np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _load().oracle_e8m0_to_f64_array(_ptr(c), c.size, _ptr(out))
+    return out
 
 
 def f64_to_bf16(x):

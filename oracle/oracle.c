@@ -25,6 +25,8 @@
  *           scales from the block absmax; per-token-group activation scales As).
  *  [LSG]    "guqiong96/Lsglang" README (SkillsMP page), section "Super Mix
  *           Prefill": the fp32-activation engine matches the CPU reference.
+ *  [XT]     "xiaotu-moe" (PyPI project page), overview: the weight-only formats the
+ *           MoE engine supports include MXFP4 (E2M1) beside BF16, FP8 and NVFP4.
  *
  * Readings where the pages are silent (each stated again in the design notes):
  *  - fused w13 rows [0, I) are gate, rows [I, 2I) are up;
@@ -32,6 +34,11 @@
  *  - INT4 byte c/2 holds code c, low nibble = even c; weight = (code - 8) * scale;
  *  - align order inside an expert's segment is ascending flat pair index;
  *    padding and tail slots hold P = T*k, unused block entries hold -1;
+ *  - MXFP4 weights (weight-only, bf16 activations, [XT] overview): E2M1 codes packed
+ *    like the INT4 codes (byte c/2, low nibble = even c), one E8M0 scale per row and
+ *    32 consecutive columns (the OCP microscaling block of 32); weight = e2m1(code) *
+ *    2^(scale - 127), with E2M1 = sign bit 3, exponent bits 2..1 (bias 1), mantissa
+ *    bit 0, exponent 0 subnormal (0.5 * mantissa); E8M0 code 255 is NaN;
  *  - routed ids outside [0, E) are dropped;
  *  - E4M3 is OCP E4M3FN, round-to-nearest-even after clamping to +-448;
  *    block scale = max(absmax, 1e-10) / 448;
@@ -273,23 +280,42 @@ int oracle_moe_align(const int32_t* topk_ids, int64_t P, int32_t E, int32_t B, i
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* Dequantized INT4 group-32 weight of row n, column c of a [N, K] matrix stored
- * as packed codes [N, K/2] (low nibble = even column) and bf16 scales [N, K/32]:
- * (code - 8) * scale, subtract then scale. Exact in fp64. */
-static double w4_weight(const uint8_t* w, const uint16_t* s, int64_t K, int64_t n, int64_t c) {
+/* E2M1 code (low 4 bits) -> value: sign bit 3, exponent bits 2..1 with bias 1,
+ * mantissa bit 0; exponent 0 is subnormal, 0.5 * mantissa. */
+double oracle_e2m1_to_f64(uint8_t c) {
+  int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
+  double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return sign ? -mag : mag;
+}
+
+/* E8M0 scale code -> 2^(code - 127); code 255 is NaN. */
+double oracle_e8m0_to_f64(uint8_t c) { return c == 255 ? NAN : ldexp(1.0, (int)c - 127); }
+
+enum { FMT_INT4 = 0, FMT_MXFP4 = 1 };
+
+/* Dequantized 4-bit weight of row n, column c of a [N, K] matrix stored as packed
+ * codes [N, K/2] (low nibble = even column) with one scale per row and 32 columns
+ * ([N, K/32]). INT4: bf16 scales, (code - 8) * scale, subtract then scale. MXFP4:
+ * E8M0 scales, e2m1(code) * 2^(scale - 127). Exact in fp64. */
+static double w4_weight(int fmt, const uint8_t* w, const void* s, int64_t K, int64_t n,
+                        int64_t c) {
   uint8_t byte = w[n * (K / 2) + c / 2];
   int code = (c & 1) ? (byte >> 4) & 0xF : byte & 0xF;
-  return ((double)code - 8.0) * oracle_bf16_to_f64(s[n * (K / 32) + c / 32]);
+  int64_t si = n * (K / 32) + c / 32;
+  if (fmt == FMT_MXFP4)
+    return oracle_e2m1_to_f64((uint8_t)code) * oracle_e8m0_to_f64(((const uint8_t*)s)[si]);
+  return ((double)code - 8.0) * oracle_bf16_to_f64(((const uint16_t*)s)[si]);
 }
 
 /* One token row of the routed MoE FFN with W4A16 experts:
  *   out[n] = sum_s w_s * sum_j h_j W2_e(n, j),  h_j = silu(g_j) * u_j,
  *   g_j = sum_c x_c W13_e(j, c),  u_j = sum_c x_c W13_e(I + j, c),
  * slots in s order, every sum sequential, all in fp64. h is kept in fp64. */
-static void w4a16_token(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
-                        const uint8_t* w2, const uint16_t* s2, const int32_t* ids,
+static void w4a16_token(int fmt, const uint16_t* x, const uint8_t* w13, const void* s13,
+                        const uint8_t* w2, const void* s2, const int32_t* ids,
                         const float* wts, int64_t t, int64_t H, int64_t I, int64_t E, int64_t k,
                         double* xrow, double* h, double* out) {
+  const int64_t ssz = fmt == FMT_MXFP4 ? 1 : 2; /* bytes per scale */
   for (int64_t c = 0; c < H; ++c) xrow[c] = oracle_bf16_to_f64(x[t * H + c]);
   for (int64_t n = 0; n < H; ++n) out[n] = 0.0;
   const int64_t w13_expert = 2 * I * (H / 2), s13_expert = 2 * I * (H / 32);
@@ -299,18 +325,18 @@ static void w4a16_token(const uint16_t* x, const uint8_t* w13, const uint16_t* s
     if (e < 0 || e >= E) continue;
     double wt = (double)wts[t * k + s];
     const uint8_t* we13 = w13 + e * w13_expert;
-    const uint16_t* se13 = s13 + e * s13_expert;
+    const uint8_t* se13 = (const uint8_t*)s13 + e * s13_expert * ssz;
     const uint8_t* we2 = w2 + e * w2_expert;
-    const uint16_t* se2 = s2 + e * s2_expert;
+    const uint8_t* se2 = (const uint8_t*)s2 + e * s2_expert * ssz;
     for (int64_t j = 0; j < I; ++j) {
       double g = 0.0, u = 0.0;
-      for (int64_t c = 0; c < H; ++c) g += xrow[c] * w4_weight(we13, se13, H, j, c);
-      for (int64_t c = 0; c < H; ++c) u += xrow[c] * w4_weight(we13, se13, H, I + j, c);
+      for (int64_t c = 0; c < H; ++c) g += xrow[c] * w4_weight(fmt, we13, se13, H, j, c);
+      for (int64_t c = 0; c < H; ++c) u += xrow[c] * w4_weight(fmt, we13, se13, H, I + j, c);
       h[j] = silu(g) * u;
     }
     for (int64_t n = 0; n < H; ++n) {
       double y = 0.0;
-      for (int64_t j = 0; j < I; ++j) y += h[j] * w4_weight(we2, se2, I, n, j);
+      for (int64_t j = 0; j < I; ++j) y += h[j] * w4_weight(fmt, we2, se2, I, n, j);
       out[n] += wt * y;
     }
   }
@@ -321,10 +347,10 @@ static void w4a16_token(const uint16_t* x, const uint8_t* w13, const uint16_t* s
  * bf16 bits; w2 [E,H,I/2] u8; s2 [E,H,I/32] bf16 bits; ids/wts [T,k].
  * out [nrows, H] fp64 before the final bf16 rounding. Rows are independent and
  * are spread over nthreads OpenMP threads; each row is computed as written. */
-int oracle_w4a16_moe(const uint16_t* x, const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
-                     const uint16_t* s2, const int32_t* ids, const float* wts, int64_t T, int64_t H,
-                     int64_t I, int64_t E, int64_t k, const int64_t* rows, int64_t nrows,
-                     double* out, int nthreads) {
+static int w4_moe(int fmt, const uint16_t* x, const uint8_t* w13, const void* s13,
+                  const uint8_t* w2, const void* s2, const int32_t* ids, const float* wts,
+                  int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const int64_t* rows,
+                  int64_t nrows, double* out, int nthreads) {
   if (!x || !w13 || !s13 || !w2 || !s2 || !ids || !wts || !out) return ORACLE_BAD_ARG;
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || H % 32 || I % 32) return ORACLE_BAD_ARG;
   if (!rows) nrows = T;
@@ -344,13 +370,31 @@ int oracle_w4a16_moe(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
 #pragma omp for schedule(dynamic, 1)
       for (int64_t r = 0; r < nrows; ++r) {
         int64_t t = rows ? rows[r] : r;
-        w4a16_token(x, w13, s13, w2, s2, ids, wts, t, H, I, E, k, xrow, h, out + r * H);
+        w4a16_token(fmt, x, w13, s13, w2, s2, ids, wts, t, H, I, E, k, xrow, h, out + r * H);
       }
     }
     free(xrow);
     free(h);
   }
   return bad ? ORACLE_BAD_ARG : ORACLE_OK;
+}
+
+int oracle_w4a16_moe(const uint16_t* x, const uint8_t* w13, const uint16_t* s13, const uint8_t* w2,
+                     const uint16_t* s2, const int32_t* ids, const float* wts, int64_t T, int64_t H,
+                     int64_t I, int64_t E, int64_t k, const int64_t* rows, int64_t nrows,
+                     double* out, int nthreads) {
+  return w4_moe(FMT_INT4, x, w13, s13, w2, s2, ids, wts, T, H, I, E, k, rows, nrows, out,
+                nthreads);
+}
+
+/* Routed MXFP4 MoE FFN (weight-only, [XT] overview): as oracle_w4a16_moe with E2M1
+ * codes and E8M0 scales s13 [E,2I,H/32] u8, s2 [E,H,I/32] u8. */
+int oracle_mxfp4_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* s13, const uint8_t* w2,
+                     const uint8_t* s2, const int32_t* ids, const float* wts, int64_t T, int64_t H,
+                     int64_t I, int64_t E, int64_t k, const int64_t* rows, int64_t nrows,
+                     double* out, int nthreads) {
+  return w4_moe(FMT_MXFP4, x, w13, s13, w2, s2, ids, wts, T, H, I, E, k, rows, nrows, out,
+                nthreads);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -449,6 +493,14 @@ void oracle_f64_to_bf16_array(const double* x, int64_t n, uint16_t* out) {
 
 void oracle_e4m3_to_f64_array(const uint8_t* c, int64_t n, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_to_f64(c[i]);
+}
+
+void oracle_e2m1_to_f64_array(const uint8_t* c, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e2m1_to_f64(c[i]);
+}
+
+void oracle_e8m0_to_f64_array(const uint8_t* c, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e8m0_to_f64(c[i]);
 }
 
 void oracle_f32_to_e4m3_array(const float* x, int64_t n, uint8_t* out) {

@@ -15,6 +15,12 @@ Block FP8 quantization kernel config guide", background section):
   fp8       1024 tokens, H 7168, I 2048, 32 experts, top-8, W8A8 block FP8
   full384   256 tokens, H 7168, I 2048, 384 experts, top-8, W4A16, uniform routing
 
+MXFP4 weights (weight-only, bf16 activations; "xiaotu-moe" project page, overview: the
+MoE engine's weight formats include MXFP4 (E2M1)), at the decode and prefill shapes:
+
+  decode_mxfp4   32 tokens, H 7168, I 2048, 48 experts, top-8, uniform routing
+  prefill_mxfp4  8192 tokens, H 7168, I 2048, 48 experts, top-8, Zipf(1.0) routing
+
 Grouped layouts (same page, SM90 grouped kernels, Figure 3 and the grouped rows of the
 measurements; rows already grouped by expert, one pair of weight 1 per row):
 
@@ -29,6 +35,9 @@ Recipe (per case, numpy default_rng(seed), draws in this order):
           w2 uniform bytes [E,H,I/2];  s2 bf16(|N(0,1)|*0.02) [E,H,I/32]
   FP8     per expert: w13 source N(0,1) [2I,H], then w2 source N(0,1) [H,I],
           each quantized in [128,128] blocks by the caller's quantizer
+  MXFP4   w13 uniform bytes [E,2I,H/2] (every E2M1 code, -0 included);
+          s13 E8M0 codes uniform in {119, 120, 121} (2^-8 .. 2^-6) [E,2I,H/32];
+          w2 uniform bytes [E,H,I/2]; s2 likewise [E,H,I/32]
 """
 from dataclasses import dataclass
 
@@ -45,7 +54,7 @@ class MoEConfig:
     I: int
     E: int
     k: int
-    fmt: str  # "w4a16" or "fp8"
+    fmt: str  # "w4a16", "mxfp4" or "fp8"
     routing: str  # "uniform" or "zipf"
     index: int  # 1-based position in the workload list; seeds are SEED_BASE + index
 
@@ -64,6 +73,8 @@ CONFIGS = {
     "prefill": MoEConfig("prefill", 8192, 7168, 2048, 48, 8, "w4a16", "zipf", 3),
     "fp8": MoEConfig("fp8", 1024, 7168, 2048, 32, 8, "fp8", "uniform", 4),
     "full384": MoEConfig("full384", 256, 7168, 2048, 384, 8, "w4a16", "uniform", 5),
+    "decode_mxfp4": MoEConfig("decode_mxfp4", 32, 7168, 2048, 48, 8, "mxfp4", "uniform", 8),
+    "prefill_mxfp4": MoEConfig("prefill_mxfp4", 8192, 7168, 2048, 48, 8, "mxfp4", "zipf", 9),
 }
 
 
@@ -138,6 +149,29 @@ def w4a16_case(cfg: MoEConfig, seed=None) -> dict:
     w2 = _bytes(rng, (E, H, I // 2))
     s2 = _scales(rng, (E, H, I // 32))
     return dict(x=x, topk_ids=ids, topk_weights=wts, w13=w13, s13=s13, w2=w2, s2=s2)
+
+
+def _e8m0(rng, shape):
+    return rng.integers(119, 122, size=shape, dtype=np.uint8)
+
+
+def mxfp4_case(cfg: MoEConfig, seed=None) -> dict:
+    """All host arrays of one MXFP4 case (see the module recipe)."""
+    if cfg.fmt != "mxfp4":
+        raise ValueError(cfg.fmt)
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    x = bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    ids, wts = routing(rng, T, E, k, cfg.routing)
+    w13 = _bytes(rng, (E, 2 * I, H // 2))
+    s13 = _e8m0(rng, (E, 2 * I, H // 32))
+    w2 = _bytes(rng, (E, H, I // 2))
+    s2 = _e8m0(rng, (E, H, I // 32))
+    return dict(x=x, topk_ids=ids, topk_weights=wts, w13=w13, s13=s13, w2=w2, s2=s2)
+
+
+def custom_mxfp4_case(T, H, I, E, k, seed, kind="uniform") -> dict:
+    return mxfp4_case(MoEConfig("custom", T, H, I, E, k, "mxfp4", kind, 0), seed=seed)
 
 
 def fp8_case(cfg: MoEConfig, quantize, seed=None) -> dict:
