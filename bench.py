@@ -8,7 +8,8 @@ graph); the per-kernel times come from a separate pass of K steps with HIP event
 around every kernel on its launch stream.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
-                  [--workload decode|prefill|fp8|full384|tiny|router|grouped_prefill|grouped_decode]
+                  [--workload decode|prefill|fp8|full384|tiny|router|grouped_prefill|grouped_decode|
+                              decode_mxfp4|prefill_mxfp4]
 
 Prints one JSON line. The default workload is the decode layer (32 tokens, hidden 7168,
 intermediate 2048, 48 local experts, top-8, INT4 group-32 weights); its value is the
@@ -43,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "fp8", "full384", "tiny", "router",
-                             "grouped_prefill", "grouped_decode"])
+                             "grouped_prefill", "grouped_decode", "decode_mxfp4",
+                             "prefill_mxfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
                     help="how the timed steps are issued: eager library calls (default), or "
@@ -59,9 +61,10 @@ def parse():
 
 def weight_bytes_per_expert(cfg):
     H, I = cfg.H, cfg.I
-    if cfg.fmt == "w4a16":
-        w13 = 2 * I * H // 2 + 2 * I * (H // 32) * 2
-        w2 = H * I // 2 + H * (I // 32) * 2
+    if cfg.fmt in ("w4a16", "mxfp4"):
+        sb = 2 if cfg.fmt == "w4a16" else 1  # bf16 or E8M0 scale bytes
+        w13 = 2 * I * H // 2 + 2 * I * (H // 32) * sb
+        w2 = H * I // 2 + H * (I // 32) * sb
     else:
         w13 = 2 * I * H + (2 * I // 128) * (H // 128) * 4
         w2 = H * I + (H // 128) * (I // 128) * 4
@@ -148,6 +151,10 @@ def main():
         cfg = inputs.CONFIGS[args.workload]
         case = inputs.w4a16_case(cfg)
         ids = case["topk_ids"]
+    elif inputs.CONFIGS[args.workload].fmt == "mxfp4":
+        cfg = inputs.CONFIGS[args.workload]
+        case = inputs.mxfp4_case(cfg)
+        ids = case["topk_ids"]
     else:
         cfg = inputs.CONFIGS[args.workload]
 
@@ -159,7 +166,8 @@ def main():
     d = to_dev(case)
     gen_s = time.time() - t_gen
 
-    fmt = binding.FORMAT_W4A16 if cfg.fmt == "w4a16" else binding.FORMAT_FP8
+    fmt = {"w4a16": binding.FORMAT_W4A16, "mxfp4": binding.FORMAT_MXFP4,
+           "fp8": binding.FORMAT_FP8}[cfg.fmt]
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
     if grouped:
         # The schedule AUTO picks from the expected rows per expert (k = 1).
@@ -185,6 +193,10 @@ def main():
     elif cfg.fmt == "w4a16":
         def step():
             binding.moe_w4a16_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
+                                      d["topk_weights"], out=out, workspace=workspace)
+    elif cfg.fmt == "mxfp4":
+        def step():
+            binding.moe_mxfp4_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
                                       d["topk_weights"], out=out, workspace=workspace)
     else:
         def step():
@@ -250,7 +262,7 @@ def main():
     w13_b, w2_b = weight_bytes_per_expert(cfg)
     weight_bytes = touched * (w13_b + w2_b)
     flops = pairs * (2 * cfg.H * 2 * cfg.I + 2 * cfg.I * cfg.H)
-    dtype = "bf16" if cfg.fmt == "w4a16" else "fp8"
+    dtype = "fp8" if cfg.fmt == "fp8" else "bf16"
     hbm_bound = chosen == binding.SCHEDULE_DECODE
     if hbm_bound:
         value, unit = weight_bytes / (ms_per_step * 1e-3) / 1e9, "GB/s"
@@ -281,6 +293,7 @@ def main():
         import oracle
         nthreads = oracle.default_threads()
         default_rows = {"tiny": cfg.T, "decode": cfg.T, "full384": 32, "prefill": 16, "fp8": 8,
+                        "decode_mxfp4": cfg.T, "prefill_mxfp4": 16,
                         "grouped_prefill": 1536, "grouped_decode": 1536}
         nrows = args.cpu_rows or default_rows[args.workload]
         valid_rows = np.flatnonzero(valid.any(axis=1))
@@ -293,6 +306,9 @@ def main():
             oracle.w4a16_grouped_contiguous(case["a"], case["w13"], case["s13"], case["w2"],
                                             case["s2"], case["m_indices"], rows=rows,
                                             nthreads=nthreads)
+        elif cfg.fmt == "mxfp4":
+            oracle.mxfp4_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
+                             case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
         elif cfg.fmt == "w4a16":
             oracle.w4a16_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
                              case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
@@ -311,7 +327,9 @@ def main():
                          f"{valid_rows.size}/{len(rows)}"}
 
     names = {"decode": "decode W4A16", "prefill": "prefill W4A16 (Zipf routing)",
-             "fp8": "block-FP8 W8A8", "full384": "full 384-expert W4A16", "tiny": "tiny W4A16"}
+             "fp8": "block-FP8 W8A8", "full384": "full 384-expert W4A16", "tiny": "tiny W4A16",
+             "decode_mxfp4": "decode MXFP4 (E2M1 + E8M0 per 32, bf16 activations)",
+             "prefill_mxfp4": "prefill MXFP4 (E2M1 + E8M0 per 32, bf16 activations; Zipf routing)"}
     if grouped:
         layout = (f"masked, {g['rows']} valid rows per expert in a budget of {g['max_m']}"
                   if masked else f"contiguous, {g['rows']} rows per expert")

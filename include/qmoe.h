@@ -12,6 +12,8 @@
  *           optimizations" (indexed kernels; H200 and Blackwell indexed decode;
  *           SM90 grouped kernels); Figure 3 (where the padding lives); "Measurements"
  *           (the grouped prefill and decode rows).
+ *   [XT]    "xiaotu-moe" (PyPI project page): overview (the MoE engine's weight
+ *           formats: BF16, FP8 (WNA16), MXFP4 (E2M1), NVFP4).
  *   [SGL]   "SGLang W8A8 Block FP8 quantization kernel config guide" (xdnf.cn):
  *           background section (E4M3, [BLOCK_N, BLOCK_K] weight blocks, per-token-group
  *           activation scales As, weight block scales Bs); kernel dispatch section
@@ -213,6 +215,31 @@ qmoe_status moe_w4a16_grouped_masked(const uint16_t* a, const uint8_t* w13, cons
                                      void* stream);
 
 /*
+ * moe_mxfp4_forward - routed MoE expert FFN with BF16 activations and MXFP4 weights
+ * ([XT] overview: MXFP4 (E2M1) is one of the weight-only formats of the MoE engine, beside
+ * BF16, FP8 (WNA16) and NVFP4). Reading: the OCP microscaling layout, one E8M0 scale per
+ * weight row and 32 consecutive k, with E2M1 codes packed two per byte like the INT4 codes.
+ *
+ *   w13, s13     [E, 2I, H/2] uint8 and [E, 2I, H/32] uint8: byte c/2 of a row holds
+ *                E2M1 code c in its low nibble for even c, high nibble for odd c (bit 3
+ *                sign, bits 2..1 exponent with bias 1, bit 0 mantissa; exponent 0 is
+ *                0.5 * mantissa); s13 holds E8M0 codes, weight(n, c) = e2m1(code) *
+ *                2^(s13[n, c/32] - 127).
+ *   w2, s2       [E, H, I/2] and [E, H, I/32] uint8: down projection, same format.
+ *   x, topk_ids, topk_weights, T, H, I, E, k, schedule, out, workspace: as
+ *   moe_w4a16_forward (out = bf16 of the same FFN sum with these weights).
+ * Scale codes must lie in 1..254 and keep every scaled weight a normal bf16 (code 255 is
+ * NaN in the format; the matrix-core converts take only the scale's exponent, so code 0
+ * and results below the bf16 normal range are not defined here). Requires H % 32 == 0
+ * and I % 32 == 0 (QMOE_ERR_UNSUPPORTED otherwise).
+ */
+qmoe_status moe_mxfp4_forward(const uint16_t* x, const uint8_t* w13, const uint8_t* s13,
+                              const uint8_t* w2, const uint8_t* s2, const int32_t* topk_ids,
+                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
+                              void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * moe_fp8_block_forward - routed MoE expert FFN, W8A8 block FP8 ([SGL] background:
  * E4M3 weights with one fp32 scale per [128, 128] block, activations E4M3 with one fp32
  * scale per token and 128-column group; block scale = absmax / 448).
@@ -258,7 +285,7 @@ qmoe_status qmoe_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t 
 
 /*
  * qmoe_plan - the schedule and align block size a forward would use.
- *   format      0 = W4A16, 1 = W8A8 block FP8.
+ *   format      0 = W4A16, 1 = W8A8 block FP8, 2 = MXFP4 (weight-only).
  *   schedule    requested qmoe_schedule (AUTO resolves here).
  *   chosen      out: QMOE_SCHEDULE_DECODE or QMOE_SCHEDULE_PREFILL.
  *   block_m     out: align block size of that schedule.

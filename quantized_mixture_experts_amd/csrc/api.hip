@@ -34,7 +34,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr size_t kRegionAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-enum Format { kW4A16 = 0, kFp8 = 1 };
+enum Format { kW4A16 = 0, kFp8 = 1, kMxfp4 = 2 };
+// The 4-bit formats share the W4A16 kernels, workspace and limits.
+bool four_bit(int fmt) { return fmt == kW4A16 || fmt == kMxfp4; }
 
 // Rows per weight pass of the decode kernels, in 16-row blocks.
 int decode_mb_for(double) { return 1; }
@@ -61,10 +63,12 @@ qmoe_status check_shape(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int
     return fail(QMOE_ERR_UNSUPPORTED, "expert count %d exceeds %d", E, QMOE_MAX_EXPERTS);
   if (schedule < QMOE_SCHEDULE_AUTO || schedule > QMOE_SCHEDULE_PREFILL)
     return fail(QMOE_ERR_INVALID_ARG, "unknown schedule %d", schedule);
-  const int q = (fmt == kW4A16) ? 32 : 128;
+  const int q = four_bit(fmt) ? 32 : 128;
   if (H % q || I % q)
     return fail(QMOE_ERR_UNSUPPORTED, "%s needs H and I multiples of %d (H=%d I=%d)",
-                fmt == kW4A16 ? "W4A16 group-32" : "block FP8 [128,128]", q, H, I);
+                fmt == kW4A16 ? "W4A16 group-32" : fmt == kMxfp4 ? "MXFP4 block-32"
+                                                                 : "block FP8 [128,128]",
+                q, H, I);
   const int64_t P = (int64_t)T * k;
   const int64_t L = P + (int64_t)E * (kSegRows - 1);
   if (L >= (int64_t(1) << 31) || (int64_t)L * (int64_t)I >= (int64_t(1) << 40))
@@ -86,17 +90,17 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   // weights once per 16-row block, so it loses to the tile kernels past about 56 routed
   // rows per expert for W4A16 (48: 0.94 vs 1.08 ms; 64: 1.19 vs 1.08 ms) and past about
   // 12 for block FP8 (8: 0.30 vs 0.38 ms; 16: 0.52 vs 0.38 ms).
-  const double crossover = fmt == kW4A16 ? 56.0 : 12.0;
+  const double crossover = four_bit(fmt) ? 56.0 : 12.0;
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= crossover ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
   p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 2;
   p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&
-            (fmt == kW4A16 ? w4a16_tiled_supported(H, I) : fp8_tiled_supported(H, I));
+            (four_bit(fmt) ? w4a16_tiled_supported(H, I) : fp8_tiled_supported(H, I));
   p.block_m = kSegRows;
   p.L = p.P + (int64_t)E * (p.block_m - 1);
   p.NB = (p.L + p.block_m - 1) / p.block_m;
   // The tile kernels address activation rows with 32-bit byte offsets.
-  if (p.tiled && fmt == kW4A16 &&
+  if (p.tiled && four_bit(fmt) &&
       (uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32))
     p.tiled = false;
   size_t cur = 0;
@@ -110,7 +114,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   p.off_ntp = take(sizeof(int32_t));
   p.off_offsets = take(sizeof(int32_t) * (E + 1));
   p.off_tiles = take(sizeof(int32_t) * (E + 1));
-  if (fmt == kW4A16) {
+  if (four_bit(fmt)) {
     p.off_xs = take(sizeof(uint16_t) * (size_t)p.L * H);
     p.off_h = take(sizeof(uint16_t) * (size_t)p.L * I);
   } else {
@@ -188,9 +192,10 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
   r.k = k;
   r.E = E;
   r.L = (int32_t)p.L;
+  const bool mx = p.fmt == kMxfp4;
   W4A16Problem prob{x, region<uint16_t>(workspace, p.off_xs), w13, s13, w2, s2,
                     region<uint16_t>(workspace, p.off_h), region<float>(workspace, p.off_out32),
-                    T, H, I};
+                    T, H, I, mx};
 
   if (p.tiled) {
     const int32_t tm = w4a16_tiled_rows();
@@ -204,7 +209,7 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
     });
     if (err != hipSuccess) return hip_fail(err, "align launch");
     err = staged(QMOE_STAGE_ALIGN, s, [&] {
-      return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s);
+      return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s, mx);
     });
     if (err != hipSuccess) return hip_fail(err, "gather launch");
     err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_tiled(prob, r, s); });
@@ -234,7 +239,7 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
   if (err != hipSuccess) return hip_fail(err, "align launch");
   // The gathered activation rows belong to the align stage's timing.
   err = staged(QMOE_STAGE_ALIGN, s, [&] {
-    return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s);
+    return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s, mx);
   });
   if (err != hipSuccess) return hip_fail(err, "gather launch");
   err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_stream(prob, r, p.mb, s); });
@@ -373,7 +378,7 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
                       int32_t schedule, int32_t* chosen, int32_t* block_m,
                       size_t* workspace_bytes) {
   g_last_error[0] = 0;
-  if (format != kW4A16 && format != kFp8)
+  if (format != kW4A16 && format != kFp8 && format != kMxfp4)
     return fail(QMOE_ERR_INVALID_ARG, "unknown format %d", format);
   qmoe_status st = check_shape(format, T, H, I, E, k, schedule);
   if (st != QMOE_OK) return st;
@@ -384,16 +389,17 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
   return QMOE_OK;
 }
 
-qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
-                              const uint8_t* w2, const uint16_t* s2, const int32_t* topk_ids,
-                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
-                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
-                              void* workspace, size_t* workspace_bytes, void* stream) {
+namespace {
+qmoe_status four_bit_forward(int fmt, const uint16_t* x, const uint8_t* w13, const void* s13,
+                             const uint8_t* w2, const void* s2, const int32_t* topk_ids,
+                             const float* topk_weights, int32_t T, int32_t H, int32_t I,
+                             int32_t E, int32_t k, int32_t schedule, uint16_t* out,
+                             void* workspace, size_t* workspace_bytes, void* stream) {
   g_last_error[0] = 0;
-  qmoe_status st = check_shape(kW4A16, T, H, I, E, k, schedule);
+  qmoe_status st = check_shape(fmt, T, H, I, E, k, schedule);
   if (st != QMOE_OK) return st;
   if (!workspace_bytes) return fail(QMOE_ERR_INVALID_ARG, "workspace_bytes is NULL");
-  const Plan p = make_plan(kW4A16, T, H, I, E, k, schedule);
+  const Plan p = make_plan(fmt, T, H, I, E, k, schedule);
   if (!workspace) {
     *workspace_bytes = p.total;
     return QMOE_OK;
@@ -409,8 +415,28 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
   if (!aligned(workspace, kRegionAlign))
     return fail(QMOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
-  return w4a16_run(p, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k, out,
+  return w4a16_run(p, x, w13, static_cast<const uint16_t*>(s13), w2,
+                   static_cast<const uint16_t*>(s2), topk_ids, topk_weights, T, H, I, E, k, out,
                    workspace, static_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                              const uint8_t* w2, const uint16_t* s2, const int32_t* topk_ids,
+                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
+                              void* workspace, size_t* workspace_bytes, void* stream) {
+  return four_bit_forward(kW4A16, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k,
+                          schedule, out, workspace, workspace_bytes, stream);
+}
+
+qmoe_status moe_mxfp4_forward(const uint16_t* x, const uint8_t* w13, const uint8_t* s13,
+                              const uint8_t* w2, const uint8_t* s2, const int32_t* topk_ids,
+                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
+                              void* workspace, size_t* workspace_bytes, void* stream) {
+  return four_bit_forward(kMxfp4, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k,
+                          schedule, out, workspace, workspace_bytes, stream);
 }
 
 qmoe_status moe_w4a16_grouped_contiguous(const uint16_t* a, const uint8_t* w13,

@@ -125,11 +125,49 @@ __device__ __forceinline__ int operand_pos8(int e) { return ((e & 3) << 1) | (e 
 // Element offset of (row r, k index k) of an [rows, K] activation matrix in the tiled
 // operand layout used for the GEMMs' activation side: the operand of one (16-row block,
 // 32-deep k group) is 64 lanes x 16 B contiguous, lane (k slice q = (k % 32) / 8) * 16 +
-// (row r % 16) holding that slice's 8 values in operand k order. Rows must come in whole
-// 16-row blocks; the footprint equals the row-major one.
+// (row r % 16) holding that slice's 8 values in operand k order, or in natural order
+// when kNatural (the order the FP4 converts produce). Rows must come in whole 16-row
+// blocks; the footprint equals the row-major one.
+template <bool kNatural = false>
 __device__ __forceinline__ size_t tiled_offset(int r, int k, int K) {
   const int m = r & 15, q = (k >> 3) & 3;
-  return (((size_t)(r >> 4) * (K >> 5) + (k >> 5)) * 64 + q * 16 + m) * 8 + operand_pos8(k & 7);
+  const int pos = kNatural ? (k & 7) : operand_pos8(k & 7);
+  return (((size_t)(r >> 4) * (K >> 5) + (k >> 5)) * 64 + q * 16 + m) * 8 + pos;
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 codes -> bf16 operand registers.
+// A 32-bit word holds 8 E2M1 codes, code j in bits 4j..4j+3 (byte j/2, low nibble for
+// even j). v_cvt_scalef32_pk_bf16_fp4 turns byte `sel` into the bf16 pair (code 2 sel,
+// code 2 sel + 1) times 2^(exponent of the fp32 scale operand): with a power-of-two
+// scale every result is exact (E2M1 has one mantissa bit), so the four pairs are the
+// dequantized weights in natural k order.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_pair_sel(uint32_t w, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, SEL));
+}
+
+// Pair `sel` (a constant after unrolling) of fp4_to_bf16.
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t w, float scale, int sel) {
+  switch (sel) {
+    case 0: return fp4_pair_sel<0>(w, scale);
+    case 1: return fp4_pair_sel<1>(w, scale);
+    case 2: return fp4_pair_sel<2>(w, scale);
+    default: return fp4_pair_sel<3>(w, scale);
+  }
+}
+
+__device__ __forceinline__ void fp4_to_bf16(uint32_t w, float scale, uint32_t (&b)[4]) {
+  b[0] = fp4_pair_sel<0>(w, scale);
+  b[1] = fp4_pair_sel<1>(w, scale);
+  b[2] = fp4_pair_sel<2>(w, scale);
+  b[3] = fp4_pair_sel<3>(w, scale);
+}
+
+// E8M0 scale code -> an fp32 whose exponent field is the code (2^(code - 127) for codes
+// 1..254), the form the FP4 converts take their scale in.
+__device__ __forceinline__ float e8m0_scale(uint32_t code) {
+  return __builtin_bit_cast(float, (code & 0xFFu) << 23);
 }
 
 // ---------------------------------------------------------------------------

@@ -49,6 +49,8 @@ struct Routing {
   int32_t P, k, E, L;
 };
 
+// The 4-bit weight formats: INT4 codes with bf16 scales (mx = false) or MXFP4 E2M1
+// codes with E8M0 scales (mx = true, s13 / s2 then point at the scale bytes).
 struct W4A16Problem {
   const uint16_t* x;  // [T, H] bf16
   uint16_t* xs;       // [L, H] bf16: x gathered by sorted row, operand k order
@@ -59,6 +61,7 @@ struct W4A16Problem {
   uint16_t* h;    // [L, I] bf16
   float* out32;   // [T, H]
   int32_t T, H, I;
+  bool mx;
 };
 
 struct Fp8Problem {
@@ -75,9 +78,10 @@ struct Fp8Problem {
   int32_t T, H, I;
 };
 
-// xs[r] = x[token of sorted row r] in the GEMM operand k order.
+// xs[r] = x[token of sorted row r] in the GEMM operand k order (natural k order for
+// the MXFP4 kernels).
 hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t* ntp, int32_t H,
-                              uint16_t* xs, hipStream_t stream);
+                              uint16_t* xs, hipStream_t stream, bool natural = false);
 
 // Decode profile: a work-group owns (expert, column chunk) and streams the weights
 // once per pass of up to 16*mb rows of that expert.

@@ -31,6 +31,13 @@
 //     contiguous.
 // gate_up fuses SiLU(gate) * up and stores h (bf16, tiled by sorted row); down scales by
 // the routing weight and scatter-adds into the fp32 output with hardware atomics.
+//
+// MXFP4 weights (E2M1 codes, E8M0 scales per 32 k; the weight-only MXFP4 format of the
+// "xiaotu-moe" project page, overview) run through the same kernels with MX = true: one
+// v_cvt_scalef32_pk_bf16_fp4 per code pair gives the exact scaled bf16 weight (the scale
+// is a power of two), so there is no zero-point term and no scale multiply after the
+// MFMA, which accumulates in place. The FP4 converts produce natural k order, so the
+// activation rows and h use the natural-order tiled layout.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -53,7 +60,7 @@ enum class Epi { GateUp, Down };
 struct StreamArgs {
   const uint16_t* act;        // [L, K] activation rows, tiled layout (tiled_offset)
   const uint8_t* w;           // [E, N, K/2]
-  const uint16_t* s;          // [E, N, K/32]
+  const uint16_t* s;          // [E, N, K/32] bf16 (INT4) or E8M0 bytes (MXFP4)
   const int32_t* sorted_ids;  // [L]
   const int32_t* offsets;     // [E + 1]
   const int32_t* expert_ids;  // [L / 16], expert of each 16-row block
@@ -74,7 +81,7 @@ struct Stage {
 constexpr int kScaleBlockSteps = 8;  // one 128 B line of bf16 scales = 64 groups = 8 steps
 constexpr int kStages = 4;           // weight register stages (loads run kStages-1 ahead)
 
-template <Epi EPI, int MB>
+template <Epi EPI, int MB, bool MX>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(2)))
     w4a16_stream_kernel(StreamArgs a) {
@@ -122,10 +129,12 @@ __global__ void __launch_bounds__(kThreads)
   const int K = a.K, G = K / 32, KB = K / 2;
   const uint8_t* wrow[2];
   const uint16_t* srow[2];
+  const uint8_t* mrow[2];  // MXFP4: the row's E8M0 scale bytes
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     wrow[t] = a.w + ((size_t)e * a.N + row[t]) * KB;
     srow[t] = a.s + ((size_t)e * a.N + row[t]) * G;
+    mrow[t] = reinterpret_cast<const uint8_t*>(a.s) + ((size_t)e * a.N + row[t]) * G;
   }
   const int nstep = G / 8;  // full 256-deep steps
   const int nchunk = (G + kChunkGroups - 1) / kChunkGroups;
@@ -172,8 +181,11 @@ __global__ void __launch_bounds__(kThreads)
         for (int i = 0; i < kChunkPieces; ++i) {
           const int g = wave + kWavesPerGroup * i;
           a_lds[buf][b][g][lane] = creg[b][i];
-          const uint32_t av[4] = {creg[b][i][0], creg[b][i][1], creg[b][i][2], creg[b][i][3]};
-          c_lds[buf][b][g][lane] = mfma_bf16_16x16x32(av, neg136, zero4);
+          if constexpr (!MX) {
+            const uint32_t av[4] = {creg[b][i][0], creg[b][i][1], creg[b][i][2],
+                                    creg[b][i][3]};
+            c_lds[buf][b][g][lane] = mfma_bf16_16x16x32(av, neg136, zero4);
+          }
         }
     };
 
@@ -228,9 +240,22 @@ __global__ void __launch_bounds__(kThreads)
         av[b][1] = v[1];
         av[b][2] = v[2];
         av[b][3] = v[3];
-        corr[b] = c_lds[buf][b][gl][lane];
+        if constexpr (!MX) corr[b] = c_lds[buf][b][gl][lane];
       }
       uint32_t bw0[4], bw1[4];
+      if constexpr (MX) {
+        // sc0, sc1: E8M0 scales in the converts' fp32 form
+        fp4_to_bf16(w0, sc0, bw0);
+        fp4_to_bf16(w1, sc1, bw1);
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          if (b < nmb) {
+            acc[0][b] = mfma_bf16_16x16x32(av[b], bw0, acc[0][b]);
+            acc[1][b] = mfma_bf16_16x16x32(av[b], bw1, acc[1][b]);
+          }
+        }
+        return;
+      }
       int4_to_bf16_biased(w0, nib, one28, bw0);
       int4_to_bf16_biased(w1, nib, one28, bw1);
 #pragma unroll
@@ -245,8 +270,9 @@ __global__ void __launch_bounds__(kThreads)
     };
 
     // A full step (eight groups) from the staged weights; gl0 = first group in chunk,
-    // sp = the step's scale piece within the current scale block.
-    auto compute = [&](Stage& st, int buf, int gl0, int sp) {
+    // sp = the step's scale piece within the current scale block, it = the step. MXFP4
+    // reads its scale bytes directly (this kernel serves only K not a multiple of 512).
+    auto compute = [&](Stage& st, int buf, int gl0, int sp, int it) {
       const u32x4 sv[2] = {s_lds[wave][0][col][sp], s_lds[wave][1][col][sp]};
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -260,9 +286,15 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int g = 4 * half + g4;
-          const uint32_t s0w = sv[0][g >> 1], s1w = sv[1][g >> 1];
-          const float sc0 = (g & 1) ? bf16_hi(s0w) : bf16_lo(s0w);
-          const float sc1 = (g & 1) ? bf16_hi(s1w) : bf16_lo(s1w);
+          float sc0, sc1;
+          if constexpr (MX) {
+            sc0 = e8m0_scale(mrow[0][it * 8 + g]);
+            sc1 = e8m0_scale(mrow[1][it * 8 + g]);
+          } else {
+            const uint32_t s0w = sv[0][g >> 1], s1w = sv[1][g >> 1];
+            sc0 = (g & 1) ? bf16_hi(s0w) : bf16_lo(s0w);
+            sc1 = (g & 1) ? bf16_hi(s1w) : bf16_lo(s1w);
+          }
           group(buf, gl0 + g, wt[0][g4], wt[1][g4], sc0, sc1);
         }
       }
@@ -293,7 +325,7 @@ __global__ void __launch_bounds__(kThreads)
           const int it = blk * kScaleBlockSteps + j;
           const int c = it / 2, buf = c & 1;
           load(st[(j + kStages - 1) % kStages], min(it + kStages - 1, last));
-          if (it < nstep) compute(st[j % kStages], buf, 8 * (j & 1), j);
+          if (it < nstep) compute(st[j % kStages], buf, 8 * (j & 1), j, it);
           if (j & 1) {
             // Chunk boundary: chunk c+1 goes to the other buffer (whose readers, chunk
             // c-1, all passed the previous barrier), then the next chunk is requested.
@@ -310,7 +342,10 @@ __global__ void __launch_bounds__(kThreads)
       const int c = g / kChunkGroups;
       const uint32_t w0 = *reinterpret_cast<const uint32_t*>(wrow[0] + g * 16 + 4 * quad);
       const uint32_t w1 = *reinterpret_cast<const uint32_t*>(wrow[1] + g * 16 + 4 * quad);
-      group(c & 1, g % kChunkGroups, w0, w1, bf16_to_f32(srow[0][g]), bf16_to_f32(srow[1][g]));
+      if constexpr (MX)
+        group(c & 1, g % kChunkGroups, w0, w1, e8m0_scale(mrow[0][g]), e8m0_scale(mrow[1][g]));
+      else
+        group(c & 1, g % kChunkGroups, w0, w1, bf16_to_f32(srow[0][g]), bf16_to_f32(srow[1][g]));
     }
 
     // Epilogue.
@@ -322,7 +357,7 @@ __global__ void __launch_bounds__(kThreads)
         if (tile_ok[0]) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            a.h[tiled_offset(rbase + r, j0 + col, a.I)] =
+            a.h[tiled_offset<MX>(rbase + r, j0 + col, a.I)] =
                 f32_to_bf16(silu_f32(acc[0][b][r]) * acc[1][b][r]);
         }
       } else {
@@ -389,7 +424,7 @@ __device__ __forceinline__ int32_t ld_invariant(const int32_t* p, int i) {
   return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
-template <Epi EPI>
+template <Epi EPI, bool MX>
 __global__ void __launch_bounds__(kPThreads)
     __attribute__((amdgpu_waves_per_eu(kPWavesPerEu)))
     w4a16_persist_kernel(StreamArgs a) {
@@ -496,24 +531,46 @@ __global__ void __launch_bounds__(kPThreads)
   // A block's scales: load i covers tile i / 2, rows 8 (i % 2) .. + 7, one 128 B line
   // per row (lane l: row + l / 8, 16 B piece l % 8, i.e. step l % 8 of the block). Pieces
   // past the end of a row are clamped into it (never used).
+  // MXFP4: the block is 64 B per row (one E8M0 byte per group), lane piece l % 8 is the
+  // step's 8 B.
   u32x4 snext[4];
   const int s_row = lane >> 3, s_piece = lane & 7;
   auto scale_block_load = [&](const Unit& d) {
-    const int off = min((d.kc & ~(kScaleUnits - 1)) * 32 + s_piece * 16, G * 2 - 16);
+    if constexpr (MX) {
+      const int off = min((d.kc & ~(kScaleUnits - 1)) * 16 + s_piece * 8, G - 8);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = tile_row0(d.cc, i >> 1) + 8 * (i & 1) + s_row;
-      snext[i] = ld16(reinterpret_cast<const uint8_t*>(a.s) + ((size_t)d.e * N + row) * G * 2 + off);
+      for (int i = 0; i < 4; ++i) {
+        const int row = tile_row0(d.cc, i >> 1) + 8 * (i & 1) + s_row;
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(
+            reinterpret_cast<const uint8_t*>(a.s) + ((size_t)d.e * N + row) * G + off);
+        snext[i] = u32x4{p[0], p[1], 0u, 0u};
+      }
+    } else {
+      const int off = min((d.kc & ~(kScaleUnits - 1)) * 32 + s_piece * 16, G * 2 - 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = tile_row0(d.cc, i >> 1) + 8 * (i & 1) + s_row;
+        snext[i] = ld16(reinterpret_cast<const uint8_t*>(a.s) + ((size_t)d.e * N + row) * G * 2 + off);
+      }
     }
   };
   auto scale_block_store = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 v = snext[i];
-      s_lds[wave][i >> 1][s_piece][0][8 * (i & 1) + s_row] =
-          f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-      s_lds[wave][i >> 1][s_piece][1][8 * (i & 1) + s_row] =
-          f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+      if constexpr (MX) {
+        s_lds[wave][i >> 1][s_piece][0][8 * (i & 1) + s_row] =
+            f32x4{e8m0_scale(v[0]), e8m0_scale(v[0] >> 8), e8m0_scale(v[0] >> 16),
+                  e8m0_scale(v[0] >> 24)};
+        s_lds[wave][i >> 1][s_piece][1][8 * (i & 1) + s_row] =
+            f32x4{e8m0_scale(v[1]), e8m0_scale(v[1] >> 8), e8m0_scale(v[1] >> 16),
+                  e8m0_scale(v[1] >> 24)};
+      } else {
+        s_lds[wave][i >> 1][s_piece][0][8 * (i & 1) + s_row] =
+            f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
+        s_lds[wave][i >> 1][s_piece][1][8 * (i & 1) + s_row] =
+            f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
+      }
     }
   };
   // First unit of the block after unit u's (the next item's first unit at an item end).
@@ -535,9 +592,11 @@ __global__ void __launch_bounds__(kPThreads)
     for (int i = 0; i < kPPieces; ++i) {
       const int g = wave + kPWaves * i;
       a_lds[buf][g][lane] = creg[i];
-      const uint32_t av[4] = {creg[i][0], creg[i][1], creg[i][2], creg[i][3]};
-      const f32x4 c = mfma_bf16_16x16x32(av, neg136, zero4);
-      if (col == 0) *reinterpret_cast<f32x4*>(&c_lds[buf][g][4 * quad]) = c;
+      if constexpr (!MX) {
+        const uint32_t av[4] = {creg[i][0], creg[i][1], creg[i][2], creg[i][3]};
+        const f32x4 c = mfma_bf16_16x16x32(av, neg136, zero4);
+        if (col == 0) *reinterpret_cast<f32x4*>(&c_lds[buf][g][4 * quad]) = c;
+      }
     }
   };
 
@@ -557,6 +616,21 @@ __global__ void __launch_bounds__(kPThreads)
 #pragma unroll
         for (int i = 0; i < 4; ++i) wt[t][i] = s.w[t][half][i];
         transpose4_rows(wt[t]);
+      }
+      if constexpr (MX) {
+        // Exact scaled weights from the converts; the MFMAs accumulate in place.
+#pragma unroll
+        for (int gb = 0; gb < 4; ++gb) {
+          const u32x4 v = a_lds[buf][8 * p + 4 * half + gb][lane];
+          const uint32_t a4[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            uint32_t bw[4];
+            fp4_to_bf16(wt[t][gb], sv[t][half][gb], bw);
+            acc[t] = mfma_bf16_16x16x32(a4, bw, acc[t]);
+          }
+        }
+        continue;
       }
 #pragma unroll
       for (int b0 = 0; b0 < 4; b0 += kPBatch) {
@@ -613,7 +687,7 @@ __global__ void __launch_bounds__(kPThreads)
       if (j0 < a.I) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          a.h[tiled_offset(rbase + r, j0 + col, a.I)] =
+          a.h[tiled_offset<MX>(rbase + r, j0 + col, a.I)] =
               f32_to_bf16(silu_f32(acc[0][r]) * acc[1][r]);
       }
     } else {
@@ -698,6 +772,7 @@ constexpr int kGatherThreads = 256;
 constexpr int kGatherWaves = kGatherThreads / kWave;
 constexpr int kGatherGroups = 32;  // 1024 columns per work-group
 
+template <bool kNatural>
 __global__ void __launch_bounds__(kGatherThreads)
     gather_rows_kernel(const uint16_t* __restrict__ x, const int32_t* __restrict__ sorted_ids,
                        const int32_t* __restrict__ ntp, int32_t P, int32_t k, int32_t H,
@@ -716,17 +791,20 @@ __global__ void __launch_bounds__(kGatherThreads)
   for (; kg + kGatherWaves < kg_end; kg += 2 * kGatherWaves) {
     const u32x4 v0 = ld16(src + kg * 32);
     const u32x4 v1 = ld16(src + (kg + kGatherWaves) * 32);
-    uint32_t p0[4], p1[4];
-    perm_act8(v0, p0);
-    perm_act8(v1, p1);
+    uint32_t p0[4] = {v0[0], v0[1], v0[2], v0[3]}, p1[4] = {v1[0], v1[1], v1[2], v1[3]};
+    if constexpr (!kNatural) {
+      perm_act8(v0, p0);
+      perm_act8(v1, p1);
+    }
     *reinterpret_cast<u32x4*>(dst + (size_t)kg * 512) =
         real ? u32x4{p0[0], p0[1], p0[2], p0[3]} : u32x4{0u, 0u, 0u, 0u};
     *reinterpret_cast<u32x4*>(dst + (size_t)(kg + kGatherWaves) * 512) =
         real ? u32x4{p1[0], p1[1], p1[2], p1[3]} : u32x4{0u, 0u, 0u, 0u};
   }
   for (; kg < kg_end; kg += kGatherWaves) {
-    uint32_t p0[4];
-    perm_act8(ld16(src + kg * 32), p0);
+    const u32x4 v0 = ld16(src + kg * 32);
+    uint32_t p0[4] = {v0[0], v0[1], v0[2], v0[3]};
+    if constexpr (!kNatural) perm_act8(v0, p0);
     *reinterpret_cast<u32x4*>(dst + (size_t)kg * 512) =
         real ? u32x4{p0[0], p0[1], p0[2], p0[3]} : u32x4{0u, 0u, 0u, 0u};
   }
@@ -749,7 +827,7 @@ int persistent_grid() {
   return n;
 }
 
-template <Epi EPI>
+template <Epi EPI, bool MX>
 hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream) {
   const bool persist = a.K % 512 == 0;
   const int waves = persist ? kPWaves : kWavesPerGroup;
@@ -760,11 +838,11 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
   args.items = E * args.chunks;
   (void)mb;  // one 16-row block per weight pass (larger passes do not fit the registers)
   if (persist) {
-    hipLaunchKernelGGL((w4a16_persist_kernel<EPI>), dim3(persistent_grid() * kPGroupsPerCu),
+    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX>), dim3(persistent_grid() * kPGroupsPerCu),
                        dim3(kPThreads), 0,
                        stream, args);
   } else {
-    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1>), dim3(xcd_major_grid(args.items)),
+    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1, MX>), dim3(xcd_major_grid(args.items)),
                        dim3(kThreads), 0, stream, args);
   }
   return hipGetLastError();
@@ -773,12 +851,17 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
 }  // namespace
 
 hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t* ntp, int32_t H,
-                              uint16_t* xs, hipStream_t stream) {
+                              uint16_t* xs, hipStream_t stream, bool natural) {
   if (r.L <= 0) return hipSuccess;
   // L is at least num_tokens_padded, a multiple of 16
   const int kchunks = (H / 32 + kGatherGroups - 1) / kGatherGroups;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3((r.L + 15) / 16, kchunks), dim3(kGatherThreads), 0,
-                     stream, x, r.sorted_ids, ntp, r.P, r.k, H, xs);
+  const dim3 grid((r.L + 15) / 16, kchunks);
+  if (natural)
+    hipLaunchKernelGGL(gather_rows_kernel<true>, grid, dim3(kGatherThreads), 0, stream, x,
+                       r.sorted_ids, ntp, r.P, r.k, H, xs);
+  else
+    hipLaunchKernelGGL(gather_rows_kernel<false>, grid, dim3(kGatherThreads), 0, stream, x,
+                       r.sorted_ids, ntp, r.P, r.k, H, xs);
   return hipGetLastError();
 }
 
@@ -791,7 +874,8 @@ hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, i
                p.h, nullptr,
                r.P, r.k, p.H, 2 * p.I, p.I, 0, 0,
                zero ? p.out32 : nullptr, zero ? (int64_t)p.T * p.H : 0};
-  return launch_stream<Epi::GateUp>(a, r.E, mb, stream);
+  return p.mx ? launch_stream<Epi::GateUp, true>(a, r.E, mb, stream)
+              : launch_stream<Epi::GateUp, false>(a, r.E, mb, stream);
 }
 
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
@@ -799,7 +883,8 @@ hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int
   StreamArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.expert_ids, r.ntp, r.topk_weights,
                nullptr, p.out32,
                r.P, r.k, p.I, p.H, p.I, 0, 0, nullptr, 0};
-  return launch_stream<Epi::Down>(a, r.E, mb, stream);
+  return p.mx ? launch_stream<Epi::Down, true>(a, r.E, mb, stream)
+              : launch_stream<Epi::Down, false>(a, r.E, mb, stream);
 }
 
 }  // namespace qmoe

@@ -29,6 +29,12 @@
 // gate_up stores h = SiLU(gate) * up (bf16, tiled layout); down stores the routing-
 // weighted rows per (token, slot) pair in fp32 and a combine kernel sums the top-k rows
 // of every token, so the prefill output does not depend on atomic ordering.
+//
+// MXFP4 weights (MX = true; E2M1 codes with E8M0 scales per 32 k, the weight-only MXFP4
+// format of the "xiaotu-moe" project page, overview): an operand word is one
+// v_cvt_scalef32_pk_bf16_fp4 of the code word with the group's power-of-two scale,
+// exact, in natural k order (the activation rows and h use the natural-order tiled
+// layout); the scales are copied one byte per group.
 #include <algorithm>
 #include <type_traits>
 
@@ -64,7 +70,7 @@ enum class TEpi { GateUp, Down };
 struct TiledArgs {
   const uint16_t* act;          // [L, K] activation rows, tiled layout
   const uint8_t* w;             // [E, N, K/2]
-  const uint16_t* s;            // [E, N, K/32]
+  const uint16_t* s;            // [E, N, K/32] bf16 (INT4) or E8M0 bytes (MXFP4)
   const int32_t* sorted_ids;    // [L]
   const int32_t* offsets;       // [E + 1] segment starts (multiples of 16)
   const int32_t* tile_offsets;  // [E + 1] 256-row tiles per expert, exclusive scan
@@ -119,7 +125,7 @@ __device__ __forceinline__ void drain_acc(f32x4 (&acc)[kRowBlocks][kColTiles]) {
     for (int t = 0; t < kColTiles; ++t) asm volatile("" : "+a"(acc[m][t]));
 }
 
-template <TEpi EPI>
+template <TEpi EPI, bool MX>
 __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // One LDS array (150 KB), in 16 B units:
   //   activation ring [stage][row block][lane], 16 KB per k group;
@@ -165,14 +171,18 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   };
   // Per-lane byte offsets stay 32-bit (host-checked) on top of uniform bases. Weight
   // words: lane (col, quad) takes 16 B of row col at quarter `quad` of a 64 B half line.
-  // Scales: lane l takes word l % 4 of the 16 B (eight groups) of row l / 4.
+  // Scales: lane l takes word l % 4 of the 16 B (eight groups) of row l / 4. MXFP4
+  // scales are one byte per group: the block's eight are words 0 and 1 of the 16 B
+  // window (words 2 and 3 hold the next block's, or zeros past the buffer, unused).
+  constexpr uint32_t kScaleBytes = MX ? 1u : 2u;
   const uint8_t* wbase = a.w + (size_t)e * a.N * (size_t)(K >> 1);
-  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(a.s + (size_t)e * a.N * (size_t)KG);
+  const uint8_t* sbase =
+      reinterpret_cast<const uint8_t*>(a.s) + (size_t)e * a.N * (size_t)KG * kScaleBytes;
   uint32_t woff[kColTiles], soff[kColTiles];
 #pragma unroll
   for (int t = 0; t < kColTiles; ++t) {
     woff[t] = (uint32_t)weight_row(t, col) * (uint32_t)(K >> 1) + 16u * quad;
-    soff[t] = (uint32_t)weight_row(t, lane >> 2) * (uint32_t)(KG * 2) + 4u * (lane & 3);
+    soff[t] = (uint32_t)weight_row(t, lane >> 2) * (uint32_t)KG * kScaleBytes + 4u * (lane & 3);
   }
 
   // Activation copies of this wave: row blocks wave*kCopiesPerWave + i of the tile.
@@ -197,7 +207,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)wbase, (short)0, (int)((uint32_t)a.N * (uint32_t)(K >> 1)), kRsrcWord3);
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)sbase, (short)0, (int)((uint32_t)a.N * (uint32_t)(KG * 2)), kRsrcWord3);
+      (void*)sbase, (short)0, (int)((uint32_t)a.N * (uint32_t)KG * kScaleBytes), kRsrcWord3);
   auto copy_act = [&](int g, int st, int i) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         ars, (__attribute__((address_space(3))) void*)a_at(st, wave * kCopiesPerWave + i), 16,
@@ -211,7 +221,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   auto copy_scale = [&](int kb, int t) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         srs, (__attribute__((address_space(3))) void*)s_at(wave, t), 4, (int)soff[t],
-        min(kb, nblocks - 1) * 16, 0, 0);
+        min(kb, nblocks - 1) * 8 * (int)kScaleBytes, 0, 0);
   };
   auto copy_group = [&](int g, int st) {
 #pragma unroll
@@ -324,6 +334,10 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
 #pragma unroll
   for (int p = 0; p < kPieces; ++p) {
     const int t = p >> 2, i = p & 3;
+    if constexpr (MX) {
+      bq[0][t][i] = fp4_pair(tw[t][0], e8m0_scale(scur[t][0]), i);
+      continue;
+    }
     const float sc = bf16_lo(scur[t][0]);
     const uint32_t pr = ((tw[t][0] >> (4 * i)) & mask) | magic;
     const f16x2 hv = __builtin_bit_cast(f16x2, pr);
@@ -395,7 +409,10 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
           for (int rr = 0; rr < 4; ++rr) ra[(q + 1) & 1][rr] = as[(4 * (q + 1) + rr) * kWave];
         }
         uint32_t shv = 0;
-        if (!odd) {
+        if constexpr (MX) {
+          // The tile's scale for group jn (byte jn of the block), at its first piece.
+          if (!odd && i == 0) sc = e8m0_scale(scur[t][jn >> 2] >> (8 * (jn & 3)));
+        } else if (!odd) {
           if (i == 0) {
             const uint32_t sw = scur[t][jn >> 1];
             sc = (jn & 1) ? bf16_hi(sw) : bf16_lo(sw);
@@ -409,7 +426,9 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
         mfma_acc(acc[m][1], a0, bc[1]);
         __builtin_amdgcn_sched_barrier(0);
         copy_slot(1);
-        if (!odd) {
+        if constexpr (MX) {
+          if (odd) bn[t][i] = fp4_pair(tw[t][jn & 3], sc, i);
+        } else if (!odd) {
           const f16x2 hv = __builtin_bit_cast(f16x2, pr);
           flo = __builtin_fmaf((float)hv.x, sc, cc);
           fhi = __builtin_fmaf((float)hv.y, sc, cc);
@@ -482,7 +501,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float gv = acc[m][tp][r], uv = acc[m][tp + kColTiles / 2][r];
-          a.h[tiled_offset(rb * 16 + 4 * quad + r, j, a.I)] = f32_to_bf16(silu_f32(gv) * uv);
+          a.h[tiled_offset<MX>(rb * 16 + 4 * quad + r, j, a.I)] = f32_to_bf16(silu_f32(gv) * uv);
         }
       }
     }
@@ -571,12 +590,16 @@ __global__ void __launch_bounds__(kCombineThreads)
 }
 
 template <TEpi EPI>
-hipError_t launch_tiled(const TiledArgs& a, int64_t max_row_tiles, hipStream_t stream) {
+hipError_t launch_tiled(const TiledArgs& a, int64_t max_row_tiles, bool mx, hipStream_t stream) {
   const int64_t items = max_row_tiles * a.col_tiles;
   if (items <= 0) return hipSuccess;
   if (items > (int64_t(1) << 30)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((w4a16_tiled_kernel<EPI>), dim3(xcd_major_grid((int)items)),
-                     dim3(kThreads), 0, stream, a);
+  if (mx)
+    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, true>), dim3(xcd_major_grid((int)items)),
+                       dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, false>), dim3(xcd_major_grid((int)items)),
+                       dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -590,7 +613,7 @@ hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, hi
   TiledArgs a{p.xs, p.w13, p.s13, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
               p.h, nullptr, r.P, r.E, p.H, 2 * p.I, p.I, p.I / 128,
               (uint32_t)((uint64_t)r.L * p.H * 2u)};
-  return launch_tiled<TEpi::GateUp>(a, (int64_t)r.P / kTileRows + r.E, stream);
+  return launch_tiled<TEpi::GateUp>(a, (int64_t)r.P / kTileRows + r.E, p.mx, stream);
 }
 
 hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, float* y,
@@ -598,7 +621,7 @@ hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, floa
   TiledArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
               nullptr, y, r.P, r.E, p.I, p.H, p.I, p.H / 256,
               (uint32_t)((uint64_t)r.L * p.I * 2u)};
-  return launch_tiled<TEpi::Down>(a, (int64_t)r.P / kTileRows + r.E, stream);
+  return launch_tiled<TEpi::Down>(a, (int64_t)r.P / kTileRows + r.E, p.mx, stream);
 }
 
 hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,

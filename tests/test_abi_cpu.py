@@ -18,7 +18,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = binding.declared_functions()
     assert {"moe_topk_softmax", "moe_align", "moe_w4a16_forward", "moe_fp8_block_forward",
-            "moe_w4a16_grouped_contiguous", "moe_w4a16_grouped_masked",
+            "moe_w4a16_grouped_contiguous", "moe_w4a16_grouped_masked", "moe_mxfp4_forward",
             "qmoe_plan", "qmoe_fp8_quantize_blocks", "qmoe_fp8_quantize_blocks_bf16",
             "qmoe_status_string", "qmoe_last_error", "qmoe_abi_version"} <= set(names)
     for n in names:
@@ -142,3 +142,37 @@ def test_grouped_layouts_check_arguments(lib, masked):
     assert _grouped(lib, masked, E=0, ws=FAKE)[0] == INVALID
     assert _grouped(lib, masked, sched=9, ws=FAKE)[0] == INVALID
     assert _grouped(lib, masked, M=0, ws=FAKE, size=need)[0] == OK  # no rows: nothing launched
+
+
+def test_mxfp4_checks_arguments_like_w4a16(lib):
+    f = lib.moe_mxfp4_forward
+    sz = ctypes.c_size_t(0)
+    assert f(*([FAKE] * 7), 32, 7168, 2048, 48, 8, 0, FAKE, None, ctypes.byref(sz), None) == OK
+    assert sz.value == _w4(lib, ws=None)[1]  # the same plan and workspace as W4A16
+    need = sz.value
+    big = ctypes.c_size_t(need)
+    assert f(*([FAKE] * 7), 32, 7168 + 16, 2048, 48, 8, 0, FAKE, FAKE, ctypes.byref(big), None) == UNSUPPORTED
+    assert f(*([FAKE] * 7), 32, 7168, 2048, 48, 49, 0, FAKE, FAKE, ctypes.byref(big), None) == INVALID
+    assert f(FAKE, FAKE, None, *([FAKE] * 4), 32, 7168, 2048, 48, 8, 0, FAKE, FAKE,
+             ctypes.byref(big), None) == INVALID
+    small = ctypes.c_size_t(need - 1)
+    assert f(*([FAKE] * 7), 32, 7168, 2048, 48, 8, 0, FAKE, FAKE, ctypes.byref(small), None) == WORKSPACE
+    assert binding.plan(binding.FORMAT_MXFP4, 8192, 7168, 2048, 48, 8)[0] == binding.SCHEDULE_PREFILL
+
+
+def test_binding_functions_reference_only_defined_names():
+    # The GPU entry points cannot run here; at least every global name their code loads
+    # must exist in the module or the builtins.
+    import builtins
+    import dis
+    import types
+    missing = []
+    for name, fn in vars(binding).items():
+        if not isinstance(fn, types.FunctionType) or fn.__module__ != binding.__name__:
+            continue
+        for ins in dis.get_instructions(fn):
+            if ins.opname in ("LOAD_GLOBAL", "LOAD_NAME"):
+                g = ins.argval
+                if g not in fn.__globals__ and not hasattr(builtins, g):
+                    missing.append((name, g))
+    assert not missing, missing

@@ -1,0 +1,88 @@
+"""GPU MXFP4 routed MoE forward (moe_mxfp4_forward through the C ABI) against the CPU
+oracle, per token row within 1e-2 relative error: the decode and prefill MXFP4 workloads
+at full size (all rows, or a seeded sample where the oracle is slow) in each schedule,
+ragged shapes on both the persistent decode kernel (K a multiple of 512) and its general
+form, and exact special cases."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import TOL, bf16_out_to_f64, report, to_dev
+from quantized_mixture_experts_amd import binding, inputs
+
+pytestmark = pytest.mark.gpu
+
+SCHEDULES = [binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL]
+_CASES = {}
+
+
+def _case(name):
+    if name not in _CASES:
+        _CASES.clear()
+        _CASES[name] = inputs.mxfp4_case(inputs.CONFIGS[name])
+    return _CASES[name]
+
+
+def _forward(case, schedule):
+    d = to_dev(case)
+    out = binding.moe_mxfp4_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
+                                    d["topk_weights"], schedule=schedule)
+    torch.cuda.synchronize()
+    return bf16_out_to_f64(out)
+
+
+def _oracle(oracle_mod, case, rows=None):
+    return oracle_mod.mxfp4_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
+                                case["topk_ids"], case["topk_weights"], rows=rows)
+
+
+@pytest.mark.parametrize("name,schedule,nrows", [
+    ("decode_mxfp4", binding.SCHEDULE_AUTO, None),
+    ("decode_mxfp4", binding.SCHEDULE_PREFILL, None),
+    ("prefill_mxfp4", binding.SCHEDULE_AUTO, 48),
+])
+def test_mxfp4_workloads(oracle_mod, name, schedule, nrows):
+    cfg = inputs.CONFIGS[name]
+    print(f"[mxfp4] {name} schedule={schedule}", flush=True)
+    case = _case(name)
+    got = _forward(case, schedule)
+    rows = inputs.sample_rows(cfg.T, nrows if nrows is not None else cfg.T, seed=cfg.seed)
+    e = report(f"{name}/sched{schedule}", got[rows], _oracle(oracle_mod, case, rows))
+    assert e.max() <= TOL
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (16, 256, 128, 8, 2),     # the tiny shape: general decode kernel, no tiles
+    (50, 800, 352, 10, 3),    # ragged against the 256-deep k step and the column chunks
+    (1, 256, 128, 1, 1),      # one token, one expert
+    (9, 32, 32, 3, 2),        # smallest block-aligned sizes
+    (40, 1024, 512, 6, 2),    # K multiples of 512: the persistent decode kernel
+    (300, 512, 768, 5, 4),    # 256-multiples: the tile kernels, > 256 rows per expert
+])
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_mxfp4_ragged_shapes(oracle_mod, T, H, I, E, k, schedule):
+    print(f"[mxfp4 ragged] T={T} H={H} I={I} E={E} k={k} schedule={schedule}", flush=True)
+    case = inputs.custom_mxfp4_case(T, H, I, E, k, seed=T + H + I + E + k)
+    got = _forward(case, schedule)
+    e = report(f"mxfp4 T={T} H={H} I={I} sched={schedule}", got, _oracle(oracle_mod, case))
+    assert e.max() <= TOL
+
+
+@pytest.mark.parametrize("schedule", SCHEDULES)
+def test_mxfp4_exact_cases(oracle_mod, schedule):
+    print(f"[mxfp4 exact] schedule={schedule}", flush=True)
+    case = inputs.custom_mxfp4_case(40, 512, 512, 4, 2, seed=3)
+    z = dict(case)
+    z["w2"] = np.full_like(case["w2"], 0x80)  # +0 and -0 codes
+    assert np.all(_forward(z, schedule) == 0.0)
+    z = dict(case)
+    z["topk_weights"] = np.zeros_like(case["topk_weights"])
+    assert np.all(_forward(z, schedule) == 0.0)
+    # ids outside [0, E) are dropped: equal to the oracle with those slots removed
+    d = dict(case)
+    ids = case["topk_ids"].copy()
+    ids[::3, 1] = -1
+    ids[1::5, 0] = 77
+    d["topk_ids"] = ids
+    e = report(f"mxfp4 dropped ids sched={schedule}", _forward(d, schedule), _oracle(oracle_mod, d))
+    assert e.max() <= TOL
