@@ -38,8 +38,15 @@ enum Format { kW4A16 = 0, kFp8 = 1, kMxfp4 = 2 };
 // The 4-bit formats share the W4A16 kernels, workspace and limits.
 bool four_bit(int fmt) { return fmt == kW4A16 || fmt == kMxfp4; }
 
-// Rows per weight pass of the decode kernels, in 16-row blocks.
+// Rows per weight pass of the FP8 decode kernels, in 16-row blocks.
 int decode_mb_for(double) { return 1; }
+// Routed rows per expert above which the 4-bit persistent decode kernel serves two
+// 16-row blocks per weight pass, measured on MI355X for hidden 7168, intermediate 2048,
+// 48 experts (one vs two blocks per pass: W4A16 at 14 rows 0.342 vs 0.355 ms, at 16
+// rows 0.427 vs 0.370 ms; MXFP4 at 10 rows 0.297 vs 0.287 ms, at 8 rows 0.253 vs
+// 0.281 ms). Below these, most experts fit one block and a second one costs MFMA and
+// activation work for nothing.
+double two_block_rows(int fmt) { return fmt == kMxfp4 ? 11.0 : 15.0; }
 
 struct Plan {
   int fmt = 0;
@@ -70,7 +77,7 @@ qmoe_status check_shape(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int
                                                                  : "block FP8 [128,128]",
                 q, H, I);
   const int64_t P = (int64_t)T * k;
-  const int64_t L = P + (int64_t)E * (kSegRows - 1);
+  const int64_t L = P + (int64_t)E * (2 * kSegRows - 1);  // the largest align block
   if (L >= (int64_t(1) << 31) || (int64_t)L * (int64_t)I >= (int64_t(1) << 40))
     return fail(QMOE_ERR_UNSUPPORTED, "too many routed pairs: T*k=%lld", (long long)P);
   return QMOE_OK;
@@ -85,24 +92,39 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   p.P = (int64_t)T * k;
   const double tok_e = tok_e_hint > 0 ? tok_e_hint : E > 0 ? (double)p.P / E : 0.0;
   p.schedule = schedule;
-  // Crossover of the two profiles, measured on MI355X for hidden 7168, intermediate 2048
-  // (quantized_mixture_experts_amd.tune_schedule): the decode profile streams the
-  // weights once per 16-row block, so it loses to the tile kernels past about 56 routed
-  // rows per expert for W4A16 (48: 0.94 vs 1.08 ms; 64: 1.19 vs 1.08 ms) and past about
-  // 12 for block FP8 (8: 0.30 vs 0.38 ms; 16: 0.52 vs 0.38 ms).
-  const double crossover = four_bit(fmt) ? 56.0 : 12.0;
+  // Crossover of the two profiles, measured on MI355X for hidden 7168, intermediate 2048,
+  // 48 experts (quantized_mixture_experts_amd.tune_schedule): the decode profile streams
+  // the weights once per pass of one or two 16-row blocks, so it loses to the tile
+  // kernels past about 76 routed rows per expert for W4A16 (72: 0.95 vs 1.02 ms; 80: 1.04
+  // vs 1.00 ms), about 104 for MXFP4 (96: 0.89 vs 0.95 ms; 112: 1.01 vs 0.97 ms) and
+  // about 12 for block FP8 (8: 0.30 vs 0.38 ms; 16: 0.52 vs 0.38 ms).
+  const double crossover = fmt == kW4A16 ? 76.0 : fmt == kMxfp4 ? 104.0 : 12.0;
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= crossover ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
-  p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 2;
   p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&
             (four_bit(fmt) ? w4a16_tiled_supported(H, I) : fp8_tiled_supported(H, I));
-  p.block_m = kSegRows;
-  p.L = p.P + (int64_t)E * (p.block_m - 1);
-  p.NB = (p.L + p.block_m - 1) / p.block_m;
+  // Rows per weight pass of the stream kernels and the align block size. The 4-bit
+  // persistent kernel serves two 16-row blocks per pass above two_block_rows() routed
+  // rows per expert (align then pads segments to 32 rows so a pass stays in one expert); the
+  // FP8 stream kernels take mb within segments of any multiple of 16.
+  auto set_blocks = [&] {
+    if (four_bit(fmt)) {
+      p.mb = (!p.tiled && tok_e > two_block_rows(fmt)) ? 2 : 1;
+      p.block_m = kSegRows * p.mb;
+    } else {
+      p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 2;
+      p.block_m = kSegRows;
+    }
+    p.L = p.P + (int64_t)E * (p.block_m - 1);
+    p.NB = (p.L + p.block_m - 1) / p.block_m;
+  };
+  set_blocks();
   // The tile kernels address activation rows with 32-bit byte offsets.
   if (p.tiled && four_bit(fmt) &&
-      (uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32))
+      (uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32)) {
     p.tiled = false;
+    set_blocks();
+  }
   size_t cur = 0;
   auto take = [&](size_t bytes) {
     size_t at = cur;

@@ -43,7 +43,7 @@ struct Routing {
   const int32_t* sorted_ids;    // [L]
   const int32_t* offsets;       // [E + 1]
   const int32_t* tile_offsets;  // [E + 1], tiles of the prefill GEMM's row-tile size
-  const int32_t* expert_ids;    // [L / kSegRows], expert of each kSegRows-row block
+  const int32_t* expert_ids;    // [L / block_m], expert of each align block (16 or 32 rows)
   const int32_t* ntp;           // rows in use (offsets[E]), on the device
   const float* topk_weights;    // [P]
   int32_t P, k, E, L;
@@ -83,8 +83,8 @@ struct Fp8Problem {
 hipError_t launch_gather_rows(const uint16_t* x, const Routing& r, const int32_t* ntp, int32_t H,
                               uint16_t* xs, hipStream_t stream, bool natural = false);
 
-// Decode profile: a work-group owns (expert, column chunk) and streams the weights
-// once per pass of up to 16*mb rows of that expert.
+// Decode profile: weights streamed once per pass of 16*mb rows of an expert. mb = 2
+// (K a multiple of 512) needs align blocks of 32 rows; the general kernel takes mb = 1.
 hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, int mb,
                                       hipStream_t stream);
 // Whether the decode gate_up launch also clears out32 (then no separate clearing launch

@@ -424,14 +424,18 @@ __device__ __forceinline__ int32_t ld_invariant(const int32_t* p, int i) {
   return ((const __attribute__((address_space(4))) int32_t*)p)[i];
 }
 
-template <Epi EPI, bool MX>
+// MB: 16-row MFMA blocks per row block (align pads every expert's segment to 16 MB
+// rows, so a row block never spans two experts). Each dequantized weight operand feeds
+// the MFMAs of all MB blocks, so a pass over the weights serves 16 MB rows.
+template <Epi EPI, bool MX, int MB>
 __global__ void __launch_bounds__(kPThreads)
     __attribute__((amdgpu_waves_per_eu(kPWavesPerEu)))
     w4a16_persist_kernel(StreamArgs a) {
-  __shared__ u32x4 a_lds[2][kChunkGroups][kWave];
+  static_assert(MB == 1 || MB == 2, "LDS holds the activation chunks of at most two blocks");
+  __shared__ u32x4 a_lds[2][MB][kChunkGroups][kWave];
   // Zero-point term of each group per activation row: the same for every column, so one
   // float per row (read by the four lanes of a row quarter at once).
-  __shared__ float c_lds[2][kChunkGroups][16];
+  __shared__ float c_lds[2][MB][kChunkGroups][16];
   // Scales of the current block as fp32, converted once when the block is staged:
   // [wave][tile][step in block][half step][row], four groups each (rows innermost, so
   // the sixteen rows a wave reads at once are 16 B apart).
@@ -449,7 +453,7 @@ __global__ void __launch_bounds__(kPThreads)
   }
   const int K = a.K, G = K / 32, KB = K / 2, N = a.N;
   const int upi = K / 512;  // units per item
-  const int items = (ld_invariant(a.ntp, 0) / kSegRows) * a.chunks;
+  const int items = (ld_invariant(a.ntp, 0) / (kSegRows * MB)) * a.chunks;
   const int nwg = gridDim.x;  // a multiple of the XCD count
   // XCD-major numbering: the work-groups of one XCD hold consecutive ranges, so the
   // column chunks of one expert (which share its activation rows) meet in one L2.
@@ -578,29 +582,42 @@ __global__ void __launch_bounds__(kPThreads)
     return min(u + min(kScaleUnits - (kc & (kScaleUnits - 1)), upi - kc), ulast);
   };
 
-  u32x4 creg[kPPieces];
+  u32x4 creg[MB][kPPieces];
   auto chunk_load = [&](const Unit& d) {
-    const u32x4* ablk = reinterpret_cast<const u32x4*>(a.act) + (size_t)d.rb * G * kWave;
 #pragma unroll
-    for (int i = 0; i < kPPieces; ++i) {
-      const int idx = threadIdx.x + kPThreads * i;  // group-in-chunk * 64 + lane
-      creg[i] = ablk[(size_t)(d.kc * kUnitGroups + idx / kWave) * kWave + idx % kWave];
+    for (int b = 0; b < MB; ++b) {
+      const u32x4* ablk =
+          reinterpret_cast<const u32x4*>(a.act) + (size_t)(d.rb * MB + b) * G * kWave;
+#pragma unroll
+      for (int i = 0; i < kPPieces; ++i) {
+        const int idx = threadIdx.x + kPThreads * i;  // group-in-chunk * 64 + lane
+        creg[b][i] = ablk[(size_t)(d.kc * kUnitGroups + idx / kWave) * kWave + idx % kWave];
+      }
     }
   };
   auto chunk_store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < kPPieces; ++i) {
-      const int g = wave + kPWaves * i;
-      a_lds[buf][g][lane] = creg[i];
-      if constexpr (!MX) {
-        const uint32_t av[4] = {creg[i][0], creg[i][1], creg[i][2], creg[i][3]};
-        const f32x4 c = mfma_bf16_16x16x32(av, neg136, zero4);
-        if (col == 0) *reinterpret_cast<f32x4*>(&c_lds[buf][g][4 * quad]) = c;
+    for (int b = 0; b < MB; ++b)
+#pragma unroll
+      for (int i = 0; i < kPPieces; ++i) {
+        const int g = wave + kPWaves * i;
+        a_lds[buf][b][g][lane] = creg[b][i];
+        if constexpr (!MX) {
+          const uint32_t av[4] = {creg[b][i][0], creg[b][i][1], creg[b][i][2], creg[b][i][3]};
+          const f32x4 c = mfma_bf16_16x16x32(av, neg136, zero4);
+          if (col == 0) *reinterpret_cast<f32x4*>(&c_lds[buf][b][g][4 * quad]) = c;
+        }
       }
-    }
   };
 
-  f32x4 acc[2] = {zero4, zero4};
+  // Groups per batch of the INT4 path: fewer with two blocks, whose products would
+  // otherwise not fit the registers.
+  constexpr int kBatch = kPBatch / MB;
+  f32x4 acc[2][MB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int b = 0; b < MB; ++b) acc[t][b] = zero4;
   // One 256-deep step: groups 8p..8p+7 of the unit's chunk, scale piece p, in batches of
   // kPBatch groups whose LDS reads and MFMAs are issued together, so neither the LDS
   // latency nor the MFMA latency is paid once per group.
@@ -621,90 +638,111 @@ __global__ void __launch_bounds__(kPThreads)
         // Exact scaled weights from the converts; the MFMAs accumulate in place.
 #pragma unroll
         for (int gb = 0; gb < 4; ++gb) {
-          const u32x4 v = a_lds[buf][8 * p + 4 * half + gb][lane];
-          const uint32_t a4[4] = {v[0], v[1], v[2], v[3]};
+          uint32_t a4[MB][4];
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+            const u32x4 v = a_lds[buf][b][8 * p + 4 * half + gb][lane];
+            a4[b][0] = v[0];
+            a4[b][1] = v[1];
+            a4[b][2] = v[2];
+            a4[b][3] = v[3];
+          }
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             uint32_t bw[4];
             fp4_to_bf16(wt[t][gb], sv[t][half][gb], bw);
-            acc[t] = mfma_bf16_16x16x32(a4, bw, acc[t]);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[t][b] = mfma_bf16_16x16x32(a4[b], bw, acc[t][b]);
           }
         }
         continue;
       }
 #pragma unroll
-      for (int b0 = 0; b0 < 4; b0 += kPBatch) {
-        u32x4 av[kPBatch];
-        f32x4 cv[kPBatch];
+      for (int b0 = 0; b0 < 4; b0 += kBatch) {
+        u32x4 av[MB][kBatch];
+        f32x4 cv[MB][kBatch];
 #pragma unroll
-        for (int gb = 0; gb < kPBatch; ++gb) {
-          const int gl = 8 * p + 4 * half + b0 + gb;
-          av[gb] = a_lds[buf][gl][lane];
-          cv[gb] = *reinterpret_cast<const f32x4*>(&c_lds[buf][gl][4 * quad]);
-        }
-        f32x4 d[2][kPBatch];
+        for (int b = 0; b < MB; ++b)
 #pragma unroll
-        for (int gb = 0; gb < kPBatch; ++gb) {
-          const uint32_t a4[4] = {av[gb][0], av[gb][1], av[gb][2], av[gb][3]};
+          for (int gb = 0; gb < kBatch; ++gb) {
+            const int gl = 8 * p + 4 * half + b0 + gb;
+            av[b][gb] = a_lds[buf][b][gl][lane];
+            cv[b][gb] = *reinterpret_cast<const f32x4*>(&c_lds[buf][b][gl][4 * quad]);
+          }
+        f32x4 d[2][MB][kBatch];
+#pragma unroll
+        for (int gb = 0; gb < kBatch; ++gb) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             uint32_t bw[4];
             int4_to_bf16_biased(wt[t][b0 + gb], nib, one28, bw);
-            d[t][gb] = mfma_bf16_16x16x32(a4, bw, cv[gb]);
+#pragma unroll
+            for (int b = 0; b < MB; ++b) {
+              const uint32_t a4[4] = {av[b][gb][0], av[b][gb][1], av[b][gb][2], av[b][gb][3]};
+              d[t][b][gb] = mfma_bf16_16x16x32(a4, bw, cv[b][gb]);
+            }
           }
         }
 #pragma unroll
-        for (int gb = 0; gb < kPBatch; ++gb) {
+        for (int gb = 0; gb < kBatch; ++gb) {
           const int g = 4 * half + b0 + gb;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            acc[t] += sv[t][half][g & 3] * d[t][gb];
-          }
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int b = 0; b < MB; ++b) acc[t][b] += sv[t][half][g & 3] * d[t][b][gb];
         }
       }
     }
   };
   // down: pair ids of this lane's four rows for the current and the next unit, and the
   // routing weights of the current unit's rows, loaded a unit ahead of their use.
-  int sid_c[4], sid_n[4];
-  float wt_c[4];
-  auto sid_load = [&](int (&sid)[4], const Unit& d) {
+  int sid_c[MB][4], sid_n[MB][4];
+  float wt_c[MB][4];
+  auto sid_load = [&](int (&sid)[MB][4], const Unit& d) {
     if constexpr (EPI == Epi::Down) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sid[r] = a.sorted_ids[d.rb * kSegRows + 4 * quad + r];
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          sid[b][r] = a.sorted_ids[(d.rb * MB + b) * kSegRows + 4 * quad + r];
     }
   };
   auto wt_load = [&]() {
     if constexpr (EPI == Epi::Down) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wt_c[r] = a.topk_weights[min(sid_c[r], a.P - 1)];
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wt_c[b][r] = a.topk_weights[min(sid_c[b][r], a.P - 1)];
     }
   };
   auto epilogue = [&](const Unit& d) {
-    const int rbase = d.rb * kSegRows + 4 * quad;
-    if constexpr (EPI == Epi::GateUp) {
-      const int j0 = (d.cc * kPWaves + wave) * 16;
-      if (j0 < a.I) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          a.h[tiled_offset<MX>(rbase + r, j0 + col, a.I)] =
-              f32_to_bf16(silu_f32(acc[0][r]) * acc[1][r]);
+    for (int b = 0; b < MB; ++b) {
+      const int rbase = (d.rb * MB + b) * kSegRows + 4 * quad;
+      if constexpr (EPI == Epi::GateUp) {
+        const int j0 = (d.cc * kPWaves + wave) * 16;
+        if (j0 < a.I) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            a.h[tiled_offset<MX>(rbase + r, j0 + col, a.I)] =
+                f32_to_bf16(silu_f32(acc[0][b][r]) * acc[1][b][r]);
+        }
+      } else {
+        const int j0 = (d.cc * kPWaves + wave) * 32;
+        (void)rbase;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int sid = sid_c[b][r];
+          if (sid >= a.P) continue;
+          float* orow = a.out32 + (size_t)(sid / a.k) * N + j0 + col;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            if (j0 + 16 * t < N) unsafeAtomicAdd(orow + 16 * t, wt_c[b][r] * acc[t][b][r]);
+        }
       }
-    } else {
-      const int j0 = (d.cc * kPWaves + wave) * 32;
-      (void)rbase;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int sid = sid_c[r];
-        if (sid >= a.P) continue;
-        float* orow = a.out32 + (size_t)(sid / a.k) * N + j0 + col;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          if (j0 + 16 * t < N) unsafeAtomicAdd(orow + 16 * t, wt_c[r] * acc[t][r]);
-      }
+      acc[0][b] = zero4;
+      acc[1][b] = zero4;
     }
-    acc[0] = zero4;
-    acc[1] = zero4;
   };
 
   // Descriptors of units u, u+1, u+2 (clamped to the range: loads past its end re-read
@@ -755,7 +793,9 @@ __global__ void __launch_bounds__(kPThreads)
     dq[kWin - 1] = desc(min(u + kWin, ulast));
     if constexpr (EPI == Epi::Down) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sid_c[r] = sid_n[r];
+      for (int b = 0; b < MB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sid_c[b][r] = sid_n[b][r];
     }
   };
   for (int u = u0; u < u1; u += kBodyUnits)
@@ -836,11 +876,14 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
   StreamArgs args = a;
   args.chunks = (extent + cols_per_group - 1) / cols_per_group;
   args.items = E * args.chunks;
-  (void)mb;  // one 16-row block per weight pass (larger passes do not fit the registers)
-  if (persist) {
-    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX>), dim3(persistent_grid() * kPGroupsPerCu),
-                       dim3(kPThreads), 0,
-                       stream, args);
+  // The persistent kernel serves mb 16-row blocks per weight pass (align made segments
+  // of 16 mb rows); the general kernel one 16-row block at a time of any segments.
+  if (persist && mb == 2) {
+    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, 2>),
+                       dim3(persistent_grid() * kPGroupsPerCu), dim3(kPThreads), 0, stream, args);
+  } else if (persist) {
+    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, 1>),
+                       dim3(persistent_grid() * kPGroupsPerCu), dim3(kPThreads), 0, stream, args);
   } else {
     hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1, MX>), dim3(xcd_major_grid(args.items)),
                        dim3(kThreads), 0, stream, args);

@@ -2,7 +2,7 @@
 expert (tok_e = T*k/E) on the current GPU and print where the prefill profile starts to
 win. The library's automatic choice (qmoe_plan) uses the crossover measured this way.
 
-  python -m quantized_mixture_experts_amd.tune_schedule [--format w4a16|fp8]
+  python -m quantized_mixture_experts_amd.tune_schedule [--format w4a16|mxfp4|fp8]
         [--H 7168] [--I 2048] [--E 48] [--k 8] [--steps 10]
 
 Seeded synthetic inputs of the benchmark recipe; one JSON line per tok_e, then a summary.
@@ -37,7 +37,7 @@ def _fp8_quant_host(v, br, bc):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--format", default="w4a16", choices=["w4a16", "fp8"])
+    ap.add_argument("--format", default="w4a16", choices=["w4a16", "mxfp4", "fp8"])
     ap.add_argument("--H", type=int, default=7168)
     ap.add_argument("--I", type=int, default=2048)
     ap.add_argument("--E", type=int, default=48)
@@ -46,10 +46,15 @@ def main():
     ap.add_argument("--tok-e", default="4,8,16,24,32,40,48,64,96,128,192,256")
     args = ap.parse_args()
     H, I, E, k = args.H, args.I, args.E, args.k
-    fmt = binding.FORMAT_W4A16 if args.format == "w4a16" else binding.FORMAT_FP8
+    fmt = {"w4a16": binding.FORMAT_W4A16, "mxfp4": binding.FORMAT_MXFP4,
+           "fp8": binding.FORMAT_FP8}[args.format]
+    four_bit = args.format in ("w4a16", "mxfp4")
+    forward = binding.moe_mxfp4_forward if args.format == "mxfp4" else binding.moe_w4a16_forward
     # one set of weights for every T
     if args.format == "w4a16":
         base = inputs.custom_w4a16_case(16, H, I, E, k, seed=5)
+    elif args.format == "mxfp4":
+        base = inputs.custom_mxfp4_case(16, H, I, E, k, seed=5)
     else:
         base = inputs.custom_fp8_case(16, H, I, E, k, seed=5, quantize=_fp8_quant_host)
     dev = {n: torch.from_numpy(np.ascontiguousarray(
@@ -63,14 +68,14 @@ def main():
         tids, twts = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
         ms = {}
         for name, sched in (("decode", binding.SCHEDULE_DECODE), ("prefill", binding.SCHEDULE_PREFILL)):
-            if args.format == "w4a16":
+            if four_bit:
                 x = torch.from_numpy(inputs.bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
                                      .view(np.int16)).cuda()
                 _, _, ws = binding.plan(fmt, T, H, I, E, k, sched)
                 work = torch.empty(ws, dtype=torch.uint8, device="cuda")
                 out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-                fn = lambda: binding.moe_w4a16_forward(x, dev["w13"], dev["s13"], dev["w2"], dev["s2"],
-                                                       tids, twts, schedule=sched, out=out, workspace=work)
+                fn = lambda: forward(x, dev["w13"], dev["s13"], dev["w2"], dev["s2"],
+                                     tids, twts, schedule=sched, out=out, workspace=work)
             else:
                 xq, xs = binding.fp8_quantize_blocks(
                     torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).cuda(), 1, 128)

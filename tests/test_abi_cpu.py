@@ -176,3 +176,19 @@ def test_binding_functions_reference_only_defined_names():
                 if g not in fn.__globals__ and not hasattr(builtins, g):
                     missing.append((name, g))
     assert not missing, missing
+
+
+def test_plan_two_block_passes_above_sixteen_rows_per_expert():
+    D = binding.SCHEDULE_DECODE
+    # 32 tokens x top-8 / 48 experts = 5.3 rows per expert: one 16-row block per pass
+    assert binding.plan(binding.FORMAT_W4A16, 32, 7168, 2048, 48, 8)[1] == 16
+    # 72 tokens: 12 rows per expert, one block for W4A16, two for MXFP4 (cheaper per MFMA)
+    assert binding.plan(binding.FORMAT_W4A16, 72, 7168, 2048, 48, 8)[1] == 16
+    assert binding.plan(binding.FORMAT_MXFP4, 72, 7168, 2048, 48, 8)[1] == 32
+    # 192 tokens: 32 rows per expert, passes of two blocks (align pads to 32 rows)
+    for fmt in (binding.FORMAT_W4A16, binding.FORMAT_MXFP4):
+        chosen, bm, ws = binding.plan(fmt, 192, 7168, 2048, 48, 8)
+        assert chosen == D and bm == 32
+    # the tile path keeps 16-row align blocks; FP8 always does
+    assert binding.plan(binding.FORMAT_W4A16, 8192, 7168, 2048, 48, 8)[1] == 16
+    assert binding.plan(binding.FORMAT_FP8, 192, 7168, 2048, 48, 8, D)[1] == 16

@@ -58,6 +58,7 @@ def test_mxfp4_workloads(oracle_mod, name, schedule, nrows):
     (9, 32, 32, 3, 2),        # smallest block-aligned sizes
     (40, 1024, 512, 6, 2),    # K multiples of 512: the persistent decode kernel
     (300, 512, 768, 5, 4),    # 256-multiples: the tile kernels, > 256 rows per expert
+    (200, 1024, 512, 8, 2),   # 50 rows per expert: two-block weight passes when decoding
 ])
 @pytest.mark.parametrize("schedule", SCHEDULES)
 def test_mxfp4_ragged_shapes(oracle_mod, T, H, I, E, k, schedule):
