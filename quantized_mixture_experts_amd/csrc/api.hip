@@ -52,7 +52,8 @@ struct Plan {
   int fmt = 0;
   int schedule = QMOE_SCHEDULE_DECODE;
   int mb = 1;
-  bool tiled = false;  // W4A16 prefill on the 256-row tile kernels
+  bool tiled = false;  // 4-bit prefill on the tile kernels
+  int32_t tile_rows = 256;  // their row tile
   int32_t block_m = kSegRows;
   int64_t P = 0, L = 0, NB = 0;
   size_t off_sorted = 0, off_expert_ids = 0, off_ntp = 0, off_offsets = 0, off_tiles = 0;
@@ -94,11 +95,12 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   p.schedule = schedule;
   // Crossover of the two profiles, measured on MI355X for hidden 7168, intermediate 2048,
   // 48 experts (quantized_mixture_experts_amd.tune_schedule): the decode profile streams
-  // the weights once per pass of one or two 16-row blocks, so it loses to the tile
-  // kernels past about 76 routed rows per expert for W4A16 (72: 0.95 vs 1.02 ms; 80: 1.04
-  // vs 1.00 ms), about 104 for MXFP4 (96: 0.89 vs 0.95 ms; 112: 1.01 vs 0.97 ms) and
-  // about 12 for block FP8 (8: 0.30 vs 0.38 ms; 16: 0.52 vs 0.38 ms).
-  const double crossover = fmt == kW4A16 ? 76.0 : fmt == kMxfp4 ? 104.0 : 12.0;
+  // the weights once per pass of one or two 16-row blocks and the tile kernels use
+  // 128-row tiles at these sizes, so decode wins up to about 44 routed rows per expert
+  // for W4A16 (40: 0.69 vs 0.71 ms; 48: 0.72 vs 0.71 ms), about 60 for MXFP4 (56: 0.61
+  // vs 0.64 ms; 64: 0.69 vs 0.64 ms) and about 12 for block FP8 (8: 0.30 vs 0.38 ms;
+  // 16: 0.52 vs 0.38 ms).
+  const double crossover = fmt == kW4A16 ? 44.0 : fmt == kMxfp4 ? 60.0 : 12.0;
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= crossover ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
   p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&
@@ -119,6 +121,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     p.NB = (p.L + p.block_m - 1) / p.block_m;
   };
   set_blocks();
+  if (four_bit(fmt)) p.tile_rows = w4a16_tiled_rows(tok_e);
   // The tile kernels address activation rows with 32-bit byte offsets.
   if (p.tiled && four_bit(fmt) &&
       (uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32)) {
@@ -220,7 +223,7 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
                     T, H, I, mx};
 
   if (p.tiled) {
-    const int32_t tm = w4a16_tiled_rows();
+    const int32_t tm = p.tile_rows;
     hipError_t err = staged(QMOE_STAGE_ALIGN, s, [&] {
       return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
                           region<int32_t>(workspace, p.off_sorted),
@@ -234,10 +237,10 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
       return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s, mx);
     });
     if (err != hipSuccess) return hip_fail(err, "gather launch");
-    err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_tiled(prob, r, s); });
+    err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_tiled(prob, r, tm, s); });
     if (err != hipSuccess) return hip_fail(err, "gate_up launch");
     float* y = region<float>(workspace, p.off_y);
-    err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_tiled(prob, r, y, s); });
+    err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_tiled(prob, r, tm, y, s); });
     if (err != hipSuccess) return hip_fail(err, "down launch");
     err = staged(QMOE_STAGE_CAST, s, [&] {
       return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);

@@ -92,15 +92,17 @@ hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, i
 bool w4a16_stream_zeroes_output(int32_t H);
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
                                     hipStream_t stream);
-// Prefill profile (W4A16): 256-row tiles of each expert segment on the matrix cores.
-// Needs H and I multiples of 256; align must have produced tile_offsets for tiles of
-// w4a16_tiled_rows() rows. down writes y[P, H] (routing-weighted fp32 row per pair) and
-// launch_combine_rows sums each token's top-k rows into the bf16 output.
+// Prefill profile (W4A16 / MXFP4): row tiles of each expert segment on the matrix
+// cores, 256 rows, or 128 when the experts hold few rows (w4a16_tiled_rows). Needs H and
+// I multiples of 256; align must have produced tile_offsets for tiles of tile_rows rows.
+// down writes y[P, H] (routing-weighted fp32 row per pair) and launch_combine_rows sums
+// each token's top-k rows into the bf16 output.
 bool w4a16_tiled_supported(int32_t H, int32_t I);
-int32_t w4a16_tiled_rows();
-hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, hipStream_t stream);
-hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, float* y,
-                                   hipStream_t stream);
+int32_t w4a16_tiled_rows(double rows_per_expert);
+hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
+                                     hipStream_t stream);
+hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
+                                   float* y, hipStream_t stream);
 hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,
                                int32_t E, int32_t H, uint16_t* out, hipStream_t stream);
 

@@ -45,25 +45,34 @@ namespace qmoe {
 
 namespace {
 
-constexpr int kTileRows = 256;                    // rows per work-group tile
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
-constexpr int kRowBlocks = kTileRows / 16;        // 16-row MFMA tiles per wave
 constexpr int kColTiles = 2;                      // 16-column MFMA tiles per wave
 constexpr int kPieces = kColTiles * 4;            // dequantized operand words per lane and group
 constexpr int kStages = 7;                        // LDS ring of activation k groups
-constexpr int kCopiesPerWave = kRowBlocks / kWaves;  // 1 KB copies per wave and group
 constexpr int kGroupsPerBlock = 8;                // k groups per 256-deep weight block
-// LDS layout in 16 B units (see the kernel).
-constexpr int kWBase = kStages * kRowBlocks * kWave;
-constexpr int kSBase = kWBase + kWaves * 2 * kColTiles * kWave;
-constexpr int kEBase = kSBase + kWaves * kColTiles * 16;
-// down: the pair id of each of the tile's rows (256 ints), copied at the start of the
-// item so the epilogue needs one round trip (the routing weights) instead of two per
-// row block.
-constexpr int kSmemUnits = kEBase + kTileRows / 4;
+
+// Tile height TR (rows per work-group tile): 256, or 128 when the experts hold few
+// rows (a 256-row tile would be mostly padding).
+template <int TR>
+struct Tile {
+  static constexpr int kRowBlocks = TR / 16;              // 16-row MFMA tiles per wave
+  static constexpr int kCopiesPerWave = kRowBlocks / kWaves;  // 1 KB copies per wave and group
+  // LDS layout in 16 B units (see the kernel).
+  static constexpr int kWBase = kStages * kRowBlocks * kWave;
+  static constexpr int kSBase = kWBase + kWaves * 2 * kColTiles * kWave;
+  static constexpr int kEBase = kSBase + kWaves * kColTiles * 16;
+  // down: the pair id of each of the tile's rows, copied at the start of the item so the
+  // epilogue needs one round trip (the routing weights) instead of two per row block.
+  static constexpr int kSmemUnits = kEBase + TR / 4;
+  static_assert(kRowBlocks == kPieces || kRowBlocks == 2 * kPieces,
+                "a dequantized piece spans one or two row blocks");
+  static_assert(kCopiesPerWave >= 1 && kRowBlocks % kWaves == 0, "copies per wave");
+};
 // Word 3 of a raw buffer resource (32-bit data format, no swizzle, no index).
 constexpr int kRsrcWord3 = 0x00020000;
+// Routed rows per expert up to which the tile kernels use 128-row tiles.
+constexpr double kSmallTileRows = 136.0;
 
 enum class TEpi { GateUp, Down };
 
@@ -117,18 +126,26 @@ __device__ __forceinline__ void mfma_acc(f32x4& acc, const u32x4& a, const u32x4
 // Orders every later read of the accumulators after at least 24 wait states following
 // the last MFMA (more than an MFMA-write to VALU-read dependency requires). The
 // accumulators pass through volatile statements, which keep their program order.
-__device__ __forceinline__ void drain_acc(f32x4 (&acc)[kRowBlocks][kColTiles]) {
+template <int RB>
+__device__ __forceinline__ void drain_acc(f32x4 (&acc)[RB][kColTiles]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
-  for (int m = 0; m < kRowBlocks; ++m)
+  for (int m = 0; m < RB; ++m)
 #pragma unroll
     for (int t = 0; t < kColTiles; ++t) asm volatile("" : "+a"(acc[m][t]));
 }
 
-template <TEpi EPI, bool MX>
+template <TEpi EPI, bool MX, int TR>
 __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
-  // One LDS array (150 KB), in 16 B units:
-  //   activation ring [stage][row block][lane], 16 KB per k group;
+  constexpr int kTileRows = TR;
+  constexpr int kRowBlocks = Tile<TR>::kRowBlocks;
+  constexpr int kCopiesPerWave = Tile<TR>::kCopiesPerWave;
+  constexpr int kWBase = Tile<TR>::kWBase;
+  constexpr int kSBase = Tile<TR>::kSBase;
+  constexpr int kEBase = Tile<TR>::kEBase;
+  constexpr int kSmemUnits = Tile<TR>::kSmemUnits;
+  // One LDS array (150 KB at TR = 256, 95 KB at 128), in 16 B units:
+  //   activation ring [stage][row block][lane], TR / 16 KB per k group;
   //   per wave, the two half blocks of weight words [half][tile][lane];
   //   per wave, the block's scales [tile][row] (16 B = eight groups per weight row).
   //   down: the tile rows' pair ids (1 KB).
@@ -377,10 +394,12 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
 #pragma unroll
       for (int m = 0; m < kRowBlocks; ++m) {
         const int q = m >> 2, r = m & 3;
-        // Row blocks 2p and 2p + 1 carry piece p of the next group's operands: its scale
-        // and codes, the two products, then the conversion (behind the next piece's mask,
-        // since a bf16 conversion right behind an MFMA needs a wait state).
-        const int p = m >> 1, odd = m & 1;
+        // With 16 row blocks, row blocks 2p and 2p + 1 carry piece p of the next group's
+        // operands: its scale and codes, the two products, then the conversion (behind the
+        // next piece's mask, since a bf16 conversion right behind an MFMA needs a wait
+        // state). With 8 row blocks, row block p carries all of piece p.
+        constexpr bool kTwoPerPiece = kRowBlocks == 2 * kPieces;
+        const int p = kTwoPerPiece ? m >> 1 : m, odd = kTwoPerPiece ? m & 1 : 0;
         const int t = p >> 2, i = p & 3;
         const u32x4& a0 = ra[q & 1][r];
         // This step's copies, issued after the barrier one per MFMA of row blocks
@@ -403,7 +422,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         copy_slot(0);
         // After the group's first MFMA, so that the wait before it does not cover them.
-        if (r == 0 && q < 3) {
+        if (r == 0 && q < kRowBlocks / 4 - 1) {
           keep_live(ra[(q + 1) & 1]);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) ra[(q + 1) & 1][rr] = as[(4 * (q + 1) + rr) * kWave];
@@ -412,6 +431,13 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
         if constexpr (MX) {
           // The tile's scale for group jn (byte jn of the block), at its first piece.
           if (!odd && i == 0) sc = e8m0_scale(scur[t][jn >> 2] >> (8 * (jn & 3)));
+        } else if (!kTwoPerPiece) {
+          if (i == 0) {
+            const uint32_t sw = scur[t][jn >> 1];
+            sc = (jn & 1) ? bf16_hi(sw) : bf16_lo(sw);
+            cc = -1032.0f * sc;
+          }
+          pr = ((tw[t][jn & 3] >> (4 * i)) & mask) | magic;
         } else if (!odd) {
           if (i == 0) {
             const uint32_t sw = scur[t][jn >> 1];
@@ -427,7 +453,11 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         copy_slot(1);
         if constexpr (MX) {
-          if (odd) bn[t][i] = fp4_pair(tw[t][jn & 3], sc, i);
+          if (odd || !kTwoPerPiece) bn[t][i] = fp4_pair(tw[t][jn & 3], sc, i);
+        } else if (!kTwoPerPiece) {
+          const f16x2 hv = __builtin_bit_cast(f16x2, pr);
+          const f32x2 f = {__builtin_fmaf((float)hv.x, sc, cc), __builtin_fmaf((float)hv.y, sc, cc)};
+          bn[t][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
         } else if (!odd) {
           const f16x2 hv = __builtin_bit_cast(f16x2, pr);
           flo = __builtin_fmaf((float)hv.x, sc, cc);
@@ -589,17 +619,27 @@ __global__ void __launch_bounds__(kCombineThreads)
   }
 }
 
-template <TEpi EPI>
-hipError_t launch_tiled(const TiledArgs& a, int64_t max_row_tiles, bool mx, hipStream_t stream) {
-  const int64_t items = max_row_tiles * a.col_tiles;
-  if (items <= 0) return hipSuccess;
-  if (items > (int64_t(1) << 30)) return hipErrorInvalidValue;
+template <TEpi EPI, int TR>
+void launch_tiled_rows(const TiledArgs& a, int64_t items, bool mx, hipStream_t stream) {
   if (mx)
-    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, true>), dim3(xcd_major_grid((int)items)),
+    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, true, TR>), dim3(xcd_major_grid((int)items)),
                        dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, false>), dim3(xcd_major_grid((int)items)),
+    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, false, TR>), dim3(xcd_major_grid((int)items)),
                        dim3(kThreads), 0, stream, a);
+}
+
+template <TEpi EPI>
+hipError_t launch_tiled(const TiledArgs& a, int64_t P, int E, int tile_rows, bool mx,
+                        hipStream_t stream) {
+  if (tile_rows != 128 && tile_rows != 256) return hipErrorInvalidValue;
+  const int64_t items = (P / tile_rows + E) * a.col_tiles;  // at most this many row tiles
+  if (items <= 0) return hipSuccess;
+  if (items > (int64_t(1) << 30)) return hipErrorInvalidValue;
+  if (tile_rows == 128)
+    launch_tiled_rows<EPI, 128>(a, items, mx, stream);
+  else
+    launch_tiled_rows<EPI, 256>(a, items, mx, stream);
   return hipGetLastError();
 }
 
@@ -607,21 +647,26 @@ hipError_t launch_tiled(const TiledArgs& a, int64_t max_row_tiles, bool mx, hipS
 
 bool w4a16_tiled_supported(int32_t H, int32_t I) { return H % 256 == 0 && I % 256 == 0; }
 
-int32_t w4a16_tiled_rows() { return kTileRows; }
+int32_t w4a16_tiled_rows(double rows_per_expert) {
+  // Measured on MI355X (hidden 7168, intermediate 2048, 48 experts): 128-row tiles win
+  // while the experts average up to about kSmallTileRows routed rows.
+  return rows_per_expert <= kSmallTileRows ? 128 : 256;
+}
 
-hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, hipStream_t stream) {
+hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
+                                     hipStream_t stream) {
   TiledArgs a{p.xs, p.w13, p.s13, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
               p.h, nullptr, r.P, r.E, p.H, 2 * p.I, p.I, p.I / 128,
               (uint32_t)((uint64_t)r.L * p.H * 2u)};
-  return launch_tiled<TEpi::GateUp>(a, (int64_t)r.P / kTileRows + r.E, p.mx, stream);
+  return launch_tiled<TEpi::GateUp>(a, r.P, r.E, tile_rows, p.mx, stream);
 }
 
-hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, float* y,
-                                   hipStream_t stream) {
+hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
+                                   float* y, hipStream_t stream) {
   TiledArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
               nullptr, y, r.P, r.E, p.I, p.H, p.I, p.H / 256,
               (uint32_t)((uint64_t)r.L * p.I * 2u)};
-  return launch_tiled<TEpi::Down>(a, (int64_t)r.P / kTileRows + r.E, p.mx, stream);
+  return launch_tiled<TEpi::Down>(a, r.P, r.E, tile_rows, p.mx, stream);
 }
 
 hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,

@@ -129,13 +129,16 @@ def test_w4a16_repeat_calls_agree():
     assert np.max(np.abs(a - b)) <= 1e-2 * np.max(np.abs(a))
 
 
-# Prefill schedule with H and I multiples of 256: the 256-row tile kernels and the
-# per-pair combine.
+# Prefill schedule with H and I multiples of 256: the tile kernels (256-row tiles, or
+# 128-row tiles up to 136 routed rows per expert) and the per-pair combine.
 _TILE_CASES = [
     (600, 512, 256, 4, 2, "uniform"),    # two row tiles per expert, ragged second tile
     (1000, 768, 512, 3, 3, "uniform"),   # every token on every expert: 4 tiles, 232-row tail
     (256, 256, 256, 1, 1, "uniform"),    # exactly one full tile; K = 256 (one weight block)
-    (300, 256, 256, 16, 4, "zipf"),      # skewed routing with empty experts
+    (300, 256, 256, 16, 4, "zipf"),      # skewed routing with empty experts (128-row tiles)
+    (128, 256, 512, 2, 2, "uniform"),    # 128-row tiles: exactly one full tile per expert
+    (640, 512, 256, 8, 2, "uniform"),    # 128-row tiles: ragged second tiles
+    (200, 768, 256, 5, 3, "zipf"),       # 128-row tiles, skewed counts
 ]
 
 
