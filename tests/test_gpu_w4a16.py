@@ -137,7 +137,7 @@ _TILE_CASES = [
     (256, 256, 256, 1, 1, "uniform"),    # exactly one full tile; K = 256 (one weight block)
     (300, 256, 256, 16, 4, "zipf"),      # skewed routing with empty experts (128-row tiles)
     (128, 256, 512, 2, 2, "uniform"),    # 128-row tiles: exactly one full tile per expert
-    (640, 512, 256, 8, 2, "uniform"),    # 128-row tiles: ragged second tiles
+    (520, 512, 256, 8, 2, "uniform"),    # 128-row tiles: ragged second tiles (130 rows per expert)
     (200, 768, 256, 5, 3, "zipf"),       # 128-row tiles, skewed counts
 ]
 
