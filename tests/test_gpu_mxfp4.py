@@ -87,3 +87,15 @@ def test_mxfp4_exact_cases(oracle_mod, schedule):
     d["topk_ids"] = ids
     e = report(f"mxfp4 dropped ids sched={schedule}", _forward(d, schedule), _oracle(oracle_mod, d))
     assert e.max() <= TOL
+
+
+def test_mxfp4_empty_batch():
+    case = inputs.custom_mxfp4_case(1, 256, 128, 4, 2, seed=1)
+    d = to_dev(case)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    for schedule in SCHEDULES:
+        out = binding.moe_mxfp4_forward(x, d["w13"], d["s13"], d["w2"], d["s2"], ids, w,
+                                        schedule=schedule)
+        assert out.shape == (0, 256)
