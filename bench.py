@@ -94,7 +94,7 @@ def traffic_record(kernel_key, launches_ok):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (got --gpus {args.gpus}); the MoE "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MoE "
               "path has no multi-GPU mode here", file=sys.stderr)
         sys.exit(2)
 
