@@ -18,7 +18,9 @@
 // One wave per token: lane l holds experts l, l + 64, ...; each of the k rounds finds
 // the best unselected expert of every lane and reduces the lanes' candidates with a
 // 64-bit key (orderable logit bits, then the inverted id), so one wave-wide maximum
-// yields both the value and the lowest id among equals.
+// yields both the value and the lowest id among equals. The keys of the first 512
+// experts are formed once and kept in registers; the wave maximum moves data with DPP
+// inside 16-lane rows and with permlane swaps across rows (no LDS round trips).
 #include <algorithm>
 
 #include "../../include/qmoe.h"
@@ -46,15 +48,39 @@ __device__ __forceinline__ uint64_t key_of(float v, int e) {
   return ((uint64_t)ordered_bits(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// x of the lane that DPP control CTRL selects (every lane has a source: quad
+// permutations and rotations within a 16-lane row).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// The larger of x and its counterpart in the paired row (16-lane rows 0<->1, 2<->3) or
+// half (rows 0-1 <-> 2-3): a permlane swap of x with itself puts the partner's value in
+// one of the two results and the lane's own in the other.
+template <bool kHalves>
+__device__ __forceinline__ uint64_t max_with_partner(uint64_t x) {
+  const uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+  const auto l = kHalves ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                         : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h = kHalves ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                         : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  return max_u64(((uint64_t)h[0] << 32) | l[0], ((uint64_t)h[1] << 32) | l[1]);
+}
+
+// Wave-wide maximum, in every lane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)x, d, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(x >> 32), d, kWave);
-    const uint64_t y = ((uint64_t)hi << 32) | lo;
-    x = y > x ? y : x;
-  }
-  return x;
+  x = max_u64(x, dpp64<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = max_u64(x, dpp64<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = max_u64(x, dpp64<0x124>(x));  // row_ror:4
+  x = max_u64(x, dpp64<0x128>(x));  // row_ror:8: every lane holds its row's maximum
+  x = max_with_partner<false>(x);
+  return max_with_partner<true>(x);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -74,23 +100,20 @@ __global__ void __launch_bounds__(kRouterThreads)
        t += (int64_t)gridDim.x * kRouterWaves) {
     const float* row = logits + t * E;
     float reg[kRegChunks];
+    uint64_t keys[kRegChunks];  // 0 past the last expert (below every real key)
 #pragma unroll
     for (int j = 0; j < kRegChunks; ++j) {
       const int e = lane + kWave * j;
       reg[j] = e < E ? row[e] : 0.f;
+      keys[j] = e < E ? key_of(reg[j], e) : 0;
     }
     // Best key of this lane's unselected experts (0: none).
     uint64_t taken = 0;  // bit j: expert lane + 64 j is selected
     auto lane_best = [&]() {
       uint64_t best = 0;
 #pragma unroll
-      for (int j = 0; j < kRegChunks; ++j) {
-        const int e = lane + kWave * j;
-        if (e < E && !((taken >> j) & 1)) {
-          const uint64_t key = key_of(reg[j], e);
-          best = key > best ? key : best;
-        }
-      }
+      for (int j = 0; j < kRegChunks; ++j)
+        if (!((taken >> j) & 1)) best = max_u64(best, keys[j]);
       for (int j = kRegChunks; j < nchunks; ++j) {
         const int e = lane + kWave * j;
         if (e < E && !((taken >> j) & 1)) {
@@ -116,14 +139,13 @@ __global__ void __launch_bounds__(kRouterThreads)
         my_x = x;
         my_e = e;
       }
-      // Every 64 slots (and at the end) the lanes write their slot's id; the weight
-      // waits for the denominator, so it goes out as exp(l - m) and is divided below.
-      if ((i & (kWave - 1)) == kWave - 1 || i == k - 1) {
+      // Every 64 slots the lanes write their slot's id, and the weight as exp(l - m),
+      // divided below once the denominator is known (k > 64 only; up to 64 slots stay
+      // in registers until the end).
+      if ((i & (kWave - 1)) == kWave - 1 && i != k - 1) {
         const int base = i & ~(kWave - 1);
-        if (lane <= i - base) {
-          ids[t * k + base + lane] = expert_map ? expert_map[my_e] : my_e;
-          weights[t * k + base + lane] = my_x;
-        }
+        ids[t * k + base + lane] = expert_map ? expert_map[my_e] : my_e;
+        weights[t * k + base + lane] = my_x;
       }
     }
     float denom = sel_sum;
@@ -136,8 +158,14 @@ __global__ void __launch_bounds__(kRouterThreads)
         if (lane + kWave * j < E) part += expf(row[lane + kWave * j] - m);
       denom = wave_sum(part);
     }
-    // Each lane divides the slots it wrote (program order: its own stores).
-    for (int s = lane; s < k; s += kWave) weights[t * k + s] = weights[t * k + s] / denom;
+    // The last batch of up to 64 slots from registers; each lane divides the earlier
+    // slots it wrote (program order: its own stores).
+    const int last = (k - 1) & ~(kWave - 1);
+    if (lane <= k - 1 - last) {
+      ids[t * k + last + lane] = expert_map ? expert_map[my_e] : my_e;
+      weights[t * k + last + lane] = my_x / denom;
+    }
+    for (int s = lane; s < last; s += kWave) weights[t * k + s] = weights[t * k + s] / denom;
   }
 }
 
