@@ -168,3 +168,16 @@ def test_w4a16_prefill_tiles_zero_weights_and_dropped_ids(oracle_mod):
     assert report("tiles dropped ids", got, ref).max() <= TOL
     case["topk_weights"][:] = 0.0
     assert np.all(_forward(case, binding.SCHEDULE_PREFILL) == 0.0)
+
+
+@pytest.mark.parametrize("schedule", [binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL])
+def test_w4a16_max_expert_count(oracle_mod, schedule):
+    # QMOE_MAX_EXPERTS experts, 512 routed pairs: most experts are empty, the routed
+    # ones hold one or two rows (decode: the general kernel at K = 512 is persistent for
+    # gate_up; prefill: 128-row tiles, one per active expert).
+    T, H, I, E, k = 64, 512, 256, 4096, 8
+    print(f"[w4a16] max experts E={E} schedule={schedule}", flush=True)
+    case = inputs.custom_w4a16_case(T, H, I, E, k, seed=4096)
+    got = _forward(case, schedule)
+    e = report(f"E={E} sched={schedule}", got, _oracle(oracle_mod, case, None))
+    assert e.max() <= TOL
