@@ -23,6 +23,7 @@ on, over the timed steps. "cpu_baseline" times the CPU oracle on a bounded sampl
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -57,6 +58,20 @@ def parse():
                     help="instead of the MoE step, run a plain device-to-device copy of MIB "
                          "MiB (the known-size reference for HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def time_oracle(fn, min_s=10.0, max_reps=100):
+    """Seconds per call of fn, repeated until about min_s of CPU work (at most max_reps
+    calls), and the number of calls."""
+    t0 = time.perf_counter()
+    fn()
+    first = time.perf_counter() - t0
+    reps = min(max_reps, max(1, math.ceil(min_s / max(first, 1e-6))))
+    t0 = time.perf_counter()
+    for _ in range(reps - 1):
+        fn()
+    total = first + (time.perf_counter() - t0)
+    return total / reps, reps
 
 
 def weight_bytes_per_expert(cfg):
@@ -292,39 +307,39 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         nthreads = oracle.default_threads()
-        default_rows = {"tiny": cfg.T, "decode": cfg.T, "full384": 32, "prefill": 16, "fp8": 8,
-                        "decode_mxfp4": cfg.T, "prefill_mxfp4": 16,
+        default_rows = {"tiny": cfg.T, "decode": cfg.T, "full384": 192, "prefill": 192, "fp8": 32,
+                        "decode_mxfp4": cfg.T, "prefill_mxfp4": 48,
                         "grouped_prefill": 1536, "grouped_decode": 1536}
         nrows = args.cpu_rows or default_rows[args.workload]
         valid_rows = np.flatnonzero(valid.any(axis=1))
         rows = valid_rows[inputs.sample_rows(valid_rows.size, nrows, seed=cfg.seed)]
-        tc = time.perf_counter()
-        if grouped and masked:
-            oracle.w4a16_grouped_masked(case["a"], case["w13"], case["s13"], case["w2"], case["s2"],
-                                        case["masked_m"], rows=rows, nthreads=nthreads)
-        elif grouped:
-            oracle.w4a16_grouped_contiguous(case["a"], case["w13"], case["s13"], case["w2"],
-                                            case["s2"], case["m_indices"], rows=rows,
-                                            nthreads=nthreads)
-        elif cfg.fmt == "mxfp4":
-            oracle.mxfp4_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
-                             case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
-        elif cfg.fmt == "w4a16":
-            oracle.w4a16_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
-                             case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
-        else:
-            oracle.fp8_moe(case["a_q"], case["a_s"], case["w13"], case["s13"], case["w2"],
-                           case["s2"], case["topk_ids"], case["topk_weights"], rows=rows,
-                           nthreads=nthreads)
-        cpu_s = time.perf_counter() - tc
+        def run_oracle():
+            if grouped and masked:
+                oracle.w4a16_grouped_masked(case["a"], case["w13"], case["s13"], case["w2"], case["s2"],
+                                            case["masked_m"], rows=rows, nthreads=nthreads)
+            elif grouped:
+                oracle.w4a16_grouped_contiguous(case["a"], case["w13"], case["s13"], case["w2"],
+                                                case["s2"], case["m_indices"], rows=rows,
+                                                nthreads=nthreads)
+            elif cfg.fmt == "mxfp4":
+                oracle.mxfp4_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
+                                 case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
+            elif cfg.fmt == "w4a16":
+                oracle.w4a16_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
+                                 case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
+            else:
+                oracle.fp8_moe(case["a_q"], case["a_s"], case["w13"], case["s13"], case["w2"],
+                               case["s2"], case["topk_ids"], case["topk_weights"], rows=rows,
+                               nthreads=nthreads)
+        cpu_s, reps = time_oracle(run_oracle)
         # The oracle loops per (row, slot) and re-reads the expert's weights for each, so
         # the full workload costs (rows holding a pair) / nrows times the sample.
         full_s = cpu_s * valid_rows.size / len(rows)
         cpu_value = (weight_bytes / full_s / 1e9) if hbm_bound else (flops / full_s / 1e12)
         cpu = {"value": round(cpu_value, 6), "unit": unit, "cores": nthreads, "kind": "oracle",
                "sample": f"{len(rows)} of {valid_rows.size} rows (all {cfg.k} slots each), "
-                         f"{cpu_s:.1f} s on {nthreads} threads, scaled by "
-                         f"{valid_rows.size}/{len(rows)}"}
+                         f"{cpu_s:.2f} s per run (mean of {reps}) on {nthreads} threads, "
+                         f"scaled by {valid_rows.size}/{len(rows)}"}
 
     names = {"decode": "decode W4A16", "prefill": "prefill W4A16 (Zipf routing)",
              "fp8": "block-FP8 W8A8", "full384": "full 384-expert W4A16", "tiny": "tiny W4A16",
@@ -396,15 +411,13 @@ def bench_router(args, np, torch, binding, inputs):
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        rows = 512
-        tc = time.perf_counter()
-        oracle.topk_softmax(logits_h[:rows], k, True, emap_h)
-        cpu_s = time.perf_counter() - tc
+        rows = T
+        cpu_s, reps = time_oracle(lambda: oracle.topk_softmax(logits_h[:rows], k, True, emap_h))
         full_s = cpu_s * T / rows
         cpu = {"value": round(nbytes / full_s / 1e9, 6), "unit": "GB/s", "cores": 1,
                "kind": "oracle",
-               "sample": f"{rows} of {T} token rows, {cpu_s:.3f} s on 1 thread, scaled by "
-                         f"{T}/{rows}"}
+               "sample": f"{rows} of {T} token rows, {cpu_s:.3f} s per run (mean of {reps}) "
+                         f"on 1 thread"}
     line = {
         "metric": "router GB/s (logits read, ids and weights written), % of HBM roofline",
         "value": round(achieved, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
