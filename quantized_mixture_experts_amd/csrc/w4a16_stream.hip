@@ -405,6 +405,8 @@ static_assert(kRing % 2 == 0 && kRing >= 4, "ring of whole units, at least two")
 // Group scales are staged per block of kScaleUnits units: 128 B (one cache line) of
 // each weight row, loaded a block ahead with whole lines per row.
 constexpr int kScaleUnits = 4;
+// f32x4 entries per staged scale piece: its two half steps of 16 rows, plus two of pad.
+constexpr int kPieceStride = 2 * 16 + 2;
 constexpr int kBodyUnits = (kRing / 2) % 2 == 0 ? kRing / 2 : kRing;
 constexpr int kWin = kRing / 2 + 1;  // unit descriptors kept ahead (the farthest load)
 
@@ -437,9 +439,12 @@ __global__ void __launch_bounds__(kPThreads)
   // float per row (read by the four lanes of a row quarter at once).
   __shared__ float c_lds[2][MB][kChunkGroups][16];
   // Scales of the current block as fp32, converted once when the block is staged:
-  // [wave][tile][step in block][half step][row], four groups each (rows innermost, so
-  // the sixteen rows a wave reads at once are 16 B apart).
-  __shared__ f32x4 s_lds[kPWaves][2][2 * kScaleUnits][2][16];
+  // [wave][tile][step in block][half step * 16 + row], four groups each (rows innermost,
+  // so the sixteen rows a wave reads at once are 16 B apart). Each piece's 2 x 16 entries
+  // are padded to kPieceStride: the block store writes eight rows of eight pieces at
+  // once, and without the pad the pieces (512 B apart) would all land on the same LDS
+  // banks.
+  __shared__ f32x4 s_lds[kPWaves][2][2 * kScaleUnits][kPieceStride];
 
   // gate_up clears the fp32 output that down accumulates into (down starts after the
   // last gate_up work-group has ended).
@@ -563,16 +568,16 @@ __global__ void __launch_bounds__(kPThreads)
     for (int i = 0; i < 4; ++i) {
       const u32x4 v = snext[i];
       if constexpr (MX) {
-        s_lds[wave][i >> 1][s_piece][0][8 * (i & 1) + s_row] =
+        s_lds[wave][i >> 1][s_piece][8 * (i & 1) + s_row] =
             f32x4{e8m0_scale(v[0]), e8m0_scale(v[0] >> 8), e8m0_scale(v[0] >> 16),
                   e8m0_scale(v[0] >> 24)};
-        s_lds[wave][i >> 1][s_piece][1][8 * (i & 1) + s_row] =
+        s_lds[wave][i >> 1][s_piece][16 + 8 * (i & 1) + s_row] =
             f32x4{e8m0_scale(v[1]), e8m0_scale(v[1] >> 8), e8m0_scale(v[1] >> 16),
                   e8m0_scale(v[1] >> 24)};
       } else {
-        s_lds[wave][i >> 1][s_piece][0][8 * (i & 1) + s_row] =
+        s_lds[wave][i >> 1][s_piece][8 * (i & 1) + s_row] =
             f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-        s_lds[wave][i >> 1][s_piece][1][8 * (i & 1) + s_row] =
+        s_lds[wave][i >> 1][s_piece][16 + 8 * (i & 1) + s_row] =
             f32x4{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
       }
     }
@@ -625,8 +630,8 @@ __global__ void __launch_bounds__(kPThreads)
     f32x4 sv[2][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      sv[0][half] = s_lds[wave][0][sp][half][col];
-      sv[1][half] = s_lds[wave][1][sp][half][col];
+      sv[0][half] = s_lds[wave][0][sp][16 * half + col];
+      sv[1][half] = s_lds[wave][1][sp][16 * half + col];
       uint32_t wt[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
