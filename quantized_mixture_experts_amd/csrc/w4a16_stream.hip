@@ -63,7 +63,7 @@ struct StreamArgs {
   const uint16_t* s;          // [E, N, K/32] bf16 (INT4) or E8M0 bytes (MXFP4)
   const int32_t* sorted_ids;  // [L]
   const int32_t* offsets;     // [E + 1]
-  const int32_t* expert_ids;  // [L / 16], expert of each 16-row block
+  const int32_t* expert_ids;  // [L / block_m], expert of each align block (16 MB rows)
   const int32_t* ntp;         // rows in use (a multiple of 16)
   const float* topk_weights;  // [P]
   uint16_t* h;                // gate_up output [L, I], tiled layout
@@ -379,8 +379,8 @@ __global__ void __launch_bounds__(kThreads)
 
 // Persistent variant for K a multiple of 512. The grid is one work-group per compute
 // unit; work-group w takes a contiguous range of units, a unit being 512 of one item's K
-// (two 256-deep steps, i.e. one activation chunk), in (16-row block, column chunk, k)
-// order. The weight ring, the activation chunk double buffer and the scale pieces run on
+// (two 256-deep steps, i.e. one activation chunk), in (row block of 16 MB rows, column
+// chunk, k) order. The weight ring, the activation chunk double buffer and the scale pieces run on
 // across item boundaries, so a work-group never waits for a pipeline refill after the
 // first, and every work-group gets the same number of units up to one. down ranges may
 // start or end inside an item: each piece adds its partial sum into the fp32 output with
@@ -416,7 +416,7 @@ __device__ __forceinline__ void unroll_units(F& f, int u, std::integer_sequence<
 }
 
 struct Unit {
-  int rb, cc, kc, e;  // 16-row block, column chunk, unit within the item's K, expert
+  int rb, cc, kc, e;  // row block (16 MB rows), column chunk, unit within the item's K, expert
 };
 
 // A read of data that no launch in flight writes, through the constant address space so

@@ -8,10 +8,11 @@
 // prefill is bound by the matrix units (same page, "Kernel optimizations"), so the
 // kernel is laid out for the matrix cores.
 //
-// gfx950 mapping. A work-group owns one (256-row tile of an expert segment, 256 weight
-// rows) output tile over eight waves, two per SIMD; each wave owns all 256 rows and 32
-// weight rows (two 16-column MFMA tiles), so every weight element is dequantized exactly
-// once per tile and reused for 16 row blocks:
+// gfx950 mapping. A work-group owns one (row tile of an expert segment, 256 weight rows)
+// output tile over eight waves, two per SIMD; the row tile is 256 rows, or 128 when the
+// experts hold few rows. Each wave owns all the tile's rows and 32 weight rows (two
+// 16-column MFMA tiles), so every weight element is dequantized exactly once per tile and
+// reused for 16 (or 8) row blocks:
 //   * activation rows (bf16, tiled layout: the operand of one 16-row block and k group
 //     is 1 KB contiguous), weight words and block scales move global -> LDS by buffer
 //     loads into LDS: activations through a ring of seven 16 KB stages, six k groups
@@ -82,7 +83,7 @@ struct TiledArgs {
   const uint16_t* s;            // [E, N, K/32] bf16 (INT4) or E8M0 bytes (MXFP4)
   const int32_t* sorted_ids;    // [L]
   const int32_t* offsets;       // [E + 1] segment starts (multiples of 16)
-  const int32_t* tile_offsets;  // [E + 1] 256-row tiles per expert, exclusive scan
+  const int32_t* tile_offsets;  // [E + 1] row tiles per expert (launch's height), exclusive scan
   const float* topk_weights;    // [P]
   uint16_t* h;                  // gate_up output [L, I], tiled layout
   float* y;                     // down output [P, N] per routed pair
