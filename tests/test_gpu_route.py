@@ -132,3 +132,16 @@ def test_router_and_bf16_quantizer_to_fp8_forward(oracle_mod):
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 5e-3
     assert np.mean(e <= TOL) >= 0.99
     assert e.max() <= 5e-2
+
+
+def test_router_bench_configuration(oracle_mod):
+    # The benchmark's router workload at full size: 8192 tokens, 384 experts, top-8,
+    # renormalized, Zipf logits, ids mapped to the share of experts 48..95.
+    T, E, k, share = 8192, 384, 8, 48
+    logits = inputs.router_logits(np.random.default_rng(97), T, E, "zipf")
+    emap = np.full(E, -1, np.int32)
+    emap[share:2 * share] = np.arange(share, dtype=np.int32)
+    ids, _ = _check(oracle_mod, logits, k, True, emap)
+    local = ids.cpu().numpy()
+    assert np.all((local == -1) | ((local >= 0) & (local < share)))
+    assert (local >= 0).any() and (local == -1).any()
