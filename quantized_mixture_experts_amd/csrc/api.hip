@@ -38,8 +38,12 @@ enum Format { kW4A16 = 0, kFp8 = 1, kMxfp4 = 2 };
 // The 4-bit formats share the W4A16 kernels, workspace and limits.
 bool four_bit(int fmt) { return fmt == kW4A16 || fmt == kMxfp4; }
 
-// Rows per weight pass of the FP8 decode kernels, in 16-row blocks.
-int decode_mb_for(double) { return 1; }
+// Rows per weight pass of the FP8 decode kernels, in 16-row blocks: four, measured on
+// MI355X at hidden 7168, intermediate 2048, 32 experts (one / two / four blocks: 0.30 /
+// 0.30 / 0.30 ms at 8 rows per expert, 0.52 / 0.37 / 0.36 ms at 16, 0.79 / 0.57 / 0.43
+// ms at 32): a pass serves up to 64 rows for one read of the weights, and an empty
+// block costs little next to the FP8 weight stream.
+int decode_mb_for(double) { return 4; }
 // Routed rows per expert above which the 4-bit persistent decode kernel serves two
 // 16-row blocks per weight pass, measured on MI355X for hidden 7168, intermediate 2048,
 // 48 experts (one vs two blocks per pass: W4A16 at 14 rows 0.342 vs 0.355 ms, at 16
@@ -98,9 +102,9 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   // the weights once per pass of one or two 16-row blocks and the tile kernels use
   // 128-row tiles at these sizes, so decode wins up to about 44 routed rows per expert
   // for W4A16 (40: 0.69 vs 0.71 ms; 48: 0.72 vs 0.71 ms), about 60 for MXFP4 (56: 0.61
-  // vs 0.64 ms; 64: 0.69 vs 0.64 ms) and about 12 for block FP8 (8: 0.30 vs 0.38 ms;
-  // 16: 0.52 vs 0.38 ms).
-  const double crossover = fmt == kW4A16 ? 44.0 : fmt == kMxfp4 ? 60.0 : 12.0;
+  // vs 0.64 ms; 64: 0.69 vs 0.64 ms) and about 20 for block FP8 with four blocks per
+  // pass (16: 0.36 vs 0.38 ms; 24: 0.40 vs 0.39 ms).
+  const double crossover = fmt == kW4A16 ? 44.0 : fmt == kMxfp4 ? 60.0 : 20.0;
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= crossover ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
   p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&
