@@ -36,6 +36,8 @@ def _load():
     lib.oracle_w4a16_moe.restype = ctypes.c_int
     lib.oracle_mxfp4_moe.argtypes = [_P] * 7 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
     lib.oracle_mxfp4_moe.restype = ctypes.c_int
+    lib.oracle_nvfp4_moe.argtypes = [_P] * 9 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
+    lib.oracle_nvfp4_moe.restype = ctypes.c_int
     lib.oracle_fp8_moe.argtypes = [_P] * 8 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
     lib.oracle_fp8_moe.restype = ctypes.c_int
     lib.oracle_fp8_quantize_blocks.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P]
@@ -148,6 +150,33 @@ def mxfp4_moe(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=N
     activations, in fp64. Returns float64 [nrows, H] (before bf16 rounding)."""
     return _w4_moe("oracle_mxfp4_moe", np.uint8, x, w13, s13, w2, s2, topk_ids, topk_weights,
                    rows, nthreads)
+
+def nvfp4_moe(x, w13, s13, g13, w2, s2, g2, topk_ids, topk_weights, rows=None, nthreads=None):
+    """Routed MoE FFN with NVFP4 weights (E2M1 codes packed like the INT4 codes, E4M3
+    scales per row and 16 columns: s13 [E,2I,H/16] uint8, s2 [E,H,I/16] uint8, fp32
+    global scales g13 [E], g2 [E]) and bf16 activations, in fp64. Returns float64
+    [nrows, H] (before bf16 rounding)."""
+    x = _c(x, np.uint16)
+    w13, s13, w2, s2 = (_c(a, np.uint8) for a in (w13, s13, w2, s2))
+    g13, g2 = _c(g13, np.float32), _c(g2, np.float32)
+    ids = _c(topk_ids, np.int32)
+    wts = _c(topk_weights, np.float32)
+    T, H = x.shape
+    E, twoI, _ = w13.shape
+    k = ids.shape[1]
+    if rows is None:
+        nrows, rp = T, None
+    else:
+        rows_arr = _c(np.asarray(rows, dtype=np.int64), np.int64)
+        nrows, rp = rows_arr.size, _ptr(rows_arr)
+    out = np.zeros((nrows, H), np.float64)
+    rc = _load().oracle_nvfp4_moe(_ptr(x), _ptr(w13), _ptr(s13), _ptr(g13), _ptr(w2), _ptr(s2),
+                                  _ptr(g2), _ptr(ids), _ptr(wts), T, H, twoI // 2, E, k, rp,
+                                  nrows, _ptr(out), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_nvfp4_moe: bad arguments")
+    return out
+
 
 def w4a16_grouped_contiguous(a, w13, s13, w2, s2, m_indices, rows=None, nthreads=None):
     """The W4A16 expert FFN on the contiguous grouped layout ("vLLM x Novita AI: Chord W4A16

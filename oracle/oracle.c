@@ -39,6 +39,10 @@
  *    32 consecutive columns (the OCP microscaling block of 32); weight = e2m1(code) *
  *    2^(scale - 127), with E2M1 = sign bit 3, exponent bits 2..1 (bias 1), mantissa
  *    bit 0, exponent 0 subnormal (0.5 * mantissa); E8M0 code 255 is NaN;
+ *  - NVFP4 weights (weight-only, [XT] overview; the "NVFP4-W4A16" checkpoints of [LSG]):
+ *    the same E2M1 codes and packing, one E4M3 scale per row and 16 consecutive columns,
+ *    and one fp32 scale per expert and projection; weight = e2m1(code) * e4m3(scale) *
+ *    global;
  *  - routed ids outside [0, E) are dropped;
  *  - E4M3 is OCP E4M3FN, round-to-nearest-even after clamping to +-448;
  *    block scale = max(absmax, 1e-10) / 448;
@@ -282,6 +286,8 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* E2M1 code (low 4 bits) -> value: sign bit 3, exponent bits 2..1 with bias 1,
  * mantissa bit 0; exponent 0 is subnormal, 0.5 * mantissa. */
+double oracle_e4m3_to_f64(uint8_t c);
+
 double oracle_e2m1_to_f64(uint8_t c) {
   int sign = (c >> 3) & 1, e = (c >> 1) & 3, m = c & 1;
   double mag = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
@@ -291,7 +297,7 @@ double oracle_e2m1_to_f64(uint8_t c) {
 /* E8M0 scale code -> 2^(code - 127); code 255 is NaN. */
 double oracle_e8m0_to_f64(uint8_t c) { return c == 255 ? NAN : ldexp(1.0, (int)c - 127); }
 
-enum { FMT_INT4 = 0, FMT_MXFP4 = 1 };
+enum { FMT_INT4 = 0, FMT_MXFP4 = 1, FMT_NVFP4 = 2 };
 
 /* Dequantized 4-bit weight of row n, column c of a [N, K] matrix stored as packed
  * codes [N, K/2] (low nibble = even column) with one scale per row and 32 columns
@@ -301,6 +307,9 @@ static double w4_weight(int fmt, const uint8_t* w, const void* s, int64_t K, int
                         int64_t c) {
   uint8_t byte = w[n * (K / 2) + c / 2];
   int code = (c & 1) ? (byte >> 4) & 0xF : byte & 0xF;
+  if (fmt == FMT_NVFP4) /* the expert's global scale is applied by the caller */
+    return oracle_e2m1_to_f64((uint8_t)code) *
+           oracle_e4m3_to_f64(((const uint8_t*)s)[n * (K / 16) + c / 16]);
   int64_t si = n * (K / 32) + c / 32;
   if (fmt == FMT_MXFP4)
     return oracle_e2m1_to_f64((uint8_t)code) * oracle_e8m0_to_f64(((const uint8_t*)s)[si]);
@@ -312,14 +321,15 @@ static double w4_weight(int fmt, const uint8_t* w, const void* s, int64_t K, int
  *   g_j = sum_c x_c W13_e(j, c),  u_j = sum_c x_c W13_e(I + j, c),
  * slots in s order, every sum sequential, all in fp64. h is kept in fp64. */
 static void w4a16_token(int fmt, const uint16_t* x, const uint8_t* w13, const void* s13,
-                        const uint8_t* w2, const void* s2, const int32_t* ids,
-                        const float* wts, int64_t t, int64_t H, int64_t I, int64_t E, int64_t k,
-                        double* xrow, double* h, double* out) {
-  const int64_t ssz = fmt == FMT_MXFP4 ? 1 : 2; /* bytes per scale */
+                        const float* g13, const uint8_t* w2, const void* s2, const float* g2,
+                        const int32_t* ids, const float* wts, int64_t t, int64_t H, int64_t I,
+                        int64_t E, int64_t k, double* xrow, double* h, double* out) {
+  const int64_t ssz = fmt == FMT_INT4 ? 2 : 1;   /* bytes per scale */
+  const int64_t blk = fmt == FMT_NVFP4 ? 16 : 32; /* columns per scale */
   for (int64_t c = 0; c < H; ++c) xrow[c] = oracle_bf16_to_f64(x[t * H + c]);
   for (int64_t n = 0; n < H; ++n) out[n] = 0.0;
-  const int64_t w13_expert = 2 * I * (H / 2), s13_expert = 2 * I * (H / 32);
-  const int64_t w2_expert = H * (I / 2), s2_expert = H * (I / 32);
+  const int64_t w13_expert = 2 * I * (H / 2), s13_expert = 2 * I * (H / blk);
+  const int64_t w2_expert = H * (I / 2), s2_expert = H * (I / blk);
   for (int64_t s = 0; s < k; ++s) {
     int32_t e = ids[t * k + s];
     if (e < 0 || e >= E) continue;
@@ -328,15 +338,20 @@ static void w4a16_token(int fmt, const uint16_t* x, const uint8_t* w13, const vo
     const uint8_t* se13 = (const uint8_t*)s13 + e * s13_expert * ssz;
     const uint8_t* we2 = w2 + e * w2_expert;
     const uint8_t* se2 = (const uint8_t*)s2 + e * s2_expert * ssz;
+    /* NVFP4: every weight of the expert's projection times its global scale */
+    const double gg13 = fmt == FMT_NVFP4 ? (double)g13[e] : 1.0;
+    const double gg2 = fmt == FMT_NVFP4 ? (double)g2[e] : 1.0;
     for (int64_t j = 0; j < I; ++j) {
       double g = 0.0, u = 0.0;
-      for (int64_t c = 0; c < H; ++c) g += xrow[c] * w4_weight(fmt, we13, se13, H, j, c);
-      for (int64_t c = 0; c < H; ++c) u += xrow[c] * w4_weight(fmt, we13, se13, H, I + j, c);
+      for (int64_t c = 0; c < H; ++c)
+        g += xrow[c] * (w4_weight(fmt, we13, se13, H, j, c) * gg13);
+      for (int64_t c = 0; c < H; ++c)
+        u += xrow[c] * (w4_weight(fmt, we13, se13, H, I + j, c) * gg13);
       h[j] = silu(g) * u;
     }
     for (int64_t n = 0; n < H; ++n) {
       double y = 0.0;
-      for (int64_t j = 0; j < I; ++j) y += h[j] * w4_weight(fmt, we2, se2, I, n, j);
+      for (int64_t j = 0; j < I; ++j) y += h[j] * (w4_weight(fmt, we2, se2, I, n, j) * gg2);
       out[n] += wt * y;
     }
   }
@@ -348,9 +363,11 @@ static void w4a16_token(int fmt, const uint16_t* x, const uint8_t* w13, const vo
  * out [nrows, H] fp64 before the final bf16 rounding. Rows are independent and
  * are spread over nthreads OpenMP threads; each row is computed as written. */
 static int w4_moe(int fmt, const uint16_t* x, const uint8_t* w13, const void* s13,
-                  const uint8_t* w2, const void* s2, const int32_t* ids, const float* wts,
-                  int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, const int64_t* rows,
-                  int64_t nrows, double* out, int nthreads) {
+                  const float* g13, const uint8_t* w2, const void* s2, const float* g2,
+                  const int32_t* ids, const float* wts, int64_t T, int64_t H, int64_t I,
+                  int64_t E, int64_t k, const int64_t* rows, int64_t nrows, double* out,
+                  int nthreads) {
+  if (fmt == FMT_NVFP4 && (!g13 || !g2)) return ORACLE_BAD_ARG;
   if (!x || !w13 || !s13 || !w2 || !s2 || !ids || !wts || !out) return ORACLE_BAD_ARG;
   if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || H % 32 || I % 32) return ORACLE_BAD_ARG;
   if (!rows) nrows = T;
@@ -370,7 +387,8 @@ static int w4_moe(int fmt, const uint16_t* x, const uint8_t* w13, const void* s1
 #pragma omp for schedule(dynamic, 1)
       for (int64_t r = 0; r < nrows; ++r) {
         int64_t t = rows ? rows[r] : r;
-        w4a16_token(fmt, x, w13, s13, w2, s2, ids, wts, t, H, I, E, k, xrow, h, out + r * H);
+        w4a16_token(fmt, x, w13, s13, g13, w2, s2, g2, ids, wts, t, H, I, E, k, xrow, h,
+                    out + r * H);
       }
     }
     free(xrow);
@@ -383,8 +401,8 @@ int oracle_w4a16_moe(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
                      const uint16_t* s2, const int32_t* ids, const float* wts, int64_t T, int64_t H,
                      int64_t I, int64_t E, int64_t k, const int64_t* rows, int64_t nrows,
                      double* out, int nthreads) {
-  return w4_moe(FMT_INT4, x, w13, s13, w2, s2, ids, wts, T, H, I, E, k, rows, nrows, out,
-                nthreads);
+  return w4_moe(FMT_INT4, x, w13, s13, NULL, w2, s2, NULL, ids, wts, T, H, I, E, k, rows, nrows,
+                out, nthreads);
 }
 
 /* Routed MXFP4 MoE FFN (weight-only, [XT] overview): as oracle_w4a16_moe with E2M1
@@ -393,8 +411,18 @@ int oracle_mxfp4_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* s13, 
                      const uint8_t* s2, const int32_t* ids, const float* wts, int64_t T, int64_t H,
                      int64_t I, int64_t E, int64_t k, const int64_t* rows, int64_t nrows,
                      double* out, int nthreads) {
-  return w4_moe(FMT_MXFP4, x, w13, s13, w2, s2, ids, wts, T, H, I, E, k, rows, nrows, out,
-                nthreads);
+  return w4_moe(FMT_MXFP4, x, w13, s13, NULL, w2, s2, NULL, ids, wts, T, H, I, E, k, rows,
+                nrows, out, nthreads);
+}
+
+/* Routed NVFP4 MoE FFN (weight-only): E2M1 codes, E4M3 scales s13 [E,2I,H/16] and
+ * s2 [E,H,I/16] (u8), fp32 global scales g13 [E] and g2 [E]. */
+int oracle_nvfp4_moe(const uint16_t* x, const uint8_t* w13, const uint8_t* s13, const float* g13,
+                     const uint8_t* w2, const uint8_t* s2, const float* g2, const int32_t* ids,
+                     const float* wts, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k,
+                     const int64_t* rows, int64_t nrows, double* out, int nthreads) {
+  return w4_moe(FMT_NVFP4, x, w13, s13, g13, w2, s2, g2, ids, wts, T, H, I, E, k, rows, nrows,
+                out, nthreads);
 }
 
 /* ------------------------------------------------------------------------- */

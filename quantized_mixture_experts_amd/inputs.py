@@ -21,6 +21,9 @@ MoE engine's weight formats include MXFP4 (E2M1)), at the decode and prefill sha
   decode_mxfp4   32 tokens, H 7168, I 2048, 48 experts, top-8, uniform routing
   prefill_mxfp4  8192 tokens, H 7168, I 2048, 48 experts, top-8, Zipf(1.0) routing
 
+NVFP4 weights (weight-only, same page's list; "NVFP4-W4A16" checkpoints in the
+"guqiong96/Lsglang" README), at the same shapes: decode_nvfp4, prefill_nvfp4.
+
 Grouped layouts (same page, SM90 grouped kernels, Figure 3 and the grouped rows of the
 measurements; rows already grouped by expert, one pair of weight 1 per row):
 
@@ -35,6 +38,8 @@ Recipe (per case, numpy default_rng(seed), draws in this order):
           w2 uniform bytes [E,H,I/2];  s2 bf16(|N(0,1)|*0.02) [E,H,I/32]
   FP8     per expert: w13 source N(0,1) [2I,H], then w2 source N(0,1) [H,I],
           each quantized in [128,128] blocks by the caller's quantizer
+  NVFP4   w13 uniform bytes; s13 E4M3 codes with exponent field 4..6 and any mantissa
+          (0.125 .. 0.9375) [E,2I,H/16]; g13 fp32 |N(0,1)|*0.02+0.01 [E]; w2, s2, g2 likewise
   MXFP4   w13 uniform bytes [E,2I,H/2] (every E2M1 code, -0 included);
           s13 E8M0 codes uniform in {119, 120, 121} (2^-8 .. 2^-6) [E,2I,H/32];
           w2 uniform bytes [E,H,I/2]; s2 likewise [E,H,I/32]
@@ -54,7 +59,7 @@ class MoEConfig:
     I: int
     E: int
     k: int
-    fmt: str  # "w4a16", "mxfp4" or "fp8"
+    fmt: str  # "w4a16", "mxfp4", "nvfp4" or "fp8"
     routing: str  # "uniform" or "zipf"
     index: int  # 1-based position in the workload list; seeds are SEED_BASE + index
 
@@ -75,6 +80,8 @@ CONFIGS = {
     "full384": MoEConfig("full384", 256, 7168, 2048, 384, 8, "w4a16", "uniform", 5),
     "decode_mxfp4": MoEConfig("decode_mxfp4", 32, 7168, 2048, 48, 8, "mxfp4", "uniform", 8),
     "prefill_mxfp4": MoEConfig("prefill_mxfp4", 8192, 7168, 2048, 48, 8, "mxfp4", "zipf", 9),
+    "decode_nvfp4": MoEConfig("decode_nvfp4", 32, 7168, 2048, 48, 8, "nvfp4", "uniform", 10),
+    "prefill_nvfp4": MoEConfig("prefill_nvfp4", 8192, 7168, 2048, 48, 8, "nvfp4", "zipf", 11),
 }
 
 
@@ -168,6 +175,33 @@ def mxfp4_case(cfg: MoEConfig, seed=None) -> dict:
     w2 = _bytes(rng, (E, H, I // 2))
     s2 = _e8m0(rng, (E, H, I // 32))
     return dict(x=x, topk_ids=ids, topk_weights=wts, w13=w13, s13=s13, w2=w2, s2=s2)
+
+
+def _e4m3_scales(rng, shape):
+    # positive E4M3 codes: exponent field 4..6, any mantissa
+    return (rng.integers(4, 7, size=shape, dtype=np.uint8) << 3) | rng.integers(0, 8, size=shape, dtype=np.uint8)
+
+
+def nvfp4_case(cfg: MoEConfig, seed=None) -> dict:
+    """All host arrays of one NVFP4 case (see the module recipe)."""
+    if cfg.fmt != "nvfp4":
+        raise ValueError(cfg.fmt)
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    x = bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
+    ids, wts = routing(rng, T, E, k, cfg.routing)
+    w13 = _bytes(rng, (E, 2 * I, H // 2))
+    s13 = _e4m3_scales(rng, (E, 2 * I, H // 16))
+    g13 = (np.abs(rng.standard_normal(E, dtype=np.float32)) * np.float32(0.02) + np.float32(0.01))
+    w2 = _bytes(rng, (E, H, I // 2))
+    s2 = _e4m3_scales(rng, (E, H, I // 16))
+    g2 = (np.abs(rng.standard_normal(E, dtype=np.float32)) * np.float32(0.02) + np.float32(0.01))
+    return dict(x=x, topk_ids=ids, topk_weights=wts, w13=w13, s13=s13, g13=g13, w2=w2, s2=s2,
+                g2=g2)
+
+
+def custom_nvfp4_case(T, H, I, E, k, seed, kind="uniform") -> dict:
+    return nvfp4_case(MoEConfig("custom", T, H, I, E, k, "nvfp4", kind, 0), seed=seed)
 
 
 def custom_mxfp4_case(T, H, I, E, k, seed, kind="uniform") -> dict:
