@@ -9,7 +9,7 @@ around every kernel on its launch stream.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
                   [--workload decode|prefill|fp8|full384|tiny|router|grouped_prefill|grouped_decode|
-                              decode_mxfp4|prefill_mxfp4]
+                              decode_mxfp4|prefill_mxfp4|decode_nvfp4|prefill_nvfp4]
 
 Prints one JSON line. The default workload is the decode layer (32 tokens, hidden 7168,
 intermediate 2048, 48 local experts, top-8, INT4 group-32 weights); its value is the
@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--workload", default="decode",
                     choices=["decode", "prefill", "fp8", "full384", "tiny", "router",
                              "grouped_prefill", "grouped_decode", "decode_mxfp4",
-                             "prefill_mxfp4"])
+                             "prefill_mxfp4", "decode_nvfp4", "prefill_nvfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
                     help="how the timed steps are issued: eager library calls (default), or "
@@ -76,8 +76,8 @@ def time_oracle(fn, min_s=10.0, max_reps=100):
 
 def weight_bytes_per_expert(cfg):
     H, I = cfg.H, cfg.I
-    if cfg.fmt in ("w4a16", "mxfp4"):
-        sb = 2 if cfg.fmt == "w4a16" else 1  # bf16 or E8M0 scale bytes
+    if cfg.fmt in ("w4a16", "mxfp4", "nvfp4"):
+        sb = {"w4a16": 2, "mxfp4": 1, "nvfp4": 2}[cfg.fmt]  # scale bytes per 32 k
         w13 = 2 * I * H // 2 + 2 * I * (H // 32) * sb
         w2 = H * I // 2 + H * (I // 32) * sb
     else:
@@ -170,6 +170,10 @@ def main():
         cfg = inputs.CONFIGS[args.workload]
         case = inputs.mxfp4_case(cfg)
         ids = case["topk_ids"]
+    elif inputs.CONFIGS[args.workload].fmt == "nvfp4":
+        cfg = inputs.CONFIGS[args.workload]
+        case = inputs.nvfp4_case(cfg)
+        ids = case["topk_ids"]
     else:
         cfg = inputs.CONFIGS[args.workload]
 
@@ -182,7 +186,7 @@ def main():
     gen_s = time.time() - t_gen
 
     fmt = {"w4a16": binding.FORMAT_W4A16, "mxfp4": binding.FORMAT_MXFP4,
-           "fp8": binding.FORMAT_FP8}[cfg.fmt]
+           "nvfp4": binding.FORMAT_NVFP4, "fp8": binding.FORMAT_FP8}[cfg.fmt]
     out = torch.empty((cfg.T, cfg.H), dtype=torch.bfloat16, device=dev)
     if grouped:
         # The schedule AUTO picks from the expected rows per expert (k = 1).
@@ -213,6 +217,11 @@ def main():
         def step():
             binding.moe_mxfp4_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
                                       d["topk_weights"], out=out, workspace=workspace)
+    elif cfg.fmt == "nvfp4":
+        def step():
+            binding.moe_nvfp4_forward(d["x"], d["w13"], d["s13"], d["g13"], d["w2"], d["s2"],
+                                      d["g2"], d["topk_ids"], d["topk_weights"], out=out,
+                                      workspace=workspace)
     else:
         def step():
             binding.moe_fp8_block_forward(d["a_q"], d["a_s"], d["w13"], d["s13"], d["w2"], d["s2"],
@@ -309,6 +318,7 @@ def main():
         nthreads = oracle.default_threads()
         default_rows = {"tiny": cfg.T, "decode": cfg.T, "full384": 192, "prefill": 192, "fp8": 32,
                         "decode_mxfp4": cfg.T, "prefill_mxfp4": 48,
+                        "decode_nvfp4": cfg.T, "prefill_nvfp4": 48,
                         "grouped_prefill": 1536, "grouped_decode": 1536}
         nrows = args.cpu_rows or default_rows[args.workload]
         valid_rows = np.flatnonzero(valid.any(axis=1))
@@ -321,6 +331,10 @@ def main():
                 oracle.w4a16_grouped_contiguous(case["a"], case["w13"], case["s13"], case["w2"],
                                                 case["s2"], case["m_indices"], rows=rows,
                                                 nthreads=nthreads)
+            elif cfg.fmt == "nvfp4":
+                oracle.nvfp4_moe(case["x"], case["w13"], case["s13"], case["g13"], case["w2"],
+                                 case["s2"], case["g2"], case["topk_ids"], case["topk_weights"],
+                                 rows=rows, nthreads=nthreads)
             elif cfg.fmt == "mxfp4":
                 oracle.mxfp4_moe(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
                                  case["topk_ids"], case["topk_weights"], rows=rows, nthreads=nthreads)
@@ -344,7 +358,10 @@ def main():
     names = {"decode": "decode W4A16", "prefill": "prefill W4A16 (Zipf routing)",
              "fp8": "block-FP8 W8A8", "full384": "full 384-expert W4A16", "tiny": "tiny W4A16",
              "decode_mxfp4": "decode MXFP4 (E2M1 + E8M0 per 32, bf16 activations)",
-             "prefill_mxfp4": "prefill MXFP4 (E2M1 + E8M0 per 32, bf16 activations; Zipf routing)"}
+             "prefill_mxfp4": "prefill MXFP4 (E2M1 + E8M0 per 32, bf16 activations; Zipf routing)",
+             "decode_nvfp4": "decode NVFP4 (E2M1 + E4M3 per 16 + fp32 per expert, bf16 activations)",
+             "prefill_nvfp4": "prefill NVFP4 (E2M1 + E4M3 per 16 + fp32 per expert, bf16 "
+                              "activations; Zipf routing)"}
     if grouped:
         layout = (f"masked, {g['rows']} valid rows per expert in a budget of {g['max_m']}"
                   if masked else f"contiguous, {g['rows']} rows per expert")

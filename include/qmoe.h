@@ -14,6 +14,8 @@
  *           (the grouped prefill and decode rows).
  *   [XT]    "xiaotu-moe" (PyPI project page): overview (the MoE engine's weight
  *           formats: BF16, FP8 (WNA16), MXFP4 (E2M1), NVFP4).
+ *   [LSG]   "guqiong96/Lsglang" README (SkillsMP page): quick start (an NVFP4-W4A16
+ *           checkpoint), supported quant formats.
  *   [SGL]   "SGLang W8A8 Block FP8 quantization kernel config guide" (xdnf.cn):
  *           background section (E4M3, [BLOCK_N, BLOCK_K] weight blocks, per-token-group
  *           activation scales As, weight block scales Bs); kernel dispatch section
@@ -241,6 +243,29 @@ qmoe_status moe_mxfp4_forward(const uint16_t* x, const uint8_t* w13, const uint8
                               void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * moe_nvfp4_forward - routed MoE expert FFN with BF16 activations and NVFP4 weights
+ * ([XT] overview: NVFP4 among the MoE engine's weight formats; [LSG] launch example: an
+ * "NVFP4-W4A16" checkpoint, i.e. weight-only). Reading: E2M1 codes packed two per byte
+ * like the INT4 codes, one E4M3 scale per weight row and 16 consecutive k, and one fp32
+ * scale per expert and projection.
+ *
+ *   w13, s13, g13  [E, 2I, H/2] uint8, [E, 2I, H/16] uint8 (E4M3FN), [E] fp32 (4-byte
+ *                  alignment suffices): weight(n, c) = e2m1(code) * e4m3(s13[n, c/16]) *
+ *                  g13[e].
+ *   w2, s2, g2     [E, H, I/2], [E, H, I/16], [E]: down projection, same format.
+ *   x, topk_ids, topk_weights, T, H, I, E, k, schedule, out, workspace: as
+ *   moe_w4a16_forward.
+ * The GPU forms each weight as bf16(e2m1 * (e4m3 * g)) (one rounding, as the INT4 prefill
+ * path rounds (q - 8) * s), accumulating in fp32. Requires H % 32 == 0 and I % 32 == 0.
+ */
+qmoe_status moe_nvfp4_forward(const uint16_t* x, const uint8_t* w13, const uint8_t* s13,
+                              const float* g13, const uint8_t* w2, const uint8_t* s2,
+                              const float* g2, const int32_t* topk_ids,
+                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
+                              void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * moe_fp8_block_forward - routed MoE expert FFN, W8A8 block FP8 ([SGL] background:
  * E4M3 weights with one fp32 scale per [128, 128] block, activations E4M3 with one fp32
  * scale per token and 128-column group; block scale = absmax / 448).
@@ -286,7 +311,7 @@ qmoe_status qmoe_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t 
 
 /*
  * qmoe_plan - the schedule and align block size a forward would use.
- *   format      0 = W4A16, 1 = W8A8 block FP8, 2 = MXFP4 (weight-only).
+ *   format      0 = W4A16, 1 = W8A8 block FP8, 2 = MXFP4, 3 = NVFP4 (weight-only).
  *   schedule    requested qmoe_schedule (AUTO resolves here).
  *   chosen      out: QMOE_SCHEDULE_DECODE or QMOE_SCHEDULE_PREFILL.
  *   block_m     out: align block size of that schedule: 16, or 32 when the 4-bit

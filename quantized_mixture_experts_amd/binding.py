@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libqmoe.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qmoe.h")
 
 SCHEDULE_AUTO, SCHEDULE_DECODE, SCHEDULE_PREFILL = 0, 1, 2
-FORMAT_W4A16, FORMAT_FP8, FORMAT_MXFP4 = 0, 1, 2
+FORMAT_W4A16, FORMAT_FP8, FORMAT_MXFP4, FORMAT_NVFP4 = 0, 1, 2, 3
 STATUS = {0: "QMOE_OK", 1: "QMOE_ERR_INVALID_ARG", 2: "QMOE_ERR_UNSUPPORTED",
           3: "QMOE_ERR_WORKSPACE", 4: "QMOE_ERR_HIP"}
 
@@ -55,6 +55,8 @@ def load():
     lib.moe_w4a16_forward.restype = _I32
     lib.moe_mxfp4_forward.argtypes = [_P] * 7 + [_I32] * 6 + [_P, _P, _SZP, _P]
     lib.moe_mxfp4_forward.restype = _I32
+    lib.moe_nvfp4_forward.argtypes = [_P] * 9 + [_I32] * 6 + [_P, _P, _SZP, _P]
+    lib.moe_nvfp4_forward.restype = _I32
     for name in ("moe_w4a16_grouped_contiguous", "moe_w4a16_grouped_masked"):
         fn = getattr(lib, name)
         fn.argtypes = [_P] * 6 + [_I32] * 6 + [_P, _P, _SZP, _P]
@@ -196,6 +198,34 @@ def moe_mxfp4_forward(x, w13, s13, w2, s2, topk_ids, topk_weights, schedule=SCHE
     return _four_bit_forward("moe_mxfp4_forward", FORMAT_MXFP4, _U8 + (torch.float8_e8m0fnu,),
                              x, w13, s13, w2, s2, topk_ids, topk_weights, schedule, out,
                              workspace, stream)
+
+def moe_nvfp4_forward(x, w13, s13, g13, w2, s2, g2, topk_ids, topk_weights,
+                      schedule=SCHEDULE_AUTO, out=None, workspace=None, stream=None):
+    """NVFP4 weights: E2M1 codes packed two per byte, E4M3 scales uint8 [.., K/16], fp32
+    scales per expert g13 [E] and g2 [E]."""
+    T, H = x.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    k = topk_ids.shape[1]
+    s8 = _U8 + (torch.float8_e4m3fn,)
+    args = [_dev(x, "x", _BF16, (T, H)),
+            _dev(w13, "w13", _U8, (E, 2 * I, H // 2)), _dev(s13, "s13", s8, (E, 2 * I, H // 16)),
+            _dev(g13, "g13", (torch.float32,), (E,)),
+            _dev(w2, "w2", _U8, (E, H, I // 2)), _dev(s2, "s2", s8, (E, H, I // 16)),
+            _dev(g2, "g2", (torch.float32,), (E,)),
+            _dev(topk_ids, "topk_ids", (torch.int32,), (T, k)),
+            _dev(topk_weights, "topk_weights", (torch.float32,), (T, k))]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    optr = _dev(out, "out", _BF16, (T, H))
+    workspace = _workspace(FORMAT_NVFP4, T, H, I, E, k, schedule, workspace, x.device)
+    wptr = _dev(workspace, "workspace", (torch.uint8,))
+    size = ctypes.c_size_t(workspace.numel())
+    _check("moe_nvfp4_forward",
+           load().moe_nvfp4_forward(*args, T, H, I, E, k, schedule, optr, wptr, ctypes.byref(size),
+                                    _stream_ptr(stream)))
+    return out
+
 
 def _grouped(name, a2, w13, s13, w2, s2, route, M, rows, expected_m, schedule, out, workspace,
              stream):

@@ -34,9 +34,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 constexpr size_t kRegionAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-enum Format { kW4A16 = 0, kFp8 = 1, kMxfp4 = 2 };
+enum Format { kW4A16 = 0, kFp8 = 1, kMxfp4 = 2, kNvfp4 = 3 };
 // The 4-bit formats share the W4A16 kernels, workspace and limits.
-bool four_bit(int fmt) { return fmt == kW4A16 || fmt == kMxfp4; }
+bool four_bit(int fmt) { return fmt == kW4A16 || fmt == kMxfp4 || fmt == kNvfp4; }
 
 // Rows per weight pass of the FP8 decode kernels, in 16-row blocks: four, measured on
 // MI355X at hidden 7168, intermediate 2048, 32 experts (one / two / four blocks: 0.30 /
@@ -78,8 +78,10 @@ qmoe_status check_shape(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int
   const int q = four_bit(fmt) ? 32 : 128;
   if (H % q || I % q)
     return fail(QMOE_ERR_UNSUPPORTED, "%s needs H and I multiples of %d (H=%d I=%d)",
-                fmt == kW4A16 ? "W4A16 group-32" : fmt == kMxfp4 ? "MXFP4 block-32"
-                                                                 : "block FP8 [128,128]",
+                fmt == kW4A16   ? "W4A16 group-32"
+                : fmt == kMxfp4 ? "MXFP4 block-32"
+                : fmt == kNvfp4 ? "NVFP4 (32-column packing)"
+                                : "block FP8 [128,128]",
                 q, H, I);
   const int64_t P = (int64_t)T * k;
   const int64_t L = P + (int64_t)E * (2 * kSegRows - 1);  // the largest align block
@@ -104,7 +106,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   // for W4A16 (40: 0.69 vs 0.71 ms; 48: 0.72 vs 0.71 ms), about 60 for MXFP4 (56: 0.61
   // vs 0.64 ms; 64: 0.69 vs 0.64 ms) and about 20 for block FP8 with four blocks per
   // pass (16: 0.36 vs 0.38 ms; 24: 0.40 vs 0.39 ms).
-  const double crossover = fmt == kW4A16 ? 44.0 : fmt == kMxfp4 ? 60.0 : 20.0;
+  const double crossover = fmt == kMxfp4 ? 60.0 : fmt == kFp8 ? 20.0 : 44.0;
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= crossover ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
   p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&
@@ -209,7 +211,8 @@ T* region(void* ws, size_t off) {
 qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
                       const uint8_t* w2, const uint16_t* s2, const int32_t* topk_ids,
                       const float* topk_weights, int32_t T, int32_t H, int32_t I, int32_t E,
-                      int32_t k, uint16_t* out, void* workspace, hipStream_t s) {
+                      int32_t k, uint16_t* out, void* workspace, hipStream_t s,
+                      const float* g13 = nullptr, const float* g2 = nullptr) {
   Routing r{};
   r.sorted_ids = region<int32_t>(workspace, p.off_sorted);
   r.offsets = region<int32_t>(workspace, p.off_offsets);
@@ -221,10 +224,13 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
   r.k = k;
   r.E = E;
   r.L = (int32_t)p.L;
-  const bool mx = p.fmt == kMxfp4;
+  const bool mx = p.fmt == kMxfp4 || p.fmt == kNvfp4;  // FP4 codes, natural k order
   W4A16Problem prob{x, region<uint16_t>(workspace, p.off_xs), w13, s13, w2, s2,
                     region<uint16_t>(workspace, p.off_h), region<float>(workspace, p.off_out32),
                     T, H, I, mx};
+  prob.nv = p.fmt == kNvfp4;
+  prob.g13 = g13;
+  prob.g2 = g2;
 
   if (p.tiled) {
     const int32_t tm = p.tile_rows;
@@ -407,7 +413,7 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
                       int32_t schedule, int32_t* chosen, int32_t* block_m,
                       size_t* workspace_bytes) {
   g_last_error[0] = 0;
-  if (format != kW4A16 && format != kFp8 && format != kMxfp4)
+  if (format != kW4A16 && format != kFp8 && format != kMxfp4 && format != kNvfp4)
     return fail(QMOE_ERR_INVALID_ARG, "unknown format %d", format);
   qmoe_status st = check_shape(format, T, H, I, E, k, schedule);
   if (st != QMOE_OK) return st;
@@ -423,7 +429,8 @@ qmoe_status four_bit_forward(int fmt, const uint16_t* x, const uint8_t* w13, con
                              const uint8_t* w2, const void* s2, const int32_t* topk_ids,
                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
-                             void* workspace, size_t* workspace_bytes, void* stream) {
+                             void* workspace, size_t* workspace_bytes, void* stream,
+                             const float* g13 = nullptr, const float* g2 = nullptr) {
   g_last_error[0] = 0;
   qmoe_status st = check_shape(fmt, T, H, I, E, k, schedule);
   if (st != QMOE_OK) return st;
@@ -443,10 +450,12 @@ qmoe_status four_bit_forward(int fmt, const uint16_t* x, const uint8_t* w13, con
     if (!aligned(q, 16)) return fail(QMOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   if (!aligned(workspace, kRegionAlign))
     return fail(QMOE_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (fmt == kNvfp4 && (!g13 || !g2 || !aligned(g13, 4) || !aligned(g2, 4)))
+    return fail(QMOE_ERR_INVALID_ARG, "g13 and g2 must be 4-byte aligned device pointers");
 
   return w4a16_run(p, x, w13, static_cast<const uint16_t*>(s13), w2,
                    static_cast<const uint16_t*>(s2), topk_ids, topk_weights, T, H, I, E, k, out,
-                   workspace, static_cast<hipStream_t>(stream));
+                   workspace, static_cast<hipStream_t>(stream), g13, g2);
 }
 }  // namespace
 
@@ -466,6 +475,16 @@ qmoe_status moe_mxfp4_forward(const uint16_t* x, const uint8_t* w13, const uint8
                               void* workspace, size_t* workspace_bytes, void* stream) {
   return four_bit_forward(kMxfp4, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k,
                           schedule, out, workspace, workspace_bytes, stream);
+}
+
+qmoe_status moe_nvfp4_forward(const uint16_t* x, const uint8_t* w13, const uint8_t* s13,
+                              const float* g13, const uint8_t* w2, const uint8_t* s2,
+                              const float* g2, const int32_t* topk_ids,
+                              const float* topk_weights, int32_t T, int32_t H, int32_t I,
+                              int32_t E, int32_t k, int32_t schedule, uint16_t* out,
+                              void* workspace, size_t* workspace_bytes, void* stream) {
+  return four_bit_forward(kNvfp4, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k,
+                          schedule, out, workspace, workspace_bytes, stream, g13, g2);
 }
 
 qmoe_status moe_w4a16_grouped_contiguous(const uint16_t* a, const uint8_t* w13,

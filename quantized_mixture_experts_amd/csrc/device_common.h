@@ -164,6 +164,36 @@ __device__ __forceinline__ void fp4_to_bf16(uint32_t w, float scale, uint32_t (&
   b[3] = fp4_pair_sel<3>(w, scale);
 }
 
+// NVFP4: the pair `sel` of a code word (codes 2 sel, 2 sel + 1) times the fp32 block
+// scale sc (the E4M3 scale of the codes' 16-column block times the expert's global
+// scale), rounded once to a bf16 pair. The FP4 convert is exact in fp32 (scale 1.0).
+typedef float qf32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 qbf16x2 __attribute__((ext_vector_type(2)));
+template <int SEL>
+__device__ __forceinline__ uint32_t nvfp4_pair_sel(uint32_t w, float sc) {
+  const auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  const qf32x2 p = {f[0] * sc, f[1] * sc};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, qbf16x2));
+}
+__device__ __forceinline__ uint32_t nvfp4_pair(uint32_t w, float sc, int sel) {
+  switch (sel) {
+    case 0: return nvfp4_pair_sel<0>(w, sc);
+    case 1: return nvfp4_pair_sel<1>(w, sc);
+    case 2: return nvfp4_pair_sel<2>(w, sc);
+    default: return nvfp4_pair_sel<3>(w, sc);
+  }
+}
+__device__ __forceinline__ void nvfp4_to_bf16(uint32_t w, float sc, uint32_t (&b)[4]) {
+  b[0] = nvfp4_pair_sel<0>(w, sc);
+  b[1] = nvfp4_pair_sel<1>(w, sc);
+  b[2] = nvfp4_pair_sel<2>(w, sc);
+  b[3] = nvfp4_pair_sel<3>(w, sc);
+}
+// E4M3 code in the low byte of v -> fp32 (gfx950's OCP E4M3FN convert).
+__device__ __forceinline__ float e4m3_low(uint32_t v) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)v, 0);
+}
+
 // E8M0 scale code -> an fp32 whose exponent field is the code (2^(code - 127) for codes
 // 1..254), the form the FP4 converts take their scale in.
 __device__ __forceinline__ float e8m0_scale(uint32_t code) {

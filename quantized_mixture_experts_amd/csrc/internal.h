@@ -49,8 +49,9 @@ struct Routing {
   int32_t P, k, E, L;
 };
 
-// The 4-bit weight formats: INT4 codes with bf16 scales (mx = false) or MXFP4 E2M1
-// codes with E8M0 scales (mx = true, s13 / s2 then point at the scale bytes).
+// The 4-bit weight formats: INT4 codes with bf16 scales (mx = false), MXFP4 E2M1 codes
+// with E8M0 scales (mx = true, s13 / s2 then point at the scale bytes), or NVFP4 E2M1
+// codes with E4M3 scales per 16 k and fp32 scales per expert g13 / g2 (mx = nv = true).
 struct W4A16Problem {
   const uint16_t* x;  // [T, H] bf16
   uint16_t* xs;       // [L, H] bf16: x gathered by sorted row, operand k order
@@ -62,6 +63,9 @@ struct W4A16Problem {
   float* out32;   // [T, H]
   int32_t T, H, I;
   bool mx;
+  bool nv = false;
+  const float* g13 = nullptr;  // [E]
+  const float* g2 = nullptr;   // [E]
 };
 
 struct Fp8Problem {

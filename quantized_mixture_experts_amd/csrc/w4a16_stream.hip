@@ -37,7 +37,10 @@
 // v_cvt_scalef32_pk_bf16_fp4 per code pair gives the exact scaled bf16 weight (the scale
 // is a power of two), so there is no zero-point term and no scale multiply after the
 // MFMA, which accumulates in place. The FP4 converts produce natural k order, so the
-// activation rows and h use the natural-order tiled layout.
+// activation rows and h use the natural-order tiled layout. NVFP4 (NV = true; E4M3
+// scales per 16 k and an fp32 scale per expert, the same page's list) converts each code
+// pair to fp32, multiplies by the block scale times the expert's scale and rounds once
+// to bf16; each lane's 8 codes of a group lie in one 16-k half, so one scale per lane.
 #include <algorithm>
 #include <atomic>
 #include <type_traits>
@@ -72,6 +75,7 @@ struct StreamArgs {
   int32_t chunks, items;      // column chunks per expert; E * chunks
   float* zero_out;            // persistent gate_up: fp32 buffer it clears first (or null)
   int64_t zero_n;             // its length in floats, a multiple of 4
+  const float* g = nullptr;   // NVFP4: [E] fp32 scale per expert of this projection
 };
 
 struct Stage {
@@ -81,7 +85,7 @@ struct Stage {
 constexpr int kScaleBlockSteps = 8;  // one 128 B line of bf16 scales = 64 groups = 8 steps
 constexpr int kStages = 4;           // weight register stages (loads run kStages-1 ahead)
 
-template <Epi EPI, int MB, bool MX>
+template <Epi EPI, int MB, bool MX, bool NV>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(2)))
     w4a16_stream_kernel(StreamArgs a) {
@@ -129,13 +133,22 @@ __global__ void __launch_bounds__(kThreads)
   const int K = a.K, G = K / 32, KB = K / 2;
   const uint8_t* wrow[2];
   const uint16_t* srow[2];
-  const uint8_t* mrow[2];  // MXFP4: the row's E8M0 scale bytes
+  const uint8_t* mrow[2];  // FP4: the row's scale bytes (E8M0 per 32 k, E4M3 per 16 k)
+  constexpr int kScalesPerGroup = NV ? 2 : 1;
+  const float gsc = NV ? a.g[e] : 1.f;
+  const int hsel = NV ? quad >> 1 : 0;  // this lane's 16-k half of a group
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     wrow[t] = a.w + ((size_t)e * a.N + row[t]) * KB;
     srow[t] = a.s + ((size_t)e * a.N + row[t]) * G;
-    mrow[t] = reinterpret_cast<const uint8_t*>(a.s) + ((size_t)e * a.N + row[t]) * G;
+    mrow[t] = reinterpret_cast<const uint8_t*>(a.s) +
+              ((size_t)e * a.N + row[t]) * G * kScalesPerGroup;
   }
+  // FP4 scale of group gg of tile t for this lane, in the form the dequantization takes.
+  auto fp4_scale = [&](int t, int gg) {
+    if constexpr (NV) return e4m3_low(mrow[t][2 * gg + hsel]) * gsc;
+    else return e8m0_scale(mrow[t][gg]);
+  };
   const int nstep = G / 8;  // full 256-deep steps
   const int nchunk = (G + kChunkGroups - 1) / kChunkGroups;
   const uint32_t neg136[4] = {kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair};
@@ -244,9 +257,14 @@ __global__ void __launch_bounds__(kThreads)
       }
       uint32_t bw0[4], bw1[4];
       if constexpr (MX) {
-        // sc0, sc1: E8M0 scales in the converts' fp32 form
-        fp4_to_bf16(w0, sc0, bw0);
-        fp4_to_bf16(w1, sc1, bw1);
+        // sc0, sc1: the scales in the form fp4_to_bf16 / nvfp4_to_bf16 take
+        if constexpr (NV) {
+          nvfp4_to_bf16(w0, sc0, bw0);
+          nvfp4_to_bf16(w1, sc1, bw1);
+        } else {
+          fp4_to_bf16(w0, sc0, bw0);
+          fp4_to_bf16(w1, sc1, bw1);
+        }
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
           if (b < nmb) {
@@ -288,8 +306,8 @@ __global__ void __launch_bounds__(kThreads)
           const int g = 4 * half + g4;
           float sc0, sc1;
           if constexpr (MX) {
-            sc0 = e8m0_scale(mrow[0][it * 8 + g]);
-            sc1 = e8m0_scale(mrow[1][it * 8 + g]);
+            sc0 = fp4_scale(0, it * 8 + g);
+            sc1 = fp4_scale(1, it * 8 + g);
           } else {
             const uint32_t s0w = sv[0][g >> 1], s1w = sv[1][g >> 1];
             sc0 = (g & 1) ? bf16_hi(s0w) : bf16_lo(s0w);
@@ -343,7 +361,7 @@ __global__ void __launch_bounds__(kThreads)
       const uint32_t w0 = *reinterpret_cast<const uint32_t*>(wrow[0] + g * 16 + 4 * quad);
       const uint32_t w1 = *reinterpret_cast<const uint32_t*>(wrow[1] + g * 16 + 4 * quad);
       if constexpr (MX)
-        group(c & 1, g % kChunkGroups, w0, w1, e8m0_scale(mrow[0][g]), e8m0_scale(mrow[1][g]));
+        group(c & 1, g % kChunkGroups, w0, w1, fp4_scale(0, g), fp4_scale(1, g));
       else
         group(c & 1, g % kChunkGroups, w0, w1, bf16_to_f32(srow[0][g]), bf16_to_f32(srow[1][g]));
     }
@@ -429,7 +447,7 @@ __device__ __forceinline__ int32_t ld_invariant(const int32_t* p, int i) {
 // MB: 16-row MFMA blocks per row block (align pads every expert's segment to 16 MB
 // rows, so a row block never spans two experts). Each dequantized weight operand feeds
 // the MFMAs of all MB blocks, so a pass over the weights serves 16 MB rows.
-template <Epi EPI, bool MX, int MB>
+template <Epi EPI, bool MX, bool NV, int MB>
 __global__ void __launch_bounds__(kPThreads)
     __attribute__((amdgpu_waves_per_eu(kPWavesPerEu)))
     w4a16_persist_kernel(StreamArgs a) {
@@ -545,7 +563,7 @@ __global__ void __launch_bounds__(kPThreads)
   u32x4 snext[4];
   const int s_row = lane >> 3, s_piece = lane & 7;
   auto scale_block_load = [&](const Unit& d) {
-    if constexpr (MX) {
+    if constexpr (MX && !NV) {
       const int off = min((d.kc & ~(kScaleUnits - 1)) * 16 + s_piece * 8, G - 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -567,7 +585,10 @@ __global__ void __launch_bounds__(kPThreads)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 v = snext[i];
-      if constexpr (MX) {
+      if constexpr (NV) {
+        // the step's 16 E4M3 bytes of this row (two per group), kept raw
+        s_lds[wave][i >> 1][s_piece][8 * (i & 1) + s_row] = __builtin_bit_cast(f32x4, v);
+      } else if constexpr (MX) {
         s_lds[wave][i >> 1][s_piece][8 * (i & 1) + s_row] =
             f32x4{e8m0_scale(v[0]), e8m0_scale(v[0] >> 8), e8m0_scale(v[0] >> 16),
                   e8m0_scale(v[0] >> 24)};
@@ -626,7 +647,8 @@ __global__ void __launch_bounds__(kPThreads)
   // One 256-deep step: groups 8p..8p+7 of the unit's chunk, scale piece p, in batches of
   // kPBatch groups whose LDS reads and MFMAs are issued together, so neither the LDS
   // latency nor the MFMA latency is paid once per group.
-  auto compute = [&](Stage& s, int buf, int p, int sp) {
+  const int hsel = NV ? quad >> 1 : 0;  // this lane's 16-k half of a group (NVFP4)
+  auto compute = [&](Stage& s, int buf, int p, int sp, float gs) {
     f32x4 sv[2][2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -655,7 +677,15 @@ __global__ void __launch_bounds__(kPThreads)
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             uint32_t bw[4];
-            fp4_to_bf16(wt[t][gb], sv[t][half][gb], bw);
+            if constexpr (NV) {
+              // byte 2 g + hsel of the step's raw scales (entry 0 holds them)
+              const int g = 4 * half + gb;
+              const u32x4 raw = __builtin_bit_cast(u32x4, sv[t][0]);
+              nvfp4_to_bf16(wt[t][gb], e4m3_low(raw[g >> 1] >> (16 * (g & 1) + 8 * hsel)) * gs,
+                            bw);
+            } else {
+              fp4_to_bf16(wt[t][gb], sv[t][half][gb], bw);
+            }
 #pragma unroll
             for (int b = 0; b < MB; ++b) acc[t][b] = mfma_bf16_16x16x32(a4[b], bw, acc[t][b]);
           }
@@ -785,10 +815,14 @@ __global__ void __launch_bounds__(kPThreads)
       scale_block_load(desc(next_block(u, kc)));
     }
     const int sp = 2 * (kc & (kScaleUnits - 1));
+    // NVFP4: the expert's global scale (a scalar load; 1 otherwise)
+    const float gs =
+        NV ? __builtin_bit_cast(float, ld_invariant(reinterpret_cast<const int32_t*>(a.g), dq[0].e))
+           : 1.f;
     load(st[(2 * U + a0) % kRing], dq[a0 / 2], a0 & 1);
-    if (live) compute(st[(2 * U) % kRing], P, 0, sp);
+    if (live) compute(st[(2 * U) % kRing], P, 0, sp, gs);
     load(st[(2 * U + 1 + a0) % kRing], dq[a1 / 2], a1 & 1);
-    if (live) compute(st[(2 * U + 1) % kRing], P, 1, sp + 1);
+    if (live) compute(st[(2 * U + 1) % kRing], P, 1, sp + 1, gs);
     if (live && (dq[0].kc == upi - 1 || u == ulast)) epilogue(dq[0]);
     chunk_store(P ^ 1);
     chunk_load(dq[2]);
@@ -872,7 +906,7 @@ int persistent_grid() {
   return n;
 }
 
-template <Epi EPI, bool MX>
+template <Epi EPI, bool MX, bool NV>
 hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream) {
   const bool persist = a.K % 512 == 0;
   const int waves = persist ? kPWaves : kWavesPerGroup;
@@ -884,13 +918,13 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
   // The persistent kernel serves mb 16-row blocks per weight pass (align made segments
   // of 16 mb rows); the general kernel one 16-row block at a time of any segments.
   if (persist && mb == 2) {
-    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, 2>),
+    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, NV, 2>),
                        dim3(persistent_grid() * kPGroupsPerCu), dim3(kPThreads), 0, stream, args);
   } else if (persist) {
-    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, 1>),
+    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, NV, 1>),
                        dim3(persistent_grid() * kPGroupsPerCu), dim3(kPThreads), 0, stream, args);
   } else {
-    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1, MX>), dim3(xcd_major_grid(args.items)),
+    hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1, MX, NV>), dim3(xcd_major_grid(args.items)),
                        dim3(kThreads), 0, stream, args);
   }
   return hipGetLastError();
@@ -922,8 +956,10 @@ hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, i
                p.h, nullptr,
                r.P, r.k, p.H, 2 * p.I, p.I, 0, 0,
                zero ? p.out32 : nullptr, zero ? (int64_t)p.T * p.H : 0};
-  return p.mx ? launch_stream<Epi::GateUp, true>(a, r.E, mb, stream)
-              : launch_stream<Epi::GateUp, false>(a, r.E, mb, stream);
+  a.g = p.g13;
+  return p.nv   ? launch_stream<Epi::GateUp, true, true>(a, r.E, mb, stream)
+         : p.mx ? launch_stream<Epi::GateUp, true, false>(a, r.E, mb, stream)
+                : launch_stream<Epi::GateUp, false, false>(a, r.E, mb, stream);
 }
 
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
@@ -931,8 +967,10 @@ hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int
   StreamArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.expert_ids, r.ntp, r.topk_weights,
                nullptr, p.out32,
                r.P, r.k, p.I, p.H, p.I, 0, 0, nullptr, 0};
-  return p.mx ? launch_stream<Epi::Down, true>(a, r.E, mb, stream)
-              : launch_stream<Epi::Down, false>(a, r.E, mb, stream);
+  a.g = p.g2;
+  return p.nv   ? launch_stream<Epi::Down, true, true>(a, r.E, mb, stream)
+         : p.mx ? launch_stream<Epi::Down, true, false>(a, r.E, mb, stream)
+                : launch_stream<Epi::Down, false, false>(a, r.E, mb, stream);
 }
 
 }  // namespace qmoe

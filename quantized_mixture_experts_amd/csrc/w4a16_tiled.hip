@@ -35,7 +35,10 @@
 // format of the "xiaotu-moe" project page, overview): an operand word is one
 // v_cvt_scalef32_pk_bf16_fp4 of the code word with the group's power-of-two scale,
 // exact, in natural k order (the activation rows and h use the natural-order tiled
-// layout); the scales are copied one byte per group.
+// layout); the scales are copied one byte per group. NVFP4 (NV = true): E4M3 scales per
+// 16 k (two bytes per group, copied like the INT4 scales) times an fp32 scale per expert;
+// an operand word is the pair converted to fp32, multiplied by that scale and rounded
+// once to bf16.
 #include <algorithm>
 #include <type_traits>
 
@@ -90,6 +93,7 @@ struct TiledArgs {
   int32_t P, E, K, N, I;
   int32_t col_tiles;            // output column tiles per row tile
   uint32_t act_bytes;           // size of act (L * K * 2 < 2^32, host-checked)
+  const float* g = nullptr;     // NVFP4: [E] fp32 scale per expert of this projection
 };
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -136,7 +140,7 @@ __device__ __forceinline__ void drain_acc(f32x4 (&acc)[RB][kColTiles]) {
     for (int t = 0; t < kColTiles; ++t) asm volatile("" : "+a"(acc[m][t]));
 }
 
-template <TEpi EPI, bool MX, int TR>
+template <TEpi EPI, bool MX, bool NV, int TR>
 __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   constexpr int kTileRows = TR;
   constexpr int kRowBlocks = Tile<TR>::kRowBlocks;
@@ -192,7 +196,9 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // Scales: lane l takes word l % 4 of the 16 B (eight groups) of row l / 4. MXFP4
   // scales are one byte per group: the block's eight are words 0 and 1 of the 16 B
   // window (words 2 and 3 hold the next block's, or zeros past the buffer, unused).
-  constexpr uint32_t kScaleBytes = MX ? 1u : 2u;
+  constexpr uint32_t kScaleBytes = (MX && !NV) ? 1u : 2u;
+  const float gsc = NV ? a.g[e] : 1.f;    // NVFP4: the expert's global scale
+  const int hsh = NV ? 8 * (quad >> 1) : 0;  // NVFP4: byte of this lane's 16-k half
   const uint8_t* wbase = a.w + (size_t)e * a.N * (size_t)(K >> 1);
   const uint8_t* sbase =
       reinterpret_cast<const uint8_t*>(a.s) + (size_t)e * a.N * (size_t)KG * kScaleBytes;
@@ -352,7 +358,10 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
 #pragma unroll
   for (int p = 0; p < kPieces; ++p) {
     const int t = p >> 2, i = p & 3;
-    if constexpr (MX) {
+    if constexpr (NV) {
+      bq[0][t][i] = nvfp4_pair(tw[t][0], e4m3_low(scur[t][0] >> hsh) * gsc, i);
+      continue;
+    } else if constexpr (MX) {
       bq[0][t][i] = fp4_pair(tw[t][0], e8m0_scale(scur[t][0]), i);
       continue;
     }
@@ -429,7 +438,10 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
           for (int rr = 0; rr < 4; ++rr) ra[(q + 1) & 1][rr] = as[(4 * (q + 1) + rr) * kWave];
         }
         uint32_t shv = 0;
-        if constexpr (MX) {
+        if constexpr (NV) {
+          // The lane's scale for group jn (byte 2 jn + its half), at the tile's first piece.
+          if (!odd && i == 0) sc = e4m3_low(scur[t][jn >> 1] >> (16 * (jn & 1) + hsh)) * gsc;
+        } else if constexpr (MX) {
           // The tile's scale for group jn (byte jn of the block), at its first piece.
           if (!odd && i == 0) sc = e8m0_scale(scur[t][jn >> 2] >> (8 * (jn & 3)));
         } else if (!kTwoPerPiece) {
@@ -453,7 +465,9 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
         mfma_acc(acc[m][1], a0, bc[1]);
         __builtin_amdgcn_sched_barrier(0);
         copy_slot(1);
-        if constexpr (MX) {
+        if constexpr (NV) {
+          if (odd || !kTwoPerPiece) bn[t][i] = nvfp4_pair(tw[t][jn & 3], sc, i);
+        } else if constexpr (MX) {
           if (odd || !kTwoPerPiece) bn[t][i] = fp4_pair(tw[t][jn & 3], sc, i);
         } else if (!kTwoPerPiece) {
           const f16x2 hv = __builtin_bit_cast(f16x2, pr);
@@ -621,26 +635,30 @@ __global__ void __launch_bounds__(kCombineThreads)
 }
 
 template <TEpi EPI, int TR>
-void launch_tiled_rows(const TiledArgs& a, int64_t items, bool mx, hipStream_t stream) {
-  if (mx)
-    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, true, TR>), dim3(xcd_major_grid((int)items)),
-                       dim3(kThreads), 0, stream, a);
+void launch_tiled_rows(const TiledArgs& a, int64_t items, bool mx, bool nv, hipStream_t stream) {
+  const dim3 grid(xcd_major_grid((int)items));
+  if (nv)
+    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, true, true, TR>), grid, dim3(kThreads), 0, stream,
+                       a);
+  else if (mx)
+    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, true, false, TR>), grid, dim3(kThreads), 0, stream,
+                       a);
   else
-    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, false, TR>), dim3(xcd_major_grid((int)items)),
-                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, false, false, TR>), grid, dim3(kThreads), 0,
+                       stream, a);
 }
 
 template <TEpi EPI>
-hipError_t launch_tiled(const TiledArgs& a, int64_t P, int E, int tile_rows, bool mx,
+hipError_t launch_tiled(const TiledArgs& a, int64_t P, int E, int tile_rows, bool mx, bool nv,
                         hipStream_t stream) {
   if (tile_rows != 128 && tile_rows != 256) return hipErrorInvalidValue;
   const int64_t items = (P / tile_rows + E) * a.col_tiles;  // at most this many row tiles
   if (items <= 0) return hipSuccess;
   if (items > (int64_t(1) << 30)) return hipErrorInvalidValue;
   if (tile_rows == 128)
-    launch_tiled_rows<EPI, 128>(a, items, mx, stream);
+    launch_tiled_rows<EPI, 128>(a, items, mx, nv, stream);
   else
-    launch_tiled_rows<EPI, 256>(a, items, mx, stream);
+    launch_tiled_rows<EPI, 256>(a, items, mx, nv, stream);
   return hipGetLastError();
 }
 
@@ -659,7 +677,8 @@ hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, in
   TiledArgs a{p.xs, p.w13, p.s13, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
               p.h, nullptr, r.P, r.E, p.H, 2 * p.I, p.I, p.I / 128,
               (uint32_t)((uint64_t)r.L * p.H * 2u)};
-  return launch_tiled<TEpi::GateUp>(a, r.P, r.E, tile_rows, p.mx, stream);
+  a.g = p.g13;
+  return launch_tiled<TEpi::GateUp>(a, r.P, r.E, tile_rows, p.mx, p.nv, stream);
 }
 
 hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
@@ -667,7 +686,8 @@ hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int 
   TiledArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
               nullptr, y, r.P, r.E, p.I, p.H, p.I, p.H / 256,
               (uint32_t)((uint64_t)r.L * p.I * 2u)};
-  return launch_tiled<TEpi::Down>(a, r.P, r.E, tile_rows, p.mx, stream);
+  a.g = p.g2;
+  return launch_tiled<TEpi::Down>(a, r.P, r.E, tile_rows, p.mx, p.nv, stream);
 }
 
 hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,

@@ -18,7 +18,7 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = binding.declared_functions()
     assert {"moe_topk_softmax", "moe_align", "moe_w4a16_forward", "moe_fp8_block_forward",
-            "moe_w4a16_grouped_contiguous", "moe_w4a16_grouped_masked", "moe_mxfp4_forward",
+            "moe_w4a16_grouped_contiguous", "moe_w4a16_grouped_masked", "moe_mxfp4_forward", "moe_nvfp4_forward",
             "qmoe_plan", "qmoe_fp8_quantize_blocks", "qmoe_fp8_quantize_blocks_bf16",
             "qmoe_status_string", "qmoe_last_error", "qmoe_abi_version"} <= set(names)
     for n in names:
@@ -158,6 +158,23 @@ def test_mxfp4_checks_arguments_like_w4a16(lib):
     small = ctypes.c_size_t(need - 1)
     assert f(*([FAKE] * 7), 32, 7168, 2048, 48, 8, 0, FAKE, FAKE, ctypes.byref(small), None) == WORKSPACE
     assert binding.plan(binding.FORMAT_MXFP4, 8192, 7168, 2048, 48, 8)[0] == binding.SCHEDULE_PREFILL
+
+
+def test_nvfp4_checks_arguments(lib):
+    f = lib.moe_nvfp4_forward
+    sz = ctypes.c_size_t(0)
+    assert f(*([FAKE] * 9), 32, 7168, 2048, 48, 8, 0, FAKE, None, ctypes.byref(sz), None) == OK
+    assert sz.value == _w4(lib, ws=None)[1]
+    big = ctypes.c_size_t(sz.value)
+    # a missing per-expert global scale (g13 or g2) is rejected
+    for i in (3, 6):
+        p = [FAKE] * 9
+        p[i] = None
+        assert f(*p, 32, 7168, 2048, 48, 8, 0, FAKE, FAKE, ctypes.byref(big), None) == INVALID
+    # K must hold whole 32-column groups (the E4M3 scales come in pairs)
+    assert f(*([FAKE] * 9), 32, 7168 + 16, 2048, 48, 8, 0, FAKE, FAKE, ctypes.byref(big), None) == UNSUPPORTED
+    small = ctypes.c_size_t(sz.value - 1)
+    assert f(*([FAKE] * 9), 32, 7168, 2048, 48, 8, 0, FAKE, FAKE, ctypes.byref(small), None) == WORKSPACE
 
 
 def test_binding_functions_reference_only_defined_names():
