@@ -61,8 +61,8 @@ typedef enum qmoe_status {
 
 /* Schedules of the forward passes. AUTO picks from routed tokens per expert,
  * tok_e = T*k/E (a host-side quantity; no device readback): the bandwidth-bound
- * decode profile up to the crossover (measured: 44 for W4A16, 60 for MXFP4, 20 for
- * block FP8), the MFMA-bound prefill profile above it
+ * decode profile up to the crossover (measured: 44 for W4A16, 60 for MXFP4, 36 for
+ * NVFP4, 20 for block FP8), the MFMA-bound prefill profile above it
  * ([CHORD] "Kernel optimizations": the per-expert routed token count, not the total,
  * decides which schedule wins; profiles tune on token counts). DECODE and PREFILL
  * force one profile; both give results within the same tolerance. */

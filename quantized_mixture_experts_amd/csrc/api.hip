@@ -106,7 +106,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   // for W4A16 (40: 0.69 vs 0.71 ms; 48: 0.72 vs 0.71 ms), about 60 for MXFP4 (56: 0.61
   // vs 0.64 ms; 64: 0.69 vs 0.64 ms) and about 20 for block FP8 with four blocks per
   // pass (16: 0.36 vs 0.38 ms; 24: 0.40 vs 0.39 ms).
-  const double crossover = fmt == kMxfp4 ? 60.0 : fmt == kFp8 ? 20.0 : 44.0;
+  const double crossover = fmt == kMxfp4 ? 60.0 : fmt == kFp8 ? 20.0 : fmt == kNvfp4 ? 36.0 : 44.0;
   if (schedule == QMOE_SCHEDULE_AUTO)
     p.schedule = tok_e <= crossover ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
   p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&

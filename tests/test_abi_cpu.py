@@ -175,6 +175,10 @@ def test_nvfp4_checks_arguments(lib):
     assert f(*([FAKE] * 9), 32, 7168 + 16, 2048, 48, 8, 0, FAKE, FAKE, ctypes.byref(big), None) == UNSUPPORTED
     small = ctypes.c_size_t(sz.value - 1)
     assert f(*([FAKE] * 9), 32, 7168, 2048, 48, 8, 0, FAKE, FAKE, ctypes.byref(small), None) == WORKSPACE
+    # NVFP4's measured crossover (36 rows per expert) sits below INT4's (44)
+    assert binding.plan(binding.FORMAT_NVFP4, 240, 7168, 2048, 48, 8)[0] == binding.SCHEDULE_PREFILL
+    assert binding.plan(binding.FORMAT_W4A16, 240, 7168, 2048, 48, 8)[0] == binding.SCHEDULE_DECODE
+    assert binding.plan(binding.FORMAT_NVFP4, 192, 7168, 2048, 48, 8)[0] == binding.SCHEDULE_DECODE
 
 
 def test_binding_functions_reference_only_defined_names():

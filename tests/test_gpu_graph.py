@@ -126,6 +126,33 @@ def test_mxfp4_graph_replays(schedule, shape):
     _check_replays(run, out, other, exact=schedule == binding.SCHEDULE_PREFILL)
 
 
+def _nvfp4_runner(case, schedule):
+    d = to_dev(case)
+    T, H = case["x"].shape
+    E, twoI, _ = case["w13"].shape
+    k = case["topk_ids"].shape[1]
+    _, _, ws = binding.plan(binding.FORMAT_NVFP4, T, H, twoI // 2, E, k, schedule)
+    work = torch.empty(ws, dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        binding.moe_nvfp4_forward(d["x"], d["w13"], d["s13"], d["g13"], d["w2"], d["s2"], d["g2"],
+                                  d["topk_ids"], d["topk_weights"], schedule=schedule, out=out,
+                                  workspace=work)
+    return run, out
+
+
+@pytest.mark.parametrize("schedule,shape", [
+    (binding.SCHEDULE_DECODE, (96, 1024, 512, 6, 2)),   # 32 rows per expert: two-block passes
+    (binding.SCHEDULE_PREFILL, (300, 512, 256, 8, 2)),  # 75 rows per expert: 128-row tiles
+])
+def test_nvfp4_graph_replays(schedule, shape):
+    print(f"[graph] nvfp4 schedule={schedule} shape={shape}", flush=True)
+    run, out = _nvfp4_runner(inputs.custom_nvfp4_case(*shape, seed=38), schedule)
+    other, _ = _nvfp4_runner(inputs.custom_nvfp4_case(*shape, seed=39), schedule)
+    _check_replays(run, out, other, exact=schedule == binding.SCHEDULE_PREFILL)
+
+
 def test_grouped_masked_graph_follows_device_counts():
     # masked_m is read on the device at replay time: rewriting it between replays (an
     # expert-parallel dispatch would) changes which rows the captured forward computes.
