@@ -316,7 +316,7 @@ qmoe_status qmoe_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t 
  *   chosen      out: QMOE_SCHEDULE_DECODE or QMOE_SCHEDULE_PREFILL.
  *   block_m     out: align block size of that schedule: 16, or 32 when the 4-bit
  *               decode kernel serves two 16-row blocks per weight pass (more than 15
- *               routed rows per expert for W4A16, 11 for MXFP4).
+ *               routed rows per expert for W4A16, 11 for MXFP4 and NVFP4).
  *   workspace_bytes out (may be NULL): workspace the forward needs.
  * Pure host computation; touches no GPU.
  */

@@ -50,7 +50,7 @@ int decode_mb_for(double) { return 4; }
 // rows 0.427 vs 0.370 ms; MXFP4 at 10 rows 0.297 vs 0.287 ms, at 8 rows 0.253 vs
 // 0.281 ms). Below these, most experts fit one block and a second one costs MFMA and
 // activation work for nothing.
-double two_block_rows(int fmt) { return fmt == kMxfp4 ? 11.0 : 15.0; }
+double two_block_rows(int fmt) { return fmt == kMxfp4 || fmt == kNvfp4 ? 11.0 : 15.0; }
 
 struct Plan {
   int fmt = 0;
