@@ -40,6 +40,14 @@ def _load():
     lib.oracle_nvfp4_moe.restype = ctypes.c_int
     lib.oracle_fp8_moe.argtypes = [_P] * 8 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
     lib.oracle_fp8_moe.restype = ctypes.c_int
+    for fn in ("oracle_w4a16_moe_experts", "oracle_mxfp4_moe_experts"):
+        getattr(lib, fn).argtypes = [_P] * 7 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.oracle_nvfp4_moe_experts.argtypes = [_P] * 9 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
+    lib.oracle_nvfp4_moe_experts.restype = ctypes.c_int
+    lib.oracle_fp8_moe_experts.argtypes = ([_P] * 8 + [_I64] * 5 + [_P, _I64, _P, ctypes.c_int]
+                                           + [_P] * 7)
+    lib.oracle_fp8_moe_experts.restype = ctypes.c_int
     lib.oracle_fp8_quantize_blocks.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P]
     lib.oracle_fp8_quantize_blocks.restype = ctypes.c_int
     lib.oracle_f64_to_bf16_array.argtypes = [_P, _I64, _P]
@@ -63,7 +71,16 @@ def _c(a, dtype):
 
 
 def default_threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+    """Every CPU this process may run on (its affinity mask), capped by OMP_NUM_THREADS
+    when that is set (the host's share for one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
 
 def align_capacity(P: int, E: int, B: int):
@@ -226,6 +243,86 @@ def fp8_moe(a_q, a_s, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthre
     if rc != 0:
         raise ValueError("oracle_fp8_moe: bad arguments")
     return out
+
+
+def _rows(rows, T):
+    if rows is None:
+        return None, T, None
+    rows_arr = _c(np.asarray(rows, dtype=np.int64), np.int64)
+    return rows_arr, rows_arr.size, _ptr(rows_arr)
+
+
+def w4a16_moe_experts(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=None):
+    """oracle_w4a16_moe's result, computed expert by expert (each weight row dequantized
+    once for all the expert's routed pairs; every sum in the same order, so the result is
+    bit-identical). For checking full-size workloads."""
+    return _w4_moe("oracle_w4a16_moe_experts", np.uint16, x, w13, s13, w2, s2, topk_ids,
+                   topk_weights, rows, nthreads)
+
+
+def mxfp4_moe_experts(x, w13, s13, w2, s2, topk_ids, topk_weights, rows=None, nthreads=None):
+    """mxfp4_moe's result, computed expert by expert (bit-identical)."""
+    return _w4_moe("oracle_mxfp4_moe_experts", np.uint8, x, w13, s13, w2, s2, topk_ids,
+                   topk_weights, rows, nthreads)
+
+
+def nvfp4_moe_experts(x, w13, s13, g13, w2, s2, g2, topk_ids, topk_weights, rows=None,
+                      nthreads=None):
+    """nvfp4_moe's result, computed expert by expert (bit-identical)."""
+    x = _c(x, np.uint16)
+    w13, s13, w2, s2 = (_c(a, np.uint8) for a in (w13, s13, w2, s2))
+    g13, g2 = _c(g13, np.float32), _c(g2, np.float32)
+    ids = _c(topk_ids, np.int32)
+    wts = _c(topk_weights, np.float32)
+    T, H = x.shape
+    E, twoI, _ = w13.shape
+    k = ids.shape[1]
+    _, nrows, rp = _rows(rows, T)
+    out = np.zeros((nrows, H), np.float64)
+    rc = _load().oracle_nvfp4_moe_experts(_ptr(x), _ptr(w13), _ptr(s13), _ptr(g13), _ptr(w2),
+                                          _ptr(s2), _ptr(g2), _ptr(ids), _ptr(wts), T, H,
+                                          twoI // 2, E, k, rp, nrows, _ptr(out),
+                                          nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_nvfp4_moe_experts: bad arguments")
+    return out
+
+
+def fp8_moe_experts(a_q, a_s, w13, s13, w2, s2, topk_ids, topk_weights, rows=None,
+                    nthreads=None, detail=False):
+    """fp8_moe's result, computed expert by expert (bit-identical). With detail=True also
+    returns a dict of per-pair arrays indexed [r * k + s] for the listed rows (r = position
+    in `rows`; dropped slots are left zero): g, u (fp64 gate and up sums), gmag, umag
+    (sum over c of |x_c W13(j, c)|, the magnitudes an accumulation error scales with), h32
+    (fp32 SiLU(g) * u before quantization), hq (its E4M3 codes), hs (fp32 scale per 128)."""
+    a_q = _c(a_q, np.uint8)
+    a_s = _c(a_s, np.float32)
+    w13 = _c(w13, np.uint8)
+    s13 = _c(s13, np.float32)
+    w2 = _c(w2, np.uint8)
+    s2 = _c(s2, np.float32)
+    ids = _c(topk_ids, np.int32)
+    wts = _c(topk_weights, np.float32)
+    T, H = a_q.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    k = ids.shape[1]
+    _, nrows, rp = _rows(rows, T)
+    out = np.zeros((nrows, H), np.float64)
+    d = None
+    dp = [None] * 7
+    if detail:
+        n = nrows * k
+        d = dict(g=np.zeros((n, I)), u=np.zeros((n, I)), gmag=np.zeros((n, I)),
+                 umag=np.zeros((n, I)), h32=np.zeros((n, I), np.float32),
+                 hq=np.zeros((n, I), np.uint8), hs=np.zeros((n, I // 128), np.float32))
+        dp = [_ptr(d[key]) for key in ("g", "u", "gmag", "umag", "h32", "hq", "hs")]
+    rc = _load().oracle_fp8_moe_experts(_ptr(a_q), _ptr(a_s), _ptr(w13), _ptr(s13), _ptr(w2),
+                                        _ptr(s2), _ptr(ids), _ptr(wts), T, H, I, E, k, rp, nrows,
+                                        _ptr(out), nthreads or default_threads(), *dp)
+    if rc != 0:
+        raise ValueError("oracle_fp8_moe_experts: bad arguments")
+    return (out, d) if detail else out
 
 
 def fp8_quantize_blocks(v, br: int, bc: int):

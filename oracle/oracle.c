@@ -534,3 +534,350 @@ void oracle_e8m0_to_f64_array(const uint8_t* c, int64_t n, double* out) {
 void oracle_f32_to_e4m3_array(const float* x, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_e4m3(x[i]);
 }
+
+/* ------------------------------------------------------------------------- */
+/* Expert-major evaluation: the same arithmetic in another loop order        */
+/* ------------------------------------------------------------------------- */
+
+/* The functions above walk token by token and dequantize every weight again for each
+ * routed pair. The functions below compute exactly the same numbers expert by expert:
+ * the routed pairs of the listed rows are grouped by expert, each weight row is
+ * dequantized once into a buffer, and every pair's dot product with it is summed
+ * sequentially over the column index, as in the per-token functions. Several pairs'
+ * sums run side by side (they are independent); no sum is split or reordered. Each
+ * pair's down output y is kept, and a token row's output is then summed over its slots in
+ * slot order. Products are formed with the same expressions, so the results are
+ * bit-identical to oracle_w4a16_moe / _mxfp4_ / _nvfp4_ / oracle_fp8_moe (pinned in
+ * tests/test_oracle_experts.py); they exist so that full-size workloads can be checked. */
+
+#define PB 8 /* pairs whose sums run side by side */
+
+typedef struct {
+  int64_t npairs;  /* routed pairs of the listed rows */
+  int64_t* start;  /* [E + 1]: expert e owns pair slots [start[e], start[e+1]) */
+  int64_t* pair;   /* [npairs]: r * k + s, r = position in the row list */
+} pair_lists;
+
+static void free_pair_lists(pair_lists* pl) {
+  free(pl->start);
+  free(pl->pair);
+}
+
+/* Groups the valid (row, slot) pairs of the listed rows by expert, ascending r*k+s. */
+static int make_pair_lists(const int32_t* ids, int64_t k, int64_t E, const int64_t* rows,
+                           int64_t nrows, pair_lists* pl) {
+  pl->start = (int64_t*)calloc((size_t)E + 1, sizeof(int64_t));
+  pl->pair = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrows * k + 1));
+  if (!pl->start || !pl->pair) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < nrows; ++r) {
+    int64_t t = rows ? rows[r] : r;
+    for (int64_t s = 0; s < k; ++s) {
+      int32_t e = ids[t * k + s];
+      if (e >= 0 && e < E) pl->start[e + 1] += 1;
+    }
+  }
+  for (int64_t e = 0; e < E; ++e) pl->start[e + 1] += pl->start[e];
+  pl->npairs = pl->start[E];
+  int64_t* fill = (int64_t*)calloc((size_t)E, sizeof(int64_t));
+  if (!fill) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; r < nrows; ++r) {
+    int64_t t = rows ? rows[r] : r;
+    for (int64_t s = 0; s < k; ++s) {
+      int32_t e = ids[t * k + s];
+      if (e < 0 || e >= E) continue;
+      pl->pair[pl->start[e] + fill[e]] = r * k + s;
+      fill[e] += 1;
+    }
+  }
+  free(fill);
+  return ORACLE_OK;
+}
+
+/* acc[q] = sum over c (sequential) of xt[c * np + q] * w[c], for the PB = 8 pairs q of a
+ * block (xt holds the pairs' activation rows transposed, np a multiple of PB). The eight
+ * sums are written out as separate variables so that they stay in registers. */
+static void dot_block(const double* xt, int64_t np, const double* w, int64_t K, double* acc) {
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0, a4 = 0.0, a5 = 0.0, a6 = 0.0, a7 = 0.0;
+  for (int64_t c = 0; c < K; ++c) {
+    const double wc = w[c];
+    const double* xc = xt + c * np;
+    a0 += xc[0] * wc;
+    a1 += xc[1] * wc;
+    a2 += xc[2] * wc;
+    a3 += xc[3] * wc;
+    a4 += xc[4] * wc;
+    a5 += xc[5] * wc;
+    a6 += xc[6] * wc;
+    a7 += xc[7] * wc;
+  }
+  acc[0] = a0;
+  acc[1] = a1;
+  acc[2] = a2;
+  acc[3] = a3;
+  acc[4] = a4;
+  acc[5] = a5;
+  acc[6] = a6;
+  acc[7] = a7;
+}
+
+/* The same with the magnitude sums mag[q] = sum_c |x_c * w_c| beside it. */
+static void dot_block_abs(const double* xt, int64_t np, const double* w, int64_t K, double* acc,
+                          double* mag) {
+  double a[PB], m[PB];
+  for (int q = 0; q < PB; ++q) a[q] = m[q] = 0.0;
+  for (int64_t c = 0; c < K; ++c) {
+    const double wc = w[c];
+    const double* xc = xt + c * np;
+    for (int q = 0; q < PB; ++q) {
+      double p = xc[q] * wc;
+      a[q] += p;
+      m[q] += fabs(p);
+    }
+  }
+  for (int q = 0; q < PB; ++q) {
+    acc[q] = a[q];
+    mag[q] = m[q];
+  }
+}
+
+enum { FMT_FP8 = 3 };
+
+/* Weight row n of expert e's [N, K] matrix, dequantized into w[0..K) exactly as the
+ * per-token functions form it. */
+static void weight_row(int fmt, const uint8_t* w, const void* s, const float* gsc, int64_t e,
+                       int64_t N, int64_t K, int64_t n, double* out) {
+  if (fmt == FMT_FP8) {
+    const uint8_t* we = w + e * N * K;
+    const float* se = (const float*)s + e * (N / 128) * (K / 128);
+    for (int64_t c = 0; c < K; ++c)
+      out[c] = oracle_e4m3_to_f64(we[n * K + c]) * (double)se[(n / 128) * (K / 128) + c / 128];
+    return;
+  }
+  const int64_t ssz = fmt == FMT_INT4 ? 2 : 1, blk = fmt == FMT_NVFP4 ? 16 : 32;
+  const uint8_t* we = w + e * N * (K / 2);
+  const uint8_t* se = (const uint8_t*)s + e * N * (K / blk) * ssz;
+  const double g = fmt == FMT_NVFP4 ? (double)gsc[e] : 1.0;
+  for (int64_t c = 0; c < K; ++c) out[c] = w4_weight(fmt, we, se, K, n, c) * g;
+}
+
+/* The routed FFN for the listed rows, expert by expert. fmt: FMT_INT4 / FMT_MXFP4 /
+ * FMT_NVFP4 (x = bf16 bits [T,H]) or FMT_FP8 (x = E4M3 a_q [T,H] with fp32 scales as
+ * [T,H/128]). out [nrows, H] fp64. The optional FP8 detail arrays (NULL to skip) receive,
+ * per pair slot r*k+s of the listed rows (untouched for dropped slots), per h column j:
+ * g, u (fp64), gmag / umag = sum_c |x_c W13(j, c)| / |x_c W13(I + j, c)|, the fp32 h
+ * before quantization, its E4M3 codes, and the fp32 scale per 128 columns. */
+static int experts_moe(int fmt, const void* xin, const float* as, const uint8_t* w13,
+                       const void* s13, const float* g13, const uint8_t* w2, const void* s2,
+                       const float* g2, const int32_t* ids, const float* wts, int64_t T,
+                       int64_t H, int64_t I, int64_t E, int64_t k, const int64_t* rows,
+                       int64_t nrows, double* out, int nthreads, double* d_g, double* d_u,
+                       double* d_gmag, double* d_umag, float* d_h32, uint8_t* d_hq,
+                       float* d_hs) {
+  const int fp8 = fmt == FMT_FP8;
+  const int q = fp8 ? 128 : 32;
+  if (!xin || !w13 || !s13 || !w2 || !s2 || !ids || !wts || !out) return ORACLE_BAD_ARG;
+  if (fp8 && !as) return ORACLE_BAD_ARG;
+  if (fmt == FMT_NVFP4 && (!g13 || !g2)) return ORACLE_BAD_ARG;
+  if (T < 0 || H <= 0 || I <= 0 || E <= 0 || k <= 0 || H % q || I % q) return ORACLE_BAD_ARG;
+  if (!rows) nrows = T;
+  for (int64_t r = 0; r < nrows; ++r) {
+    int64_t t = rows ? rows[r] : r;
+    if (t < 0 || t >= T) return ORACLE_BAD_ARG;
+  }
+  const int detail = fp8 && d_h32;
+  pair_lists pl;
+  if (make_pair_lists(ids, k, E, rows, nrows, &pl) != ORACLE_OK) {
+    free_pair_lists(&pl);
+    return ORACLE_BAD_ARG;
+  }
+  double* y = (double*)calloc((size_t)(nrows * k) * (size_t)H, sizeof(double));
+  int bad = y == NULL;
+  const int nt = nthreads > 0 ? nthreads : 1;
+  for (int64_t e = 0; e < E && !bad; ++e) {
+    const int64_t ne = pl.start[e + 1] - pl.start[e];
+    if (ne == 0) continue;
+    const int64_t np = (ne + PB - 1) / PB * PB; /* padded with zero rows, results unused */
+    const int64_t* pe = pl.pair + pl.start[e];
+    double* xt = (double*)calloc((size_t)(H * np), sizeof(double));
+    double* gg = (double*)malloc(sizeof(double) * (size_t)(np * I));
+    double* uu = (double*)malloc(sizeof(double) * (size_t)(np * I));
+    double* gm = detail ? (double*)malloc(sizeof(double) * (size_t)(np * I)) : NULL;
+    double* um = detail ? (double*)malloc(sizeof(double) * (size_t)(np * I)) : NULL;
+    double* hh = (double*)malloc(sizeof(double) * (size_t)(np * I));
+    if (!xt || !gg || !uu || !hh || (detail && (!gm || !um))) {
+      bad = 1;
+    } else {
+      /* the pairs' activation rows, transposed: xt[c * np + p] */
+      for (int64_t p = 0; p < ne; ++p) {
+        int64_t t = rows ? rows[pe[p] / k] : pe[p] / k;
+        for (int64_t c = 0; c < H; ++c)
+          xt[c * np + p] = fp8 ? oracle_e4m3_to_f64(((const uint8_t*)xin)[t * H + c]) *
+                                     (double)as[t * (H / 128) + c / 128]
+                               : oracle_bf16_to_f64(((const uint16_t*)xin)[t * H + c]);
+      }
+#pragma omp parallel num_threads(nt)
+      {
+        double* wg = (double*)malloc(sizeof(double) * (size_t)H);
+        double* wu = (double*)malloc(sizeof(double) * (size_t)H);
+        if (!wg || !wu) {
+#pragma omp atomic write
+          bad = 1;
+        } else {
+          /* g_j = sum_c x_c W13(j, c), u_j = sum_c x_c W13(I + j, c) */
+#pragma omp for schedule(dynamic, 4)
+          for (int64_t j = 0; j < I; ++j) {
+            weight_row(fmt, w13, s13, g13, e, 2 * I, H, j, wg);
+            weight_row(fmt, w13, s13, g13, e, 2 * I, H, I + j, wu);
+            for (int64_t p0 = 0; p0 < np; p0 += PB) {
+              double ag[PB], au[PB], mg[PB], mu[PB];
+              if (detail) {
+                dot_block_abs(xt + p0, np, wg, H, ag, mg);
+                dot_block_abs(xt + p0, np, wu, H, au, mu);
+              } else {
+                dot_block(xt + p0, np, wg, H, ag);
+                dot_block(xt + p0, np, wu, H, au);
+              }
+              for (int qq = 0; qq < PB; ++qq) {
+                gg[(p0 + qq) * I + j] = ag[qq];
+                uu[(p0 + qq) * I + j] = au[qq];
+                if (detail) {
+                  gm[(p0 + qq) * I + j] = mg[qq];
+                  um[(p0 + qq) * I + j] = mu[qq];
+                }
+              }
+            }
+          }
+        }
+        free(wg);
+        free(wu);
+      }
+    }
+    if (!bad) {
+      /* h = silu(g) * u; block FP8 requantizes it per 128 columns (F0 on its fp32 value) */
+      for (int64_t p = 0; p < np; ++p) {
+        double* hp = hh + p * I;
+        for (int64_t j = 0; j < I; ++j) hp[j] = silu(gg[p * I + j]) * uu[p * I + j];
+        if (fp8 && p < ne) {
+          float* h32 = (float*)malloc(sizeof(float) * (size_t)I);
+          uint8_t* hq = (uint8_t*)malloc((size_t)I);
+          float* hs = (float*)malloc(sizeof(float) * (size_t)(I / 128));
+          if (!h32 || !hq || !hs) {
+            bad = 1;
+          } else {
+            for (int64_t j = 0; j < I; ++j) h32[j] = (float)hp[j];
+            oracle_fp8_quantize_blocks(h32, 1, I, 1, 128, hq, hs);
+            for (int64_t j = 0; j < I; ++j)
+              hp[j] = oracle_e4m3_to_f64(hq[j]) * (double)hs[j / 128];
+            if (detail) {
+              const int64_t slot = pe[p];
+              memcpy(d_g + slot * I, gg + p * I, sizeof(double) * (size_t)I);
+              memcpy(d_u + slot * I, uu + p * I, sizeof(double) * (size_t)I);
+              memcpy(d_gmag + slot * I, gm + p * I, sizeof(double) * (size_t)I);
+              memcpy(d_umag + slot * I, um + p * I, sizeof(double) * (size_t)I);
+              memcpy(d_h32 + slot * I, h32, sizeof(float) * (size_t)I);
+              memcpy(d_hq + slot * I, hq, (size_t)I);
+              memcpy(d_hs + slot * (I / 128), hs, sizeof(float) * (size_t)(I / 128));
+            }
+          }
+          free(h32);
+          free(hq);
+          free(hs);
+        }
+      }
+    }
+    if (!bad) {
+      /* y_n = sum_j h_j W2(n, j), transposed h for the side-by-side sums */
+      double* ht = (double*)malloc(sizeof(double) * (size_t)(I * np));
+      if (!ht) {
+        bad = 1;
+      } else {
+        for (int64_t p = 0; p < np; ++p)
+          for (int64_t j = 0; j < I; ++j) ht[j * np + p] = hh[p * I + j];
+#pragma omp parallel num_threads(nt)
+        {
+          double* wr = (double*)malloc(sizeof(double) * (size_t)I);
+          if (!wr) {
+#pragma omp atomic write
+            bad = 1;
+          } else {
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t n = 0; n < H; ++n) {
+              weight_row(fmt, w2, s2, g2, e, H, I, n, wr);
+              for (int64_t p0 = 0; p0 < np; p0 += PB) {
+                double ay[PB];
+                dot_block(ht + p0, np, wr, I, ay);
+                for (int qq = 0; qq < PB && p0 + qq < ne; ++qq) y[pe[p0 + qq] * H + n] = ay[qq];
+              }
+            }
+          }
+          free(wr);
+        }
+      }
+      free(ht);
+    }
+    free(xt);
+    free(gg);
+    free(uu);
+    free(gm);
+    free(um);
+    free(hh);
+  }
+  if (!bad) {
+    /* out[r] = sum over the row's valid slots, in slot order, of w_s * y_s */
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+      int64_t t = rows ? rows[r] : r;
+      double* o = out + r * H;
+      for (int64_t n = 0; n < H; ++n) o[n] = 0.0;
+      for (int64_t s = 0; s < k; ++s) {
+        int32_t e = ids[t * k + s];
+        if (e < 0 || e >= E) continue;
+        double wt = (double)wts[t * k + s];
+        const double* ys = y + (r * k + s) * H;
+        for (int64_t n = 0; n < H; ++n) o[n] += wt * ys[n];
+      }
+    }
+  }
+  free(y);
+  free_pair_lists(&pl);
+  return bad ? ORACLE_BAD_ARG : ORACLE_OK;
+}
+
+int oracle_w4a16_moe_experts(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                             const uint8_t* w2, const uint16_t* s2, const int32_t* ids,
+                             const float* wts, int64_t T, int64_t H, int64_t I, int64_t E,
+                             int64_t k, const int64_t* rows, int64_t nrows, double* out,
+                             int nthreads) {
+  return experts_moe(FMT_INT4, x, NULL, w13, s13, NULL, w2, s2, NULL, ids, wts, T, H, I, E, k,
+                     rows, nrows, out, nthreads, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+}
+
+int oracle_mxfp4_moe_experts(const uint16_t* x, const uint8_t* w13, const uint8_t* s13,
+                             const uint8_t* w2, const uint8_t* s2, const int32_t* ids,
+                             const float* wts, int64_t T, int64_t H, int64_t I, int64_t E,
+                             int64_t k, const int64_t* rows, int64_t nrows, double* out,
+                             int nthreads) {
+  return experts_moe(FMT_MXFP4, x, NULL, w13, s13, NULL, w2, s2, NULL, ids, wts, T, H, I, E, k,
+                     rows, nrows, out, nthreads, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+}
+
+int oracle_nvfp4_moe_experts(const uint16_t* x, const uint8_t* w13, const uint8_t* s13,
+                             const float* g13, const uint8_t* w2, const uint8_t* s2,
+                             const float* g2, const int32_t* ids, const float* wts, int64_t T,
+                             int64_t H, int64_t I, int64_t E, int64_t k, const int64_t* rows,
+                             int64_t nrows, double* out, int nthreads) {
+  return experts_moe(FMT_NVFP4, x, NULL, w13, s13, g13, w2, s2, g2, ids, wts, T, H, I, E, k,
+                     rows, nrows, out, nthreads, NULL, NULL, NULL, NULL, NULL, NULL, NULL);
+}
+
+/* Block FP8, expert by expert; the detail arrays may be NULL (see experts_moe). */
+int oracle_fp8_moe_experts(const uint8_t* aq, const float* as, const uint8_t* w13,
+                           const float* s13, const uint8_t* w2, const float* s2,
+                           const int32_t* ids, const float* wts, int64_t T, int64_t H, int64_t I,
+                           int64_t E, int64_t k, const int64_t* rows, int64_t nrows, double* out,
+                           int nthreads, double* d_g, double* d_u, double* d_gmag, double* d_umag,
+                           float* d_h32, uint8_t* d_hq, float* d_hs) {
+  if (d_h32 && (!d_g || !d_u || !d_gmag || !d_umag || !d_hq || !d_hs)) return ORACLE_BAD_ARG;
+  return experts_moe(FMT_FP8, aq, as, w13, s13, NULL, w2, s2, NULL, ids, wts, T, H, I, E, k,
+                     rows, nrows, out, nthreads, d_g, d_u, d_gmag, d_umag, d_h32, d_hq, d_hs);
+}
