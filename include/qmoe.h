@@ -325,6 +325,46 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
                       size_t* workspace_bytes);
 
 /*
+ * qmoe_workspace_regions - where a forward keeps its intermediate results inside its
+ * workspace (diagnostics: once a forward has completed on its stream, the caller may read
+ * them, for instance to compare the block-FP8 path's quantized h with a reference).
+ *   format, T, H, I, E, k, schedule: as qmoe_plan (the indexed forwards' workspace; the
+ *               grouped entry points place the same regions first).
+ *   offsets     [QMOE_NUM_REGIONS] int64 out: byte offset of each region from the start
+ *               of the workspace, or -1 when the plan has no such region.
+ *   sizes       [QMOE_NUM_REGIONS] int64 out, or NULL: the region's size in bytes (0 when
+ *               absent).
+ * The regions, by sorted row r (the align order, L = T*k + E*(block_m - 1) rows):
+ *   SORTED_IDS int32 [L], EXPERT_IDS int32 [ceil(L / block_m)], NUM_TOKENS_PADDED int32
+ *   [1], EXPERT_OFFSETS int32 [E + 1], TILE_OFFSETS int32 [E + 1] (prefill tiles);
+ *   XS (4-bit formats) bf16 [L, H], the gathered activation rows in the GEMM operand
+ *   layout; H (4-bit formats) bf16 [L, I], SiLU(gate) * up in that layout;
+ *   H32 (block FP8, decode schedule) fp32 [L, I], SiLU(gate) * up before quantization;
+ *   HQ (block FP8) E4M3 codes [L, I] of h, HS (block FP8) fp32 [L, I / 128] scales;
+ *   OUT32 fp32 [T, H] (decode schedule); Y fp32 [T*k, H] (prefill tiles: one weighted row
+ *   per routed pair). Rows at or past num_tokens_padded, padding rows, and the regions a
+ *   schedule does not use hold unspecified values.
+ * Pure host computation; touches no GPU.
+ */
+enum {
+  QMOE_REGION_SORTED_IDS = 0,
+  QMOE_REGION_EXPERT_IDS = 1,
+  QMOE_REGION_NUM_TOKENS_PADDED = 2,
+  QMOE_REGION_EXPERT_OFFSETS = 3,
+  QMOE_REGION_TILE_OFFSETS = 4,
+  QMOE_REGION_XS = 5,
+  QMOE_REGION_H = 6,
+  QMOE_REGION_H32 = 7,
+  QMOE_REGION_HQ = 8,
+  QMOE_REGION_HS = 9,
+  QMOE_REGION_OUT32 = 10,
+  QMOE_REGION_Y = 11,
+  QMOE_NUM_REGIONS = 12
+};
+qmoe_status qmoe_workspace_regions(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E,
+                                   int32_t k, int32_t schedule, int64_t* offsets, int64_t* sizes);
+
+/*
  * Stage timing (diagnostics and benchmarking). The stages of a forward, in launch
  * order, are QMOE_STAGE_ZERO (clear the fp32 combine buffer), QMOE_STAGE_ALIGN,
  * QMOE_STAGE_GATE_UP (gate_up GEMM + SiLU*up), QMOE_STAGE_REQUANT (block-FP8 only:

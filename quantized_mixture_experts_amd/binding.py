@@ -69,6 +69,8 @@ def load():
     lib.qmoe_fp8_quantize_blocks_bf16.restype = _I32
     lib.qmoe_plan.argtypes = [_I32] * 7 + [ctypes.POINTER(_I32), ctypes.POINTER(_I32), _SZP]
     lib.qmoe_plan.restype = _I32
+    lib.qmoe_workspace_regions.argtypes = [_I32] * 7 + [ctypes.POINTER(_I64)] * 2
+    lib.qmoe_workspace_regions.restype = _I32
     _lib = lib
     return lib
 
@@ -119,6 +121,20 @@ def plan(fmt, T, H, I, E, k, schedule=SCHEDULE_AUTO):
     _check("qmoe_plan", load().qmoe_plan(fmt, T, H, I, E, k, schedule, ctypes.byref(chosen),
                                          ctypes.byref(bm), ctypes.byref(ws)))
     return chosen.value, bm.value, ws.value
+
+
+REGIONS = ("sorted_ids", "expert_ids", "num_tokens_padded", "expert_offsets", "tile_offsets",
+           "xs", "h", "h32", "hq", "hs", "out32", "y")
+
+
+def workspace_regions(fmt, T, H, I, E, k, schedule=SCHEDULE_AUTO):
+    """{region name: (byte offset, bytes)} of a forward's workspace, for the regions the
+    plan has (qmoe_workspace_regions); host only."""
+    n = len(REGIONS)
+    offs, sizes = (_I64 * n)(), (_I64 * n)()
+    _check("qmoe_workspace_regions",
+           load().qmoe_workspace_regions(fmt, T, H, I, E, k, schedule, offs, sizes))
+    return {name: (offs[i], sizes[i]) for i, name in enumerate(REGIONS) if offs[i] >= 0}
 
 
 def moe_topk_softmax(logits, k, renormalize=True, expert_map=None, stream=None):

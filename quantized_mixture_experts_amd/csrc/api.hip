@@ -52,6 +52,8 @@ int decode_mb_for(double) { return 4; }
 // activation work for nothing.
 double two_block_rows(int fmt) { return fmt == kMxfp4 || fmt == kNvfp4 ? 11.0 : 15.0; }
 
+constexpr size_t kNoRegion = ~size_t(0);
+
 struct Plan {
   int fmt = 0;
   int schedule = QMOE_SCHEDULE_DECODE;
@@ -60,6 +62,10 @@ struct Plan {
   int32_t tile_rows = 256;  // their row tile
   int32_t block_m = kSegRows;
   int64_t P = 0, L = 0, NB = 0;
+  // Workspace regions, indexed by the QMOE_REGION_* values: byte offset (kNoRegion when
+  // the plan has no such region) and size.
+  size_t off[QMOE_NUM_REGIONS];
+  size_t len[QMOE_NUM_REGIONS];
   size_t off_sorted = 0, off_expert_ids = 0, off_ntp = 0, off_offsets = 0, off_tiles = 0;
   size_t off_xs = 0, off_h = 0, off_h32 = 0, off_hq = 0, off_hs = 0, off_out32 = 0, off_y = 0;
   size_t total = 0;
@@ -134,30 +140,46 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     p.tiled = false;
     set_blocks();
   }
+  for (int i = 0; i < QMOE_NUM_REGIONS; ++i) {
+    p.off[i] = kNoRegion;
+    p.len[i] = 0;
+  }
   size_t cur = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = cur;
+  auto take = [&](int region, size_t bytes) {
+    p.off[region] = cur;
+    p.len[region] = bytes;
     cur = round_up(cur + bytes, kRegionAlign);
-    return at;
   };
-  p.off_sorted = take(sizeof(int32_t) * p.L);
-  p.off_expert_ids = take(sizeof(int32_t) * p.NB);
-  p.off_ntp = take(sizeof(int32_t));
-  p.off_offsets = take(sizeof(int32_t) * (E + 1));
-  p.off_tiles = take(sizeof(int32_t) * (E + 1));
+  take(QMOE_REGION_SORTED_IDS, sizeof(int32_t) * p.L);
+  take(QMOE_REGION_EXPERT_IDS, sizeof(int32_t) * p.NB);
+  take(QMOE_REGION_NUM_TOKENS_PADDED, sizeof(int32_t));
+  take(QMOE_REGION_EXPERT_OFFSETS, sizeof(int32_t) * (E + 1));
+  take(QMOE_REGION_TILE_OFFSETS, sizeof(int32_t) * (E + 1));
   if (four_bit(fmt)) {
-    p.off_xs = take(sizeof(uint16_t) * (size_t)p.L * H);
-    p.off_h = take(sizeof(uint16_t) * (size_t)p.L * I);
+    take(QMOE_REGION_XS, sizeof(uint16_t) * (size_t)p.L * H);
+    take(QMOE_REGION_H, sizeof(uint16_t) * (size_t)p.L * I);
   } else {
-    if (!p.tiled) p.off_h32 = take(sizeof(float) * (size_t)p.L * I);  // quantized afterwards
-    p.off_hq = take((size_t)p.L * I);
-    p.off_hs = take(sizeof(float) * (size_t)p.L * (I / 128));
+    if (!p.tiled) take(QMOE_REGION_H32, sizeof(float) * (size_t)p.L * I);  // quantized afterwards
+    take(QMOE_REGION_HQ, (size_t)p.L * I);
+    take(QMOE_REGION_HS, sizeof(float) * (size_t)p.L * (I / 128));
   }
   if (p.tiled)
-    p.off_y = take(sizeof(float) * (size_t)p.P * H);
+    take(QMOE_REGION_Y, sizeof(float) * (size_t)p.P * H);
   else
-    p.off_out32 = take(sizeof(float) * (size_t)T * H);
+    take(QMOE_REGION_OUT32, sizeof(float) * (size_t)T * H);
   p.total = cur;
+  p.off_sorted = p.off[QMOE_REGION_SORTED_IDS];
+  p.off_expert_ids = p.off[QMOE_REGION_EXPERT_IDS];
+  p.off_ntp = p.off[QMOE_REGION_NUM_TOKENS_PADDED];
+  p.off_offsets = p.off[QMOE_REGION_EXPERT_OFFSETS];
+  p.off_tiles = p.off[QMOE_REGION_TILE_OFFSETS];
+  p.off_xs = p.off[QMOE_REGION_XS];
+  p.off_h = p.off[QMOE_REGION_H];
+  p.off_h32 = p.off[QMOE_REGION_H32];
+  p.off_hq = p.off[QMOE_REGION_HQ];
+  p.off_hs = p.off[QMOE_REGION_HS];
+  p.off_out32 = p.off[QMOE_REGION_OUT32];
+  p.off_y = p.off[QMOE_REGION_Y];
   return p;
 }
 
@@ -202,9 +224,10 @@ hipError_t staged(int stage, hipStream_t s, F&& launch) {
   return err;
 }
 
+// Pointer to a workspace region; null for a region the plan does not have.
 template <typename T>
 T* region(void* ws, size_t off) {
-  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+  return off == kNoRegion ? nullptr : reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
 // The W4A16 forward after argument checks: align, gather, gate_up, down, combine.
@@ -421,6 +444,23 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
   if (chosen) *chosen = p.schedule;
   if (block_m) *block_m = p.block_m;
   if (workspace_bytes) *workspace_bytes = p.total;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_workspace_regions(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E,
+                                   int32_t k, int32_t schedule, int64_t* offsets, int64_t* sizes) {
+  g_last_error[0] = 0;
+  if (format != kW4A16 && format != kFp8 && format != kMxfp4 && format != kNvfp4)
+    return fail(QMOE_ERR_INVALID_ARG, "unknown format %d", format);
+  if (!offsets) return fail(QMOE_ERR_INVALID_ARG, "offsets is NULL");
+  qmoe_status st = check_shape(format, T, H, I, E, k, schedule);
+  if (st != QMOE_OK) return st;
+  const Plan p = make_plan(format, T, H, I, E, k, schedule);
+  for (int i = 0; i < QMOE_NUM_REGIONS; ++i) {
+    const bool has = p.off[i] != kNoRegion;
+    offsets[i] = has ? (int64_t)p.off[i] : -1;
+    if (sizes) sizes[i] = has ? (int64_t)p.len[i] : 0;
+  }
   return QMOE_OK;
 }
 
