@@ -1,31 +1,18 @@
 """GPU block-FP8 path against the CPU oracle: the E4M3 block quantizer bit-exact, and the
-W8A8 routed MoE forward within 1e-2 per token row (full-size workload on sampled rows,
-ragged shapes in full)."""
+W8A8 routed MoE forward under the rule of fp8_rule.py (every h code of every routed pair
+equal to the oracle's, or inside its interval where the exact h lies within the matrix
+cores' error of an E4M3 rounding midpoint; every output element within 1e-2 of its row's
+maximum plus the largest change those flagged codes can make). The 1024-token layer is
+compared on all rows and held to 1e-2 on every row."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, bf16_out_to_f64, report, to_dev
+import fp8_rule
+from gpu_util import bf16_out_to_f64, to_dev
 from quantized_mixture_experts_amd import binding, inputs
 
 pytestmark = pytest.mark.gpu
-
-# Small-shape criterion for the W8A8 path. The fp8 matrix cores sum the 128 products of
-# a block with an error of up to ~1e-4 of the sum of their magnitudes (measured on
-# gfx950, for v_mfma_scale_f32_16x16x128_f8f6f4 and for four chained
-# v_mfma_f32_16x16x32_fp8_fp8 alike), where exact fp32 accumulation would give ~1e-7. The
-# E4M3 requantization of h is a step function, so such differences flip single h codes;
-# at small H and I one flipped code moves its token row by up to a few 1e-2 (the oracle's
-# own output moves by up to 1.3e-2 per row when h is perturbed by 1e-5 relative on the
-# 300x256x384 case). Flips are local to a row, while an indexing or scaling fault moves
-# the whole output, so small shapes are held to: normwise error <= 5e-3, at least 99% of
-# the rows within TOL, no row beyond 5e-2. The full-size workload keeps TOL on every row.
-def _check_edge(name, got, ref):
-    e = report(name, got, ref)
-    norm = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    assert norm <= 5e-3
-    assert np.mean(e <= TOL) >= 0.99
-    assert e.max() <= 5e-2
 
 
 @pytest.mark.parametrize("R,C,br,bc", [(300, 520, 128, 128), (37, 1024, 1, 128), (5, 7, 2, 3),
@@ -58,17 +45,25 @@ def test_bf16_activation_quantizer_bit_exact(oracle_mod, T, H):
 
 
 def _forward(case, schedule):
+    """The forward's output (fp64 [T, H]), its workspace bytes and region map."""
+    T, H = case["a_q"].shape
+    E, twoI, _ = case["w13"].shape
+    k = case["topk_ids"].shape[1]
     d = to_dev(case)
+    regions = binding.workspace_regions(binding.FORMAT_FP8, T, H, twoI // 2, E, k, schedule)
+    need = binding.plan(binding.FORMAT_FP8, T, H, twoI // 2, E, k, schedule)[2]
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
     out = binding.moe_fp8_block_forward(d["a_q"], d["a_s"], d["w13"], d["s13"], d["w2"],
                                         d["s2"], d["topk_ids"], d["topk_weights"],
-                                        schedule=schedule)
+                                        schedule=schedule, workspace=ws)
     torch.cuda.synchronize()
-    return bf16_out_to_f64(out)
+    return bf16_out_to_f64(out), ws.cpu().numpy(), regions
 
 
-def _oracle(oracle_mod, case, rows):
-    return oracle_mod.fp8_moe(case["a_q"], case["a_s"], case["w13"], case["s13"], case["w2"],
-                              case["s2"], case["topk_ids"], case["topk_weights"], rows=rows)
+def _check(oracle_mod, name, case, schedule, ref_det=None, full_tol=False):
+    E = case["w13"].shape[0]
+    got, ws, regions = _forward(case, schedule)
+    return fp8_rule.check(oracle_mod, name, case, E, got, ws, regions, ref_det, full_tol)
 
 
 _FP8_CASE = {}
@@ -77,15 +72,16 @@ _FP8_CASE = {}
 @pytest.mark.parametrize("schedule", [binding.SCHEDULE_AUTO, binding.SCHEDULE_DECODE,
                                       binding.SCHEDULE_PREFILL])
 def test_fp8_workload(oracle_mod, schedule):
+    # All 1024 token rows; the oracle runs once for the three schedules. Every row within
+    # 1e-2 (no flip allowance at this size), and every h code inside the rule.
     cfg = inputs.CONFIGS["fp8"]
     print(f"[fp8] full workload schedule={schedule}", flush=True)
     if "case" not in _FP8_CASE:
         _FP8_CASE["case"] = inputs.fp8_case(cfg, oracle_mod.fp8_quantize_blocks)
     case = _FP8_CASE["case"]
-    got = _forward(case, schedule)
-    rows = inputs.sample_rows(cfg.T, 24, seed=cfg.seed)
-    ref = _oracle(oracle_mod, case, rows)
-    assert report(f"fp8/sched{schedule}", got[rows], ref).max() <= TOL
+    ref_det = _FP8_CASE.get("ref_det")
+    _FP8_CASE["ref_det"] = _check(oracle_mod, f"fp8 workload sched={schedule}", case, schedule,
+                                  ref_det, full_tol=True)
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [(40, 384, 256, 6, 3), (1, 128, 128, 1, 1), (80, 256, 384, 3, 2)])
@@ -93,33 +89,30 @@ def test_fp8_workload(oracle_mod, schedule):
 def test_fp8_ragged(oracle_mod, T, H, I, E, k, schedule):
     print(f"[fp8] ragged T={T} H={H} I={I} E={E} k={k} schedule={schedule}", flush=True)
     case = inputs.custom_fp8_case(T, H, I, E, k, seed=T + H + I, quantize=oracle_mod.fp8_quantize_blocks)
-    got = _forward(case, schedule)
-    ref = _oracle(oracle_mod, case, None)
-    _check_edge(f"fp8 ragged {T}x{H}x{I}", got, ref)
+    _check(oracle_mod, f"ragged {T}x{H}x{I} E{E} k{k} sched={schedule}", case, schedule)
 
 
 def test_fp8_zero_routing_weights():
     import oracle
     case = inputs.custom_fp8_case(10, 256, 128, 4, 2, seed=3, quantize=oracle.fp8_quantize_blocks)
     case["topk_weights"][:] = 0
-    assert np.all(_forward(case, binding.SCHEDULE_AUTO) == 0.0)
+    assert np.all(_forward(case, binding.SCHEDULE_AUTO)[0] == 0.0)
 
 
 # Prefill schedule with H % 256 == 0 and I % 128 == 0: the 128-row tile kernels, the h
-# requantization and the per-pair combine.
+# requantization and the per-pair combine; the decode schedule on the same shapes.
 @pytest.mark.parametrize("T,H,I,E,k,kind", [
     (600, 512, 256, 4, 2, "uniform"),     # several row tiles per expert, ragged last tile
     (300, 256, 384, 16, 4, "zipf"),       # skewed routing, empty experts, 3 gate column tiles
     (128, 256, 128, 1, 1, "uniform"),     # exactly one full tile; K = 256 and K = 128
     (700, 768, 512, 3, 3, "uniform"),     # every token on every expert
 ])
-def test_fp8_prefill_tiles(oracle_mod, T, H, I, E, k, kind):
-    print(f"[fp8] tiles T={T} H={H} I={I} E={E} k={k} {kind}", flush=True)
+@pytest.mark.parametrize("schedule", [binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL])
+def test_fp8_prefill_tiles(oracle_mod, T, H, I, E, k, kind, schedule):
+    print(f"[fp8] tiles T={T} H={H} I={I} E={E} k={k} {kind} schedule={schedule}", flush=True)
     case = inputs.custom_fp8_case(T, H, I, E, k, seed=T * 3 + I,
                                   quantize=oracle_mod.fp8_quantize_blocks, kind=kind)
-    got = _forward(case, binding.SCHEDULE_PREFILL)
-    ref = _oracle(oracle_mod, case, None)
-    _check_edge(f"fp8 tiles {T}x{H}x{I} E{E}", got, ref)
+    _check(oracle_mod, f"tiles {T}x{H}x{I} E{E} sched={schedule}", case, schedule)
 
 
 def test_fp8_prefill_tiles_dropped_ids_and_determinism(oracle_mod):
@@ -127,8 +120,8 @@ def test_fp8_prefill_tiles_dropped_ids_and_determinism(oracle_mod):
                                   quantize=oracle_mod.fp8_quantize_blocks)
     case["topk_ids"][::4, 0] = -1
     case["topk_ids"][2::7, 2] = 6
-    a = _forward(case, binding.SCHEDULE_PREFILL)
-    b = _forward(case, binding.SCHEDULE_PREFILL)
+    a = _forward(case, binding.SCHEDULE_PREFILL)[0]
+    b = _forward(case, binding.SCHEDULE_PREFILL)[0]
     assert np.array_equal(a, b)
-    ref = _oracle(oracle_mod, case, None)
-    _check_edge("fp8 tiles dropped ids", a, ref)
+    for schedule in (binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL):
+        _check(oracle_mod, f"dropped ids sched={schedule}", case, schedule)

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, bf16_out_to_f64, report, to_dev
+from gpu_util import TOL, bf16_out_to_f64, report, tile_cover_rows, to_dev
 from quantized_mixture_experts_amd import binding, inputs
 
 pytestmark = pytest.mark.gpu
@@ -73,15 +73,21 @@ def test_grouped_workloads_full_size(oracle_mod, name):
     g = inputs.GROUPED[name]
     print(f"[grouped workload] {name}", flush=True)
     case = inputs.grouped_case(name)
+    # At least 512 rows: the first and last row of every expert's run (and of each 128-row
+    # piece of it) plus seeded random rows; the masked layout's sample also holds rows past
+    # the counts, which must be exactly zero.
     if g["layout"] == "contiguous":
         got = _contiguous(case, binding.SCHEDULE_AUTO, g["rows"])
-        rows = inputs.sample_rows(got.shape[0], 40, seed=g["seed"])
+        rows = tile_cover_rows(case["m_indices"].reshape(-1, 1), g["E"], 512, seed=g["seed"])
         ref = oracle_mod.w4a16_grouped_contiguous(case["a"], case["w13"], case["s13"], case["w2"],
                                                   case["s2"], case["m_indices"], rows=rows)
         valid = case["m_indices"][rows] >= 0
     else:
         got = _masked(case, binding.SCHEDULE_AUTO, g["rows"])
-        rows = inputs.sample_rows(got.shape[0], 48, seed=g["seed"])
+        n = np.clip(case["masked_m"], 0, g["max_m"])
+        flat_ids = np.where(np.arange(g["max_m"])[None, :] < n[:, None],
+                            np.arange(g["E"])[:, None], -1).reshape(-1, 1)
+        rows = tile_cover_rows(flat_ids, g["E"], 512, seed=g["seed"])
         ref = oracle_mod.w4a16_grouped_masked(case["a"], case["w13"], case["s13"], case["w2"],
                                               case["s2"], case["masked_m"], rows=rows)
         valid = rows % g["max_m"] < g["rows"]

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, bf16_out_to_f64, report, to_dev
+from gpu_util import TOL, bf16_out_to_f64, report, tile_cover_rows, to_dev
 from quantized_mixture_experts_amd import binding, inputs
 
 pytestmark = pytest.mark.gpu
@@ -39,15 +39,20 @@ def _oracle(oracle_mod, case, rows=None):
 @pytest.mark.parametrize("name,schedule,nrows", [
     ("decode_mxfp4", binding.SCHEDULE_AUTO, None),
     ("decode_mxfp4", binding.SCHEDULE_PREFILL, None),
-    ("prefill_mxfp4", binding.SCHEDULE_AUTO, 48),
+    ("prefill_mxfp4", binding.SCHEDULE_AUTO, 512),
 ])
 def test_mxfp4_workloads(oracle_mod, name, schedule, nrows):
     cfg = inputs.CONFIGS[name]
     print(f"[mxfp4] {name} schedule={schedule}", flush=True)
     case = _case(name)
     got = _forward(case, schedule)
-    rows = inputs.sample_rows(cfg.T, nrows if nrows is not None else cfg.T, seed=cfg.seed)
-    e = report(f"{name}/sched{schedule}", got[rows], _oracle(oracle_mod, case, rows))
+    # all rows of the decode layer; for the prefill layer every 128-row piece of every
+    # expert's segment (so every row tile) holds a checked row, at least nrows in all
+    rows = (np.arange(cfg.T, dtype=np.int64) if nrows is None
+            else tile_cover_rows(case["topk_ids"], cfg.E, nrows, seed=cfg.seed))
+    ref = oracle_mod.mxfp4_moe_experts(case["x"], case["w13"], case["s13"], case["w2"], case["s2"],
+                                     case["topk_ids"], case["topk_weights"], rows=rows)
+    e = report(f"{name}/sched{schedule}", got[rows], ref)
     assert e.max() <= TOL
 
 

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, bf16_out_to_f64, report, to_dev
+from gpu_util import TOL, bf16_out_to_f64, report, tile_cover_rows, to_dev
 from quantized_mixture_experts_amd import binding, inputs
 
 pytestmark = pytest.mark.gpu
@@ -30,15 +30,21 @@ def _oracle(oracle_mod, c, rows=None):
 @pytest.mark.parametrize("name,schedule,nrows", [
     ("decode_nvfp4", binding.SCHEDULE_AUTO, None),
     ("decode_nvfp4", binding.SCHEDULE_PREFILL, None),
-    ("prefill_nvfp4", binding.SCHEDULE_AUTO, 48),
+    ("prefill_nvfp4", binding.SCHEDULE_AUTO, 512),
 ])
 def test_nvfp4_workloads(oracle_mod, name, schedule, nrows):
     cfg = inputs.CONFIGS[name]
     print(f"[nvfp4] {name} schedule={schedule}", flush=True)
     case = inputs.nvfp4_case(cfg)
     got = _forward(case, schedule)
-    rows = inputs.sample_rows(cfg.T, nrows if nrows is not None else cfg.T, seed=cfg.seed)
-    e = report(f"{name}/sched{schedule}", got[rows], _oracle(oracle_mod, case, rows))
+    # all rows of the decode layer; for the prefill layer every 128-row piece of every
+    # expert's segment (so every row tile) holds a checked row, at least nrows in all
+    rows = (np.arange(cfg.T, dtype=np.int64) if nrows is None
+            else tile_cover_rows(case["topk_ids"], cfg.E, nrows, seed=cfg.seed))
+    ref = oracle_mod.nvfp4_moe_experts(case["x"], case["w13"], case["s13"], case["g13"], case["w2"],
+                                     case["s2"], case["g2"], case["topk_ids"], case["topk_weights"],
+                                     rows=rows)
+    e = report(f"{name}/sched{schedule}", got[rows], ref)
     assert e.max() <= TOL
 
 
@@ -46,7 +52,8 @@ def test_nvfp4_workloads(oracle_mod, name, schedule, nrows):
     (16, 256, 128, 8, 2),     # the general decode kernel (K not a multiple of 512)
     (50, 800, 352, 10, 3),    # ragged against the 256-deep k step and the column chunks
     (9, 32, 32, 3, 2),        # smallest sizes
-    (40, 1024, 512, 6, 2),    # persistent decode kernel, one block per pass
+    (30, 1024, 512, 8, 2),    # persistent decode kernel, 7.5 rows per expert: one block per pass
+    (40, 1024, 512, 6, 2),    # persistent decode kernel, 13.3 rows per expert: two blocks per pass
     (200, 1024, 512, 8, 2),   # 50 rows per expert: two blocks per pass; 128-row tiles
     (300, 512, 768, 2, 2),    # 300 rows per expert: 256-row tiles
 ])

@@ -106,8 +106,10 @@ def test_router_to_w4a16_forward_under_expert_parallelism(oracle_mod, schedule):
 
 def test_router_and_bf16_quantizer_to_fp8_forward(oracle_mod):
     # bf16 activations quantized on the GPU (E4M3 per token and 128 columns) and routed
-    # on the GPU, then the block-FP8 forward; the oracle quantizes and routes the same way.
-    from gpu_util import TOL, bf16_out_to_f64, report
+    # on the GPU, then the block-FP8 forward; the oracle quantizes and routes the same way,
+    # and the forward is held to the W8A8 rule (fp8_rule.py) on the oracle's routing.
+    import fp8_rule
+    from gpu_util import bf16_out_to_f64
     T, H, I, E, k = 400, 512, 256, 8, 2
     print("[route+quant->fp8]", flush=True)
     case = inputs.custom_fp8_case(T, H, I, E, k, seed=55, quantize=oracle_mod.fp8_quantize_blocks)
@@ -116,22 +118,19 @@ def test_router_and_bf16_quantizer_to_fp8_forward(oracle_mod):
     a_q, a_s = binding.fp8_quantize_blocks(torch.from_numpy(x.view(np.int16)).cuda(), 1, 128)
     ids, wts = binding.moe_topk_softmax(torch.from_numpy(logits).cuda(), k)
     dev = {n: torch.from_numpy(case[n]).cuda() for n in ("w13", "s13", "w2", "s2")}
+    need = binding.plan(binding.FORMAT_FP8, T, H, I, E, k)[2]
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     out = binding.moe_fp8_block_forward(a_q, a_s, dev["w13"], dev["s13"], dev["w2"], dev["s2"],
-                                        ids, wts)
+                                        ids, wts, workspace=ws)
     torch.cuda.synchronize()
     rq, rs = oracle_mod.fp8_quantize_blocks(inputs.bf16_value(x), 1, 128)
     rids, rw = oracle_mod.topk_softmax(logits, k)
     assert np.array_equal(a_q.cpu().numpy(), rq) and np.array_equal(a_s.cpu().numpy(), rs)
-    ref = oracle_mod.fp8_moe(rq, rs, case["w13"], case["s13"], case["w2"], case["s2"], rids,
-                             rw.astype(np.float32))
-    # The W8A8 small-shape criterion (the fp8 matrix cores' block sums flip single E4M3
-    # codes of h; a flip moves one row, a fault the whole output): normwise <= 5e-3, at
-    # least 99% of the rows within TOL, none beyond 5e-2.
-    got = bf16_out_to_f64(out)
-    e = report("router+quantizer->fp8", got, ref)
-    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) <= 5e-3
-    assert np.mean(e <= TOL) >= 0.99
-    assert e.max() <= 5e-2
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    chain = dict(case, a_q=rq, a_s=rs, topk_ids=rids, topk_weights=rw.astype(np.float32))
+    regions = binding.workspace_regions(binding.FORMAT_FP8, T, H, I, E, k)
+    fp8_rule.check(oracle_mod, "router+quantizer->fp8", chain, E, bf16_out_to_f64(out),
+                   ws.cpu().numpy(), regions)
 
 
 def test_router_bench_configuration(oracle_mod):
