@@ -18,7 +18,14 @@ workloads report TFLOP/s of the routed expert FLOPs. The grouped workloads take 
 already grouped by expert (contiguous: 48 experts x 128 rows; masked: 48 experts x 32
 valid rows in a budget of 64), one pair of weight 1 per row. The "roofline" object covers the
 dominant kernel (the gate_up GEMM), timed with HIP events recorded on the stream it runs
-on, over the timed steps. "cpu_baseline" times the CPU oracle on a bounded sample.
+on, over the timed steps. "cpu_baseline" times the CPU oracle on a bounded sample, on every
+CPU the process may use (and on one CPU for the decode-sized layers), with the host's CPU
+model and core count.
+
+The metric has two halves: decode GB/s and prefill TFLOP/s. The default run (workload
+decode) therefore also times the 8192-token Zipf-routed prefill layer with the same K and W
+and reports it as the "prefill" object of the same line (its own value, ms_per_step,
+stage times, roofline against the bf16 matrix-core peak and CPU baseline).
 """
 import argparse
 import hashlib
@@ -48,6 +55,9 @@ def parse():
                              "grouped_prefill", "grouped_decode", "decode_mxfp4",
                              "prefill_mxfp4", "decode_nvfp4", "prefill_nvfp4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the default decode workload, skip the prefill leg (the metric's "
+                         "TFLOP/s half, reported as the \"prefill\" object)")
     ap.add_argument("--launch", default="eager", choices=["eager", "graph"],
                     help="how the timed steps are issued: eager library calls (default), or "
                          "replays of one captured HIP graph of the forward (slower on this "
@@ -106,39 +116,45 @@ def traffic_record(kernel_key, launches_ok):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MoE "
-              "path has no multi-GPU mode here", file=sys.stderr)
-        sys.exit(2)
+def host_cpu_info():
+    """The CPU the oracle baseline runs on: model name, logical CPUs of the host, and the
+    CPUs this process may run on (its affinity mask, capped by OMP_NUM_THREADS when set:
+    the share of the host that belongs to this GPU)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    import oracle
+    return {"model": model, "nproc": os.cpu_count(), "usable": oracle.default_threads()}
 
-    import numpy as np
-    import torch
 
-    if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
-        return
+WORKLOAD_NAMES = {
+    "decode": "decode W4A16", "prefill": "prefill W4A16 (Zipf routing)",
+    "fp8": "block-FP8 W8A8", "full384": "full 384-expert W4A16", "tiny": "tiny W4A16",
+    "decode_mxfp4": "decode MXFP4 (E2M1 + E8M0 per 32, bf16 activations)",
+    "prefill_mxfp4": "prefill MXFP4 (E2M1 + E8M0 per 32, bf16 activations; Zipf routing)",
+    "decode_nvfp4": "decode NVFP4 (E2M1 + E4M3 per 16 + fp32 per expert, bf16 activations)",
+    "prefill_nvfp4": "prefill NVFP4 (E2M1 + E4M3 per 16 + fp32 per expert, bf16 "
+                     "activations; Zipf routing)"}
+# Token rows of the CPU-oracle sample per workload: about 10 s of oracle work on 16 CPUs.
+CPU_ROWS = {"full384": 192, "prefill": 192, "fp8": 32, "prefill_mxfp4": 48,
+            "prefill_nvfp4": 48, "grouped_prefill": 1536, "grouped_decode": 1536}
+# Workloads whose oracle also runs on one CPU (the latency-sized layers), and its sample.
+ONE_CORE_ROWS = {"tiny": 16, "decode": 8, "decode_mxfp4": 2, "decode_nvfp4": 2}
 
-    from quantized_mixture_experts_amd import binding, inputs
 
-    if not os.path.exists(binding.LIB_PATH):
-        import __graft_entry__
-        __graft_entry__.build()
-    lib = binding.load()
+def measure(workload, steps, warmup, launch, cpu_rows, cpu, np, torch, binding, inputs, lib):
+    """Times one workload: an instrumented pass (per-stage HIP events on the launch stream,
+    for the per-kernel times and the roofline), then K plain steps (`value`,
+    `ms_per_step`). Returns the result fields as a dict."""
     import ctypes
 
-    if args.workload == "router":
-        bench_router(args, np, torch, binding, inputs)
-        return
-
-    grouped = inputs.GROUPED.get(args.workload)
+    grouped = inputs.GROUPED.get(workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_gen = time.time()
@@ -149,7 +165,7 @@ def main():
 
     if grouped:
         g = grouped
-        case = inputs.grouped_case(args.workload)
+        case = inputs.grouped_case(workload)
         masked = g["layout"] == "masked"
         if masked:
             counts = np.clip(case["masked_m"], 0, g["max_m"])
@@ -160,22 +176,22 @@ def main():
             rows_total = case["a"].shape[0]
             ids = case["m_indices"].reshape(-1, 1)
         # k = 1: every row is one pair of weight 1
-        cfg = inputs.MoEConfig(args.workload, rows_total, g["H"], g["I"], g["E"], 1, "w4a16",
+        cfg = inputs.MoEConfig(workload, rows_total, g["H"], g["I"], g["E"], 1, "w4a16",
                                "grouped", 0)
-    elif inputs.CONFIGS[args.workload].fmt == "w4a16":
-        cfg = inputs.CONFIGS[args.workload]
+    elif inputs.CONFIGS[workload].fmt == "w4a16":
+        cfg = inputs.CONFIGS[workload]
         case = inputs.w4a16_case(cfg)
         ids = case["topk_ids"]
-    elif inputs.CONFIGS[args.workload].fmt == "mxfp4":
-        cfg = inputs.CONFIGS[args.workload]
+    elif inputs.CONFIGS[workload].fmt == "mxfp4":
+        cfg = inputs.CONFIGS[workload]
         case = inputs.mxfp4_case(cfg)
         ids = case["topk_ids"]
-    elif inputs.CONFIGS[args.workload].fmt == "nvfp4":
-        cfg = inputs.CONFIGS[args.workload]
+    elif inputs.CONFIGS[workload].fmt == "nvfp4":
+        cfg = inputs.CONFIGS[workload]
         case = inputs.nvfp4_case(cfg)
         ids = case["topk_ids"]
     else:
-        cfg = inputs.CONFIGS[args.workload]
+        cfg = inputs.CONFIGS[workload]
 
         def gpu_quant(v, br, bc):
             q, s = binding.fp8_quantize_blocks(torch.from_numpy(v).to(dev), br, bc)
@@ -228,20 +244,19 @@ def main():
                                           d["topk_ids"], d["topk_weights"], out=out,
                                           workspace=workspace)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     # Instrumented pass: K eager steps with HIP events recorded by the library around every
     # stage launch on the launch stream; the per-kernel times (and the roofline) come from
-    # these events.
-    # Room for every launch of a stage: align holds up to three per forward (the grouped
-    # layouts' per-row routing, the sort, the row gather).
-    if lib.qmoe_timing_begin(args.steps * 3) != 0:
+    # these events. Room for every launch of a stage: align holds up to three per forward
+    # (the grouped layouts' per-row routing, the sort, the row gather).
+    if lib.qmoe_timing_begin(steps * 3) != 0:
         raise RuntimeError(lib.qmoe_last_error())
     torch.cuda.synchronize()
     te0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     te1 = time.perf_counter()
@@ -251,14 +266,14 @@ def main():
         raise RuntimeError(lib.qmoe_last_error())
     stage_names = ["zero", "align", "gate_up", "requant", "down", "cast"]
     # Per forward: a stage can hold more than one launch (align = sort + row gather).
-    stage_ms = {n: (ms_sum[i] / args.steps if counts[i] else None)
+    stage_ms = {n: (ms_sum[i] / steps if counts[i] else None)
                 for i, n in enumerate(stage_names)}
-    instrumented_ms = (te1 - te0) * 1e3 / args.steps
+    instrumented_ms = (te1 - te0) * 1e3 / steps
 
     # Timed pass: K steps without instrumentation, as one captured graph replayed K times
     # (the forward's kernels are launched on the capturing stream; nothing in it allocates
     # or synchronizes) or as eager calls.
-    if args.launch == "graph":
+    if launch == "graph":
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
@@ -271,15 +286,15 @@ def main():
         run = graph.replay
     else:
         run = step
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         run()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         run()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / steps
     valid = (ids >= 0) & (ids < cfg.E)
     touched = int(np.unique(ids[valid]).size)
     pairs = int(valid.sum())  # routed (row, expert) pairs
@@ -306,24 +321,20 @@ def main():
         peak = MFMA_PEAK_TFLOPS[dtype]
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-    kernel_key = f"{args.workload}/gate_up"
+    kernel_key = f"{workload}/gate_up"
     roof["kernel"] = kernel_key
     roof["kernel_ms"] = round(gu_ms, 4)
     roof["algorithmic_per_launch"] = per_launch
     roof["traffic"] = traffic_record(kernel_key, counts[2] > 0)
 
-    cpu = None
-    if not args.no_cpu_baseline:
+    cpu_base = None
+    if cpu:
         import oracle
-        nthreads = oracle.default_threads()
-        default_rows = {"tiny": cfg.T, "decode": cfg.T, "full384": 192, "prefill": 192, "fp8": 32,
-                        "decode_mxfp4": cfg.T, "prefill_mxfp4": 48,
-                        "decode_nvfp4": cfg.T, "prefill_nvfp4": 48,
-                        "grouped_prefill": 1536, "grouped_decode": 1536}
-        nrows = args.cpu_rows or default_rows[args.workload]
+        host = host_cpu_info()
+        nthreads = host["usable"]
         valid_rows = np.flatnonzero(valid.any(axis=1))
-        rows = valid_rows[inputs.sample_rows(valid_rows.size, nrows, seed=cfg.seed)]
-        def run_oracle():
+
+        def run_oracle(rows, nthreads):
             if grouped and masked:
                 oracle.w4a16_grouped_masked(case["a"], case["w13"], case["s13"], case["w2"], case["s2"],
                                             case["masked_m"], rows=rows, nthreads=nthreads)
@@ -345,49 +356,107 @@ def main():
                 oracle.fp8_moe(case["a_q"], case["a_s"], case["w13"], case["s13"], case["w2"],
                                case["s2"], case["topk_ids"], case["topk_weights"], rows=rows,
                                nthreads=nthreads)
-        cpu_s, reps = time_oracle(run_oracle)
-        # The oracle loops per (row, slot) and re-reads the expert's weights for each, so
-        # the full workload costs (rows holding a pair) / nrows times the sample.
-        full_s = cpu_s * valid_rows.size / len(rows)
-        cpu_value = (weight_bytes / full_s / 1e9) if hbm_bound else (flops / full_s / 1e12)
-        cpu = {"value": round(cpu_value, 6), "unit": unit, "cores": nthreads, "kind": "oracle",
-               "sample": f"{len(rows)} of {valid_rows.size} rows (all {cfg.k} slots each), "
-                         f"{cpu_s:.2f} s per run (mean of {reps}) on {nthreads} threads, "
-                         f"scaled by {valid_rows.size}/{len(rows)}"}
 
-    names = {"decode": "decode W4A16", "prefill": "prefill W4A16 (Zipf routing)",
-             "fp8": "block-FP8 W8A8", "full384": "full 384-expert W4A16", "tiny": "tiny W4A16",
-             "decode_mxfp4": "decode MXFP4 (E2M1 + E8M0 per 32, bf16 activations)",
-             "prefill_mxfp4": "prefill MXFP4 (E2M1 + E8M0 per 32, bf16 activations; Zipf routing)",
-             "decode_nvfp4": "decode NVFP4 (E2M1 + E4M3 per 16 + fp32 per expert, bf16 activations)",
-             "prefill_nvfp4": "prefill NVFP4 (E2M1 + E4M3 per 16 + fp32 per expert, bf16 "
-                              "activations; Zipf routing)"}
+        def timed(nrows, nthreads):
+            rows = valid_rows[inputs.sample_rows(valid_rows.size, nrows, seed=cfg.seed)]
+            cpu_s, reps = time_oracle(lambda: run_oracle(rows, nthreads))
+            # The oracle loops per (row, slot) and re-reads the expert's weights for each,
+            # so the full workload costs (rows holding a pair) / nrows times the sample.
+            full_s = cpu_s * valid_rows.size / len(rows)
+            v = (weight_bytes / full_s / 1e9) if hbm_bound else (flops / full_s / 1e12)
+            sample = (f"{len(rows)} of {valid_rows.size} rows (all {cfg.k} slots each), "
+                      f"{cpu_s:.2f} s per run (mean of {reps}) on {nthreads} threads, "
+                      f"scaled by {valid_rows.size}/{len(rows)}")
+            return round(v, 6), sample
+
+        v, sample = timed(cpu_rows or CPU_ROWS.get(workload, cfg.T), nthreads)
+        cpu_base = {"value": v, "unit": unit, "cores": nthreads, "kind": "oracle",
+                    "sample": sample, "host": host}
+        if workload in ONE_CORE_ROWS:
+            v1, sample1 = timed(ONE_CORE_ROWS[workload], 1)
+            cpu_base["one_core"] = {"value": v1, "unit": unit, "cores": 1, "sample": sample1}
+
     if grouped:
         layout = (f"masked, {g['rows']} valid rows per expert in a budget of {g['max_m']}"
                   if masked else f"contiguous, {g['rows']} rows per expert")
-        workload = (f"grouped W4A16 ({layout}): {cfg.T} rows, hidden {cfg.H}, intermediate "
-                    f"{cfg.I}, {cfg.E} experts, one pair of weight 1 per row")
+        name = (f"grouped W4A16 ({layout}): {cfg.T} rows, hidden {cfg.H}, intermediate "
+                f"{cfg.I}, {cfg.E} experts, one pair of weight 1 per row")
     else:
-        workload = (f"{names[args.workload]}: {cfg.T} tokens, hidden {cfg.H}, intermediate "
-                    f"{cfg.I}, {cfg.E} experts, top-{cfg.k}")
-    line = {
-        "metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
-        "data": "synthetic (seeded; random-init quantized expert weights)",
-        "config": {"workload": workload,
+        name = (f"{WORKLOAD_NAMES[workload]}: {cfg.T} tokens, hidden {cfg.H}, intermediate "
+                f"{cfg.I}, {cfg.E} experts, top-{cfg.k}")
+    return {
+        "value": round(value, 3), "unit": unit, "ms_per_step": round(ms_per_step, 4),
+        "dtype": dtype,
+        "config": {"workload": name,
                    "tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "experts": cfg.E,
                    "top_k": cfg.k, "schedule": ["auto", "decode", "prefill"][chosen],
                    "routed_pairs": pairs, "touched_experts": touched,
                    "weight_bytes": weight_bytes, "flops": flops},
-        "launch": args.launch,
+        "launch": launch,
         "instrumented_ms_per_step": round(instrumented_ms, 4),
         "stage_ms": {k: (round(v, 4) if v is not None else None) for k, v in stage_ms.items()},
         "roofline": roof,
-        "cpu_baseline": cpu,
-        "device": torch.cuda.get_device_name(0),
+        "cpu_baseline": cpu_base,
         "input_gen_s": round(gen_s, 1),
     }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the MoE "
+              "path has no multi-GPU mode here", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.steps}))
+        return
+
+    from quantized_mixture_experts_amd import binding, inputs
+
+    if not os.path.exists(binding.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    lib = binding.load()
+
+    if args.workload == "router":
+        bench_router(args, np, torch, binding, inputs)
+        return
+
+    cpu = not args.no_cpu_baseline
+    res = measure(args.workload, args.steps, args.warmup, args.launch, args.cpu_rows, cpu,
+                  np, torch, binding, inputs, lib)
+    line = {
+        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": res["dtype"],
+        "data": "synthetic (seeded; random-init quantized expert weights)",
+        "config": res["config"],
+    }
+    for key in ("launch", "instrumented_ms_per_step", "stage_ms", "roofline", "cpu_baseline",
+                "input_gen_s"):
+        line[key] = res[key]
+    # The metric's second half: the default run also times the 8192-token Zipf prefill
+    # layer (TFLOP/s against the bf16 matrix-core peak), with the same K and W.
+    if args.workload == "decode" and not args.no_prefill:
+        torch.cuda.empty_cache()
+        pre = measure("prefill", args.steps, args.warmup, args.launch, 0, cpu,
+                      np, torch, binding, inputs, lib)
+        line["prefill"] = {k: pre[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                                "instrumented_ms_per_step", "stage_ms",
+                                                "roofline", "cpu_baseline", "input_gen_s")}
+        line["prefill"]["steps"] = args.steps
+        line["prefill"]["warmup"] = args.warmup
+    line["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(line), flush=True)
 
 
