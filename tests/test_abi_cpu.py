@@ -213,3 +213,30 @@ def test_plan_two_block_passes_above_sixteen_rows_per_expert():
     # the tile path keeps 16-row align blocks; FP8 always does
     assert binding.plan(binding.FORMAT_W4A16, 8192, 7168, 2048, 48, 8)[1] == 16
     assert binding.plan(binding.FORMAT_FP8, 192, 7168, 2048, 48, 8, D)[1] == 16
+
+
+@pytest.mark.parametrize("fmt,T,E,sched", [(binding.FORMAT_W4A16, 32, 48, 0),
+                                           (binding.FORMAT_W4A16, 8192, 48, 0),
+                                           (binding.FORMAT_FP8, 1024, 32, 1),
+                                           (binding.FORMAT_FP8, 1024, 32, 2),
+                                           (binding.FORMAT_MXFP4, 200, 8, 1)])
+def test_workspace_regions_tile_the_workspace(fmt, T, E, sched):
+    # regions are 256-byte aligned, disjoint, in increasing order and end within the plan's
+    # workspace size; each schedule has exactly the regions its launches use
+    H, I, k = 7168, 2048, 8
+    regions = binding.workspace_regions(fmt, T, H, I, E, k, sched)
+    chosen, bm, total = binding.plan(fmt, T, H, I, E, k, sched)
+    spans = sorted(regions.values())
+    for (o, n), (o2, _) in zip(spans, spans[1:]):
+        assert o % 256 == 0 and o + n <= o2
+    assert spans[-1][0] + spans[-1][1] <= total
+    L = T * k + E * (bm - 1)
+    assert regions["sorted_ids"][1] == 4 * L
+    four_bit = fmt != binding.FORMAT_FP8
+    assert ("xs" in regions) == four_bit and ("h" in regions) == four_bit
+    assert ("hq" in regions) == (not four_bit)
+    tiled = chosen == binding.SCHEDULE_PREFILL
+    assert ("y" in regions) == tiled and ("out32" in regions) == (not tiled)
+    if not four_bit:
+        assert ("h32" in regions) == (not tiled)
+        assert regions["hq"][1] == L * I and regions["hs"][1] == 4 * L * (I // 128)
