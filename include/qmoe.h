@@ -171,6 +171,29 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
                               void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * moe_w4a16_forward_noalloc - moe_w4a16_forward without a workspace argument, for callers
+ * that cannot allocate device memory around the call (code under stream capture into a
+ * hipGraph, tight serving loops, harnesses that forbid hipMalloc). Its scratch is a
+ * static device array of QMOE_NOALLOC_SCRATCH_BYTES per GPU, held from the library's
+ * load until the process ends; nothing is allocated or freed, here or later.
+ *   Arguments and result as moe_w4a16_forward (same kernels, same output).
+ *   A forward whose plan needs more scratch than that (moe_w4a16_forward's workspace size
+ *   for the same shapes and schedule) returns QMOE_ERR_UNSUPPORTED before touching the
+ *   GPU: 64 MiB covers decode batches (the 32-token, 48-expert layer of hidden 7168 needs
+ *   18 MB), not large prefill batches.
+ *   Every call on one GPU shares that GPU's array, so calls that overlap in time on one GPU
+ *   (different streams, or different host threads without ordering) race and must be
+ *   serialized by the caller; consecutive calls on one stream are safe (every region is
+ *   written before it is read in each call).
+ */
+#define QMOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+qmoe_status moe_w4a16_forward_noalloc(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                                      const uint8_t* w2, const uint16_t* s2,
+                                      const int32_t* topk_ids, const float* topk_weights,
+                                      int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                      int32_t schedule, uint16_t* out, void* stream);
+
+/*
  * moe_w4a16_grouped_contiguous - the W4A16 expert FFN on the contiguous grouped layout
  * ([CHORD] "Kernel optimizations", SM90 grouped kernels, and Figure 3: the rows are
  * concatenated expert by expert, each expert's run padded, with an int32 expert index

@@ -53,6 +53,8 @@ def load():
     lib.moe_topk_softmax.restype = _I32
     lib.moe_w4a16_forward.argtypes = [_P] * 7 + [_I32] * 6 + [_P, _P, _SZP, _P]
     lib.moe_w4a16_forward.restype = _I32
+    lib.moe_w4a16_forward_noalloc.argtypes = [_P] * 7 + [_I32] * 6 + [_P, _P]
+    lib.moe_w4a16_forward_noalloc.restype = _I32
     lib.moe_mxfp4_forward.argtypes = [_P] * 7 + [_I32] * 6 + [_P, _P, _SZP, _P]
     lib.moe_mxfp4_forward.restype = _I32
     lib.moe_nvfp4_forward.argtypes = [_P] * 9 + [_I32] * 6 + [_P, _P, _SZP, _P]
@@ -206,6 +208,29 @@ def moe_w4a16_forward(x, w13, s13, w2, s2, topk_ids, topk_weights, schedule=SCHE
                       out=None, workspace=None, stream=None):
     return _four_bit_forward("moe_w4a16_forward", FORMAT_W4A16, _BF16, x, w13, s13, w2, s2,
                              topk_ids, topk_weights, schedule, out, workspace, stream)
+
+
+def moe_w4a16_forward_noalloc(x, w13, s13, w2, s2, topk_ids, topk_weights,
+                              schedule=SCHEDULE_AUTO, out=None, stream=None):
+    """moe_w4a16_forward on the library's static per-GPU scratch instead of a workspace
+    (nothing is allocated by the library; `out` may be given so that nothing is allocated
+    here either). Shapes whose plan needs more than the scratch holds raise QMoEError."""
+    T, H = x.shape
+    E, twoI, _ = w13.shape
+    I = twoI // 2
+    k = topk_ids.shape[1]
+    args = [_dev(x, "x", _BF16, (T, H)),
+            _dev(w13, "w13", _U8, (E, 2 * I, H // 2)), _dev(s13, "s13", _BF16, (E, 2 * I, H // 32)),
+            _dev(w2, "w2", _U8, (E, H, I // 2)), _dev(s2, "s2", _BF16, (E, H, I // 32)),
+            _dev(topk_ids, "topk_ids", (torch.int32,), (T, k)),
+            _dev(topk_weights, "topk_weights", (torch.float32,), (T, k))]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+    optr = _dev(out, "out", _BF16, (T, H))
+    _check("moe_w4a16_forward_noalloc",
+           load().moe_w4a16_forward_noalloc(*args, T, H, I, E, k, schedule, optr,
+                                            _stream_ptr(stream)))
+    return out
 
 
 def moe_mxfp4_forward(x, w13, s13, w2, s2, topk_ids, topk_weights, schedule=SCHEDULE_AUTO,

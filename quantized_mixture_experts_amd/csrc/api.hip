@@ -508,6 +508,63 @@ qmoe_status moe_w4a16_forward(const uint16_t* x, const uint8_t* w13, const uint1
                           schedule, out, workspace, workspace_bytes, stream);
 }
 
+// Scratch of moe_w4a16_forward_noalloc: one array per GPU, in device memory for the life
+// of the process. Host code never uses the name itself (on the host it is only a
+// stand-in symbol, not a device address): its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+static __device__ __align__(256) uint8_t scratch[QMOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on its first use).
+qmoe_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_fail(err, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QMOE_ERR_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr) return hip_fail(err, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QMOE_OK;
+}
+}  // namespace
+
+qmoe_status moe_w4a16_forward_noalloc(const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                                      const uint8_t* w2, const uint16_t* s2,
+                                      const int32_t* topk_ids, const float* topk_weights,
+                                      int32_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                      int32_t schedule, uint16_t* out, void* stream) {
+  g_last_error[0] = 0;
+  qmoe_status st = check_shape(kW4A16, T, H, I, E, k, schedule);
+  if (st != QMOE_OK) return st;
+  const Plan p = make_plan(kW4A16, T, H, I, E, k, schedule);
+  if (p.total > (size_t)QMOE_NOALLOC_SCRATCH_BYTES)
+    return fail(QMOE_ERR_UNSUPPORTED,
+                "this forward needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use moe_w4a16_forward with a workspace)",
+                p.total, (size_t)QMOE_NOALLOC_SCRATCH_BYTES);
+  if (T == 0) return QMOE_OK;
+  const void* ptrs[] = {x, w13, s13, w2, s2, topk_ids, topk_weights, out};
+  for (const void* q : ptrs)
+    if (!q) return fail(QMOE_ERR_INVALID_ARG, "NULL tensor pointer");
+  for (const void* q : ptrs)
+    if (!aligned(q, 16)) return fail(QMOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != QMOE_OK) return st;
+  return w4a16_run(p, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k, out, ws,
+                   static_cast<hipStream_t>(stream));
+}
+
 qmoe_status moe_mxfp4_forward(const uint16_t* x, const uint8_t* w13, const uint8_t* s13,
                               const uint8_t* w2, const uint8_t* s2, const int32_t* topk_ids,
                               const float* topk_weights, int32_t T, int32_t H, int32_t I,

@@ -240,3 +240,18 @@ def test_workspace_regions_tile_the_workspace(fmt, T, E, sched):
     if not four_bit:
         assert ("h32" in regions) == (not tiled)
         assert regions["hq"][1] == L * I and regions["hs"][1] == 4 * L * (I // 128)
+
+
+def test_noalloc_forward_rejects_plans_beyond_its_scratch(lib):
+    # The 8192-token prefill layer needs about 2.9 GB: rejected before any GPU work (the
+    # fake pointers are never read); the 32-token decode layer fits in the 64 MiB.
+    T, H, I, E, k = 8192, 7168, 2048, 48, 8
+    assert binding.plan(binding.FORMAT_W4A16, T, H, I, E, k)[2] > (64 << 20)
+    assert binding.plan(binding.FORMAT_W4A16, 32, H, I, E, k)[2] <= (64 << 20)
+    st = lib.moe_w4a16_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, H, I, E, k, 0,
+                                       FAKE, None)
+    assert st == UNSUPPORTED
+    assert b"scratch" in lib.qmoe_last_error()
+    st = lib.moe_w4a16_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 7169, I, E,
+                                       k, 0, FAKE, None)
+    assert st == UNSUPPORTED
