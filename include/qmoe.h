@@ -352,7 +352,8 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
  * workspace (diagnostics: once a forward has completed on its stream, the caller may read
  * them, for instance to compare the block-FP8 path's quantized h with a reference).
  *   format, T, H, I, E, k, schedule: as qmoe_plan (the indexed forwards' workspace; the
- *               grouped entry points place the same regions first).
+ *               grouped entry points' workspace starts with the same regions for their
+ *               row count and k = 1, except Y, which they do not use).
  *   offsets     [QMOE_NUM_REGIONS] int64 out: byte offset of each region from the start
  *               of the workspace, or -1 when the plan has no such region.
  *   sizes       [QMOE_NUM_REGIONS] int64 out, or NULL: the region's size in bytes (0 when

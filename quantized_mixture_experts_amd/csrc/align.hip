@@ -16,6 +16,8 @@
 //   4. it writes its segment's sentinel padding and expert_ids, and a strided share
 //      of the tail past off[E].
 // The result is bit-identical to a stable counting sort on the host.
+#include <algorithm>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -151,7 +153,113 @@ __global__ void __launch_bounds__(kAlignThreads)
   }
 }
 
+// Masked grouped layout: the rows arrive grouped by expert, expert g owning rows
+// g * max_m + [0, c_g) with c_g = masked_m[g] clamped to [0, max_m] ("vLLM x Novita AI:
+// Chord W4A16 INT4 MoE Kernel for Kimi K2.x", SM90 grouped kernels: a per-expert row
+// budget with a device-side count of valid rows). The align outputs follow from the counts
+// alone: segment g holds those row indices in order, padded to B with the sentinel
+// P = E * max_m, so there is nothing to sort. Every work-group scans the E counts in LDS
+// and fills a grid-strided share of sorted_ids and expert_ids; work-group 0 writes the
+// offsets. The same pass writes the routing weight 1 of every row and, when `out` is
+// given, clears the output rows past each count (the prefill tiles write only valid rows).
+constexpr int kMaskedThreads = 256;
+static_assert(kMaskedThreads == kAlignThreads, "block_exclusive_scan assumes kAlignThreads");
+
+__global__ void __launch_bounds__(kMaskedThreads)
+    masked_align_kernel(const int32_t* __restrict__ masked_m, int32_t E, int32_t max_m, int32_t B,
+                        int32_t L, int32_t NB, int32_t* __restrict__ sorted_ids,
+                        int32_t* __restrict__ expert_ids, int32_t* __restrict__ num_tokens_padded,
+                        int32_t* __restrict__ expert_offsets, int32_t tile_m,
+                        int32_t* __restrict__ tile_offsets, float* __restrict__ ones,
+                        uint16_t* __restrict__ out, int32_t H) {
+  extern __shared__ int32_t lds[];
+  int32_t* cnt = lds;          // [E]
+  int32_t* off = lds + E;      // [E + 1]
+  int32_t* toff = off + E + 1; // [E + 1]
+  int32_t* tmp = toff + E + 1; // [kAlignWaves]
+  const int tid = threadIdx.x;
+  const int P = E * max_m;
+  for (int e = tid; e < E; e += kMaskedThreads) cnt[e] = min(max(masked_m[e], 0), max_m);
+  __syncthreads();
+  const int per = (E + kMaskedThreads - 1) / kMaskedThreads;
+  const int e0 = tid * per;
+  int my_rows = 0, my_tiles = 0;
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    my_rows += (cnt[e] + B - 1) / B * B;
+    if (tile_m > 0) my_tiles += (cnt[e] + tile_m - 1) / tile_m;
+  }
+  int total_rows, total_tiles;
+  int rbase = block_exclusive_scan(my_rows, tmp, &total_rows);
+  int tbase = block_exclusive_scan(my_tiles, tmp, &total_tiles);
+  for (int e = e0; e < e0 + per && e < E; ++e) {
+    off[e] = rbase;
+    toff[e] = tbase;
+    rbase += (cnt[e] + B - 1) / B * B;
+    if (tile_m > 0) tbase += (cnt[e] + tile_m - 1) / tile_m;
+  }
+  if (tid == 0) {
+    off[E] = total_rows;
+    toff[E] = total_tiles;
+  }
+  __syncthreads();
+  const int ntp = off[E];
+  if (blockIdx.x == 0) {
+    if (tid == 0) num_tokens_padded[0] = ntp;
+    if (expert_offsets)
+      for (int e = tid; e <= E; e += kMaskedThreads) expert_offsets[e] = off[e];
+    if (tile_offsets)
+      for (int e = tid; e <= E; e += kMaskedThreads) tile_offsets[e] = toff[e];
+  }
+  // expert of sorted position r < ntp: the largest g with off[g] <= r
+  auto expert_at = [&](int r) {
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= r) lo = mid;
+      else hi = mid;
+    }
+    return lo;
+  };
+  const int stride = gridDim.x * kMaskedThreads;
+  for (int r = blockIdx.x * kMaskedThreads + tid; r < L; r += stride) {
+    int v = P;
+    if (r < ntp) {
+      const int g = expert_at(r), i = r - off[g];
+      if (i < cnt[g]) v = g * max_m + i;
+    }
+    sorted_ids[r] = v;
+  }
+  for (int b = blockIdx.x * kMaskedThreads + tid; b < NB; b += stride)
+    expert_ids[b] = b * B < ntp ? expert_at(b * B) : -1;
+  for (int r = blockIdx.x * kMaskedThreads + tid; r < P; r += stride) ones[r] = 1.f;
+  if (out) {
+    // rows past each count: H / 8 pieces of 16 B per row
+    const int pieces = H >> 3;
+    const int64_t n = (int64_t)P * pieces;
+    for (int64_t i = (int64_t)blockIdx.x * kMaskedThreads + tid; i < n;
+         i += (int64_t)stride) {
+      const int row = (int)(i / pieces), g = row / max_m;
+      if (row - g * max_m >= cnt[g])
+        reinterpret_cast<u32x4*>(out + (size_t)row * H)[i - (int64_t)row * pieces] =
+            u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_masked_align(const int32_t* masked_m, int32_t E, int32_t max_m, int32_t B,
+                               int32_t L, int32_t NB, int32_t* sorted_ids, int32_t* expert_ids,
+                               int32_t* ntp, int32_t* expert_offsets, int32_t tile_m,
+                               int32_t* tile_offsets, float* ones, uint16_t* out, int32_t H,
+                               hipStream_t stream) {
+  const int64_t work = std::max<int64_t>(L, out ? (int64_t)E * max_m * (H / 8) / 8 : (int64_t)L);
+  const int grid = (int)std::min<int64_t>(std::max<int64_t>(1, work / (kMaskedThreads * 4)), 512);
+  hipLaunchKernelGGL(masked_align_kernel, dim3(grid), dim3(kMaskedThreads), align_lds_bytes(E),
+                     stream, masked_m, E, max_m, B, L, NB, sorted_ids, expert_ids, ntp,
+                     expert_offsets, tile_m, tile_offsets, ones, out, H);
+  return hipGetLastError();
+}
 
 size_t align_lds_bytes(int32_t E) {
   return sizeof(int32_t) * ((size_t)E + 2 * ((size_t)E + 1) + kAlignWaves);

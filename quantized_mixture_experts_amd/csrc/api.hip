@@ -98,8 +98,10 @@ qmoe_status check_shape(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int
 
 // tok_e_hint > 0 replaces the routed-rows-per-expert estimate T * k / E that picks the
 // schedule (the grouped layouts pass the caller's expected rows per expert).
+// direct_out: the forward writes the output rows without per-pair fp32 rows (one pair of
+// weight 1 per row: the grouped layouts), so the plan has no Y region.
 Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t schedule,
-               double tok_e_hint = -1.0) {
+               double tok_e_hint = -1.0, bool direct_out = false) {
   Plan p;
   p.fmt = fmt;
   p.P = (int64_t)T * k;
@@ -163,10 +165,11 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     take(QMOE_REGION_HQ, (size_t)p.L * I);
     take(QMOE_REGION_HS, sizeof(float) * (size_t)p.L * (I / 128));
   }
-  if (p.tiled)
-    take(QMOE_REGION_Y, sizeof(float) * (size_t)p.P * H);
-  else
+  if (p.tiled) {
+    if (!direct_out) take(QMOE_REGION_Y, sizeof(float) * (size_t)p.P * H);
+  } else {
     take(QMOE_REGION_OUT32, sizeof(float) * (size_t)T * H);
+  }
   p.total = cur;
   p.off_sorted = p.off[QMOE_REGION_SORTED_IDS];
   p.off_expert_ids = p.off[QMOE_REGION_EXPERT_IDS];
@@ -230,12 +233,8 @@ T* region(void* ws, size_t off) {
   return off == kNoRegion ? nullptr : reinterpret_cast<T*>(static_cast<char*>(ws) + off);
 }
 
-// The W4A16 forward after argument checks: align, gather, gate_up, down, combine.
-qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
-                      const uint8_t* w2, const uint16_t* s2, const int32_t* topk_ids,
-                      const float* topk_weights, int32_t T, int32_t H, int32_t I, int32_t E,
-                      int32_t k, uint16_t* out, void* workspace, hipStream_t s,
-                      const float* g13 = nullptr, const float* g2 = nullptr) {
+Routing routing_view(const Plan& p, void* workspace, const float* topk_weights, int32_t k,
+                     int32_t E) {
   Routing r{};
   r.sorted_ids = region<int32_t>(workspace, p.off_sorted);
   r.offsets = region<int32_t>(workspace, p.off_offsets);
@@ -247,6 +246,33 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
   r.k = k;
   r.E = E;
   r.L = (int32_t)p.L;
+  return r;
+}
+
+// align of the indexed forwards: the routed pairs sorted to expert segments of block_m
+// rows (and the prefill tiles' offsets when the plan uses the tile kernels).
+hipError_t w4a16_align(const Plan& p, const int32_t* topk_ids, int32_t E, void* workspace,
+                       hipStream_t s) {
+  return staged(QMOE_STAGE_ALIGN, s, [&] {
+    return launch_align(topk_ids, (int32_t)p.P, E, p.block_m, (int32_t)p.L, (int32_t)p.NB,
+                        region<int32_t>(workspace, p.off_sorted),
+                        region<int32_t>(workspace, p.off_expert_ids),
+                        region<int32_t>(workspace, p.off_ntp),
+                        region<int32_t>(workspace, p.off_offsets), p.tiled ? p.tile_rows : 0,
+                        p.tiled ? region<int32_t>(workspace, p.off_tiles) : nullptr, s);
+  });
+}
+
+// The 4-bit forward after align: row gather (where the kernels need it), gate_up, down,
+// combine or cast. direct_out (one pair of weight 1 per row, the grouped layouts): on the
+// prefill tiles, down writes the bf16 output rows itself and there is no combine pass.
+qmoe_status w4a16_after_align(const Plan& p, const uint16_t* x, const uint8_t* w13,
+                              const uint16_t* s13, const uint8_t* w2, const uint16_t* s2,
+                              const int32_t* topk_ids, const float* topk_weights, int32_t T,
+                              int32_t H, int32_t I, int32_t E, int32_t k, uint16_t* out,
+                              void* workspace, hipStream_t s, const float* g13 = nullptr,
+                              const float* g2 = nullptr, bool direct_out = false) {
+  const Routing r = routing_view(p, workspace, topk_weights, k, E);
   const bool mx = p.fmt == kMxfp4 || p.fmt == kNvfp4;  // FP4 codes, natural k order
   W4A16Problem prob{x, region<uint16_t>(workspace, p.off_xs), w13, s13, w2, s2,
                     region<uint16_t>(workspace, p.off_h), region<float>(workspace, p.off_out32),
@@ -254,31 +280,27 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
   prob.nv = p.fmt == kNvfp4;
   prob.g13 = g13;
   prob.g2 = g2;
+  const int32_t* ntp = region<int32_t>(workspace, p.off_ntp);
 
   if (p.tiled) {
     const int32_t tm = p.tile_rows;
     hipError_t err = staged(QMOE_STAGE_ALIGN, s, [&] {
-      return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
-                          region<int32_t>(workspace, p.off_sorted),
-                          region<int32_t>(workspace, p.off_expert_ids),
-                          region<int32_t>(workspace, p.off_ntp),
-                          region<int32_t>(workspace, p.off_offsets), tm,
-                          region<int32_t>(workspace, p.off_tiles), s);
-    });
-    if (err != hipSuccess) return hip_fail(err, "align launch");
-    err = staged(QMOE_STAGE_ALIGN, s, [&] {
-      return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s, mx);
+      return launch_gather_rows(x, r, ntp, H, prob.xs, s, mx);
     });
     if (err != hipSuccess) return hip_fail(err, "gather launch");
     err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_tiled(prob, r, tm, s); });
     if (err != hipSuccess) return hip_fail(err, "gate_up launch");
     float* y = region<float>(workspace, p.off_y);
-    err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_tiled(prob, r, tm, y, s); });
-    if (err != hipSuccess) return hip_fail(err, "down launch");
-    err = staged(QMOE_STAGE_CAST, s, [&] {
-      return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);
+    err = staged(QMOE_STAGE_DOWN, s, [&] {
+      return launch_w4a16_down_tiled(prob, r, tm, y, s, direct_out ? out : nullptr);
     });
-    if (err != hipSuccess) return hip_fail(err, "combine launch");
+    if (err != hipSuccess) return hip_fail(err, "down launch");
+    if (!direct_out) {
+      err = staged(QMOE_STAGE_CAST, s, [&] {
+        return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);
+      });
+      if (err != hipSuccess) return hip_fail(err, "combine launch");
+    }
     return QMOE_OK;
   }
 
@@ -287,19 +309,14 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
     err = staged(QMOE_STAGE_ZERO, s, [&] { return launch_zero_f32(prob.out32, (int64_t)T * H, s); });
     if (err != hipSuccess) return hip_fail(err, "zero launch");
   }
-  err = staged(QMOE_STAGE_ALIGN, s, [&] {
-    return launch_align(topk_ids, r.P, E, p.block_m, r.L, (int32_t)p.NB,
-                        region<int32_t>(workspace, p.off_sorted),
-                        region<int32_t>(workspace, p.off_expert_ids),
-                        region<int32_t>(workspace, p.off_ntp),
-                        region<int32_t>(workspace, p.off_offsets), 0, nullptr, s);
-  });
-  if (err != hipSuccess) return hip_fail(err, "align launch");
-  // The gathered activation rows belong to the align stage's timing.
-  err = staged(QMOE_STAGE_ALIGN, s, [&] {
-    return launch_gather_rows(x, r, region<int32_t>(workspace, p.off_ntp), H, prob.xs, s, mx);
-  });
-  if (err != hipSuccess) return hip_fail(err, "gather launch");
+  // The gathered activation rows belong to the align stage's timing; the persistent
+  // decode gate_up reads the rows of x itself.
+  if (!w4a16_stream_reads_rows(H, p.mb)) {
+    err = staged(QMOE_STAGE_ALIGN, s, [&] {
+      return launch_gather_rows(x, r, ntp, H, prob.xs, s, mx);
+    });
+    if (err != hipSuccess) return hip_fail(err, "gather launch");
+  }
   err = staged(QMOE_STAGE_GATE_UP, s, [&] { return launch_w4a16_gateup_stream(prob, r, p.mb, s); });
   if (err != hipSuccess) return hip_fail(err, "gate_up launch");
   err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_stream(prob, r, p.mb, s); });
@@ -311,10 +328,28 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
   return QMOE_OK;
 }
 
+// The indexed 4-bit forward after argument checks: align, then the rest.
+qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, const uint16_t* s13,
+                      const uint8_t* w2, const uint16_t* s2, const int32_t* topk_ids,
+                      const float* topk_weights, int32_t T, int32_t H, int32_t I, int32_t E,
+                      int32_t k, uint16_t* out, void* workspace, hipStream_t s,
+                      const float* g13 = nullptr, const float* g2 = nullptr) {
+  hipError_t err = w4a16_align(p, topk_ids, E, workspace, s);
+  if (err != hipSuccess) return hip_fail(err, "align launch");
+  return w4a16_after_align(p, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k, out,
+                           workspace, s, g13, g2);
+}
+
 // Grouped layouts: the rows arrive grouped by expert (the layout an expert-parallel
 // dispatch hands over), each row one pair of routing weight 1, so the forward is the
 // indexed one with k = 1 and the row's expert as its only id. `route` is m_indices
 // (contiguous) or masked_m (masked, then M is max_m and there are E * M rows).
+//   masked: the align outputs come from the counts alone (no sort), in the same pass as
+//     the unit weights;
+//   contiguous: the unit weights (and cleared padding rows) in one pass, then align over
+//     m_indices, which need not be sorted;
+//   either: on the prefill tiles down writes the bf16 rows itself (no per-pair fp32 rows,
+//     no combine); on the decode schedule gate_up reads the rows of `a` directly.
 qmoe_status w4a16_grouped(bool masked, const uint16_t* a, const uint8_t* w13, const uint16_t* s13,
                           const uint8_t* w2, const uint16_t* s2, const int32_t* route,
                           int32_t M, int32_t H, int32_t I, int32_t E, int32_t expected_m,
@@ -333,10 +368,10 @@ qmoe_status w4a16_grouped(bool masked, const uint16_t* a, const uint8_t* w13, co
   qmoe_status st = check_shape(kW4A16, T, H, I, E, 1, schedule);
   if (st != QMOE_OK) return st;
   if (!workspace_bytes) return fail(QMOE_ERR_INVALID_ARG, "workspace_bytes is NULL");
-  const Plan p = make_plan(kW4A16, T, H, I, E, 1, schedule, expected_m > 0 ? expected_m : -1.0);
+  const Plan p = make_plan(kW4A16, T, H, I, E, 1, schedule, expected_m > 0 ? expected_m : -1.0,
+                           /*direct_out=*/true);
   const size_t off_ones = p.total;
-  const size_t off_ids = off_ones + round_up(sizeof(float) * (size_t)T, kRegionAlign);
-  const size_t total = off_ids + (masked ? round_up(sizeof(int32_t) * (size_t)T, kRegionAlign) : 0);
+  const size_t total = off_ones + round_up(sizeof(float) * (size_t)T, kRegionAlign);
   if (!workspace) {
     *workspace_bytes = total;
     return QMOE_OK;
@@ -357,13 +392,32 @@ qmoe_status w4a16_grouped(bool masked, const uint16_t* a, const uint8_t* w13, co
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* ones = region<float>(workspace, off_ones);
-  int32_t* ids = masked ? region<int32_t>(workspace, off_ids) : nullptr;
-  hipError_t err = staged(QMOE_STAGE_ALIGN, s, [&] {
-    return launch_grouped_routing(masked ? route : nullptr, M, T, ids, ones, s);
-  });
-  if (err != hipSuccess) return hip_fail(err, "grouped routing launch");
-  return w4a16_run(p, a, w13, s13, w2, s2, masked ? ids : route, ones, T, H, I, E, 1, out,
-                   workspace, s);
+  // the prefill tiles write only the valid rows: the routing pass clears the others
+  uint16_t* clear = p.tiled ? out : nullptr;
+  hipError_t err;
+  if (masked) {
+    err = staged(QMOE_STAGE_ALIGN, s, [&] {
+      return launch_masked_align(route, E, M, p.block_m, (int32_t)p.L, (int32_t)p.NB,
+                                 region<int32_t>(workspace, p.off_sorted),
+                                 region<int32_t>(workspace, p.off_expert_ids),
+                                 region<int32_t>(workspace, p.off_ntp),
+                                 region<int32_t>(workspace, p.off_offsets),
+                                 p.tiled ? p.tile_rows : 0,
+                                 p.tiled ? region<int32_t>(workspace, p.off_tiles) : nullptr,
+                                 ones, clear, H, s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "masked align launch");
+  } else {
+    err = staged(QMOE_STAGE_ALIGN, s, [&] {
+      return launch_grouped_routing(route, E, T, ones, clear, H, s);
+    });
+    if (err != hipSuccess) return hip_fail(err, "grouped routing launch");
+    err = w4a16_align(p, route, E, workspace, s);
+    if (err != hipSuccess) return hip_fail(err, "align launch");
+  }
+  // topk_ids is only read by the combine pass, which the grouped layouts do not run
+  return w4a16_after_align(p, a, w13, s13, w2, s2, masked ? nullptr : route, ones, T, H, I, E, 1,
+                           out, workspace, s, nullptr, nullptr, /*direct_out=*/true);
 }
 
 }  // namespace

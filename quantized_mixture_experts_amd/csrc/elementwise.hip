@@ -86,20 +86,25 @@ __global__ void __launch_bounds__(kEwThreads)
   }
 }
 
-// Per-row routing of the grouped layouts: every row is one pair of routing weight 1.
-// With masked_m, row g * max_m + r belongs to expert g when r < masked_m[g] and is
-// padding (-1, dropped by align) otherwise, so a count above max_m means all max_m rows
-// and a negative count none.
+// Per-row routing of the contiguous grouped layout: every row is one pair of routing
+// weight 1; a row whose index lies outside [0, E) is padding, and its output row is
+// cleared when `out` is given (the prefill tiles write only the valid rows).
 __global__ void __launch_bounds__(kEwThreads)
-    grouped_routing_kernel(const int32_t* __restrict__ masked_m, int32_t max_m, int32_t n,
-                           int32_t* __restrict__ ids, float* __restrict__ ones) {
+    grouped_routing_kernel(const int32_t* __restrict__ ids, int32_t E, int32_t n,
+                           float* __restrict__ ones, uint16_t* __restrict__ out, int32_t H) {
   const int32_t stride = (int32_t)gridDim.x * kEwThreads;
-  for (int32_t i = (int32_t)blockIdx.x * kEwThreads + threadIdx.x; i < n; i += stride) {
+  for (int32_t i = (int32_t)blockIdx.x * kEwThreads + threadIdx.x; i < n; i += stride)
     ones[i] = 1.f;
-    if (masked_m) {
-      const int32_t g = i / max_m;
-      ids[i] = i - g * max_m < masked_m[g] ? g : -1;
-    }
+  if (!out) return;
+  const int pieces = H >> 3;
+  const int64_t total = (int64_t)n * pieces;
+  for (int64_t i = (int64_t)blockIdx.x * kEwThreads + threadIdx.x; i < total;
+       i += (int64_t)stride) {
+    const int32_t row = (int32_t)(i / pieces);
+    const int32_t e = ids[row];
+    if (e < 0 || e >= E)
+      reinterpret_cast<u32x4*>(out + (size_t)row * H)[i - (int64_t)row * pieces] =
+          u32x4{0u, 0u, 0u, 0u};
   }
 }
 
@@ -149,13 +154,14 @@ hipError_t launch_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t
   return launch_quantize(v, R, C, br, bc, q, scale, stream);
 }
 
-hipError_t launch_grouped_routing(const int32_t* masked_m, int32_t max_m, int32_t n, int32_t* ids,
-                                  float* ones, hipStream_t stream) {
+hipError_t launch_grouped_routing(const int32_t* ids, int32_t E, int32_t n, float* ones,
+                                  uint16_t* out, int32_t H, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  if (masked_m && (max_m <= 0 || !ids)) return hipErrorInvalidValue;
-  const int32_t blocks = std::min<int32_t>((n + kEwThreads - 1) / kEwThreads, 1024);
-  hipLaunchKernelGGL(grouped_routing_kernel, dim3(blocks), dim3(kEwThreads), 0, stream, masked_m,
-                     max_m, n, ids, ones);
+  if (out && (!ids || H % 8)) return hipErrorInvalidValue;
+  const int64_t work = out ? (int64_t)n * (H / 8) : n;
+  const int32_t blocks = (int32_t)std::min<int64_t>((work + kEwThreads - 1) / kEwThreads, 1024);
+  hipLaunchKernelGGL(grouped_routing_kernel, dim3(blocks), dim3(kEwThreads), 0, stream, ids, E, n,
+                     ones, out, H);
   return hipGetLastError();
 }
 

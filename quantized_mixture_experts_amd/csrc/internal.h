@@ -21,6 +21,14 @@ hipError_t launch_align(const int32_t* ids, int32_t P, int32_t E, int32_t B, int
                         int32_t* expert_offsets, int32_t tile_m, int32_t* tile_offsets,
                         hipStream_t stream);
 
+// Masked grouped layout: the align outputs from the per-expert counts (no sort), the
+// routing weight 1 of every row, and (out != null) cleared output rows past each count.
+hipError_t launch_masked_align(const int32_t* masked_m, int32_t E, int32_t max_m, int32_t B,
+                               int32_t L, int32_t NB, int32_t* sorted_ids, int32_t* expert_ids,
+                               int32_t* ntp, int32_t* expert_offsets, int32_t tile_m,
+                               int32_t* tile_offsets, float* ones, uint16_t* out, int32_t H,
+                               hipStream_t stream);
+
 // --- elementwise helpers (elementwise.hip) --------------------------------
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);
 hipError_t launch_cast_f32_bf16(const float* src, uint16_t* dst, int64_t n, hipStream_t stream);
@@ -29,10 +37,10 @@ hipError_t launch_fp8_quantize_blocks(const float* v, int64_t R, int64_t C, int3
 hipError_t launch_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t C, int32_t br,
                                            int32_t bc, uint8_t* q, float* scale,
                                            hipStream_t stream);
-// Grouped layouts: ones[0, n) = 1 and, when masked_m is not null, ids[g * max_m + r] = g
-// for r < masked_m[g], else -1.
-hipError_t launch_grouped_routing(const int32_t* masked_m, int32_t max_m, int32_t n, int32_t* ids,
-                                  float* ones, hipStream_t stream);
+// Contiguous grouped layout: ones[0, n) = 1 and, when out is not null, output row r
+// (H bf16) cleared where ids[r] lies outside [0, E) (a padding row).
+hipError_t launch_grouped_routing(const int32_t* ids, int32_t E, int32_t n, float* ones,
+                                  uint16_t* out, int32_t H, hipStream_t stream);
 
 // --- grouped expert GEMMs ---------------------------------------------------
 // Routing view shared by the expert GEMMs: segments of the sorted pair list, each a
@@ -94,6 +102,9 @@ hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, i
 // Whether the decode gate_up launch also clears out32 (then no separate clearing launch
 // is needed before down).
 bool w4a16_stream_zeroes_output(int32_t H);
+// Whether the decode gate_up launch with mb blocks per pass reads the activation rows of x
+// itself (then the gathered copy xs is not needed).
+bool w4a16_stream_reads_rows(int32_t H, int mb);
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
                                     hipStream_t stream);
 // Prefill profile (W4A16 / MXFP4): row tiles of each expert segment on the matrix
@@ -105,8 +116,10 @@ bool w4a16_tiled_supported(int32_t H, int32_t I);
 int32_t w4a16_tiled_rows(double rows_per_expert);
 hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
                                      hipStream_t stream);
+// out16 != null (one pair per row, k = 1): down writes bf16(w * row) straight into the
+// output row of each pair instead of fp32 rows into y, so no combine pass is needed.
 hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
-                                   float* y, hipStream_t stream);
+                                   float* y, hipStream_t stream, uint16_t* out16 = nullptr);
 hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,
                                int32_t E, int32_t H, uint16_t* out, hipStream_t stream);
 

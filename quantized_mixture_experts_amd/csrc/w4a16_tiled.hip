@@ -94,6 +94,7 @@ struct TiledArgs {
   int32_t col_tiles;            // output column tiles per row tile
   uint32_t act_bytes;           // size of act (L * K * 2 < 2^32, host-checked)
   const float* g = nullptr;     // NVFP4: [E] fp32 scale per expert of this projection
+  uint16_t* out16 = nullptr;    // down with one pair per row: bf16 output [P, N] instead of y
 };
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -577,10 +578,18 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             if (pair[mm][r] < a.P) {
-              float* yrow = a.y + (size_t)pair[mm][r] * a.N;
+              if (a.out16) {
+                // one pair per row: the pair's output row is final
+                uint16_t* orow = a.out16 + (size_t)pair[mm][r] * a.N;
 #pragma unroll
-              for (int t = 0; t < kColTiles; ++t)
-                yrow[weight_row(t, col)] = wt[mm][r] * acc[m][t][r];
+                for (int t = 0; t < kColTiles; ++t)
+                  orow[weight_row(t, col)] = f32_to_bf16(wt[mm][r] * acc[m][t][r]);
+              } else {
+                float* yrow = a.y + (size_t)pair[mm][r] * a.N;
+#pragma unroll
+                for (int t = 0; t < kColTiles; ++t)
+                  yrow[weight_row(t, col)] = wt[mm][r] * acc[m][t][r];
+              }
             }
           }
         }
@@ -682,11 +691,12 @@ hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, in
 }
 
 hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
-                                   float* y, hipStream_t stream) {
+                                   float* y, hipStream_t stream, uint16_t* out16) {
   TiledArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
               nullptr, y, r.P, r.E, p.I, p.H, p.I, p.H / 256,
               (uint32_t)((uint64_t)r.L * p.I * 2u)};
   a.g = p.g2;
+  a.out16 = out16;
   return launch_tiled<TEpi::Down>(a, r.P, r.E, tile_rows, p.mx, p.nv, stream);
 }
 

@@ -128,9 +128,12 @@ def test_grouped_layouts_check_arguments(lib, masked):
     st, need = _grouped(lib, masked)
     assert st == OK
     rows = 48 * 128 if masked else 128
-    # the indexed forward's workspace at k = 1, plus the weights of 1 (and the masked ids)
-    base = _w4(lib, T=rows, k=1, ws=None)[1]
-    assert need >= base + 4 * rows and need <= base + 8 * rows + 512
+    # the indexed forward's regions at k = 1 without the per-pair fp32 rows (the grouped
+    # layouts write their output rows directly), plus the weights of 1
+    regions = binding.workspace_regions(binding.FORMAT_W4A16, rows, 7168, 2048, 48, 1)
+    end = max(o + n for name, (o, n) in regions.items() if name != "y")
+    base = (end + 255) // 256 * 256
+    assert need == base + (4 * rows + 255) // 256 * 256
     assert _grouped(lib, masked, ws=FAKE, size=need - 1)[0] == WORKSPACE
     assert _grouped(lib, masked, ws=FAKE, size=need, route=None)[0] == INVALID
     assert _grouped(lib, masked, ws=FAKE, size=need, route=FAKE + 2)[0] == INVALID
