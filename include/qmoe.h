@@ -365,9 +365,11 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
  *   layout; H (4-bit formats) bf16 [L, I], SiLU(gate) * up in that layout;
  *   H32 (block FP8, decode schedule) fp32 [L, I], SiLU(gate) * up before quantization;
  *   HQ (block FP8) E4M3 codes [L, I] of h, HS (block FP8) fp32 [L, I / 128] scales;
- *   OUT32 fp32 [T, H] (decode schedule); Y fp32 [T*k, H] (prefill tiles: one weighted row
- *   per routed pair). Rows at or past num_tokens_padded, padding rows, and the regions a
- *   schedule does not use hold unspecified values.
+ *   OUT32 fp32 [T, H] (decode schedule); Y fp32 [S, T*k, H] (prefill tiles: one weighted
+ *   row per routed pair and K slice; S > 1 when the down GEMM splits K because its output
+ *   tiles would not fill the GPU, S = Y's size / (4 T k H)). Rows at or past
+ *   num_tokens_padded, padding rows, and the regions a schedule does not use hold
+ *   unspecified values.
  * Pure host computation; touches no GPU.
  */
 enum {

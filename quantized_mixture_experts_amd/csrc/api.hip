@@ -2,6 +2,7 @@
 // layout and the launch sequence. Everything here is host code; no call reads a
 // device value back, allocates, frees or synchronizes.
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -35,6 +36,9 @@ constexpr size_t kRegionAlign = 256;
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 enum Format { kW4A16 = 0, kFp8 = 1, kMxfp4 = 2, kNvfp4 = 3 };
+// Compute units the planner fills (MI355X: 256). A plan is pure host computation, so the
+// device is not queried; a GPU with fewer units only gets more tiles per unit.
+constexpr double kPlanComputeUnits = 256.0;
 // The 4-bit formats share the W4A16 kernels, workspace and limits.
 bool four_bit(int fmt) { return fmt == kW4A16 || fmt == kMxfp4 || fmt == kNvfp4; }
 
@@ -60,6 +64,7 @@ struct Plan {
   int mb = 1;
   bool tiled = false;  // 4-bit prefill on the tile kernels
   int32_t tile_rows = 256;  // their row tile
+  int32_t kslices = 1;      // split-K of the prefill down GEMM (4-bit tile kernels)
   int32_t block_m = kSegRows;
   int64_t P = 0, L = 0, NB = 0;
   // Workspace regions, indexed by the QMOE_REGION_* values: byte offset (kNoRegion when
@@ -136,9 +141,32 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   };
   set_blocks();
   if (four_bit(fmt)) p.tile_rows = w4a16_tiled_rows(tok_e);
-  // The tile kernels address activation rows with 32-bit byte offsets.
+  // Split-K of the 4-bit prefill down GEMM where its output tiles would not fill the chip
+  // ([CHORD] "Kernel optimizations": a shape guard decides when down splits K): the tile
+  // kernels hold one work-group per compute unit, so when the expected tiles leave most of
+  // the kPlanComputeUnits idle, each tile's K (I / 256 blocks) is split into the largest
+  // power of two of slices that still fits one wave. The routed rows of an expert are
+  // counted high: mean plus two standard deviations of a uniform top-k routing's count,
+  // Binomial(T, k / E), whose variance is rows * (1 - k / E). A split that spills into a
+  // second wave costs more than it saves (measured on MI355X at 1024 tokens, 2 experts,
+  // top-1: an expert one 256-row tile larger than its mean, 2 slices, +8 %).
+  if (p.tiled && four_bit(fmt) && !direct_out && p.P > 0) {
+    const double e_eff = std::min<double>(E, (double)p.P);
+    const double rows_e = (double)p.P / e_eff;
+    const double sd = std::sqrt(rows_e * std::max(0.0, 1.0 - (double)k / E));
+    const double tiles = e_eff * std::ceil((rows_e + 2.0 * sd) / p.tile_rows);
+    const double items = tiles * (H / 256);
+    const int nblk = I / 256;
+    while (p.kslices * 2 <= nblk && nblk % (p.kslices * 2) == 0 &&
+           items * p.kslices * 2 <= kPlanComputeUnits)
+      p.kslices *= 2;
+  }
+  // The 4-bit tile kernels address activation rows with 32-bit byte offsets, and one
+  // expert's weights (I * H bytes of codes in either GEMM) through a buffer resource whose
+  // size is a signed 32-bit count; larger shapes run on the stream kernels.
   if (p.tiled && four_bit(fmt) &&
-      (uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32)) {
+      ((uint64_t)p.L * (uint64_t)std::max(H, I) * 2u >= (uint64_t(1) << 32) ||
+       (uint64_t)I * (uint64_t)H >= (uint64_t(1) << 31))) {
     p.tiled = false;
     set_blocks();
   }
@@ -166,7 +194,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     take(QMOE_REGION_HS, sizeof(float) * (size_t)p.L * (I / 128));
   }
   if (p.tiled) {
-    if (!direct_out) take(QMOE_REGION_Y, sizeof(float) * (size_t)p.P * H);
+    if (!direct_out) take(QMOE_REGION_Y, sizeof(float) * (size_t)p.kslices * p.P * H);
   } else {
     take(QMOE_REGION_OUT32, sizeof(float) * (size_t)T * H);
   }
@@ -292,12 +320,12 @@ qmoe_status w4a16_after_align(const Plan& p, const uint16_t* x, const uint8_t* w
     if (err != hipSuccess) return hip_fail(err, "gate_up launch");
     float* y = region<float>(workspace, p.off_y);
     err = staged(QMOE_STAGE_DOWN, s, [&] {
-      return launch_w4a16_down_tiled(prob, r, tm, y, s, direct_out ? out : nullptr);
+      return launch_w4a16_down_tiled(prob, r, tm, y, s, direct_out ? out : nullptr, p.kslices);
     });
     if (err != hipSuccess) return hip_fail(err, "down launch");
     if (!direct_out) {
       err = staged(QMOE_STAGE_CAST, s, [&] {
-        return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);
+        return launch_combine_rows(y, topk_ids, T, k, E, H, out, s, p.kslices);
       });
       if (err != hipSuccess) return hip_fail(err, "combine launch");
     }

@@ -118,10 +118,16 @@ hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, in
                                      hipStream_t stream);
 // out16 != null (one pair per row, k = 1): down writes bf16(w * row) straight into the
 // output row of each pair instead of fp32 rows into y, so no combine pass is needed.
+// kslices > 1 (split-K): each output tile's K is split into that many slices (it must
+// divide I / 256), slice q writing its partial rows to y + q * P * H (y is [kslices, P, H]).
 hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
-                                   float* y, hipStream_t stream, uint16_t* out16 = nullptr);
+                                   float* y, hipStream_t stream, uint16_t* out16 = nullptr,
+                                   int kslices = 1);
+// out[t] = bf16 of the sum over the K slices (in order) of the sums over token t's valid
+// slots (in order) of the rows of y ([slices, T*k, H]).
 hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,
-                               int32_t E, int32_t H, uint16_t* out, hipStream_t stream);
+                               int32_t E, int32_t H, uint16_t* out, hipStream_t stream,
+                               int32_t slices = 1);
 
 // Prefill profile (block FP8): 128-row tiles; needs H % 256 == 0 and I % 128 == 0 and
 // at most 64 k blocks; align must have produced tile_offsets for fp8_tiled_rows() rows.

@@ -95,6 +95,7 @@ struct TiledArgs {
   uint32_t act_bytes;           // size of act (L * K * 2 < 2^32, host-checked)
   const float* g = nullptr;     // NVFP4: [E] fp32 scale per expert of this projection
   uint16_t* out16 = nullptr;    // down with one pair per row: bf16 output [P, N] instead of y
+  int32_t kslices = 1;          // split-K (down): K slices per output tile; y is [kslices, P, N]
 };
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -168,12 +169,15 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = lane & 15, quad = lane >> 4;
 
-  // XCD-aware item order over the real tile count: XCD x takes a contiguous range.
-  const int total = a.tile_offsets[a.E] * a.col_tiles;
+  // XCD-aware item order over the real tile count: XCD x takes a contiguous range. An
+  // item is (row tile, column tile, K slice); with a.kslices > 1 (split-K, down only) the
+  // slices of an output tile are neighbours.
+  const int total = a.tile_offsets[a.E] * a.col_tiles * a.kslices;
   const int per = (total + kNumXcd - 1) / kNumXcd;
   const int xi = blockIdx.x / kNumXcd;
-  const int item = (blockIdx.x % kNumXcd) * per + xi;
-  if (xi >= per || item >= total) return;
+  const int item_k = (blockIdx.x % kNumXcd) * per + xi;
+  if (xi >= per || item_k >= total) return;
+  const int item = item_k / a.kslices, slice = item_k - item * a.kslices;
   const int rtile = item / a.col_tiles, ctile = item % a.col_tiles;
   const int e = expert_of_tile(a.tile_offsets, a.E, rtile);
   const int seg1 = a.offsets[e + 1];
@@ -181,7 +185,10 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   const int rb0 = row0 >> 4;
   const int rb_last = (seg1 >> 4) - 1;
   const int K = a.K, KG = K >> 5;
-  const int nsteps = KG, nblocks = K >> 8;
+  // This item's 256-deep weight blocks: all of K, or its slice. Offsets below keep the
+  // full-K strides and start at the slice's first block; the loop runs over the slice.
+  const int nblocks = (K >> 8) / a.kslices, kb_first = slice * nblocks;
+  const int nsteps = nblocks * kGroupsPerBlock;
 
   // Weight row of tile t for column c of this wave.
   auto weight_row = [&](int t, int c) {
@@ -206,8 +213,10 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   uint32_t woff[kColTiles], soff[kColTiles];
 #pragma unroll
   for (int t = 0; t < kColTiles; ++t) {
-    woff[t] = (uint32_t)weight_row(t, col) * (uint32_t)(K >> 1) + 16u * quad;
-    soff[t] = (uint32_t)weight_row(t, lane >> 2) * (uint32_t)KG * kScaleBytes + 4u * (lane & 3);
+    woff[t] = (uint32_t)weight_row(t, col) * (uint32_t)(K >> 1) + 16u * quad +
+              (uint32_t)kb_first * 128u;
+    soff[t] = (uint32_t)weight_row(t, lane >> 2) * (uint32_t)KG * kScaleBytes + 4u * (lane & 3) +
+              (uint32_t)kb_first * kGroupsPerBlock * kScaleBytes;
   }
 
   // Activation copies of this wave: row blocks wave*kCopiesPerWave + i of the tile.
@@ -215,7 +224,8 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
 #pragma unroll
   for (int i = 0; i < kCopiesPerWave; ++i) {
     const int rb = min(rb0 + wave * kCopiesPerWave + i, rb_last);
-    aoff[i] = (uint32_t)rb * (uint32_t)(KG * 1024) + lane * 16u;
+    aoff[i] = (uint32_t)rb * (uint32_t)(KG * 1024) + lane * 16u +
+              (uint32_t)kb_first * kGroupsPerBlock * 1024u;
   }
 
   // All global reads of the loop are asynchronous LDS copies whose completion this code
@@ -585,7 +595,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
                 for (int t = 0; t < kColTiles; ++t)
                   orow[weight_row(t, col)] = f32_to_bf16(wt[mm][r] * acc[m][t][r]);
               } else {
-                float* yrow = a.y + (size_t)pair[mm][r] * a.N;
+                float* yrow = a.y + ((size_t)slice * a.P + pair[mm][r]) * a.N;
 #pragma unroll
                 for (int t = 0; t < kColTiles; ++t)
                   yrow[weight_row(t, col)] = wt[mm][r] * acc[m][t][r];
@@ -598,15 +608,17 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   }
 }
 
-// out[t, :] = bf16(sum of y[t*k + s, :] over the valid slots s of token t, in slot
-// order). A thread owns 8 columns of one token; the rows of up to kSlotBatch slots are
-// requested before any is summed.
+// out[t, :] = bf16(sum over the K slices q (in order) of the sum over the valid slots s of
+// token t (in slot order) of y[q, t*k + s, :]). A thread owns 8 columns of one token; the
+// rows of up to kSlotBatch slots of a slice are requested before any is summed.
 constexpr int kCombineThreads = 256;
 constexpr int kSlotBatch = 8;
 
 __global__ void __launch_bounds__(kCombineThreads)
     combine_rows_kernel(const float* __restrict__ y, const int32_t* __restrict__ ids,
-                        int32_t T, int32_t k, int32_t E, int32_t H, uint16_t* __restrict__ out) {
+                        int32_t T, int32_t k, int32_t E, int32_t H, int32_t slices,
+                        uint16_t* __restrict__ out) {
+  const int64_t slice_stride = (int64_t)T * k * H;
   const int chunks = H >> 3;
   const int64_t items = (int64_t)T * chunks;
   for (int64_t i = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x; i < items;
@@ -614,23 +626,26 @@ __global__ void __launch_bounds__(kCombineThreads)
     const int64_t t = i / chunks;
     const int c = (int)(i - t * chunks) * 8;
     f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < k; s0 += kSlotBatch) {
-      f32x4 vl[kSlotBatch], vh[kSlotBatch];
-      bool ok[kSlotBatch];
+    for (int q = 0; q < slices; ++q) {
+      const float* yq = y + q * slice_stride;
+      for (int s0 = 0; s0 < k; s0 += kSlotBatch) {
+        f32x4 vl[kSlotBatch], vh[kSlotBatch];
+        bool ok[kSlotBatch];
 #pragma unroll
-      for (int s = 0; s < kSlotBatch; ++s) {
-        const int64_t pair = t * k + s0 + s;
-        const int id = (s0 + s < k) ? ids[pair] : -1;
-        ok[s] = id >= 0 && id < E;
-        const float* row = y + (ok[s] ? pair : 0) * H + c;
-        vl[s] = *reinterpret_cast<const f32x4*>(row);
-        vh[s] = *reinterpret_cast<const f32x4*>(row + 4);
-      }
+        for (int s = 0; s < kSlotBatch; ++s) {
+          const int64_t pair = t * k + s0 + s;
+          const int id = (s0 + s < k) ? ids[pair] : -1;
+          ok[s] = id >= 0 && id < E;
+          const float* row = yq + (ok[s] ? pair : 0) * H + c;
+          vl[s] = *reinterpret_cast<const f32x4*>(row);
+          vh[s] = *reinterpret_cast<const f32x4*>(row + 4);
+        }
 #pragma unroll
-      for (int s = 0; s < kSlotBatch; ++s) {
-        if (ok[s]) {
-          lo += vl[s];
-          hi += vh[s];
+        for (int s = 0; s < kSlotBatch; ++s) {
+          if (ok[s]) {
+            lo += vl[s];
+            hi += vh[s];
+          }
         }
       }
     }
@@ -661,7 +676,8 @@ template <TEpi EPI>
 hipError_t launch_tiled(const TiledArgs& a, int64_t P, int E, int tile_rows, bool mx, bool nv,
                         hipStream_t stream) {
   if (tile_rows != 128 && tile_rows != 256) return hipErrorInvalidValue;
-  const int64_t items = (P / tile_rows + E) * a.col_tiles;  // at most this many row tiles
+  // at most this many row tiles, times the column tiles and K slices of each
+  const int64_t items = (P / tile_rows + E) * a.col_tiles * a.kslices;
   if (items <= 0) return hipSuccess;
   if (items > (int64_t(1) << 30)) return hipErrorInvalidValue;
   if (tile_rows == 128)
@@ -691,22 +707,25 @@ hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, in
 }
 
 hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
-                                   float* y, hipStream_t stream, uint16_t* out16) {
+                                   float* y, hipStream_t stream, uint16_t* out16, int kslices) {
+  if (kslices < 1 || (p.I / 256) % kslices || (out16 && kslices != 1)) return hipErrorInvalidValue;
   TiledArgs a{p.h, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets, r.topk_weights,
               nullptr, y, r.P, r.E, p.I, p.H, p.I, p.H / 256,
               (uint32_t)((uint64_t)r.L * p.I * 2u)};
   a.g = p.g2;
   a.out16 = out16;
+  a.kslices = kslices;
   return launch_tiled<TEpi::Down>(a, r.P, r.E, tile_rows, p.mx, p.nv, stream);
 }
 
 hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,
-                               int32_t E, int32_t H, uint16_t* out, hipStream_t stream) {
+                               int32_t E, int32_t H, uint16_t* out, hipStream_t stream,
+                               int32_t slices) {
   const int64_t items = (int64_t)T * (H / 8);
   if (items <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((items + kCombineThreads - 1) / kCombineThreads, 16384);
   hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
-                     stream, y, topk_ids, T, k, E, H, out);
+                     stream, y, topk_ids, T, k, E, H, slices, out);
   return hipGetLastError();
 }
 

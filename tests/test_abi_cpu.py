@@ -258,3 +258,33 @@ def test_noalloc_forward_rejects_plans_beyond_its_scratch(lib):
     st = lib.moe_w4a16_forward_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 32, 7169, I, E,
                                        k, 0, FAKE, None)
     assert st == UNSUPPORTED
+
+
+@pytest.mark.parametrize("T,H,I,E,k,slices", [
+    (8192, 7168, 2048, 48, 8, 1),   # the prefill layer fills the GPU: no split
+    (1024, 7168, 2048, 4, 2, 1),    # 224 down tiles: no split
+    (1024, 7168, 2048, 2, 1, 1),    # 2 x 512 rows, counted high: 3 tiles each, 2 slices spill
+    (512, 7168, 2048, 2, 2, 2),     # top-2 of 2 experts: exactly 512 rows each, 2 slices
+    (128, 7168, 2048, 1, 1, 8),     # 28 down tiles: 8 slices
+    (96, 7168, 2048, 4, 2, 2),      # 48 rows per expert, 128-row tiles: 112 tiles, 2 slices
+    (300, 1024, 1024, 2, 1, 4),     # 8 down tiles, K = 1024 (4 blocks): 4 slices
+    (300, 1024, 2048, 2, 1, 8),     # 8 slices
+    (200, 1024, 1024, 3, 2, 4),
+    (160, 512, 512, 1, 1, 2),
+    (600, 512, 256, 4, 2, 1),       # K = 256: one block, nothing to split
+])
+def test_split_k_plan(T, H, I, E, k, slices):
+    regions = binding.workspace_regions(binding.FORMAT_W4A16, T, H, I, E, k,
+                                        binding.SCHEDULE_PREFILL)
+    assert regions["y"][1] == slices * 4 * T * k * H
+
+
+def test_tile_kernels_limited_to_32_bit_weight_offsets():
+    # one expert's weights must stay below 2^31 bytes of codes for the tile kernels' buffer
+    # resources; at I * H = 2^31 the prefill schedule runs on the stream kernels instead
+    big = binding.workspace_regions(binding.FORMAT_W4A16, 64, 65536, 32768, 4, 2,
+                                    binding.SCHEDULE_PREFILL)
+    assert "out32" in big and "y" not in big
+    ok = binding.workspace_regions(binding.FORMAT_W4A16, 64, 65536, 16384, 4, 2,
+                                   binding.SCHEDULE_PREFILL)
+    assert "y" in ok

@@ -104,3 +104,13 @@ def test_mxfp4_empty_batch():
         out = binding.moe_mxfp4_forward(x, d["w13"], d["s13"], d["w2"], d["s2"], ids, w,
                                         schedule=schedule)
         assert out.shape == (0, 256)
+
+
+def test_mxfp4_prefill_split_k(oracle_mod):
+    # two experts: the down tiles split K into four slices summed by the combine pass
+    print("[mxfp4] split-K", flush=True)
+    c = inputs.custom_mxfp4_case(300, 1024, 1024, 2, 2, seed=77)
+    d = to_dev(c)
+    out = binding.moe_mxfp4_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"], d["topk_weights"], schedule=binding.SCHEDULE_PREFILL)
+    torch.cuda.synchronize()
+    assert report("mxfp4 split-K", bf16_out_to_f64(out), oracle_mod.mxfp4_moe(c["x"], c["w13"], c["s13"], c["w2"], c["s2"], c["topk_ids"], c["topk_weights"])).max() <= TOL

@@ -98,3 +98,13 @@ def test_nvfp4_empty_batch():
         out = binding.moe_nvfp4_forward(x, d["w13"], d["s13"], d["g13"], d["w2"], d["s2"], d["g2"],
                                         ids, w, schedule=schedule)
         assert out.shape == (0, 256)
+
+
+def test_nvfp4_prefill_split_k(oracle_mod):
+    # two experts: the down tiles split K into four slices summed by the combine pass
+    print("[nvfp4] split-K", flush=True)
+    c = inputs.custom_nvfp4_case(300, 1024, 1024, 2, 2, seed=78)
+    d = to_dev(c)
+    out = binding.moe_nvfp4_forward(d["x"], d["w13"], d["s13"], d["g13"], d["w2"], d["s2"], d["g2"], d["topk_ids"], d["topk_weights"], schedule=binding.SCHEDULE_PREFILL)
+    torch.cuda.synchronize()
+    assert report("nvfp4 split-K", bf16_out_to_f64(out), oracle_mod.nvfp4_moe(c["x"], c["w13"], c["s13"], c["g13"], c["w2"], c["s2"], c["g2"], c["topk_ids"], c["topk_weights"])).max() <= TOL

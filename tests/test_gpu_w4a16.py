@@ -169,6 +169,25 @@ def test_w4a16_prefill_tiles(oracle_mod, T, H, I, E, k, kind):
     assert report(f"tiles {T}x{H}x{I} E{E}", got, ref).max() <= TOL
 
 
+# Split-K of the down GEMM: few experts leave the down tiles far from filling the GPU, so
+# the plan splits each tile's K (I / 256 blocks) into slices whose partial rows the combine
+# pass sums (the slice count each shape gets is pinned in test_abi_cpu.py).
+@pytest.mark.parametrize("T,H,I,E,k,kind", [
+    (300, 1024, 1024, 2, 1, "uniform"),   # 4 slices
+    (300, 1024, 2048, 2, 1, "uniform"),   # 8 slices
+    (200, 1024, 1024, 3, 2, "zipf"),      # 4 slices, skewed, two pairs per token
+    (160, 512, 512, 1, 1, "uniform"),     # 2 slices, one expert
+])
+def test_w4a16_prefill_split_k(oracle_mod, T, H, I, E, k, kind):
+    print(f"[w4a16] split-K T={T} H={H} I={I} E={E} k={k} {kind}", flush=True)
+    case = inputs.custom_w4a16_case(T, H, I, E, k, seed=T * 5 + I, kind=kind)
+    case["topk_ids"][::9, -1] = -1  # dropped slots
+    got = _forward(case, binding.SCHEDULE_PREFILL)
+    ref = _oracle(oracle_mod, case, None)
+    assert report(f"split-K {T}x{H}x{I} E{E}", got, ref).max() <= TOL
+    assert np.array_equal(got, _forward(case, binding.SCHEDULE_PREFILL))  # deterministic
+
+
 def test_w4a16_prefill_tiles_deterministic():
     case = inputs.custom_w4a16_case(600, 512, 256, 4, 2, seed=11)
     a = _forward(case, binding.SCHEDULE_PREFILL)
