@@ -20,3 +20,16 @@ def oracle_mod():
 
     oracle._load()
     return oracle
+
+
+def pytest_sessionstart(session):
+    # Sanitizer runs (tests/test_sanitizers_cpu.py) point the tests at instrumented builds
+    # of the library and the oracle through these variables; unset, the in-tree builds load.
+    lib = os.environ.get("QMOE_TEST_LIBRARY")
+    if lib:
+        from quantized_mixture_experts_amd import binding
+        binding.LIB_PATH = lib
+    olib = os.environ.get("QMOE_TEST_ORACLE_LIBRARY")
+    if olib:
+        import oracle
+        oracle._LIB_PATH = olib
