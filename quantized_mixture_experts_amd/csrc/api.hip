@@ -325,7 +325,7 @@ qmoe_status w4a16_after_align(const Plan& p, const uint16_t* x, const uint8_t* w
     if (err != hipSuccess) return hip_fail(err, "down launch");
     if (!direct_out) {
       err = staged(QMOE_STAGE_CAST, s, [&] {
-        return launch_combine_rows(y, topk_ids, T, k, E, H, out, s, p.kslices);
+        return launch_combine_rows(y, topk_ids, topk_weights, T, k, E, H, out, s, p.kslices);
       });
       if (err != hipSuccess) return hip_fail(err, "combine launch");
     }
@@ -746,7 +746,7 @@ qmoe_status moe_fp8_block_forward(const uint8_t* a_q, const float* a_scale, cons
     err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_fp8_down_tiled(prob, r, y, s); });
     if (err != hipSuccess) return hip_fail(err, "down launch");
     err = staged(QMOE_STAGE_CAST, s, [&] {
-      return launch_combine_rows(y, topk_ids, T, k, E, H, out, s);
+      return launch_combine_rows(y, topk_ids, nullptr, T, k, E, H, out, s);
     });
     if (err != hipSuccess) return hip_fail(err, "combine launch");
     return QMOE_OK;

@@ -219,6 +219,13 @@ __device__ __forceinline__ int xcd_major_item(int block, int grid, int items) {
   return item < items ? item : -1;
 }
 
+// A read of data that no launch in flight writes, through the constant address space so
+// that a uniform index becomes a scalar load: a vector load would enter the in-order
+// vector memory counter, and waiting for it would also wait for outstanding prefetches.
+__device__ __forceinline__ int32_t ld_invariant(const int32_t* p, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 // With the accurate exponential: for h that is requantized to E4M3 (a step function),
 // where the fast exponential's ~1e-6 relative error flips codes measurably often.

@@ -9,9 +9,9 @@
 // families").
 //
 // gfx950 mapping. A work-group owns one (128-row tile of an expert segment, 256 weight
-// rows) output tile; its four waves each own the 128 rows and 64 weight rows: 8 x 4
-// MFMA tiles, 128 fp32 accumulators per lane, kept in VGPRs because every 128-deep block
-// is promoted with a VALU multiply-add:
+// rows) output tile; its eight waves, two per SIMD, each own 64 rows and 64 weight rows:
+// 4 x 4 MFMA tiles, 64 fp32 accumulators per lane, kept in VGPRs because every 128-deep
+// block is promoted with a VALU multiply-add:
 //   * one v_mfma_scale_f32_16x16x128_f8f6f4 (block scales pinned to 1.0) is one k block;
 //     its fp32 result d is added as acc += d * (As[row] * Bs), the scales being general
 //     fp32 values (a power-of-two block scale cannot carry them);

@@ -107,17 +107,20 @@ bool w4a16_stream_zeroes_output(int32_t H);
 bool w4a16_stream_reads_rows(int32_t H, int mb);
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
                                     hipStream_t stream);
+// Work-groups of a persistent launch: one per compute unit, a multiple of the XCD count.
+int persistent_grid();
 // Prefill profile (W4A16 / MXFP4): row tiles of each expert segment on the matrix
 // cores, 256 rows, or 128 when the experts hold few rows (w4a16_tiled_rows). Needs H and
 // I multiples of 256; align must have produced tile_offsets for tiles of tile_rows rows.
-// down writes y[P, H] (routing-weighted fp32 row per pair) and launch_combine_rows sums
-// each token's top-k rows into the bf16 output.
+// down writes y[P, H] (fp32 row per pair, not yet weighted) and launch_combine_rows sums
+// each token's top-k rows, times their routing weights, into the bf16 output.
 bool w4a16_tiled_supported(int32_t H, int32_t I);
 int32_t w4a16_tiled_rows(double rows_per_expert);
 hipError_t launch_w4a16_gateup_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
                                      hipStream_t stream);
-// out16 != null (one pair per row, k = 1): down writes bf16(w * row) straight into the
-// output row of each pair instead of fp32 rows into y, so no combine pass is needed.
+// out16 != null (one pair per row, k = 1, routing weights 1): down writes bf16(row)
+// straight into the output row of each pair instead of fp32 rows into y, so no combine
+// pass is needed.
 // kslices > 1 (split-K): each output tile's K is split into that many slices (it must
 // divide I / 256), slice q writing its partial rows to y + q * P * H (y is [kslices, P, H]).
 hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int tile_rows,
@@ -125,9 +128,11 @@ hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int 
                                    int kslices = 1);
 // out[t] = bf16 of the sum over the K slices (in order) of the sums over token t's valid
 // slots (in order) of the rows of y ([slices, T*k, H]).
-hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,
-                               int32_t E, int32_t H, uint16_t* out, hipStream_t stream,
-                               int32_t slices = 1);
+// wts: the routing weights [T * k] to apply to the rows of y, or null when y's rows are
+// already weighted.
+hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, const float* wts,
+                               int32_t T, int32_t k, int32_t E, int32_t H, uint16_t* out,
+                               hipStream_t stream, int32_t slices = 1);
 
 // Prefill profile (block FP8): 128-row tiles; needs H % 256 == 0 and I % 128 == 0 and
 // at most 64 k blocks; align must have produced tile_offsets for fp8_tiled_rows() rows.

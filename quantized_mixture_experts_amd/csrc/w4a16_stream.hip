@@ -440,13 +440,6 @@ struct Unit {
   int rb, cc, kc, e;  // row block (16 MB rows), column chunk, unit within the item's K, expert
 };
 
-// A read of data that no launch in flight writes, through the constant address space so
-// that a uniform index becomes a scalar load: a vector load would enter the in-order
-// vector memory counter, and waiting for it would also wait for the weight prefetches.
-__device__ __forceinline__ int32_t ld_invariant(const int32_t* p, int i) {
-  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
-}
-
 // MB: 16-row MFMA blocks per row block (align pads every expert's segment to 16 MB
 // rows, so a row block never spans two experts). Each dequantized weight operand feeds
 // the MFMAs of all MB blocks, so a pass over the weights serves 16 MB rows.
@@ -935,7 +928,9 @@ __global__ void __launch_bounds__(kGatherThreads)
   }
 }
 
-// One work-group per compute unit (the persistent kernel's resources allow no second),
+}  // namespace
+
+// One work-group per compute unit (the persistent kernels' resources allow no second),
 // rounded down to a multiple of the XCD count; queried once per device.
 int persistent_grid() {
   static std::atomic<int> cached[64];
@@ -951,6 +946,8 @@ int persistent_grid() {
   }
   return n;
 }
+
+namespace {
 
 template <Epi EPI, bool MX, bool NV, bool DX>
 void launch_persist(const StreamArgs& args, int mb, hipStream_t stream) {

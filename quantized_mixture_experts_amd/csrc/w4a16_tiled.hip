@@ -9,8 +9,10 @@
 // kernel is laid out for the matrix cores.
 //
 // gfx950 mapping. A work-group owns one (row tile of an expert segment, 256 weight rows)
-// output tile over eight waves, two per SIMD; the row tile is 256 rows, or 128 when the
-// experts hold few rows. Each wave owns all the tile's rows and 32 weight rows (two
+// output tile at a time over eight waves, two per SIMD; the row tile is 256 rows, or 128
+// when the experts hold few rows. The launch is persistent (one work-group per compute
+// unit, a static XCD-major deal of the tiles): the copy pipeline runs on from one tile
+// into the next, so a tile's start and its epilogue do not wait for a pipeline refill. Each wave owns all the tile's rows and 32 weight rows (two
 // 16-column MFMA tiles), so every weight element is dequantized exactly once per tile and
 // reused for 16 (or 8) row blocks:
 //   * activation rows (bf16, tiled layout: the operand of one 16-row block and k group
@@ -66,9 +68,11 @@ struct Tile {
   static constexpr int kWBase = kStages * kRowBlocks * kWave;
   static constexpr int kSBase = kWBase + kWaves * 2 * kColTiles * kWave;
   static constexpr int kEBase = kSBase + kWaves * kColTiles * 16;
-  // down: the pair id of each of the tile's rows, copied at the start of the item so the
-  // epilogue needs one round trip (the routing weights) instead of two per row block.
-  static constexpr int kSmemUnits = kEBase + TR / 4;
+  // down: the pair id of each of the tile's rows, in two buffers (the current item's, and
+  // the next one's, copied while the current item runs), so the epilogue needs one round
+  // trip (the routing weights) instead of two per row block.
+  static constexpr int kIdUnits = TR / 4;
+  static constexpr int kSmemUnits = kEBase + 2 * kIdUnits;
   static_assert(kRowBlocks == kPieces || kRowBlocks == 2 * kPieces,
                 "a dequantized piece spans one or two row blocks");
   static_assert(kCopiesPerWave >= 1 && kRowBlocks % kWaves == 0, "copies per wave");
@@ -102,12 +106,13 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-// Largest e with toff[e] <= m, for 0 <= m < toff[E] (skips empty experts).
+// Largest e with toff[e] <= m, for 0 <= m < toff[E] (skips empty experts). Scalar
+// loads: toff is written by an earlier launch.
 __device__ __forceinline__ int expert_of_tile(const int32_t* toff, int E, int m) {
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (toff[mid] <= m) lo = mid;
+    if (ld_invariant(toff, mid) <= m) lo = mid;
     else hi = mid;
   }
   return lo;
@@ -155,7 +160,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   //   activation ring [stage][row block][lane], TR / 16 KB per k group;
   //   per wave, the two half blocks of weight words [half][tile][lane];
   //   per wave, the block's scales [tile][row] (16 B = eight groups per weight row).
-  //   down: the tile rows' pair ids (1 KB).
+  //   down: two buffers of the tile rows' pair ids (TR * 4 B each).
   // A single object also keeps the compiler from adding conservative waits between the
   // asynchronous copies and the reads of other staging areas.
   __shared__ u32x4 smem[kSmemUnits];
@@ -169,29 +174,26 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = lane & 15, quad = lane >> 4;
 
-  // XCD-aware item order over the real tile count: XCD x takes a contiguous range. An
-  // item is (row tile, column tile, K slice); with a.kslices > 1 (split-K, down only) the
-  // slices of an output tile are neighbours.
-  const int total = a.tile_offsets[a.E] * a.col_tiles * a.kslices;
+  // Persistent schedule. The grid is at most one work-group per compute unit; the items
+  // (row tile, column tile, K slice; with a.kslices > 1, split-K for down, the slices of
+  // an output tile are neighbours) are dealt XCD-major: XCD x owns the contiguous range
+  // [x per, (x + 1) per), and its wpx work-groups take every wpx-th item of it, so the
+  // items that run at once on one XCD are neighbours sharing activation rows in its L2.
+  const int total = ld_invariant(a.tile_offsets, a.E) * a.col_tiles * a.kslices;
+  const int wpx = gridDim.x / kNumXcd;
+  const int xcd = blockIdx.x % kNumXcd;
   const int per = (total + kNumXcd - 1) / kNumXcd;
-  const int xi = blockIdx.x / kNumXcd;
-  const int item_k = (blockIdx.x % kNumXcd) * per + xi;
-  if (xi >= per || item_k >= total) return;
-  const int item = item_k / a.kslices, slice = item_k - item * a.kslices;
-  const int rtile = item / a.col_tiles, ctile = item % a.col_tiles;
-  const int e = expert_of_tile(a.tile_offsets, a.E, rtile);
-  const int seg1 = a.offsets[e + 1];
-  const int row0 = a.offsets[e] + (rtile - a.tile_offsets[e]) * kTileRows;
-  const int rb0 = row0 >> 4;
-  const int rb_last = (seg1 >> 4) - 1;
+  const int iend = min(total, (xcd + 1) * per);
+  int item_k = xcd * per + blockIdx.x / kNumXcd;
+  if (item_k >= iend) return;
   const int K = a.K, KG = K >> 5;
-  // This item's 256-deep weight blocks: all of K, or its slice. Offsets below keep the
+  // An item's 256-deep weight blocks: all of K, or its slice. Offsets below keep the
   // full-K strides and start at the slice's first block; the loop runs over the slice.
-  const int nblocks = (K >> 8) / a.kslices, kb_first = slice * nblocks;
+  const int nblocks = (K >> 8) / a.kslices;
   const int nsteps = nblocks * kGroupsPerBlock;
 
-  // Weight row of tile t for column c of this wave.
-  auto weight_row = [&](int t, int c) {
+  // Weight row of tile t for column c of this wave in column tile ctile.
+  auto weight_row = [&](int ctile, int t, int c) {
     if constexpr (EPI == TEpi::GateUp) {
       const int j = ctile * 128 + wave * (kColTiles * 8) + (t % (kColTiles / 2)) * 16 + c;
       return (t < kColTiles / 2) ? j : a.I + j;
@@ -199,68 +201,122 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
       return ctile * 256 + wave * (kColTiles * 16) + t * 16 + c;
     }
   };
-  // Per-lane byte offsets stay 32-bit (host-checked) on top of uniform bases. Weight
-  // words: lane (col, quad) takes 16 B of row col at quarter `quad` of a 64 B half line.
-  // Scales: lane l takes word l % 4 of the 16 B (eight groups) of row l / 4. MXFP4
-  // scales are one byte per group: the block's eight are words 0 and 1 of the 16 B
-  // window (words 2 and 3 hold the next block's, or zeros past the buffer, unused).
+  // Byte offsets stay 32-bit (host-checked). Weight words: lane (col, quad) takes 16 B of
+  // row col at quarter `quad` of a 64 B half line. Scales: lane l takes word l % 4 of the
+  // 16 B (eight groups) of row l / 4. MXFP4 scales are one byte per group: the block's
+  // eight are words 0 and 1 of the 16 B window (words 2 and 3 hold the next block's, or
+  // zeros past the buffer, unused). A copy's vector offset is a fixed per-lane part plus
+  // its item's uniform part (the buffer's range check covers both); the scalar offset
+  // is the step's position within the item.
   constexpr uint32_t kScaleBytes = (MX && !NV) ? 1u : 2u;
-  const float gsc = NV ? a.g[e] : 1.f;    // NVFP4: the expert's global scale
   const int hsh = NV ? 8 * (quad >> 1) : 0;  // NVFP4: byte of this lane's 16-k half
-  const uint8_t* wbase = a.w + (size_t)e * a.N * (size_t)(K >> 1);
-  const uint8_t* sbase =
-      reinterpret_cast<const uint8_t*>(a.s) + (size_t)e * a.N * (size_t)KG * kScaleBytes;
-  uint32_t woff[kColTiles], soff[kColTiles];
-#pragma unroll
-  for (int t = 0; t < kColTiles; ++t) {
-    woff[t] = (uint32_t)weight_row(t, col) * (uint32_t)(K >> 1) + 16u * quad +
-              (uint32_t)kb_first * 128u;
-    soff[t] = (uint32_t)weight_row(t, lane >> 2) * (uint32_t)KG * kScaleBytes + 4u * (lane & 3) +
-              (uint32_t)kb_first * kGroupsPerBlock * kScaleBytes;
-  }
+  const uint32_t a_lane = (uint32_t)lane * 16u;
+  const uint32_t w_lane = (uint32_t)col * (uint32_t)(K >> 1) + 16u * quad;
+  const uint32_t s_lane = (uint32_t)(lane >> 2) * (uint32_t)KG * kScaleBytes + 4u * (lane & 3);
+  const __amdgpu_buffer_rsrc_t ars =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, kRsrcWord3);
 
-  // Activation copies of this wave: row blocks wave*kCopiesPerWave + i of the tile.
-  uint32_t aoff[kCopiesPerWave];
+  // What the copies need of an item: the uniform parts of their offsets (weight tile 1
+  // lies a fixed distance past tile 0: I rows for gate_up, 16 for down) and its expert's
+  // weight and scale buffers. What the epilogue needs of the current item: Rows.
+  const uint32_t tile1_rows = EPI == TEpi::GateUp ? (uint32_t)a.I : 16u;
+  const uint32_t w_tile1 = tile1_rows * (uint32_t)(K >> 1);
+  const uint32_t s_tile1 = tile1_rows * (uint32_t)KG * kScaleBytes;
+  struct Src {
+    uint32_t abase[kCopiesPerWave], wbase, sbase;
+    const uint8_t* wb;  // the expert's weight words and scales
+    const uint8_t* sb;
+    float gsc;  // NVFP4: the expert's global scale
+  };
+  const int w_records = (int)((uint32_t)a.N * (uint32_t)(K >> 1));
+  const int s_records = (int)((uint32_t)a.N * (uint32_t)KG * kScaleBytes);
+  struct Rows {
+    int row0, rb_last, ctile, slice;
+  };
+  auto item_rows = [&](int ik, int& e) {
+    Rows it;
+    const int item = ik / a.kslices;
+    it.slice = ik - item * a.kslices;
+    const int rtile = item / a.col_tiles;
+    it.ctile = item - rtile * a.col_tiles;
+    e = expert_of_tile(a.tile_offsets, a.E, rtile);
+    it.row0 = ld_invariant(a.offsets, e) + (rtile - ld_invariant(a.tile_offsets, e)) * kTileRows;
+    it.rb_last = (ld_invariant(a.offsets, e + 1) >> 4) - 1;
+    return it;
+  };
+  auto item_src = [&](const Rows& it, int e) {
+    Src c;
+    const uint32_t kb_first = (uint32_t)(it.slice * nblocks);
 #pragma unroll
-  for (int i = 0; i < kCopiesPerWave; ++i) {
-    const int rb = min(rb0 + wave * kCopiesPerWave + i, rb_last);
-    aoff[i] = (uint32_t)rb * (uint32_t)(KG * 1024) + lane * 16u +
-              (uint32_t)kb_first * kGroupsPerBlock * 1024u;
+    for (int i = 0; i < kCopiesPerWave; ++i) {
+      const int rb = min((it.row0 >> 4) + wave * kCopiesPerWave + i, it.rb_last);
+      c.abase[i] = (uint32_t)rb * (uint32_t)(KG * 1024) + kb_first * kGroupsPerBlock * 1024u;
+    }
+    const uint32_t wr = (uint32_t)weight_row(it.ctile, 0, 0);
+    c.wbase = wr * (uint32_t)(K >> 1) + kb_first * 128u;
+    c.sbase = wr * (uint32_t)KG * kScaleBytes + kb_first * kGroupsPerBlock * kScaleBytes;
+    c.wb = a.w + (size_t)e * a.N * (size_t)(K >> 1);
+    c.sb = reinterpret_cast<const uint8_t*>(a.s) + (size_t)e * a.N * (size_t)KG * kScaleBytes;
+    c.gsc = 1.f;
+    if constexpr (NV)
+      c.gsc = __builtin_bit_cast(float, ld_invariant(reinterpret_cast<const int32_t*>(a.g), e));
+    return c;
+  };
+  // cur: the item being computed; nrows / nsrc: the next one of this work-group. The
+  // copies read from cp: cur's source until step 1 of cur's last block, from there on
+  // (the first copy of a group or block past cur's end) the next item's, with goff and
+  // boff the group and block that item starts at in cur's numbering. Without a next item
+  // cp stays and the copies past the end repeat cur's last group and block.
+  int e_cur = 0, e_nxt = 0;
+  Rows cur = item_rows(item_k, e_cur);
+  Src cp = item_src(cur, e_cur);
+  float gsc_cur = cp.gsc;
+  int goff = 0, boff = 0;
+  bool has_next = item_k + wpx < iend;
+  Rows nrows = cur;
+  Src nsrc = cp;
+  if (has_next) {
+    nrows = item_rows(item_k + wpx, e_nxt);
+    nsrc = item_src(nrows, e_nxt);
   }
 
   // All global reads of the loop are asynchronous LDS copies whose completion this code
-  // tracks itself with vmcnt (the compiler does not count them). They are issued in a
-  // fixed order and never skipped: past the end they repeat the last group or block, so
-  // the counts below hold at the tail as well. Per 8-group block and wave: kCopiesPerWave
-  // activation copies every step, the next block's first half of weight words and its
-  // scales at j = 1 (2 kColTiles), its second half at j = 5 (kColTiles).
-  // Copies are buffer loads into LDS: the loop-invariant per-lane offset is the vector
-  // offset and the step's byte offset the scalar one, so a copy needs no vector address
-  // arithmetic. Reads past a buffer's size return zeros.
-  const __amdgpu_buffer_rsrc_t ars =
-      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)wbase, (short)0, (int)((uint32_t)a.N * (uint32_t)(K >> 1)), kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)sbase, (short)0, (int)((uint32_t)a.N * (uint32_t)KG * kScaleBytes), kRsrcWord3);
-  auto copy_act = [&](int g, int st, int i) {
+  // tracks itself with vmcnt (the compiler does not count these). They are issued in a
+  // fixed order and never skipped, so the counts below hold at every step: past the end
+  // of an item they fetch the next item's first groups and weight block, or, after the
+  // work-group's last item, repeat the last group or block. Per 8-group block and wave:
+  // kCopiesPerWave activation copies every step, the next block's first half of weight
+  // words and its scales at j = 1 (2 kColTiles), its second half at j = 5 (kColTiles).
+  // Anything else issued between them (the epilogue's stores and loads, the next item's
+  // pair ids) is younger than the copies a later wait counts on; since loads complete in
+  // issue order, it can only make such a wait wait longer, never too little. Reads past a
+  // buffer's size return zeros.
+  // Activation group gg of cur's numbering (gg >= nsteps: the next item's).
+  auto copy_act = [&](int gg, int st_, int i) {
+    const int gl = min(gg - goff, nsteps - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        ars, (__attribute__((address_space(3))) void*)a_at(st, wave * kCopiesPerWave + i), 16,
-        (int)aoff[i], min(g, nsteps - 1) * 1024, 0, 0);
+        ars, (__attribute__((address_space(3))) void*)a_at(st_, wave * kCopiesPerWave + i), 16,
+        (int)(a_lane + cp.abase[i]), gl * 1024, 0, 0);
   };
+  // Weight words and scales of block kb of cur's numbering (kb >= nblocks: the next
+  // item's).
   auto copy_words = [&](int kb, int hf, int t) {
+    const int kl = min(kb - boff, nblocks - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        wrs, (__attribute__((address_space(3))) void*)w_at(wave, hf, t), 16, (int)woff[t],
-        min(kb, nblocks - 1) * 128 + 64 * hf, 0, 0);
+        __builtin_amdgcn_make_buffer_rsrc((void*)cp.wb, (short)0, w_records, kRsrcWord3),
+        (__attribute__((address_space(3))) void*)w_at(wave, hf, t), 16,
+        (int)(w_lane + cp.wbase + (t ? w_tile1 : 0u)), kl * 128 + 64 * hf, 0, 0);
   };
   auto copy_scale = [&](int kb, int t) {
+    const int kl = min(kb - boff, nblocks - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        srs, (__attribute__((address_space(3))) void*)s_at(wave, t), 4, (int)soff[t],
-        min(kb, nblocks - 1) * 8 * (int)kScaleBytes, 0, 0);
+        __builtin_amdgcn_make_buffer_rsrc((void*)cp.sb, (short)0, s_records, kRsrcWord3),
+        (__attribute__((address_space(3))) void*)s_at(wave, t), 4,
+        (int)(s_lane + cp.sbase + (t ? s_tile1 : 0u)), kl * 8 * (int)kScaleBytes, 0, 0);
   };
-  auto copy_group = [&](int g, int st) {
+  auto copy_group = [&](int g, int st_) {
 #pragma unroll
-    for (int i = 0; i < kCopiesPerWave; ++i) copy_act(g, st, i);
+    for (int i = 0; i < kCopiesPerWave; ++i) copy_act(g, st_, i);
   };
   auto copy_half = [&](int kb, int hf) {
 #pragma unroll
@@ -269,6 +325,18 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   auto copy_scales = [&](int kb) {
 #pragma unroll
     for (int t = 0; t < kColTiles; ++t) copy_scale(kb, t);
+  };
+  // down: the pair ids of an item's rows (row0 + 64 wave + lane, clamped into the segment;
+  // rows past it are not stored) into id buffer buf, by the first TR / 64 waves.
+  auto copy_ids = [&](const Rows& it, int buf) {
+    if (EPI == TEpi::Down && wave < kTileRows / kWave) {
+      const int r = min(it.row0 + wave * kWave + lane, it.rb_last * 16 + 15);
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(a.sorted_ids + r),
+          (__attribute__((address_space(3))) void*)&smem[kEBase + buf * Tile<TR>::kIdUnits +
+                                                         wave * (kWave / 4)],
+          4, 0, 0);
+    }
   };
 
   f32x4 acc[kRowBlocks][kColTiles];
@@ -319,16 +387,11 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // first half of weight words and its scales (2 kColTiles), at j = 5 its second half
   // (kColTiles). The staged words are read into registers one step before use (j = 2:
   // second half of this block; j = 6: first half and scales of the next block). The
-  // prologue issues the same sequence for the steps before group 0.
-  if (EPI == TEpi::Down && wave < kTileRows / kWave) {
-    // Pair ids of rows row0 + 64 wave + lane (clamped into the segment; rows past it
-    // are not stored), by the first four waves. Older than every copy below, so the
-    // waits below cover it.
-    const int r = min(row0 + wave * kWave + lane, rb_last * 16 + 15);
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(a.sorted_ids + r),
-        (__attribute__((address_space(3))) void*)&smem[kEBase + wave * (kWave / 4)], 4, 0, 0);
-  }
+  // prologue issues the same sequence for the steps before group 0 of the work-group's
+  // first item; a later item's first groups and block come from the previous item's
+  // last steps.
+  // The first item's pair ids: older than every copy below, so the waits below cover it.
+  copy_ids(cur, 0);
   copy_group(0, 0);  // step -7 (j = 1)
   copy_half(0, 0);
   copy_scales(0);
@@ -370,7 +433,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   for (int p = 0; p < kPieces; ++p) {
     const int t = p >> 2, i = p & 3;
     if constexpr (NV) {
-      bq[0][t][i] = nvfp4_pair(tw[t][0], e4m3_low(scur[t][0] >> hsh) * gsc, i);
+      bq[0][t][i] = nvfp4_pair(tw[t][0], e4m3_low(scur[t][0] >> hsh) * gsc_cur, i);
       continue;
     } else if constexpr (MX) {
       bq[0][t][i] = fp4_pair(tw[t][0], e8m0_scale(scur[t][0]), i);
@@ -384,12 +447,23 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
     bq[0][t][i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
   }
 
-  int st = 0;  // stage of group g
+  int st = 0;    // stage of group g
+  int ibuf = 0;  // id buffer of cur
+  for (;;) {
   for (int kb = 0; kb < nblocks; ++kb) {
     auto step = [&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const int g = kb * kGroupsPerBlock + j;
       const int jn = (j + 1) & 7;
+      // From step 1 of the last block on, the copies fetch the next item's data.
+      if (j == 1 && kb == nblocks - 1 && has_next) {
+        cp = nsrc;
+        goff = nsteps;
+        boff = nblocks;
+      }
+      // NVFP4: the global scale of the item whose group jn this step dequantizes (the
+      // last step of an item dequantizes the next item's group 0).
+      const float gsc = (j == 7 && kb == nblocks - 1) ? cp.gsc : gsc_cur;
       // Operand registers written by VALU instructions at the end of the last step.
       asm volatile("s_nop 1");
       if (j == 3) {
@@ -509,6 +583,9 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
           wait_vmcnt<kLater + kPrev>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
+          // After the item's first barrier every wave has finished the previous item's
+          // epilogue, which read the id buffer that the next item's pair ids go to.
+          if (j == 0 && kb == 0 && has_next) copy_ids(nrows, ibuf ^ 1);
           // (This step's copies follow, spread over the next MFMAs.)
           if (j == 2) {
             // Second half of this block (copied at j = 5 of the last block): younger
@@ -539,21 +616,20 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
     step(std::integral_constant<int, 6>{});
     step(std::integral_constant<int, 7>{});
   }
-  // No copy may still be landing in LDS when the work-group's LDS is released.
-  wait_vmcnt<0>();
   // The matrix-core results must be settled before ordinary instructions read them.
   drain_acc(acc);
 
-  // Epilogue. Lane (col, quad) holds rows 4*quad + r of each 16-row block, column col.
+  // Epilogue of cur. Lane (col, quad) holds rows 4*quad + r of each 16-row block, column
+  // col.
   if constexpr (EPI == TEpi::GateUp) {
 #pragma unroll
     for (int m = 0; m < kRowBlocks; ++m) {
-      const int rb = rb0 + m;
-      if (rb > rb_last) break;
+      const int rb = (cur.row0 >> 4) + m;
+      if (rb > cur.rb_last) break;
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tp = 0; tp < kColTiles / 2; ++tp) {
-        const int j = ctile * 128 + wave * (kColTiles * 8) + tp * 16 + col;
+        const int j = cur.ctile * 128 + wave * (kColTiles * 8) + tp * 16 + col;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float gv = acc[m][tp][r], uv = acc[m][tp + kColTiles / 2][r];
@@ -562,62 +638,81 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
       }
     }
   } else {
-    // Pair ids from LDS, then the routing weights of eight row blocks requested before
-    // any is used (two round trips per tile instead of one per row block).
-    const int* ep = reinterpret_cast<const int*>(&smem[kEBase]);
+    // Rows of the pairs (ids from LDS, four row blocks per read batch), unweighted: the
+    // combine applies the routing weights, so the epilogue makes no global reads.
+    const int* ep = reinterpret_cast<const int*>(&smem[kEBase + ibuf * Tile<TR>::kIdUnits]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      int pair[kRowBlocks / 2][4];
-      float wt[kRowBlocks / 2][4];
+    for (int m0 = 0; m0 < kRowBlocks; m0 += 4) {
+      if ((cur.row0 >> 4) + m0 > cur.rb_last) break;
+      u32x4 pv[4];
 #pragma unroll
-      for (int mm = 0; mm < kRowBlocks / 2; ++mm) {
-        const u32x4 v =
-            *reinterpret_cast<const u32x4*>(ep + (h * (kRowBlocks / 2) + mm) * 16 + 4 * quad);
+      for (int mm = 0; mm < 4; ++mm)
+        pv[mm] = *reinterpret_cast<const u32x4*>(ep + (m0 + mm) * 16 + 4 * quad);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pair[mm][r] = (int)v[r];
-      }
+      for (int mm = 0; mm < 4; ++mm) {
+        const int m = m0 + mm;
+        if ((cur.row0 >> 4) + m > cur.rb_last) break;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mm = 0; mm < kRowBlocks / 2; ++mm)
+        for (int r = 0; r < 4; ++r) {
+          const int pair = (int)pv[mm][r];
+          if (pair < a.P) {
+            if (a.out16) {
+              // one pair per row, of routing weight 1: the pair's output row is final
+              uint16_t* orow = a.out16 + (size_t)pair * a.N;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) wt[mm][r] = a.topk_weights[min(pair[mm][r], a.P - 1)];
+              for (int t = 0; t < kColTiles; ++t)
+                orow[weight_row(cur.ctile, t, col)] = f32_to_bf16(acc[m][t][r]);
+            } else {
+              float* yrow = a.y + ((size_t)cur.slice * a.P + pair) * a.N;
 #pragma unroll
-      for (int mm = 0; mm < kRowBlocks / 2; ++mm) {
-        const int m = h * (kRowBlocks / 2) + mm;
-        if (rb0 + m <= rb_last) {
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (pair[mm][r] < a.P) {
-              if (a.out16) {
-                // one pair per row: the pair's output row is final
-                uint16_t* orow = a.out16 + (size_t)pair[mm][r] * a.N;
-#pragma unroll
-                for (int t = 0; t < kColTiles; ++t)
-                  orow[weight_row(t, col)] = f32_to_bf16(wt[mm][r] * acc[m][t][r]);
-              } else {
-                float* yrow = a.y + ((size_t)slice * a.P + pair[mm][r]) * a.N;
-#pragma unroll
-                for (int t = 0; t < kColTiles; ++t)
-                  yrow[weight_row(t, col)] = wt[mm][r] * acc[m][t][r];
-              }
+              for (int t = 0; t < kColTiles; ++t) yrow[weight_row(cur.ctile, t, col)] = acc[m][t][r];
             }
           }
         }
       }
     }
   }
+  if (!has_next) break;
+  // On to the next item: its first groups, block and pair ids are already on their way.
+  item_k += wpx;
+  cur = nrows;
+  gsc_cur = cp.gsc;
+  goff = 0;
+  boff = 0;
+  ibuf ^= 1;
+  has_next = item_k + wpx < iend;
+  if (has_next) {
+    nrows = item_rows(item_k + wpx, e_nxt);
+    nsrc = item_src(nrows, e_nxt);
+  }
+#pragma unroll
+  for (int m = 0; m < kRowBlocks; ++m)
+#pragma unroll
+    for (int t = 0; t < kColTiles; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // The next item's first operands, read by the last step, are read again here so that
+  // they hold no registers during the epilogue (st is the stage of its group 0).
+  {
+    const u32x4* as0 = a_at(st, 0) + lane;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ra[0][r] = as0[r * kWave];
+  }
+  }
+  // No copy may still be landing in LDS when the work-group's LDS is released.
+  wait_vmcnt<0>();
 }
 
 // out[t, :] = bf16(sum over the K slices q (in order) of the sum over the valid slots s of
-// token t (in slot order) of y[q, t*k + s, :]). A thread owns 8 columns of one token; the
+// token t (in slot order) of w[t*k + s] * y[q, t*k + s, :]), w the routing weights (or 1
+// when wts is null: rows already weighted). A thread owns 8 columns of one token; the
 // rows of up to kSlotBatch slots of a slice are requested before any is summed.
 constexpr int kCombineThreads = 256;
 constexpr int kSlotBatch = 8;
 
 __global__ void __launch_bounds__(kCombineThreads)
     combine_rows_kernel(const float* __restrict__ y, const int32_t* __restrict__ ids,
-                        int32_t T, int32_t k, int32_t E, int32_t H, int32_t slices,
-                        uint16_t* __restrict__ out) {
+                        const float* __restrict__ wts, int32_t T, int32_t k, int32_t E,
+                        int32_t H, int32_t slices, uint16_t* __restrict__ out) {
   const int64_t slice_stride = (int64_t)T * k * H;
   const int chunks = H >> 3;
   const int64_t items = (int64_t)T * chunks;
@@ -630,12 +725,14 @@ __global__ void __launch_bounds__(kCombineThreads)
       const float* yq = y + q * slice_stride;
       for (int s0 = 0; s0 < k; s0 += kSlotBatch) {
         f32x4 vl[kSlotBatch], vh[kSlotBatch];
+        float wv[kSlotBatch];
         bool ok[kSlotBatch];
 #pragma unroll
         for (int s = 0; s < kSlotBatch; ++s) {
           const int64_t pair = t * k + s0 + s;
           const int id = (s0 + s < k) ? ids[pair] : -1;
           ok[s] = id >= 0 && id < E;
+          wv[s] = (wts && ok[s]) ? wts[pair] : 1.f;
           const float* row = yq + (ok[s] ? pair : 0) * H + c;
           vl[s] = *reinterpret_cast<const f32x4*>(row);
           vh[s] = *reinterpret_cast<const f32x4*>(row + 4);
@@ -643,8 +740,13 @@ __global__ void __launch_bounds__(kCombineThreads)
 #pragma unroll
         for (int s = 0; s < kSlotBatch; ++s) {
           if (ok[s]) {
-            lo += vl[s];
-            hi += vh[s];
+            if (wts) {
+              lo += wv[s] * vl[s];
+              hi += wv[s] * vh[s];
+            } else {
+              lo += vl[s];
+              hi += vh[s];
+            }
           }
         }
       }
@@ -660,7 +762,8 @@ __global__ void __launch_bounds__(kCombineThreads)
 
 template <TEpi EPI, int TR>
 void launch_tiled_rows(const TiledArgs& a, int64_t items, bool mx, bool nv, hipStream_t stream) {
-  const dim3 grid(xcd_major_grid((int)items));
+  // persistent: at most one work-group per compute unit, a multiple of the XCD count
+  const dim3 grid(std::min(xcd_major_grid((int)items), persistent_grid()));
   if (nv)
     hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, true, true, TR>), grid, dim3(kThreads), 0, stream,
                        a);
@@ -718,14 +821,14 @@ hipError_t launch_w4a16_down_tiled(const W4A16Problem& p, const Routing& r, int 
   return launch_tiled<TEpi::Down>(a, r.P, r.E, tile_rows, p.mx, p.nv, stream);
 }
 
-hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, int32_t T, int32_t k,
-                               int32_t E, int32_t H, uint16_t* out, hipStream_t stream,
-                               int32_t slices) {
+hipError_t launch_combine_rows(const float* y, const int32_t* topk_ids, const float* wts,
+                               int32_t T, int32_t k, int32_t E, int32_t H, uint16_t* out,
+                               hipStream_t stream, int32_t slices) {
   const int64_t items = (int64_t)T * (H / 8);
   if (items <= 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((items + kCombineThreads - 1) / kCombineThreads, 16384);
   hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0,
-                     stream, y, topk_ids, T, k, E, H, slices, out);
+                     stream, y, topk_ids, wts, T, k, E, H, slices, out);
   return hipGetLastError();
 }
 
