@@ -365,8 +365,8 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
  *   layout; H (4-bit formats) bf16 [L, I], SiLU(gate) * up in that layout;
  *   H32 (block FP8, decode schedule) fp32 [L, I], SiLU(gate) * up before quantization;
  *   HQ (block FP8) E4M3 codes [L, I] of h, HS (block FP8) fp32 [L, I / 128] scales;
- *   OUT32 fp32 [T, H] (decode schedule); Y fp32 [S, T*k, H] (prefill tiles: one weighted
- *   row per routed pair and K slice; S > 1 when the down GEMM splits K because its output
+ *   OUT32 fp32 [T, H] (decode schedule); Y fp32 [S, T*k, H] (prefill tiles: one row per
+ *   routed pair and K slice, before its routing weight; S > 1 when the down GEMM splits K because its output
  *   tiles would not fill the GPU, S = Y's size / (4 T k H)). Rows at or past
  *   num_tokens_padded, padding rows, and the regions a schedule does not use hold
  *   unspecified values.
@@ -391,11 +391,32 @@ qmoe_status qmoe_workspace_regions(int32_t format, int32_t T, int32_t H, int32_t
                                    int32_t k, int32_t schedule, int64_t* offsets, int64_t* sizes);
 
 /*
+ * qmoe_set_tuning - schedule overrides for tuning and measurement: the per-shape kernel
+ * configuration that a tuning run picks by timing the candidates ("SGLang W8A8 Block FP8
+ * quantization kernel config guide", tuning section; the shape guards of "vLLM x Novita
+ * AI: Chord W4A16 INT4 MoE Kernel for Kimi K2.x", "Kernel optimizations"). Process-wide;
+ * 0 keeps the library's own choice. They apply to every later qmoe_plan,
+ * qmoe_workspace_regions and forward call of the 4-bit formats (W4A16, MXFP4, NVFP4):
+ *   tile_rows      128 or 256: row tile of the prefill tile kernels.
+ *   rows_per_pass  16 or 32: rows per weight pass of the decode kernels (the align block).
+ *   kslices        1, 2, 4, ..., 64: K slices of the prefill down GEMM, used where it
+ *                  divides I / 256 (else 1); the grouped entry points never split K.
+ *   tile_grid      1: one work-group per prefill tile instead of the persistent grid of
+ *                  one work-group per compute unit.
+ * A change between qmoe_plan and the forward it sized changes the workspace that forward
+ * needs: set them before planning, and not while another thread plans or runs a forward.
+ * Invalid values return QMOE_ERR_INVALID_ARG and change nothing. Touches no GPU.
+ */
+qmoe_status qmoe_set_tuning(int32_t tile_rows, int32_t rows_per_pass, int32_t kslices,
+                            int32_t tile_grid);
+
+/*
  * Stage timing (diagnostics and benchmarking). The stages of a forward, in launch
  * order, are QMOE_STAGE_ZERO (clear the fp32 combine buffer), QMOE_STAGE_ALIGN,
  * QMOE_STAGE_GATE_UP (gate_up GEMM + SiLU*up), QMOE_STAGE_REQUANT (block-FP8 only:
- * E4M3 requantization of h), QMOE_STAGE_DOWN (down GEMM + weighted scatter-add) and
- * QMOE_STAGE_CAST (fp32 -> bf16 output).
+ * E4M3 requantization of h), QMOE_STAGE_DOWN (down GEMM; on the decode schedule with the
+ * weighted scatter-add) and QMOE_STAGE_CAST (fp32 -> bf16 output; on the prefill tiles
+ * the routing-weighted sum of each token's top-k rows).
  *
  * qmoe_timing_begin(max_calls): the next max_calls forward calls in this process
  *   record a HIP event pair around each stage's launch, on the forward's stream.

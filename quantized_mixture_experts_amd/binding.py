@@ -73,6 +73,8 @@ def load():
     lib.qmoe_plan.restype = _I32
     lib.qmoe_workspace_regions.argtypes = [_I32] * 7 + [ctypes.POINTER(_I64)] * 2
     lib.qmoe_workspace_regions.restype = _I32
+    lib.qmoe_set_tuning.argtypes = [_I32] * 4
+    lib.qmoe_set_tuning.restype = _I32
     _lib = lib
     return lib
 
@@ -137,6 +139,12 @@ def workspace_regions(fmt, T, H, I, E, k, schedule=SCHEDULE_AUTO):
     _check("qmoe_workspace_regions",
            load().qmoe_workspace_regions(fmt, T, H, I, E, k, schedule, offs, sizes))
     return {name: (offs[i], sizes[i]) for i, name in enumerate(REGIONS) if offs[i] >= 0}
+
+
+def set_tuning(tile_rows=0, rows_per_pass=0, kslices=0, tile_grid=0):
+    """Process-wide schedule overrides of the 4-bit formats (qmoe_set_tuning); 0 keeps the
+    library's choice. Set before planning; set_tuning() restores the defaults. Host only."""
+    _check("qmoe_set_tuning", load().qmoe_set_tuning(tile_rows, rows_per_pass, kslices, tile_grid))
 
 
 def moe_topk_softmax(logits, k, renormalize=True, expert_map=None, stream=None):

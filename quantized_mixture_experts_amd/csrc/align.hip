@@ -25,15 +25,19 @@ namespace qmoe {
 
 namespace {
 
-constexpr int kAlignThreads = 256;
+// 1024 threads: a routed prefill batch (tens of thousands of pairs) takes a few passes of
+// kRun ids per thread, not tens.
+constexpr int kAlignThreads = 1024;
 constexpr int kAlignWaves = kAlignThreads / kWave;
 // Pair ids per thread and pass: all of a pass's loads are in flight at once, so a pass
 // costs one memory latency instead of kRun.
 constexpr int kRun = 16;
 
-// Exclusive scan of v over the work-group; returns this thread's prefix, writes the
-// total to *total. Uses kAlignWaves ints of LDS at `tmp`.
+// Exclusive scan of v over a work-group of NT threads; returns this thread's prefix,
+// writes the total to *total. Uses NT / 64 ints of LDS at `tmp`.
+template <int NT>
 __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  constexpr int kWaves = NT / kWave;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   int incl = v;
 #pragma unroll
@@ -45,7 +49,7 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
   __syncthreads();
   int wave_base = 0, sum = 0;
 #pragma unroll
-  for (int w = 0; w < kAlignWaves; ++w) {
+  for (int w = 0; w < kWaves; ++w) {
     int tw = tmp[w];
     if (w < wave) wave_base += tw;
     sum += tw;
@@ -94,8 +98,8 @@ __global__ void __launch_bounds__(kAlignThreads)
     if (tile_m > 0) my_tiles += (cnt[e] + tile_m - 1) / tile_m;
   }
   int total_rows, total_tiles;
-  int rbase = block_exclusive_scan(my_rows, tmp, &total_rows);
-  int tbase = block_exclusive_scan(my_tiles, tmp, &total_tiles);
+  int rbase = block_exclusive_scan<kAlignThreads>(my_rows, tmp, &total_rows);
+  int tbase = block_exclusive_scan<kAlignThreads>(my_tiles, tmp, &total_tiles);
   for (int e = e0; e < e0 + per && e < E; ++e) {
     off[e] = rbase;
     toff[e] = tbase;
@@ -142,7 +146,7 @@ __global__ void __launch_bounds__(kAlignThreads)
 #pragma unroll
     for (int j = 0; j < kRun; ++j) n += (cur[j] == me);
     int all;
-    int pos = seg0 + running + block_exclusive_scan(n, tmp, &all);
+    int pos = seg0 + running + block_exclusive_scan<kAlignThreads>(n, tmp, &all);
     const int i0 = base + tid * kRun;
 #pragma unroll
     for (int j = 0; j < kRun; ++j)
@@ -163,7 +167,7 @@ __global__ void __launch_bounds__(kAlignThreads)
 // offsets. The same pass writes the routing weight 1 of every row and, when `out` is
 // given, clears the output rows past each count (the prefill tiles write only valid rows).
 constexpr int kMaskedThreads = 256;
-static_assert(kMaskedThreads == kAlignThreads, "block_exclusive_scan assumes kAlignThreads");
+static_assert(kMaskedThreads <= kAlignThreads, "align_lds_bytes sizes the scan's LDS");
 
 __global__ void __launch_bounds__(kMaskedThreads)
     masked_align_kernel(const int32_t* __restrict__ masked_m, int32_t E, int32_t max_m, int32_t B,
@@ -189,8 +193,8 @@ __global__ void __launch_bounds__(kMaskedThreads)
     if (tile_m > 0) my_tiles += (cnt[e] + tile_m - 1) / tile_m;
   }
   int total_rows, total_tiles;
-  int rbase = block_exclusive_scan(my_rows, tmp, &total_rows);
-  int tbase = block_exclusive_scan(my_tiles, tmp, &total_tiles);
+  int rbase = block_exclusive_scan<kMaskedThreads>(my_rows, tmp, &total_rows);
+  int tbase = block_exclusive_scan<kMaskedThreads>(my_tiles, tmp, &total_tiles);
   for (int e = e0; e < e0 + per && e < E; ++e) {
     off[e] = rbase;
     toff[e] = tbase;

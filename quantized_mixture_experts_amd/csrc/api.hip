@@ -2,6 +2,7 @@
 // layout and the launch sequence. Everything here is host code; no call reads a
 // device value back, allocates, frees or synchronizes.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -57,6 +58,9 @@ int decode_mb_for(double) { return 4; }
 double two_block_rows(int fmt) { return fmt == kMxfp4 || fmt == kNvfp4 ? 11.0 : 15.0; }
 
 constexpr size_t kNoRegion = ~size_t(0);
+
+// Schedule overrides of qmoe_set_tuning (0: the library's own choice).
+std::atomic<int32_t> g_tune_tile_rows{0}, g_tune_rows_per_pass{0}, g_tune_kslices{0};
 
 struct Plan {
   int fmt = 0;
@@ -131,6 +135,7 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   auto set_blocks = [&] {
     if (four_bit(fmt)) {
       p.mb = (!p.tiled && tok_e > two_block_rows(fmt)) ? 2 : 1;
+      if (!p.tiled && g_tune_rows_per_pass.load()) p.mb = g_tune_rows_per_pass.load() / kSegRows;
       p.block_m = kSegRows * p.mb;
     } else {
       p.mb = p.schedule == QMOE_SCHEDULE_DECODE ? decode_mb_for(tok_e) : 2;
@@ -140,7 +145,8 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     p.NB = (p.L + p.block_m - 1) / p.block_m;
   };
   set_blocks();
-  if (four_bit(fmt)) p.tile_rows = w4a16_tiled_rows(tok_e);
+  if (four_bit(fmt)) p.tile_rows = g_tune_tile_rows.load() ? g_tune_tile_rows.load()
+                                                           : w4a16_tiled_rows(tok_e);
   // Split-K of the 4-bit prefill down GEMM where its output tiles would not fill the chip
   // ([CHORD] "Kernel optimizations": a shape guard decides when down splits K): the tile
   // kernels hold one work-group per compute unit, so when the expected tiles leave most of
@@ -160,6 +166,8 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     while (p.kslices * 2 <= nblk && nblk % (p.kslices * 2) == 0 &&
            items * p.kslices * 2 <= kPlanComputeUnits)
       p.kslices *= 2;
+    const int32_t ks = g_tune_kslices.load();
+    if (ks) p.kslices = nblk % ks == 0 ? ks : 1;
   }
   // The 4-bit tile kernels address activation rows with 32-bit byte offsets, and one
   // expert's weights (I * H bytes of codes in either GEMM) through a buffer resource whose
@@ -526,6 +534,24 @@ qmoe_status qmoe_plan(int32_t format, int32_t T, int32_t H, int32_t I, int32_t E
   if (chosen) *chosen = p.schedule;
   if (block_m) *block_m = p.block_m;
   if (workspace_bytes) *workspace_bytes = p.total;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_set_tuning(int32_t tile_rows, int32_t rows_per_pass, int32_t kslices,
+                            int32_t tile_grid) {
+  g_last_error[0] = 0;
+  if (tile_rows != 0 && tile_rows != 128 && tile_rows != 256)
+    return fail(QMOE_ERR_INVALID_ARG, "tile_rows %d: 0, 128 or 256", tile_rows);
+  if (rows_per_pass != 0 && rows_per_pass != 16 && rows_per_pass != 32)
+    return fail(QMOE_ERR_INVALID_ARG, "rows_per_pass %d: 0, 16 or 32", rows_per_pass);
+  if (kslices < 0 || kslices > 64 || (kslices & (kslices - 1)))
+    return fail(QMOE_ERR_INVALID_ARG, "kslices %d: 0 or a power of two up to 64", kslices);
+  if (tile_grid != 0 && tile_grid != 1)
+    return fail(QMOE_ERR_INVALID_ARG, "tile_grid %d: 0 or 1", tile_grid);
+  g_tune_tile_rows.store(tile_rows);
+  g_tune_rows_per_pass.store(rows_per_pass);
+  g_tune_kslices.store(kslices);
+  set_tiled_one_per_tile(tile_grid == 1);
   return QMOE_OK;
 }
 

@@ -109,6 +109,8 @@ hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int
                                     hipStream_t stream);
 // Work-groups of a persistent launch: one per compute unit, a multiple of the XCD count.
 int persistent_grid();
+// Tile kernels with one work-group per tile instead of the persistent grid (tuning).
+void set_tiled_one_per_tile(bool on);
 // Prefill profile (W4A16 / MXFP4): row tiles of each expert segment on the matrix
 // cores, 256 rows, or 128 when the experts hold few rows (w4a16_tiled_rows). Needs H and
 // I multiples of 256; align must have produced tile_offsets for tiles of tile_rows rows.

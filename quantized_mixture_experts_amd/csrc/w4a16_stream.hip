@@ -906,18 +906,20 @@ __global__ void __launch_bounds__(kGatherThreads)
   const int kg_end = min(KG, (int)(blockIdx.y + 1) * kGatherGroups);
   uint16_t* dst = xs + ((size_t)rb * KG * 64 + lane) * 8;
   int kg = blockIdx.y * kGatherGroups + wave;
-  for (; kg + kGatherWaves < kg_end; kg += 2 * kGatherWaves) {
-    const u32x4 v0 = ld16(src + kg * 32);
-    const u32x4 v1 = ld16(src + (kg + kGatherWaves) * 32);
-    uint32_t p0[4] = {v0[0], v0[1], v0[2], v0[3]}, p1[4] = {v1[0], v1[1], v1[2], v1[3]};
-    if constexpr (!kNatural) {
-      perm_act8(v0, p0);
-      perm_act8(v1, p1);
+  // A whole range: all of this wave's loads are issued before the first store.
+  constexpr int kPer = kGatherGroups / kGatherWaves;
+  if (kg + (kPer - 1) * kGatherWaves < kg_end) {
+    u32x4 v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = ld16(src + (kg + i * kGatherWaves) * 32);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      uint32_t p0[4] = {v[i][0], v[i][1], v[i][2], v[i][3]};
+      if constexpr (!kNatural) perm_act8(v[i], p0);
+      *reinterpret_cast<u32x4*>(dst + (size_t)(kg + i * kGatherWaves) * 512) =
+          real ? u32x4{p0[0], p0[1], p0[2], p0[3]} : u32x4{0u, 0u, 0u, 0u};
     }
-    *reinterpret_cast<u32x4*>(dst + (size_t)kg * 512) =
-        real ? u32x4{p0[0], p0[1], p0[2], p0[3]} : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(dst + (size_t)(kg + kGatherWaves) * 512) =
-        real ? u32x4{p1[0], p1[1], p1[2], p1[3]} : u32x4{0u, 0u, 0u, 0u};
+    return;
   }
   for (; kg < kg_end; kg += kGatherWaves) {
     const u32x4 v0 = ld16(src + kg * 32);

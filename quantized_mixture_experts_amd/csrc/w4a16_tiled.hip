@@ -42,6 +42,7 @@
 // an operand word is the pair converted to fp32, multiplied by that scale and rounded
 // once to bf16.
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -760,10 +761,14 @@ __global__ void __launch_bounds__(kCombineThreads)
   }
 }
 
+std::atomic<bool> g_one_per_tile{false};
+
 template <TEpi EPI, int TR>
 void launch_tiled_rows(const TiledArgs& a, int64_t items, bool mx, bool nv, hipStream_t stream) {
   // persistent: at most one work-group per compute unit, a multiple of the XCD count
-  const dim3 grid(std::min(xcd_major_grid((int)items), persistent_grid()));
+  // (or, for tuning, one per tile: then each work-group runs a single item)
+  const int all = xcd_major_grid((int)items);
+  const dim3 grid(g_one_per_tile.load() ? all : std::min(all, persistent_grid()));
   if (nv)
     hipLaunchKernelGGL((w4a16_tiled_kernel<EPI, true, true, TR>), grid, dim3(kThreads), 0, stream,
                        a);
@@ -791,6 +796,8 @@ hipError_t launch_tiled(const TiledArgs& a, int64_t P, int E, int tile_rows, boo
 }
 
 }  // namespace
+
+void set_tiled_one_per_tile(bool on) { g_one_per_tile.store(on); }
 
 bool w4a16_tiled_supported(int32_t H, int32_t I) { return H % 256 == 0 && I % 256 == 0; }
 

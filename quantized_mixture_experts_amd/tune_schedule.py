@@ -1,11 +1,19 @@
-"""Measure the decode and prefill schedules of a layer shape across routed tokens per
-expert (tok_e = T*k/E) on the current GPU and print where the prefill profile starts to
-win. The library's automatic choice (qmoe_plan) uses the crossover measured this way.
+"""Measure the schedule configurations of a layer shape across routed rows per expert
+(tok_e = T*k/E) on the current GPU, report the fastest per tok_e and how close the
+library's automatic choice (qmoe_plan) comes to it. The thresholds the library uses (the
+decode/prefill crossover, rows per decode pass, the prefill row tile, the down split-K
+guard) were measured this way.
 
   python -m quantized_mixture_experts_amd.tune_schedule [--format w4a16|mxfp4|nvfp4|fp8]
-        [--H 7168] [--I 2048] [--E 48] [--k 8] [--steps 10]
+        [--H 7168] [--I 2048] [--E 48] [--k 8] [--kind uniform|zipf] [--steps 10]
+        [--tok-e 4,8,...]
 
-Seeded synthetic inputs of the benchmark recipe; one JSON line per tok_e, then a summary.
+Candidates (the 4-bit formats, forced through qmoe_set_tuning): decode with 16 or 32 rows
+per weight pass, prefill with 128- or 256-row tiles (split-K and the persistent grid as
+the library plans them); for the faster tile height also prefill without split-K and with
+one work-group per tile instead of the persistent grid, which shows what each of the two
+buys. Block FP8: decode against prefill. Seeded synthetic inputs of the benchmark recipe;
+one JSON line per tok_e, then a markdown table.
 """
 import argparse
 import json
@@ -42,13 +50,14 @@ def main():
     ap.add_argument("--I", type=int, default=2048)
     ap.add_argument("--E", type=int, default=48)
     ap.add_argument("--k", type=int, default=8)
+    ap.add_argument("--kind", default="uniform", choices=["uniform", "zipf"])
     ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--tok-e", default="4,8,16,24,32,40,48,64,96,128,192,256")
+    ap.add_argument("--tok-e", default="4,8,16,24,32,40,48,64,96,128,160,192,256")
     args = ap.parse_args()
     H, I, E, k = args.H, args.I, args.E, args.k
     fmt = {"w4a16": binding.FORMAT_W4A16, "mxfp4": binding.FORMAT_MXFP4,
            "nvfp4": binding.FORMAT_NVFP4, "fp8": binding.FORMAT_FP8}[args.format]
-    four_bit = args.format in ("w4a16", "mxfp4", "nvfp4")
+    four_bit = args.format != "fp8"
     # one set of weights for every T
     if args.format == "w4a16":
         base = inputs.custom_w4a16_case(16, H, I, E, k, seed=5)
@@ -63,47 +72,92 @@ def main():
         for n in ("w13", "s13", "w2", "s2", "g13", "g2") if n in base}
 
     def forward(x, tids, twts, **kw):
-        w = (dev["w13"], dev["s13"], dev["w2"], dev["s2"])
+        if args.format == "fp8":
+            return binding.moe_fp8_block_forward(x[0], x[1], dev["w13"], dev["s13"], dev["w2"],
+                                                 dev["s2"], tids, twts, **kw)
         if args.format == "nvfp4":
             return binding.moe_nvfp4_forward(x, dev["w13"], dev["s13"], dev["g13"], dev["w2"],
                                              dev["s2"], dev["g2"], tids, twts, **kw)
         f = binding.moe_mxfp4_forward if args.format == "mxfp4" else binding.moe_w4a16_forward
-        return f(x, *w, tids, twts, **kw)
+        return f(x, dev["w13"], dev["s13"], dev["w2"], dev["s2"], tids, twts, **kw)
+
+    def measure(x, tids, twts, T, sched, **tune):
+        binding.set_tuning(**tune)
+        try:
+            _, _, ws = binding.plan(fmt, T, H, I, E, k, sched)
+            work = torch.empty(max(ws, 1), dtype=torch.uint8, device="cuda")
+            out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+            return _time(lambda: forward(x, tids, twts, schedule=sched, out=out, workspace=work),
+                         args.steps)
+        finally:
+            binding.set_tuning()
+
+    D, PF = binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL
     rows = []
     for te in [int(v) for v in args.tok_e.split(",")]:
         T = max(1, te * E // k)
         rng = np.random.default_rng(1000 + te)
-        ids, wts = inputs.routing(rng, T, E, k, "uniform")
+        ids, wts = inputs.routing(rng, T, E, k, args.kind)
         tids, twts = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
-        ms = {}
-        for name, sched in (("decode", binding.SCHEDULE_DECODE), ("prefill", binding.SCHEDULE_PREFILL)):
-            if four_bit:
-                x = torch.from_numpy(inputs.bf16_bits(rng.standard_normal((T, H), dtype=np.float32))
-                                     .view(np.int16)).cuda()
-                _, _, ws = binding.plan(fmt, T, H, I, E, k, sched)
-                work = torch.empty(ws, dtype=torch.uint8, device="cuda")
-                out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-                fn = lambda: forward(x, tids, twts, schedule=sched, out=out, workspace=work)
-            else:
-                xq, xs = binding.fp8_quantize_blocks(
-                    torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).cuda(), 1, 128)
-                _, _, ws = binding.plan(fmt, T, H, I, E, k, sched)
-                work = torch.empty(ws, dtype=torch.uint8, device="cuda")
-                out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
-                fn = lambda: binding.moe_fp8_block_forward(xq, xs, dev["w13"], dev["s13"], dev["w2"],
-                                                           dev["s2"], tids, twts, schedule=sched,
-                                                           out=out, workspace=work)
-            ms[name] = _time(fn, args.steps)
-        auto = binding.plan(fmt, T, H, I, E, k)[0]
-        row = {"format": args.format, "tok_e": te, "T": T, "decode_ms": round(ms["decode"], 4),
-               "prefill_ms": round(ms["prefill"], 4),
-               "faster": "decode" if ms["decode"] <= ms["prefill"] else "prefill",
-               "auto": "decode" if auto == binding.SCHEDULE_DECODE else "prefill"}
+        xf = rng.standard_normal((T, H), dtype=np.float32)
+        if four_bit:
+            x = torch.from_numpy(inputs.bf16_bits(xf).view(np.int16)).cuda()
+            cand = {"decode/16": measure(x, tids, twts, T, D, rows_per_pass=16),
+                    "decode/32": measure(x, tids, twts, T, D, rows_per_pass=32),
+                    "prefill/128": measure(x, tids, twts, T, PF, tile_rows=128),
+                    "prefill/256": measure(x, tids, twts, T, PF, tile_rows=256)}
+            tr = 128 if cand["prefill/128"] <= cand["prefill/256"] else 256
+            extra = {"no_split_k": measure(x, tids, twts, T, PF, tile_rows=tr, kslices=1),
+                     "one_wg_per_tile": measure(x, tids, twts, T, PF, tile_rows=tr, tile_grid=1)}
+            sched, block_m, _ = binding.plan(fmt, T, H, I, E, k)
+            auto_ms = measure(x, tids, twts, T, binding.SCHEDULE_AUTO)
+            slices = binding.workspace_regions(fmt, T, H, I, E, k, PF).get("y", (0, 0))[1] // (
+                4 * T * k * H) if T * k else 0
+        else:
+            x = binding.fp8_quantize_blocks(torch.from_numpy(xf).cuda(), 1, 128)
+            cand = {"decode": measure(x, tids, twts, T, D), "prefill": measure(x, tids, twts, T, PF)}
+            extra, tr, slices = {}, None, None
+            sched, block_m, _ = binding.plan(fmt, T, H, I, E, k)
+            auto_ms = measure(x, tids, twts, T, binding.SCHEDULE_AUTO)
+        best = min(cand, key=cand.get)
+        row = {"format": args.format, "kind": args.kind, "tok_e": te, "T": T,
+               "candidates_ms": {n: round(v, 4) for n, v in cand.items()},
+               "best": best, "best_ms": round(cand[best], 4),
+               "auto": {"schedule": "decode" if sched == D else "prefill", "block_m": block_m,
+                        "ms": round(auto_ms, 4)},
+               "auto_over_best": round(auto_ms / cand[best], 3)}
+        if four_bit:
+            pf = cand[f"prefill/{tr}"]
+            row["prefill_tile_rows"] = tr
+            row["prefill_down_slices"] = slices
+            row["split_k_gain"] = round(extra["no_split_k"] / pf, 3)
+            row["persistent_gain"] = round(extra["one_wg_per_tile"] / pf, 3)
         rows.append(row)
         print(json.dumps(row), flush=True)
-    first = next((r["tok_e"] for r in rows if r["faster"] == "prefill"), None)
-    print(json.dumps({"summary": f"prefill first faster at tok_e = {first}",
-                      "auto_mismatches": [r["tok_e"] for r in rows if r["faster"] != r["auto"]]}))
+
+    # markdown summary
+    if four_bit:
+        print(f"\n| tok_e | T | decode 16 / 32 rows (ms) | prefill 128 / 256 rows (ms) | best | "
+              f"auto (ms, / best) | down slices | no split-K / split | one per tile / "
+              f"persistent |")
+        print("|---|---|---|---|---|---|---|---|---|")
+        for r in rows:
+            c = r["candidates_ms"]
+            print(f"| {r['tok_e']} | {r['T']} | {c['decode/16']} / {c['decode/32']} | "
+                  f"{c['prefill/128']} / {c['prefill/256']} | {r['best']} | "
+                  f"{r['auto']['schedule']} {r['auto']['ms']} ({r['auto_over_best']}) | "
+                  f"{r['prefill_down_slices']} | {r['split_k_gain']} | {r['persistent_gain']} |")
+    else:
+        print("\n| tok_e | T | decode (ms) | prefill (ms) | best | auto (ms, / best) |")
+        print("|---|---|---|---|---|---|")
+        for r in rows:
+            c = r["candidates_ms"]
+            print(f"| {r['tok_e']} | {r['T']} | {c['decode']} | {c['prefill']} | {r['best']} | "
+                  f"{r['auto']['schedule']} {r['auto']['ms']} ({r['auto_over_best']}) |")
+    print(json.dumps({"summary": "auto within 5% of best at tok_e " + str(
+        [r["tok_e"] for r in rows if r["auto_over_best"] <= 1.05]),
+        "auto_off_by_more": [(r["tok_e"], r["auto_over_best"]) for r in rows
+                             if r["auto_over_best"] > 1.05]}), flush=True)
 
 
 if __name__ == "__main__":

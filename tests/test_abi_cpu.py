@@ -288,3 +288,40 @@ def test_tile_kernels_limited_to_32_bit_weight_offsets():
     ok = binding.workspace_regions(binding.FORMAT_W4A16, 64, 65536, 16384, 4, 2,
                                    binding.SCHEDULE_PREFILL)
     assert "y" in ok
+
+
+def test_tuning_overrides_validate_and_reach_the_plan():
+    S = binding
+    W, F, M = S.FORMAT_W4A16, S.FORMAT_FP8, S.FORMAT_MXFP4
+
+    def y_slices(fmt, T, H, I, E, k):
+        return S.workspace_regions(fmt, T, H, I, E, k, S.SCHEDULE_PREFILL)["y"][1] // (4 * T * k * H)
+
+    base_block = S.plan(W, 32, 7168, 2048, 48, 8, S.SCHEDULE_DECODE)[1]
+    base_fp8 = S.plan(F, 32, 7168, 2048, 48, 8, S.SCHEDULE_DECODE)
+    base_slices = y_slices(W, 300, 1024, 1024, 2, 1)
+    try:
+        for bad in ({"tile_rows": 64}, {"rows_per_pass": 8}, {"kslices": 3}, {"kslices": 128},
+                    {"tile_grid": 2}, {"kslices": -1}):
+            S.set_tuning(rows_per_pass=32)
+            with pytest.raises(S.QMoEError):
+                S.set_tuning(**bad)
+            # a rejected call changes nothing
+            assert S.plan(W, 32, 7168, 2048, 48, 8, S.SCHEDULE_DECODE)[1] == 32
+        S.set_tuning(rows_per_pass=32)
+        assert S.plan(W, 32, 7168, 2048, 48, 8, S.SCHEDULE_DECODE)[1] == 32
+        assert S.plan(M, 8, 7168, 2048, 48, 8, S.SCHEDULE_DECODE)[1] == 32
+        assert S.plan(F, 32, 7168, 2048, 48, 8, S.SCHEDULE_DECODE) == base_fp8
+        S.set_tuning(rows_per_pass=16)
+        assert S.plan(W, 400, 7168, 2048, 48, 8, S.SCHEDULE_DECODE)[1] == 16
+        for ks in (1, 2, 4):
+            S.set_tuning(kslices=ks)
+            assert y_slices(W, 300, 1024, 1024, 2, 1) == ks
+        S.set_tuning(kslices=8)  # does not divide I / 256 = 4: no split
+        assert y_slices(W, 300, 1024, 1024, 2, 1) == 1
+        S.set_tuning(tile_rows=128, tile_grid=1)
+        assert y_slices(W, 300, 1024, 1024, 2, 1) >= 1
+    finally:
+        S.set_tuning()
+    assert S.plan(W, 32, 7168, 2048, 48, 8, S.SCHEDULE_DECODE)[1] == base_block
+    assert y_slices(W, 300, 1024, 1024, 2, 1) == base_slices

@@ -188,6 +188,32 @@ def test_w4a16_prefill_split_k(oracle_mod, T, H, I, E, k, kind):
     assert np.array_equal(got, _forward(case, binding.SCHEDULE_PREFILL))  # deterministic
 
 
+@pytest.mark.parametrize("T,H,I,E,k,kind", [(600, 1024, 1024, 3, 2, "zipf"),
+                                            (200, 512, 768, 5, 3, "uniform")])
+def test_w4a16_tuning_overrides(oracle_mod, T, H, I, E, k, kind):
+    """Every forced schedule configuration (qmoe_set_tuning) matches the oracle, and the
+    persistent grid and one work-group per tile compute each tile identically."""
+    print(f"[w4a16] tuning overrides T={T} H={H} I={I} E={E} k={k} {kind}", flush=True)
+    case = inputs.custom_w4a16_case(T, H, I, E, k, seed=T + 3 * I, kind=kind)
+    case["topk_ids"][::7, 0] = -1  # dropped slots
+    ref = _oracle(oracle_mod, case, None)
+    try:
+        for tr in (128, 256):
+            for ks in (1, 2):
+                binding.set_tuning(tile_rows=tr, kslices=ks)
+                pers = _forward(case, binding.SCHEDULE_PREFILL)
+                binding.set_tuning(tile_rows=tr, kslices=ks, tile_grid=1)
+                one = _forward(case, binding.SCHEDULE_PREFILL)
+                assert np.array_equal(pers, one)
+                assert report(f"tuned prefill rows={tr} slices={ks}", pers, ref).max() <= TOL
+        for rpp in (16, 32):
+            binding.set_tuning(rows_per_pass=rpp)
+            got = _forward(case, binding.SCHEDULE_DECODE)
+            assert report(f"tuned decode rows/pass={rpp}", got, ref).max() <= TOL
+    finally:
+        binding.set_tuning()
+
+
 def test_w4a16_prefill_tiles_deterministic():
     case = inputs.custom_w4a16_case(600, 512, 256, 4, 2, seed=11)
     a = _forward(case, binding.SCHEDULE_PREFILL)
