@@ -123,9 +123,16 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   // for W4A16 (40: 0.69 vs 0.71 ms; 48: 0.72 vs 0.71 ms), about 60 for MXFP4 (56: 0.61
   // vs 0.64 ms; 64: 0.69 vs 0.64 ms) and about 20 for block FP8 with four blocks per
   // pass (16: 0.36 vs 0.38 ms; 24: 0.40 vs 0.39 ms).
+  // (NVFP4, with the same sweep: 32: 0.47 vs 0.56 ms; 40: 0.57 vs 0.56 ms.) With few
+  // experts the routed pairs are few and the prefill tiles leave most of the GPU idle:
+  // the 4-bit decode profile stays ahead up to about ten times the crossover in routed
+  // pairs at any rows per expert (W4A16 at 8, 4 and 2 experts, top-2, top-1, top-1:
+  // decode ahead up to 48, 96 and 192 rows per expert, prefill from 64, 128 and 256).
   const double crossover = fmt == kMxfp4 ? 60.0 : fmt == kFp8 ? 20.0 : fmt == kNvfp4 ? 36.0 : 44.0;
   if (schedule == QMOE_SCHEDULE_AUTO)
-    p.schedule = tok_e <= crossover ? QMOE_SCHEDULE_DECODE : QMOE_SCHEDULE_PREFILL;
+    p.schedule = (tok_e <= crossover || (four_bit(fmt) && (double)p.P <= 10.2 * crossover))
+                     ? QMOE_SCHEDULE_DECODE
+                     : QMOE_SCHEDULE_PREFILL;
   p.tiled = p.schedule == QMOE_SCHEDULE_PREFILL &&
             (four_bit(fmt) ? w4a16_tiled_supported(H, I) : fp8_tiled_supported(H, I));
   // Rows per weight pass of the stream kernels and the align block size. The 4-bit
@@ -134,7 +141,12 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   // FP8 stream kernels take mb within segments of any multiple of 16.
   auto set_blocks = [&] {
     if (four_bit(fmt)) {
-      p.mb = (!p.tiled && tok_e > two_block_rows(fmt)) ? 2 : 1;
+      // Two blocks per pass also need enough routed pairs: with few experts a second pass
+      // over an expert's weights costs less than the work-groups that two-block passes
+      // leave idle (W4A16 at 8, 4 and 2 experts: one block ahead up to 24, 48 and 96 rows
+      // per expert, two from 32, 64 and 128, i.e. above about 15 x two_block_rows pairs).
+      p.mb = (!p.tiled && tok_e > two_block_rows(fmt) && (double)p.P > 15.0 * two_block_rows(fmt))
+                 ? 2 : 1;
       if (!p.tiled && g_tune_rows_per_pass.load()) p.mb = g_tune_rows_per_pass.load() / kSegRows;
       p.block_m = kSegRows * p.mb;
     } else {
@@ -147,6 +159,22 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
   set_blocks();
   if (four_bit(fmt)) p.tile_rows = g_tune_tile_rows.load() ? g_tune_tile_rows.load()
                                                            : w4a16_tiled_rows(tok_e);
+  // 256-row tiles that would not fill the GPU while 128-row tiles fit in one wave: the
+  // smaller tiles keep more compute units busy for the same one wave (measured on MI355X at
+  // hidden 7168, intermediate 2048: 8 experts, top-2, at 160 and 192 rows per expert, and
+  // 4 or 2 experts, top-1, at 256 to 512, 128-row tiles 5-11 % faster; where 128-row tiles
+  // need a second wave, 256-row ones stay faster, e.g. 4 experts at 512 rows by 13 %).
+  // Rows per expert are counted high, as for split-K below.
+  if (four_bit(fmt) && p.tiled && !g_tune_tile_rows.load() && p.tile_rows == 256 && p.P > 0) {
+    const double e_eff = std::min<double>(E, (double)p.P);
+    const double rows_e = (double)p.P / e_eff;
+    const double sd = std::sqrt(rows_e * std::max(0.0, 1.0 - (double)k / E));
+    auto gate_up_items = [&](double tr) {
+      return e_eff * std::ceil((rows_e + 2.0 * sd) / tr) * (I / 128);
+    };
+    if (gate_up_items(256.0) < kPlanComputeUnits && gate_up_items(128.0) <= kPlanComputeUnits)
+      p.tile_rows = 128;
+  }
   // Split-K of the 4-bit prefill down GEMM where its output tiles would not fill the chip
   // ([CHORD] "Kernel optimizations": a shape guard decides when down splits K): the tile
   // kernels hold one work-group per compute unit, so when the expected tiles leave most of

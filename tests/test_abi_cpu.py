@@ -218,6 +218,24 @@ def test_plan_two_block_passes_above_sixteen_rows_per_expert():
     assert binding.plan(binding.FORMAT_FP8, 192, 7168, 2048, 48, 8, D)[1] == 16
 
 
+def test_plan_schedule_with_few_experts():
+    W, D, PF = binding.FORMAT_W4A16, binding.SCHEDULE_DECODE, binding.SCHEDULE_PREFILL
+    # 48 experts, top-8: decode up to 44 rows per expert, prefill from 48
+    assert binding.plan(W, 240, 7168, 2048, 48, 8)[0] == D
+    assert binding.plan(W, 288, 7168, 2048, 48, 8)[0] == PF
+    # few experts: decode while the routed pairs stay under ~450, at any rows per expert
+    assert binding.plan(W, 192, 7168, 2048, 8, 2)[0] == D       # 48 rows, 384 pairs
+    assert binding.plan(W, 256, 7168, 2048, 8, 2)[0] == PF      # 64 rows, 512 pairs
+    assert binding.plan(W, 384, 7168, 2048, 4, 1)[0] == D       # 96 rows
+    assert binding.plan(W, 512, 7168, 2048, 4, 1)[0] == PF      # 128 rows
+    # two-block passes need more than ~225 routed pairs as well as 16 rows per expert
+    assert binding.plan(W, 96, 7168, 2048, 8, 2)[1] == 16       # 24 rows, 192 pairs
+    assert binding.plan(W, 128, 7168, 2048, 8, 2)[1] == 32      # 32 rows, 256 pairs
+    assert binding.plan(W, 192, 7168, 2048, 4, 1)[1] == 16      # 48 rows, 192 pairs
+    # block FP8 keeps its rows-per-expert crossover
+    assert binding.plan(binding.FORMAT_FP8, 96, 7168, 2048, 4, 1)[0] == PF
+
+
 @pytest.mark.parametrize("fmt,T,E,sched", [(binding.FORMAT_W4A16, 32, 48, 0),
                                            (binding.FORMAT_W4A16, 8192, 48, 0),
                                            (binding.FORMAT_FP8, 1024, 32, 1),
@@ -263,8 +281,8 @@ def test_noalloc_forward_rejects_plans_beyond_its_scratch(lib):
 @pytest.mark.parametrize("T,H,I,E,k,slices", [
     (8192, 7168, 2048, 48, 8, 1),   # the prefill layer fills the GPU: no split
     (1024, 7168, 2048, 4, 2, 1),    # 224 down tiles: no split
-    (1024, 7168, 2048, 2, 1, 1),    # 2 x 512 rows, counted high: 3 tiles each, 2 slices spill
-    (512, 7168, 2048, 2, 2, 2),     # top-2 of 2 experts: exactly 512 rows each, 2 slices
+    (1024, 7168, 2048, 2, 1, 1),    # 2 x 512 rows, counted high: 5 tiles of 128 each, 280 tiles
+    (512, 7168, 2048, 2, 2, 1),     # 128-row tiles (256-row ones fill a quarter wave): 224 tiles, one wave
     (128, 7168, 2048, 1, 1, 8),     # 28 down tiles: 8 slices
     (96, 7168, 2048, 4, 2, 2),      # 48 rows per expert, 128-row tiles: 112 tiles, 2 slices
     (300, 1024, 1024, 2, 1, 4),     # 8 down tiles, K = 1024 (4 blocks): 4 slices
