@@ -344,6 +344,9 @@ qmoe_status w4a16_after_align(const Plan& p, const uint16_t* x, const uint8_t* w
   prob.nv = p.fmt == kNvfp4;
   prob.g13 = g13;
   prob.g2 = g2;
+  // One pair per row: the routing pass has cleared the padding rows of out, gate_up
+  // clears the routed rows of out32, and only those are cast.
+  prob.routed_rows_only = direct_out;
   const int32_t* ntp = region<int32_t>(workspace, p.off_ntp);
 
   if (p.tiled) {
@@ -386,7 +389,8 @@ qmoe_status w4a16_after_align(const Plan& p, const uint16_t* x, const uint8_t* w
   err = staged(QMOE_STAGE_DOWN, s, [&] { return launch_w4a16_down_stream(prob, r, p.mb, s); });
   if (err != hipSuccess) return hip_fail(err, "down launch");
   err = staged(QMOE_STAGE_CAST, s, [&] {
-    return launch_cast_f32_bf16(prob.out32, out, (int64_t)T * H, s);
+    return direct_out ? launch_cast_routed_rows(prob.out32, r.sorted_ids, ntp, r.P, r.L, H, out, s)
+                      : launch_cast_f32_bf16(prob.out32, out, (int64_t)T * H, s);
   });
   if (err != hipSuccess) return hip_fail(err, "cast launch");
   return QMOE_OK;
@@ -456,8 +460,8 @@ qmoe_status w4a16_grouped(bool masked, const uint16_t* a, const uint8_t* w13, co
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* ones = region<float>(workspace, off_ones);
-  // the prefill tiles write only the valid rows: the routing pass clears the others
-  uint16_t* clear = p.tiled ? out : nullptr;
+  // The kernels write only the valid rows: the routing pass clears the others.
+  uint16_t* clear = out;
   hipError_t err;
   if (masked) {
     err = staged(QMOE_STAGE_ALIGN, s, [&] {

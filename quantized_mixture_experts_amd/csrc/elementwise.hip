@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(kEwThreads)
 
 // Per-row routing of the contiguous grouped layout: every row is one pair of routing
 // weight 1; a row whose index lies outside [0, E) is padding, and its output row is
-// cleared when `out` is given (the prefill tiles write only the valid rows).
+// cleared when `out` is given (the kernels after it write only the valid rows).
 __global__ void __launch_bounds__(kEwThreads)
     grouped_routing_kernel(const int32_t* __restrict__ ids, int32_t E, int32_t n,
                            float* __restrict__ ones, uint16_t* __restrict__ out, int32_t H) {
@@ -162,6 +162,48 @@ hipError_t launch_grouped_routing(const int32_t* ids, int32_t E, int32_t n, floa
   const int32_t blocks = (int32_t)std::min<int64_t>((work + kEwThreads - 1) / kEwThreads, 1024);
   hipLaunchKernelGGL(grouped_routing_kernel, dim3(blocks), dim3(kEwThreads), 0, stream, ids, E, n,
                      ones, out, H);
+  return hipGetLastError();
+}
+
+namespace {
+// out[sid] = bf16(out32[sid]) for the routed rows of a one-pair-per-row layout (k = 1: the
+// pair id is the row), found through the sorted rows below num_tokens_padded; the other
+// rows of out are left as they are. One work-group per (16 sorted rows, 1024 columns); a
+// thread takes 4 columns of every row, all rows' loads issued before any store.
+constexpr int kCastRowCols = 4 * kEwThreads;
+__global__ void __launch_bounds__(kEwThreads)
+    cast_routed_rows_kernel(const float* __restrict__ out32, const int32_t* __restrict__ sorted_ids,
+                            const int32_t* __restrict__ ntp, int32_t P, int32_t H,
+                            uint16_t* __restrict__ out) {
+  const int rb = blockIdx.x;
+  if (rb * 16 >= ntp[0]) return;
+  const int c = blockIdx.y * kCastRowCols + 4 * (int)threadIdx.x;
+  if (c >= H) return;
+  int sid[16];
+  f32x4 v[16];
+#pragma unroll
+  for (int m = 0; m < 16; ++m) sid[m] = sorted_ids[rb * 16 + m];
+#pragma unroll
+  for (int m = 0; m < 16; ++m)
+    v[m] = *reinterpret_cast<const f32x4*>(out32 + (size_t)(sid[m] < P ? sid[m] : 0) * H + c);
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    if (sid[m] >= P) continue;
+    const uint32_t lo = (uint32_t)f32_to_bf16(v[m].x) | ((uint32_t)f32_to_bf16(v[m].y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v[m].z) | ((uint32_t)f32_to_bf16(v[m].w) << 16);
+    *reinterpret_cast<uint2*>(out + (size_t)sid[m] * H + c) = uint2{lo, hi};
+  }
+}
+}  // namespace
+
+hipError_t launch_cast_routed_rows(const float* out32, const int32_t* sorted_ids,
+                                   const int32_t* ntp, int32_t P, int32_t L, int32_t H,
+                                   uint16_t* out, hipStream_t stream) {
+  if (L <= 0 || P <= 0) return hipSuccess;
+  if (H % 4) return hipErrorInvalidValue;
+  const dim3 grid((L + 15) / 16, (H + kCastRowCols - 1) / kCastRowCols);
+  hipLaunchKernelGGL(cast_routed_rows_kernel, grid, dim3(kEwThreads), 0, stream, out32, sorted_ids,
+                     ntp, P, H, out);
   return hipGetLastError();
 }
 

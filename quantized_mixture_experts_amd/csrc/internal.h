@@ -41,6 +41,11 @@ hipError_t launch_fp8_quantize_blocks_bf16(const uint16_t* v, int64_t R, int64_t
 // (H bf16) cleared where ids[r] lies outside [0, E) (a padding row).
 hipError_t launch_grouped_routing(const int32_t* ids, int32_t E, int32_t n, float* ones,
                                   uint16_t* out, int32_t H, hipStream_t stream);
+// One pair per row (k = 1): out[sid] = bf16(out32[sid]) for every sorted row below
+// num_tokens_padded whose pair id sid is below P; other rows of out are not written.
+hipError_t launch_cast_routed_rows(const float* out32, const int32_t* sorted_ids,
+                                   const int32_t* ntp, int32_t P, int32_t L, int32_t H,
+                                   uint16_t* out, hipStream_t stream);
 
 // --- grouped expert GEMMs ---------------------------------------------------
 // Routing view shared by the expert GEMMs: segments of the sorted pair list, each a
@@ -74,6 +79,9 @@ struct W4A16Problem {
   bool nv = false;
   const float* g13 = nullptr;  // [E]
   const float* g2 = nullptr;   // [E]
+  // One pair per row (k = 1, the grouped layouts): the decode gate_up clears only the
+  // routed rows of out32 (the others are never read: the cast takes the routed rows).
+  bool routed_rows_only = false;
 };
 
 struct Fp8Problem {

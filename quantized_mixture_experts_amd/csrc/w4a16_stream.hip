@@ -79,6 +79,9 @@ struct StreamArgs {
   // Persistent gate_up: the activation rows [T, K] in their natural layout, read by token
   // through sorted_ids (then `act` is unused and no gathered copy is needed).
   const uint16_t* x = nullptr;
+  // Persistent gate_up with one pair per row (k = 1): clear only the rows of zero_out
+  // (K floats each) that a sorted row routes, not all of it.
+  bool zero_routed = false;
 };
 
 struct Stage {
@@ -465,7 +468,18 @@ __global__ void __launch_bounds__(kPThreads)
   // gate_up clears the fp32 output that down accumulates into (down starts after the
   // last gate_up work-group has ended).
   if constexpr (EPI == Epi::GateUp) {
-    if (a.zero_out) {
+    if (a.zero_out && a.zero_routed) {
+      const int row4 = a.K / 4;
+      const int64_t n4 = (int64_t)ld_invariant(a.ntp, 0) * row4;
+      for (int64_t i = (int64_t)blockIdx.x * kPThreads + threadIdx.x; i < n4;
+           i += (int64_t)gridDim.x * kPThreads) {
+        const int r = (int)(i / row4);
+        const int sid = a.sorted_ids[r];
+        if (sid < a.P)
+          reinterpret_cast<f32x4*>(a.zero_out + (size_t)sid * a.K)[i - (int64_t)r * row4] =
+              f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else if (a.zero_out) {
       const int64_t n4 = a.zero_n / 4;
       for (int64_t i = (int64_t)blockIdx.x * kPThreads + threadIdx.x; i < n4;
            i += (int64_t)gridDim.x * kPThreads)
@@ -1018,6 +1032,7 @@ hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, i
                zero ? p.out32 : nullptr, zero ? (int64_t)p.T * p.H : 0};
   a.g = p.g13;
   a.x = p.x;
+  a.zero_routed = p.routed_rows_only;
   return p.nv   ? launch_stream<Epi::GateUp, true, true>(a, r.E, mb, stream)
          : p.mx ? launch_stream<Epi::GateUp, true, false>(a, r.E, mb, stream)
                 : launch_stream<Epi::GateUp, false, false>(a, r.E, mb, stream);
