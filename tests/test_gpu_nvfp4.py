@@ -53,7 +53,7 @@ def test_nvfp4_workloads(oracle_mod, name, schedule, nrows):
     (50, 800, 352, 10, 3),    # ragged against the 256-deep k step and the column chunks
     (9, 32, 32, 3, 2),        # smallest sizes
     (30, 1024, 512, 8, 2),    # persistent decode kernel, 7.5 rows per expert: one block per pass
-    (40, 1024, 512, 6, 2),    # persistent decode kernel, 13.3 rows per expert: two blocks per pass
+    (90, 1024, 512, 6, 2),    # persistent decode kernel, 30 rows per expert, 180 pairs: two blocks per pass
     (200, 1024, 512, 8, 2),   # 50 rows per expert: two blocks per pass; 128-row tiles
     (300, 512, 768, 2, 2),    # 300 rows per expert: 256-row tiles
 ])
