@@ -206,6 +206,16 @@ Plan make_plan(int fmt, int32_t T, int32_t H, int32_t I, int32_t E, int32_t k, i
     p.tiled = false;
     set_blocks();
   }
+  // The block-FP8 tile kernels copy activation rows (T x H codes for gate_up, L x I for
+  // down) and one expert's weights (2I x H codes) through buffer resources whose size is
+  // a signed 32-bit count.
+  if (p.tiled && fmt == kFp8 &&
+      ((uint64_t)T * (uint64_t)H >= (uint64_t(1) << 31) ||
+       (uint64_t)p.L * (uint64_t)I >= (uint64_t(1) << 31) ||
+       (uint64_t)2 * I * (uint64_t)H >= (uint64_t(1) << 31))) {
+    p.tiled = false;
+    set_blocks();
+  }
   for (int i = 0; i < QMOE_NUM_REGIONS; ++i) {
     p.off[i] = kNoRegion;
     p.len[i] = 0;

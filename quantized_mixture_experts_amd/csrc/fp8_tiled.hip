@@ -16,10 +16,12 @@
 //     its fp32 result d is added as acc += d * (As[row] * Bs), the scales being general
 //     fp32 values (a power-of-two block scale cannot carry them);
 //   * activation rows (gathered by token for gate_up, sorted rows of h for down), their
-//     scales and the weights of each k block go global -> LDS by global_load_lds into a
-//     ring of three stages; every wave waits on its own copies with vmcnt (the compiler
-//     does not count these) before the stage's barrier, which sits in the middle of the
-//     step so the last MFMAs cover it;
+//     scales and the weights of each k block go global -> LDS by buffer loads to LDS
+//     into a ring of three stages, eight lanes per 128 B row line (the MFMA's lane order,
+//     sixteen rows per sixteen lanes, moves a third of the bytes per clock), placed with
+//     a swizzle that keeps the MFMA-order reads free of bank conflicts; every wave waits
+//     on its own copies with vmcnt (the compiler does not count these) before the
+//     stage's barrier, which sits in the middle of the step so the last MFMAs cover it;
 // gate_up quantizes SiLU(gate) * up to E4M3 per row and 128 columns in its epilogue (the
 // tile's 128 h columns are one block; the rows' maxima meet through LDS); down stores
 // the routing-weighted rows per (token, slot) pair, summed per token by the combine
@@ -83,7 +85,13 @@ struct Fp8TiledArgs {
   float* y;                     // down output [P, N]
   int32_t P, k, E, K, N, I;
   int32_t col_tiles;
+  // Sizes in bytes of act, act_scale, ws and one expert's weights (N * K), each < 2^31
+  // (host-checked): the copies go through buffer resources of these sizes.
+  uint32_t act_bytes, scale_bytes, ws_bytes, w_expert_bytes;
 };
+
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle, no index).
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -101,7 +109,7 @@ __device__ __forceinline__ int expert_of_tile(const int32_t* toff, int E, int m)
   return lo;
 }
 
-// LDS destination operand of global_load_lds.
+// LDS destination operand of a buffer load to LDS.
 #define QMOE_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <FEpi EPI>
@@ -152,43 +160,69 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
     }
   };
 
-  // Per-lane source pointers (64-bit: the activation and weight matrices can pass 4 GB).
+  // Operand copies. A copy instruction moves 8 rows x 128 B (one k block of each row):
+  // lane l takes row l / 8 of the eight and a 16 B piece of it, so every eight
+  // consecutive lanes read one whole 128 B line. (With the MFMA's own lane order, where
+  // consecutive lanes are consecutive rows, the address path delivers a third of the
+  // bytes per clock.) The copy lands lane-linear in LDS; the piece a lane fetches is its
+  // slot XOR (row ^ half) within the row, so that the MFMA-order reads below, which take
+  // pieces 2 quad and 2 quad + 1 of row col for sixteen rows at once, fall on distinct
+  // banks. In LDS a 16-row block is [half (rows 0-7, 8-15)][row][slot], 128 units of 16 B.
+  // Copies go through buffer resources (32-bit byte offsets; weights per expert).
+  const int crow = lane >> 3, cslot = lane & 7;
+  auto piece_of = [&](int h8) { return (uint32_t)(cslot ^ crow ^ h8) * 16u; };
+  const __amdgpu_buffer_rsrc_t ars =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.act_scale, (short)0, (int)a.scale_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.w + (size_t)e * a.N * (size_t)K), (short)0, (int)a.w_expert_bytes, kRsrcWord3);
   // Wave w copies activation row block w, the scales of rows 16w .. 16w+15 and weight
   // column tiles 4 wc + 2 wr and 4 wc + 2 wr + 1.
-  const uint8_t* abase;
+  uint32_t a_off[2];
   {
     const int rb = min(rb0 + wave, rb_last);
-    abase = a.act + (size_t)act_row(rb * 16 + col) * K + 32 * quad;
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+      a_off[h8] = (uint32_t)act_row(rb * 16 + 8 * h8 + crow) * (uint32_t)K + piece_of(h8);
   }
-  const float* sbase;
+  uint32_t s_off;
   {
     const int r = min(row0 + wave * kScaleRowsPerWave + (lane & (kScaleRowsPerWave - 1)),
                       rb_last * 16 + 15);  // lanes 16..63 repeat lanes 0..15
-    sbase = a.act_scale + (size_t)act_row(r) * KB;
+    s_off = (uint32_t)act_row(r) * (uint32_t)KB * 4u;
   }
   const int my_tile0 = wc * kColTiles + 2 * wr;
-  const uint8_t* wbase[2];
+  uint32_t w_off[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    wbase[i] = a.w + ((size_t)e * a.N + weight_row(my_tile0 + i, col)) * (size_t)K + 32 * quad;
+#pragma unroll
+    for (int h8 = 0; h8 < 2; ++h8)
+      w_off[i][h8] = (uint32_t)weight_row(my_tile0 + i, 8 * h8 + crow) * (uint32_t)K + piece_of(h8);
+  // Read side: this lane's two pieces (k bytes 32 quad .. 32 quad + 31 of row col) of a
+  // 16-row block, in 16 B units from the block's start.
+  int rd_off[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+    rd_off[hh] = (col >> 3) * kWave + (col & 7) * 8 + ((2 * quad + hh) ^ (col & 7) ^ (col >> 3));
 
   auto stage_at = [&](int st) { return &smem[st * kStageUnits]; };
   auto copy_step = [&](int g, int st) {
     const int kb = min(g, KB - 1);
     u32x4* s = stage_at(st);
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      __builtin_amdgcn_global_load_lds((const void*)(abase + kb * 128 + 16 * p),
-                                       QMOE_LDS(s + (wave * 2 + p) * kWave), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(sbase + kb), QMOE_LDS(s + kAUnits + wave * 16), 4,
-                                     0, 0);
+    for (int h8 = 0; h8 < 2; ++h8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, QMOE_LDS(s + (wave * 2 + h8) * kWave), 16,
+                                               (int)a_off[h8], kb * 128, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, QMOE_LDS(s + kAUnits + wave * 16), 4, (int)s_off,
+                                             kb * 4, 0, 0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(wbase[i] + kb * 128 + 16 * p),
-            QMOE_LDS(s + kAUnits + kAsUnits + ((my_tile0 + i) * 2 + p) * kWave), 16, 0, 0);
+      for (int h8 = 0; h8 < 2; ++h8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wrs, QMOE_LDS(s + kAUnits + kAsUnits + ((my_tile0 + i) * 2 + h8) * kWave), 16,
+            (int)w_off[i][h8], kb * 128, 0, 0);
   };
 
   // Weight block scales of this wave for the whole K: row 0 for tiles 0-1, row 1 for
@@ -197,9 +231,10 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int nb = weight_row(wc * kColTiles + 2 * h, 0) >> 7;
-    const float* src = a.ws + ((size_t)e * (a.N >> 7) + nb) * KB + min(lane, KB - 1);
-    __builtin_amdgcn_global_load_lds((const void*)src, QMOE_LDS(bs_lds + h * (kMaxKBlocks / 4)), 4, 0,
-                                     0);
+    const uint32_t off = ((uint32_t)(e * (a.N >> 7) + nb) * KB + min(lane, KB - 1)) * 4u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.ws, (short)0, (int)a.ws_bytes, kRsrcWord3),
+        QMOE_LDS(bs_lds + h * (kMaxKBlocks / 4)), 4, (int)off, 0, 0, 0);
   }
 
   f32x4 acc[kMyBlocks][kColTiles];
@@ -228,7 +263,7 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
     for (int t = 0; t < kColTiles; ++t)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
-        bv[t][p] = s[kAUnits + kAsUnits + ((wc * kColTiles + t) * 2 + p) * kWave + lane];
+        bv[t][p] = s[kAUnits + kAsUnits + (wc * kColTiles + t) * 2 * kWave + rd_off[p]];
     // Row block m's operands are read one block ahead; the stage's last reads are issued
     // before the next-to-last block's MFMAs, so the barrier can follow those and the last
     // block's MFMAs cover it. The four MFMA results of block m are promoted into the
@@ -237,7 +272,7 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
     auto as_blk = [&](int rbt) {
       return *reinterpret_cast<const f32x4*>(as_f + rbt * 64 + 4 * quad);
     };
-    u32x4 av[2] = {s[(rbt0 * 2) * kWave + lane], s[(rbt0 * 2 + 1) * kWave + lane]};
+    u32x4 av[2] = {s[rbt0 * 2 * kWave + rd_off[0]], s[rbt0 * 2 * kWave + rd_off[1]]};
     f32x4 as4 = as_blk(rbt0);
     f32x4 dprev[kColTiles];
     f32x4 scprev0 = zero4, scprev1 = zero4;
@@ -249,8 +284,8 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
       f32x4 as4n = as4;
       if (m < kMyBlocks) {
         if (m + 1 < kMyBlocks) {
-          avn[0] = s[((rbt0 + m + 1) * 2) * kWave + lane];
-          avn[1] = s[((rbt0 + m + 1) * 2 + 1) * kWave + lane];
+          avn[0] = s[(rbt0 + m + 1) * 2 * kWave + rd_off[0]];
+          avn[1] = s[(rbt0 + m + 1) * 2 * kWave + rd_off[1]];
           as4n = as_blk(rbt0 + m + 1);
         }
 #pragma unroll
@@ -393,14 +428,20 @@ int32_t fp8_tiled_rows() { return kTileRows; }
 
 hipError_t launch_fp8_gateup_tiled(const Fp8Problem& p, const Routing& r, hipStream_t stream) {
   Fp8TiledArgs a{p.a_q, p.a_scale, p.w13, p.s13, r.sorted_ids, r.offsets, r.tile_offsets,
-                 r.topk_weights, p.hq, p.hs, nullptr, r.P, r.k, r.E, p.H, 2 * p.I, p.I, p.I / 128};
+                 r.topk_weights, p.hq, p.hs, nullptr, r.P, r.k, r.E, p.H, 2 * p.I, p.I, p.I / 128,
+                 (uint32_t)((uint64_t)p.T * p.H), (uint32_t)((uint64_t)p.T * (p.H / 128) * 4u),
+                 (uint32_t)((uint64_t)r.E * (2 * p.I / 128) * (p.H / 128) * 4u),
+                 (uint32_t)((uint64_t)2 * p.I * p.H)};
   return launch_fp8_tiled<FEpi::GateUp>(a, (int64_t)r.P / kTileRows + r.E, stream);
 }
 
 hipError_t launch_fp8_down_tiled(const Fp8Problem& p, const Routing& r, float* y,
                                  hipStream_t stream) {
   Fp8TiledArgs a{p.hq, p.hs, p.w2, p.s2, r.sorted_ids, r.offsets, r.tile_offsets,
-                 r.topk_weights, nullptr, nullptr, y, r.P, r.k, r.E, p.I, p.H, p.I, p.H / 256};
+                 r.topk_weights, nullptr, nullptr, y, r.P, r.k, r.E, p.I, p.H, p.I, p.H / 256,
+                 (uint32_t)((uint64_t)r.L * p.I), (uint32_t)((uint64_t)r.L * (p.I / 128) * 4u),
+                 (uint32_t)((uint64_t)r.E * (p.H / 128) * (p.I / 128) * 4u),
+                 (uint32_t)((uint64_t)p.H * p.I)};
   return launch_fp8_tiled<FEpi::Down>(a, (int64_t)r.P / kTileRows + r.E, stream);
 }
 

@@ -574,7 +574,7 @@ __global__ void __launch_bounds__(kPThreads)
   // step's 8 B.
   u32x4 snext[4];
   const int s_row = lane >> 3, s_piece = lane & 7;
-  auto scale_block_load = [&](const Unit& d) {
+  auto scale_block_load = [&](u32x4 (&dst)[4], const Unit& d) {
     if constexpr (MX && !NV) {
       const int off = min((d.kc & ~(kScaleUnits - 1)) * 16 + s_piece * 8, G - 8);
 #pragma unroll
@@ -582,21 +582,21 @@ __global__ void __launch_bounds__(kPThreads)
         const int row = tile_row0(d.cc, i >> 1) + 8 * (i & 1) + s_row;
         const uint32_t* p = reinterpret_cast<const uint32_t*>(
             reinterpret_cast<const uint8_t*>(a.s) + ((size_t)d.e * N + row) * G + off);
-        snext[i] = u32x4{p[0], p[1], 0u, 0u};
+        dst[i] = u32x4{p[0], p[1], 0u, 0u};
       }
     } else {
       const int off = min((d.kc & ~(kScaleUnits - 1)) * 32 + s_piece * 16, G * 2 - 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = tile_row0(d.cc, i >> 1) + 8 * (i & 1) + s_row;
-        snext[i] = ld16(reinterpret_cast<const uint8_t*>(a.s) + ((size_t)d.e * N + row) * G * 2 + off);
+        dst[i] = ld16(reinterpret_cast<const uint8_t*>(a.s) + ((size_t)d.e * N + row) * G * 2 + off);
       }
     }
   };
-  auto scale_block_store = [&]() {
+  auto scale_block_store = [&](const u32x4 (&src)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const u32x4 v = snext[i];
+      const u32x4 v = src[i];
       if constexpr (NV) {
         // the step's 16 E4M3 bytes of this row (two per group), kept raw
         s_lds[wave][i >> 1][s_piece][8 * (i & 1) + s_row] = __builtin_bit_cast(f32x4, v);
@@ -627,13 +627,16 @@ __global__ void __launch_bounds__(kPThreads)
   int rb_cache = -1;
   int tok_cache[MB];
   // DX: token of this lane's activation row (row `col` of the 16-row block rb16), or -1 for
-  // a padding row. The block's sixteen pair ids come through scalar loads, which do not
-  // enter the vector memory counter that the weight ring waits on.
+  // a padding row. The block's sixteen pair ids come through scalar loads (the block index
+  // is made wave-uniform explicitly; from a per-lane address they would be vector loads),
+  // which do not enter the vector memory counter: waiting for them does not wait for the
+  // weight loads in flight.
   auto row_token = [&](int rb16) {
+    const int32_t* ids = a.sorted_ids + __builtin_amdgcn_readfirstlane(rb16) * 16;
     int sid = 0;
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-      const int v = ld_invariant(a.sorted_ids, rb16 * 16 + m);
+      const int v = ld_invariant(ids, m);
       sid = (col == m) ? v : sid;
     }
     return sid < a.P ? sid / a.k : -1;
@@ -833,23 +836,27 @@ __global__ void __launch_bounds__(kPThreads)
     }
   };
 
-  // Descriptors of units u, u+1, u+2 (clamped to the range: loads past its end re-read
-  // the last unit, which the cache serves, and are never used).
   // Descriptors of units u .. u + kWin - 1, clamped to the range (loads past its end
   // re-read the last unit, which the cache serves, and are never used).
   Unit dq[kWin];
 #pragma unroll
   for (int i = 0; i < kWin; ++i) dq[i] = desc(min(u0 + i, ulast));
+  // The scales of the first two blocks are loaded ahead of the weight ring: the loop
+  // waits for the prefetched block's scales at the next block start, and the compiler
+  // counts that wait over every path into the loop, this one included. Loaded after the
+  // ring, they would be the youngest loads on this path, and the wait would drain the
+  // ring at every block start.
   sid_load(sid_c, dq[0]);
-  scale_block_load(dq[0]);
+  u32x4 sfirst[4];
+  scale_block_load(sfirst, dq[0]);
+  scale_block_load(snext, desc(next_block(u0, dq[0].kc)));
   chunk_load(dq[0]);
   Stage st[kRing];
 #pragma unroll
   for (int j = 0; j < kRing - 1; ++j) load(st[j], dq[j / 2], j & 1);
   chunk_store(0);
   chunk_load(dq[1]);
-  scale_block_store();
-  scale_block_load(desc(next_block(u0, dq[0].kc)));
+  scale_block_store(sfirst);
   __syncthreads();
 
   // Unit u at position U of the unrolled body uses activation buffer and scale registers
@@ -864,8 +871,8 @@ __global__ void __launch_bounds__(kPThreads)
     sid_load(sid_n, dq[1]);
     const int kc = dq[0].kc;
     if (live && u != u0 && (kc & (kScaleUnits - 1)) == 0) {
-      scale_block_store();
-      scale_block_load(desc(next_block(u, kc)));
+      scale_block_store(snext);
+      scale_block_load(snext, desc(next_block(u, kc)));
     }
     const int sp = 2 * (kc & (kScaleUnits - 1));
     // NVFP4: the expert's global scale (a scalar load; 1 otherwise)
@@ -965,14 +972,10 @@ int persistent_grid() {
 
 namespace {
 
-template <Epi EPI, bool MX, bool NV, bool DX>
-void launch_persist(const StreamArgs& args, int mb, hipStream_t stream) {
-  if (mb == 2)
-    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, NV, 2, DX>),
-                       dim3(persistent_grid() * kPGroupsPerCu), dim3(kPThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, NV, 1, DX>),
-                       dim3(persistent_grid() * kPGroupsPerCu), dim3(kPThreads), 0, stream, args);
+template <Epi EPI, bool MX, bool NV, int MB, bool DX>
+void launch_persist(const StreamArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, NV, MB, DX>),
+                     dim3(persistent_grid() * kPGroupsPerCu), dim3(kPThreads), 0, stream, args);
 }
 
 template <Epi EPI, bool MX, bool NV>
@@ -986,11 +989,19 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
   args.items = E * args.chunks;
   // The persistent kernel serves mb 16-row blocks per weight pass (align made segments
   // of 16 mb rows); the general kernel one 16-row block at a time of any segments.
-  if (persist && EPI == Epi::GateUp && mb == 1) {
-    // gate_up reads the rows of x directly (no gathered copy)
-    launch_persist<EPI, MX, NV, true>(args, mb, stream);
-  } else if (persist) {
-    launch_persist<EPI, MX, NV, false>(args, mb, stream);
+  if (persist) {
+    // gate_up with one block per pass reads the rows of x directly (no gathered copy)
+    if constexpr (EPI == Epi::GateUp) {
+      if (mb == 1)
+        launch_persist<EPI, MX, NV, 1, true>(args, stream);
+      else
+        launch_persist<EPI, MX, NV, 2, false>(args, stream);
+    } else {
+      if (mb == 2)
+        launch_persist<EPI, MX, NV, 2, false>(args, stream);
+      else
+        launch_persist<EPI, MX, NV, 1, false>(args, stream);
+    }
   } else {
     hipLaunchKernelGGL((w4a16_stream_kernel<EPI, 1, MX, NV>), dim3(xcd_major_grid(args.items)),
                        dim3(kThreads), 0, stream, args);
