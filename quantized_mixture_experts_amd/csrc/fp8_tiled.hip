@@ -252,28 +252,49 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 
   const int rbt0 = wr * kMyBlocks;  // first row block of this wave within the tile
-  int st = 0;
-  for (int g = 0; g < KB; ++g) {
-    const u32x4* s = stage_at(st);
-    const float* as_f = reinterpret_cast<const float*>(s + kAUnits);
-    const float bs0 = reinterpret_cast<const float*>(bs_lds)[g];
-    const float bs1 = reinterpret_cast<const float*>(bs_lds + kMaxKBlocks / 4)[g];
-    u32x4 bv[kColTiles][2];
+  // Scales of tile row r were copied by wave r / 16, to its 64-float slice.
+  auto as_blk = [&](const u32x4* s, int rbt) {
+    return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(s + kAUnits) +
+                                           rbt * 64 + 4 * quad);
+  };
+  // A step's first operands: its weight tiles, the first row block of activations and
+  // their scales, the weight block scales. Read for step g + 1 right after step g's
+  // barrier (its copies are complete by then), so that these reads overlap step g's last
+  // MFMAs instead of stalling the start of step g + 1.
+  // Two operand sets, used by alternate steps (the loop runs two steps per pass): a step
+  // reads the next step's first operands into the other set, with no register copies
+  // between steps that would wait for those reads.
+  struct Ops {
+    u32x4 bv[kColTiles][2], av[2];
+    f32x4 as4;
+    float bs0, bs1;
+  };
+  auto read_first = [&](const u32x4* s, int g, Ops& o) {
 #pragma unroll
     for (int t = 0; t < kColTiles; ++t)
 #pragma unroll
       for (int p = 0; p < 2; ++p)
-        bv[t][p] = s[kAUnits + kAsUnits + (wc * kColTiles + t) * 2 * kWave + rd_off[p]];
+        o.bv[t][p] = s[kAUnits + kAsUnits + (wc * kColTiles + t) * 2 * kWave + rd_off[p]];
+    o.av[0] = s[rbt0 * 2 * kWave + rd_off[0]];
+    o.av[1] = s[rbt0 * 2 * kWave + rd_off[1]];
+    o.as4 = as_blk(s, rbt0);
+    const int gc = min(g, KB - 1);
+    o.bs0 = reinterpret_cast<const float*>(bs_lds)[gc];
+    o.bs1 = reinterpret_cast<const float*>(bs_lds + kMaxKBlocks / 4)[gc];
+  };
+  Ops opa, opb;
+  read_first(stage_at(0), 0, opa);
+  int st = 0;
+  auto step = [&](int g, Ops& cur, Ops& nxt) {
+    const u32x4* s = stage_at(st);
+    const int stn = (st == kStages - 1) ? 0 : st + 1;
+    u32x4 av[2] = {cur.av[0], cur.av[1]};
+    f32x4 as4 = cur.as4;
+    const float bs0 = cur.bs0, bs1 = cur.bs1;
     // Row block m's operands are read one block ahead; the stage's last reads are issued
     // before the next-to-last block's MFMAs, so the barrier can follow those and the last
     // block's MFMAs cover it. The four MFMA results of block m are promoted into the
     // accumulators while block m+1's MFMAs run (no VALU waits on a fresh MFMA result).
-    // Scales of tile row r were copied by wave r / 16, to its 64-float slice.
-    auto as_blk = [&](int rbt) {
-      return *reinterpret_cast<const f32x4*>(as_f + rbt * 64 + 4 * quad);
-    };
-    u32x4 av[2] = {s[rbt0 * 2 * kWave + rd_off[0]], s[rbt0 * 2 * kWave + rd_off[1]]};
-    f32x4 as4 = as_blk(rbt0);
     f32x4 dprev[kColTiles];
     f32x4 scprev0 = zero4, scprev1 = zero4;
     __builtin_amdgcn_sched_barrier(0);
@@ -286,11 +307,11 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
         if (m + 1 < kMyBlocks) {
           avn[0] = s[(rbt0 + m + 1) * 2 * kWave + rd_off[0]];
           avn[1] = s[(rbt0 + m + 1) * 2 * kWave + rd_off[1]];
-          as4n = as_blk(rbt0 + m + 1);
+          as4n = as_blk(s, rbt0 + m + 1);
         }
 #pragma unroll
         for (int t = 0; t < kColTiles; ++t) {
-          const u32x4 bb[2] = {bv[t][0], bv[t][1]};
+          const u32x4 bb[2] = {cur.bv[t][0], cur.bv[t][1]};
           dcur[t] = mfma_fp8_16x16x128(av, bb, zero4);
         }
       }
@@ -318,6 +339,9 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         copy_step(g + kStages, st);
+        // Step g + 1's stage is complete (every wave waited for its copies before the
+        // barrier); past the last step it holds re-read blocks, never used.
+        read_first(stage_at(stn), g + 1, nxt);
         __builtin_amdgcn_sched_barrier(0);
       }
       av[0] = avn[0];
@@ -328,8 +352,14 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     }
-    st = (st == kStages - 1) ? 0 : st + 1;
+    st = stn;
+  };
+  int g = 0;
+  for (; g + 1 < KB; g += 2) {
+    step(g, opa, opb);
+    step(g + 1, opb, opa);
   }
+  if (g < KB) step(g, opa, opb);
   wait_vmcnt<0>();
 
   if constexpr (EPI == FEpi::GateUp) {
