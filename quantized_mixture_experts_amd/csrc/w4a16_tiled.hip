@@ -159,15 +159,16 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   constexpr int kSmemUnits = Tile<TR>::kSmemUnits;
   // One LDS array (150 KB at TR = 256, 95 KB at 128), in 16 B units:
   //   activation ring [stage][row block][lane], TR / 16 KB per k group;
-  //   per wave, the two half blocks of weight words [half][tile][lane];
+  //   per wave, the block's weight words [tile][8-row half][row][slot] (whole 128 B
+  //   lines, pieces swizzled; see copy_words);
   //   per wave, the block's scales [tile][row] (16 B = eight groups per weight row).
   //   down: two buffers of the tile rows' pair ids (TR * 4 B each).
   // A single object also keeps the compiler from adding conservative waits between the
   // asynchronous copies and the reads of other staging areas.
   __shared__ u32x4 smem[kSmemUnits];
   auto a_at = [&](int st, int rb) { return &smem[(st * kRowBlocks + rb) * kWave]; };
-  auto w_at = [&](int wv, int hf, int t) {
-    return &smem[kWBase + ((wv * 2 + hf) * kColTiles + t) * kWave];
+  auto w_at = [&](int wv, int t, int h8) {
+    return &smem[kWBase + ((wv * kColTiles + t) * 2 + h8) * kWave];
   };
   auto s_at = [&](int wv, int t) { return &smem[kSBase + (wv * kColTiles + t) * 16]; };
 
@@ -212,7 +213,21 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   constexpr uint32_t kScaleBytes = (MX && !NV) ? 1u : 2u;
   const int hsh = NV ? 8 * (quad >> 1) : 0;  // NVFP4: byte of this lane's 16-k half
   const uint32_t a_lane = (uint32_t)lane * 16u;
-  const uint32_t w_lane = (uint32_t)col * (uint32_t)(K >> 1) + 16u * quad;
+  // Weight words are copied a whole 128 B line (one 256-deep block of a row) per eight
+  // lanes: lane l takes row 8 h8 + l / 8 of the tile and the line's 16 B piece
+  // (l % 8) ^ (l / 8) ^ h8 into LDS slot l % 8 of that row. (With the MFMA's lane order,
+  // sixteen rows across sixteen lanes, the address path moves a third of the bytes per
+  // clock.) Lane (col, quad) then reads piece 4 hf + quad of row col from slot
+  // (4 hf + quad) ^ (col % 8) ^ (col / 8), which keeps sixteen lanes on distinct banks.
+  uint32_t w_lane[2];
+#pragma unroll
+  for (int h8 = 0; h8 < 2; ++h8)
+    w_lane[h8] = (uint32_t)(8 * h8 + (lane >> 3)) * (uint32_t)(K >> 1) +
+                 16u * (uint32_t)((lane & 7) ^ (lane >> 3) ^ h8);
+  int w_rd[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+    w_rd[hf] = (col >> 3) * kWave + (col & 7) * 8 + ((4 * hf + quad) ^ (col & 7) ^ (col >> 3));
   const uint32_t s_lane = (uint32_t)(lane >> 2) * (uint32_t)KG * kScaleBytes + 4u * (lane & 3);
   const __amdgpu_buffer_rsrc_t ars =
       __builtin_amdgcn_make_buffer_rsrc((void*)a.act, (short)0, (int)a.act_bytes, kRsrcWord3);
@@ -286,8 +301,8 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // fixed order and never skipped, so the counts below hold at every step: past the end
   // of an item they fetch the next item's first groups and weight block, or, after the
   // work-group's last item, repeat the last group or block. Per 8-group block and wave:
-  // kCopiesPerWave activation copies every step, the next block's first half of weight
-  // words and its scales at j = 1 (2 kColTiles), its second half at j = 5 (kColTiles).
+  // kCopiesPerWave activation copies every step, the next block's weight words at j = 1
+  // (2 kColTiles: two 8-row halves per tile), its scales at j = 2 (kColTiles).
   // Anything else issued between them (the epilogue's stores and loads, the next item's
   // pair ids) is younger than the copies a later wait counts on; since loads complete in
   // issue order, it can only make such a wait wait longer, never too little. Reads past a
@@ -301,12 +316,12 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   };
   // Weight words and scales of block kb of cur's numbering (kb >= nblocks: the next
   // item's).
-  auto copy_words = [&](int kb, int hf, int t) {
+  auto copy_words = [&](int kb, int t, int h8) {
     const int kl = min(kb - boff, nblocks - 1);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         __builtin_amdgcn_make_buffer_rsrc((void*)cp.wb, (short)0, w_records, kRsrcWord3),
-        (__attribute__((address_space(3))) void*)w_at(wave, hf, t), 16,
-        (int)(w_lane + cp.wbase + (t ? w_tile1 : 0u)), kl * 128 + 64 * hf, 0, 0);
+        (__attribute__((address_space(3))) void*)w_at(wave, t, h8), 16,
+        (int)(w_lane[h8] + cp.wbase + (t ? w_tile1 : 0u)), kl * 128, 0, 0);
   };
   auto copy_scale = [&](int kb, int t) {
     const int kl = min(kb - boff, nblocks - 1);
@@ -319,9 +334,11 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
 #pragma unroll
     for (int i = 0; i < kCopiesPerWave; ++i) copy_act(g, st_, i);
   };
-  auto copy_half = [&](int kb, int hf) {
+  auto copy_block_words = [&](int kb) {
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t) copy_words(kb, hf, t);
+    for (int t = 0; t < kColTiles; ++t)
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) copy_words(kb, t, h8);
   };
   auto copy_scales = [&](int kb) {
 #pragma unroll
@@ -360,7 +377,7 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   u32x4 wnext[kColTiles], snext[kColTiles];
   auto read_staged_half = [&](int hf) {
 #pragma unroll
-    for (int t = 0; t < kColTiles; ++t) wnext[t] = w_at(wave, hf, t)[lane];
+    for (int t = 0; t < kColTiles; ++t) wnext[t] = w_at(wave, t, 0)[w_rd[hf]];
   };
   auto read_staged_scales = [&]() {
 #pragma unroll
@@ -385,29 +402,27 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
   // Issue schedule (per wave). Step g issues, after its barrier (one copy per MFMA of the
   // last three row blocks), the copies of activation group g + kStages into the stage
   // group g has just released (kCopiesPerWave); at block position j = 1 the next block's
-  // first half of weight words and its scales (2 kColTiles), at j = 5 its second half
-  // (kColTiles). The staged words are read into registers one step before use (j = 2:
-  // second half of this block; j = 6: first half and scales of the next block). The
-  // prologue issues the same sequence for the steps before group 0 of the work-group's
-  // first item; a later item's first groups and block come from the previous item's
-  // last steps.
+  // weight words (whole lines, 2 kColTiles), at j = 2 its scales (kColTiles). The staged
+  // words are read into registers one step or more before use (j = 0: second half of
+  // this block, before the copies at j = 1 overwrite it; j = 6: first half and scales of
+  // the next block). The prologue issues the same sequence for the steps before group 0
+  // of the work-group's first item; a later item's first groups and block come from the
+  // previous item's last steps.
   // The first item's pair ids: older than every copy below, so the waits below cover it.
   copy_ids(cur, 0);
   copy_group(0, 0);  // step -7 (j = 1)
-  copy_half(0, 0);
+  copy_block_words(0);
+  copy_group(1, 1);  // step -6 (j = 2)
   copy_scales(0);
-  copy_group(1, 1);  // step -6
   copy_group(2, 2);  // step -5
   copy_group(3, 3);  // step -4
-  copy_group(4, 4);  // step -3 (j = 5)
-  copy_half(0, 1);
-  copy_group(5, 5);  // step -2 (j = 6): younger than the scales are copies 1..5 and a half
-  wait_vmcnt<5 * kCopiesPerWave + kColTiles>();
+  copy_group(4, 4);  // step -3
+  copy_group(5, 5);  // step -2 (j = 6): younger than the scales are copies 2..5
+  wait_vmcnt<4 * kCopiesPerWave>();
   read_staged_half(0);
   read_staged_scales();
-  // step -1 (j = 7): group 0's copies; younger are 8 weight copies and copies 1..5 and
-  // the second half
-  wait_vmcnt<2 * kColTiles + 5 * kCopiesPerWave + kColTiles>();
+  // step -1 (j = 7): group 0's copies; younger are the words, the scales and copies 1..5
+  wait_vmcnt<3 * kColTiles + 5 * kCopiesPerWave>();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   copy_group(6, 6);
@@ -500,18 +515,17 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
         const u32x4& a0 = ra[q & 1][r];
         // This step's copies, issued after the barrier one per MFMA of row blocks
         // kRowBlocks-3 .. kRowBlocks-1 (a run of copies stalls the wave), in a fixed
-        // order: activation group g + kStages, then at j = 1 the next block's first half
-        // of weight words and its scales, at j = 5 its second half.
+        // order: activation group g + kStages, then at j = 1 the next block's weight
+        // words, at j = 2 its scales.
         auto copy_slot = [&](int k) {
           if (m < kRowBlocks - 3) return;
           const int c = (m - (kRowBlocks - 3)) * kColTiles + k;
           if (c < kCopiesPerWave) {
             copy_act(g + kStages, st, c);
-          } else if (c < kCopiesPerWave + kColTiles) {
-            if (j == 1) copy_words(kb + 1, 0, c - kCopiesPerWave);
-            else if (j == 5) copy_words(kb + 1, 1, c - kCopiesPerWave);
           } else if (c < kCopiesPerWave + 2 * kColTiles) {
-            if (j == 1) copy_scale(kb + 1, c - kCopiesPerWave - kColTiles);
+            const int w = c - kCopiesPerWave;
+            if (j == 1) copy_words(kb + 1, w >> 1, w & 1);
+            else if (j == 2 && w < kColTiles) copy_scale(kb + 1, w);
           }
         };
         mfma_acc(acc[m][0], a0, bc[0]);
@@ -578,9 +592,9 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
           // while the last row blocks' MFMAs run (register set 0 is free again).
           wait_lds_reads();
           constexpr int kLater = (kStages - 2) * kCopiesPerWave;
-          constexpr int w1 = 2 * kColTiles, w5 = kColTiles;
-          constexpr int kPrev = w1 + w5 - ((j == 1 || j == 0) ? w1 : 0) -
-                                ((j == 5 || j == 4) ? w5 : 0);
+          constexpr int w1 = 2 * kColTiles, w2 = kColTiles;
+          constexpr int kPrev = w1 + w2 - ((j == 1 || j == 0) ? w1 : 0) -
+                                ((j == 2 || j == 1) ? w2 : 0);
           wait_vmcnt<kLater + kPrev>();
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
@@ -588,15 +602,16 @@ __global__ void __launch_bounds__(kThreads) w4a16_tiled_kernel(TiledArgs a) {
           // epilogue, which read the id buffer that the next item's pair ids go to.
           if (j == 0 && kb == 0 && has_next) copy_ids(nrows, ibuf ^ 1);
           // (This step's copies follow, spread over the next MFMAs.)
-          if (j == 2) {
-            // Second half of this block (copied at j = 5 of the last block): younger
-            // are four steps of activation copies and the next first half and scales.
-            wait_vmcnt<4 * kCopiesPerWave + 2 * kColTiles>();
+          if (j == 0) {
+            // Second half of this block's words (copied at j = 1 of the last block;
+            // younger are its scales and six steps of activation copies), read before
+            // the copies at j = 1, behind the next barrier, overwrite them.
+            wait_vmcnt<6 * kCopiesPerWave + kColTiles>();
             read_staged_half(1);
           } else if (j == 6) {
-            // Next block's first half and scales (copied at j = 1): younger are four
-            // steps of activation copies and the next second half.
-            wait_vmcnt<4 * kCopiesPerWave + kColTiles>();
+            // Next block's first half and scales (copied at j = 1 and 2): younger are
+            // three steps of activation copies.
+            wait_vmcnt<3 * kCopiesPerWave>();
             read_staged_half(0);
             read_staged_scales();
           }
