@@ -54,11 +54,12 @@ constexpr int kScaleRowsPerWave = kTileRows / kWaves;  // 16 activation scale ro
 constexpr int kCopiesPerStep = 2 + 1 + 2 * 2;
 constexpr int kMaxKBlocks = 64;  // per-wave weight-scale rows held in LDS (K <= 8192)
 
-// LDS layout in 16 B units: per stage the activation planes [block][plane][lane], the
-// activation scales (per wave 64 floats: its 16 rows, then three copies of them, so that
-// every lane of the copy is active and the loop body stays one basic block), and the
-// weight planes [column tile][plane][lane]; then per wave the weight block scales for the
-// whole K (two rows: gate and up for gate_up, the same block twice for down).
+// LDS layout in 16 B units: per stage the activation blocks and the weight column tiles,
+// each 16 rows as [8-row half][row][slot] (see the copies), and the activation scales
+// (per wave 64 floats: its 16 rows, then three copies of them, so that every lane of the
+// copy is active and the loop body stays one basic block); then per wave the weight
+// block scales for the whole K (two rows: gate and up for gate_up, the same block twice
+// for down); then the gate_up epilogue's partial row maxima.
 constexpr int kAUnits = kRowBlocks * 2 * kWave;       // 1024
 constexpr int kAsUnits = kWaves * 64 / 4;             // 128
 constexpr int kBUnits = kTileCols * 2 * kWave;        // 2048
@@ -140,7 +141,9 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
   const int K = a.K, KB = K >> 7;
 
   // Weight row of column tile tt (0..15) of the work-group tile, column c: for gate_up,
-  // quarter tt / 4 covers 32 h columns, its tiles 0-1 the gate rows and 2-3 the up rows.
+  // quarter tt / 4 covers 32 h columns, its tiles 0-1 the gate rows and 2-3 the up rows
+  // (a wave's gate and up rows lie in two [128, 128] weight blocks); for down a quarter's
+  // 64 rows lie in one block.
   auto weight_row = [&](int tt, int c) {
     if constexpr (EPI == FEpi::GateUp) {
       const int t = tt & 3;
@@ -226,7 +229,7 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
   };
 
   // Weight block scales of this wave for the whole K: row 0 for tiles 0-1, row 1 for
-  // tiles 2-3 (gate / up for gate_up; the same block for down).
+  // tiles 2-3 (gate / up for gate_up; down has one block row, copied to both).
   u32x4* bs_lds = &smem[kBsBase + wave * 2 * (kMaxKBlocks / 4)];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -296,6 +299,8 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
     // block's MFMAs cover it. The four MFMA results of block m are promoted into the
     // accumulators while block m+1's MFMAs run (no VALU waits on a fresh MFMA result).
     f32x4 dprev[kColTiles];
+    // down: one block scale for all four tiles (one product per row block).
+    constexpr bool kOneScale = EPI == FEpi::Down;
     f32x4 scprev0 = zero4, scprev1 = zero4;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -318,7 +323,7 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
       if (m > 0) {
 #pragma unroll
         for (int t = 0; t < kColTiles; ++t) {
-          const f32x4 sc = (t < 2) ? scprev0 : scprev1;
+          const f32x4 sc = (kOneScale || t < 2) ? scprev0 : scprev1;
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             acc[m - 1][t][r] = __builtin_fmaf(dprev[t][r], sc[r], acc[m - 1][t][r]);
@@ -328,7 +333,7 @@ __global__ void __launch_bounds__(kThreads) fp8_tiled_kernel(Fp8TiledArgs a) {
 #pragma unroll
         for (int t = 0; t < kColTiles; ++t) dprev[t] = dcur[t];
         scprev0 = as4 * bs0;
-        scprev1 = as4 * bs1;
+        if (!kOneScale) scprev1 = as4 * bs1;
       }
       if (m == kMyBlocks - 2) {
         // All reads of this stage were issued; once they and the copies of step g+1
