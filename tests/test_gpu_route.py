@@ -1,7 +1,8 @@
 """GPU router (moe_topk_softmax) against the oracle: expert ids bit-exact, weights within
-1e-5 relative. The GPU forms the weights in fp32: exp (about 2 ulp), a sum of at most
-E/64 + 6 terms per lane and across the wave (at most (E/64 + 6) * 2^-24 relative, 4.4e-6
-at E = 4096) and one division; the oracle in fp64."""
+1e-5 relative. The GPU forms the weights in fp32: exp(x) for x = l - m <= 0 as 2^(x log2 e)
+(relative error about |x| * 2^-24 from the product's rounding plus an ulp: 1.3e-6 at
+x = -20), a sum of at most E/64 + 6 terms per lane and across the wave (at most
+(E/64 + 6) * 2^-24 relative, 4.2e-6 at E = 4096) and one division; the oracle in fp64."""
 import numpy as np
 import pytest
 import torch
@@ -39,20 +40,25 @@ def _check(oracle_mod, logits, k, renormalize=True, expert_map=None):
     (4, 4096, 8, "uniform", False),    # the largest expert count
     (3, 200, 100, "uniform", True),    # k > 64: slots written in two batches
     (16, 384, 384, "uniform", False),  # k = E
+    (64, 512, 8, "zipf", True),        # the largest count held in registers (8 per lane)
+    (16, 513, 16, "uniform", False),   # the smallest count scanned from memory
 ])
 def test_router_matches_oracle(oracle_mod, T, E, k, kind, renorm):
     rng = np.random.default_rng(T * 131 + E * 7 + k)
     _check(oracle_mod, inputs.router_logits(rng, T, E, kind), k, renorm)
 
 
-def test_router_ties_and_signed_zeros(oracle_mod):
-    rng = np.random.default_rng(3)
-    # logits on a coarse grid: many exact ties, which keep the lower id first
-    logits = (np.round(rng.standard_normal((300, 48)) * 2.0) / 2.0).astype(np.float32)
+@pytest.mark.parametrize("E", [48, 384, 600])
+def test_router_ties_and_signed_zeros(oracle_mod, E):
+    rng = np.random.default_rng(3 + E)
+    # logits on a coarse grid: many exact ties, within a lane's experts and across lanes,
+    # which keep the lower id first
+    logits = (np.round(rng.standard_normal((300, E)) * 2.0) / 2.0).astype(np.float32)
     logits[:5, :] = 0.0
     logits[:5, ::2] = -0.0
     _check(oracle_mod, logits, 8)
     _check(oracle_mod, logits, 8, renormalize=False)
+    _check(oracle_mod, logits[:40], min(70, E))
 
 
 def test_router_expert_map_and_empty(oracle_mod):
