@@ -109,6 +109,51 @@ def test_w4a16_decode_persistent_shapes(oracle_mod, T, H, I, E, k, kind):
     assert report(f"persistent {T}x{H}x{I}x{E}", got, ref).max() <= TOL
 
 
+# The decode gate_up that reads the token rows builds the align result itself (one pair
+# per thread: up to 512 pairs, and up to 256 experts): the forward and the align arrays it
+# leaves in the workspace against the oracle, at those limits, just past them (align then
+# runs as its own launch) and with dropped ids. The workspace starts as 0xFF bytes, so
+# every array must have been written.
+@pytest.mark.parametrize("T,H,I,E,k,drop", [
+    (64, 512, 256, 256, 8, True),    # 512 pairs over 256 experts: the largest built in-kernel
+    (65, 512, 256, 128, 8, False),   # 520 pairs: align launch
+    (20, 1024, 512, 257, 4, False),  # 257 experts: align launch
+    (9, 512, 256, 8, 3, True),       # a few pairs, some ids outside [0, E)
+])
+def test_w4a16_decode_align_in_kernel(oracle_mod, T, H, I, E, k, drop):
+    print(f"[w4a16] align in kernel T={T} H={H} I={I} E={E} k={k} drop={drop}", flush=True)
+    case = inputs.custom_w4a16_case(T, H, I, E, k, seed=T * 3 + E)
+    if drop:
+        case["topk_ids"][::3, -1] = np.resize(np.array([-1, E, E + 7], np.int32),
+                                               case["topk_ids"][::3, -1].shape)
+    fmt, sch = binding.FORMAT_W4A16, binding.SCHEDULE_DECODE
+    _, block_m, need = binding.plan(fmt, T, H, I, E, k, sch)
+    assert block_m == 16
+    regions = binding.workspace_regions(fmt, T, H, I, E, k, sch)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    d = to_dev(case)
+    out = binding.moe_w4a16_forward(d["x"], d["w13"], d["s13"], d["w2"], d["s2"], d["topk_ids"],
+                                    d["topk_weights"], schedule=sch, workspace=ws)
+    torch.cuda.synchronize()
+    ref = _oracle(oracle_mod, case, None)
+    assert report(f"align in kernel {T}x{E}", bf16_out_to_f64(out), ref).max() <= TOL
+    sorted_ids, expert_ids, ntp, offsets = oracle_mod.moe_align(case["topk_ids"], E, 16)
+    wsn = ws.cpu().numpy()
+
+    def region(name):
+        off, size = regions[name]
+        return wsn[off:off + size].view(np.int32)
+
+    got_sorted, got_eids = region("sorted_ids"), region("expert_ids")
+    P = T * k
+    n, nb = min(got_sorted.size, sorted_ids.size), min(got_eids.size, expert_ids.size)
+    assert np.array_equal(got_sorted[:n], sorted_ids[:n]) and np.all(got_sorted[n:] == P)
+    assert np.array_equal(got_eids[:nb], expert_ids[:nb]) and np.all(got_eids[nb:] == -1)
+    assert int(region("num_tokens_padded")[0]) == ntp
+    if "expert_offsets" in regions:
+        assert np.array_equal(region("expert_offsets")[:E + 1], offsets)
+
+
 def test_w4a16_zero_routing_weights_give_exact_zero():
     case = inputs.custom_w4a16_case(20, 256, 128, 8, 2, seed=5)
     case["topk_weights"][:] = 0.0
