@@ -489,6 +489,7 @@ __global__ void __launch_bounds__(kPThreads)
   // (f_off[E] = rows in use).
   constexpr int kFR = FA ? kFuseMaxPairs + kFuseMaxExperts * (kSegRows - 1) : 1;
   constexpr int kFE = FA ? kFuseMaxExperts : 1;
+  __shared__ __align__(16) int32_t f_ids[FA ? kFuseMaxPairs : 1];
   __shared__ int32_t f_sorted[kFR];
   __shared__ int32_t f_eid[(kFR + kSegRows - 1) / kSegRows];
   __shared__ int32_t f_wcnt[FA ? kPWaves : 1][kFE];
@@ -496,23 +497,30 @@ __global__ void __launch_bounds__(kPThreads)
   __shared__ int32_t f_off[kFE + 1];
   if constexpr (FA) {
     // Pair p = thread p (P <= kPThreads). Its rank among the earlier pairs of its expert:
-    // within its wave from a ballot of the lanes holding the same expert, plus the pairs
-    // of that expert in the earlier waves. Stable in p, as align's counting sort.
+    // the lower lanes of its wave holding the same expert (a scan of the wave's 64 ids in
+    // LDS, four per broadcast read), plus that expert's pairs in the earlier waves. Stable
+    // in p, as align's counting sort.
     const int tid = threadIdx.x, fw = tid / kWave, fl = lane_id();
     const int P = a.P, E = a.E;
-    for (int i = tid; i < kPWaves * E; i += kPThreads) f_wcnt[i / E][i % E] = 0;
     const int v = tid < P ? a.fuse_ids[tid] : -1;
+    for (int i = tid; i < kPWaves * E; i += kPThreads) f_wcnt[i / E][i % E] = 0;
     const bool ok = (unsigned)v < (unsigned)E;  // ids outside [0, E) are dropped
+    f_ids[tid] = ok ? v : -1;
     __syncthreads();
-    int rank = 0;
-    for (uint64_t left = __ballot(ok); left;) {  // one pass per distinct expert in the wave
-      const int lead = __builtin_ctzll(left);
-      const int tv = __builtin_amdgcn_readlane(v, lead);
-      const uint64_t m = __ballot(ok && v == tv);
-      if (ok && v == tv) rank = __builtin_popcountll(m & ((uint64_t(1) << fl) - 1));
-      if (fl == lead) f_wcnt[fw][tv] = __builtin_popcountll(m);
-      left &= ~m;
+    int rank = 0, same = 0;
+#pragma unroll
+    for (int j = 0; j < kWave; j += 4) {
+      const int4 q = *reinterpret_cast<const int4*>(&f_ids[fw * kWave + j]);
+      const int qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool eq = qv[i] == v;
+        same += eq;
+        rank += eq && j + i < fl;
+      }
     }
+    // the wave's first pair of each expert records the wave's count of it
+    if (ok && rank == 0) f_wcnt[fw][v] = same;
     __syncthreads();
     if (fw == 0) {
       // per expert: the waves' counts become exclusive prefixes, their sum the count; an
