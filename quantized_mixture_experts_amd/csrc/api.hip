@@ -340,14 +340,12 @@ hipError_t w4a16_align(const Plan& p, const int32_t* topk_ids, int32_t E, void* 
 // The 4-bit forward after align: row gather (where the kernels need it), gate_up, down,
 // combine or cast. direct_out (one pair of weight 1 per row, the grouped layouts): on the
 // prefill tiles, down writes the bf16 output rows itself and there is no combine pass.
-// fuse_align: no align ran; the decode gate_up builds its result from topk_ids.
 qmoe_status w4a16_after_align(const Plan& p, const uint16_t* x, const uint8_t* w13,
                               const uint16_t* s13, const uint8_t* w2, const uint16_t* s2,
                               const int32_t* topk_ids, const float* topk_weights, int32_t T,
                               int32_t H, int32_t I, int32_t E, int32_t k, uint16_t* out,
                               void* workspace, hipStream_t s, const float* g13 = nullptr,
-                              const float* g2 = nullptr, bool direct_out = false,
-                              bool fuse_align = false) {
+                              const float* g2 = nullptr, bool direct_out = false) {
   const Routing r = routing_view(p, workspace, topk_weights, k, E);
   const bool mx = p.fmt == kMxfp4 || p.fmt == kNvfp4;  // FP4 codes, natural k order
   W4A16Problem prob{x, region<uint16_t>(workspace, p.off_xs), w13, s13, w2, s2,
@@ -360,14 +358,6 @@ qmoe_status w4a16_after_align(const Plan& p, const uint16_t* x, const uint8_t* w
   // clears the routed rows of out32, and only those are cast.
   prob.routed_rows_only = direct_out;
   const int32_t* ntp = region<int32_t>(workspace, p.off_ntp);
-  if (fuse_align) {
-    prob.fuse_ids = topk_ids;
-    prob.align_sorted = region<int32_t>(workspace, p.off_sorted);
-    prob.align_eids = region<int32_t>(workspace, p.off_expert_ids);
-    prob.align_ntp = region<int32_t>(workspace, p.off_ntp);
-    prob.align_offsets = region<int32_t>(workspace, p.off_offsets);
-    prob.align_NB = (int32_t)p.NB;
-  }
 
   if (p.tiled) {
     const int32_t tm = p.tile_rows;
@@ -422,15 +412,10 @@ qmoe_status w4a16_run(const Plan& p, const uint16_t* x, const uint8_t* w13, cons
                       const float* topk_weights, int32_t T, int32_t H, int32_t I, int32_t E,
                       int32_t k, uint16_t* out, void* workspace, hipStream_t s,
                       const float* g13 = nullptr, const float* g2 = nullptr) {
-  // Few pairs on the decode schedule: gate_up builds the align result itself.
-  const bool fuse = !p.tiled && p.block_m == kSegRows &&
-                    w4a16_stream_fuses_align(H, p.mb, p.P, E);
-  if (!fuse) {
-    hipError_t err = w4a16_align(p, topk_ids, E, workspace, s);
-    if (err != hipSuccess) return hip_fail(err, "align launch");
-  }
+  hipError_t err = w4a16_align(p, topk_ids, E, workspace, s);
+  if (err != hipSuccess) return hip_fail(err, "align launch");
   return w4a16_after_align(p, x, w13, s13, w2, s2, topk_ids, topk_weights, T, H, I, E, k, out,
-                           workspace, s, g13, g2, false, fuse);
+                           workspace, s, g13, g2);
 }
 
 // Grouped layouts: the rows arrive grouped by expert (the layout an expert-parallel

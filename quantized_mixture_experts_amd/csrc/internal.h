@@ -82,15 +82,6 @@ struct W4A16Problem {
   // One pair per row (k = 1, the grouped layouts): the decode gate_up clears only the
   // routed rows of out32 (the others are never read: the cast takes the routed rows).
   bool routed_rows_only = false;
-  // Indexed decode whose gate_up builds the align result itself (w4a16_stream_fuses_align):
-  // the routed ids [P], and the align outputs it stores for the later kernels (the
-  // Routing's sorted rows, block experts, row count and offsets, NB blocks).
-  const int32_t* fuse_ids = nullptr;
-  int32_t* align_sorted = nullptr;
-  int32_t* align_eids = nullptr;
-  int32_t* align_ntp = nullptr;
-  int32_t* align_offsets = nullptr;
-  int32_t align_NB = 0;
 };
 
 struct Fp8Problem {
@@ -122,9 +113,6 @@ bool w4a16_stream_zeroes_output(int32_t H);
 // Whether the decode gate_up launch with mb blocks per pass reads the activation rows of x
 // itself (then the gathered copy xs is not needed).
 bool w4a16_stream_reads_rows(int32_t H, int mb);
-// Whether that gate_up can also build the align result of P routed pairs over E experts
-// itself (then no align launch precedes it).
-bool w4a16_stream_fuses_align(int32_t H, int mb, int64_t P, int32_t E);
 hipError_t launch_w4a16_down_stream(const W4A16Problem& p, const Routing& r, int mb,
                                     hipStream_t stream);
 // Work-groups of a persistent launch: one per compute unit, a multiple of the XCD count.

@@ -82,17 +82,6 @@ struct StreamArgs {
   // Persistent gate_up with one pair per row (k = 1): clear only the rows of zero_out
   // (K floats each) that a sorted row routes, not all of it.
   bool zero_routed = false;
-  // Persistent gate_up reading the rows of x, indexed forward with few pairs: the routed
-  // ids [P] from which every work-group builds the align result (sorted rows, block
-  // experts, padded row count) in its own LDS, so no align launch precedes it. Work-group
-  // 0 also stores that result where align would (L sorted rows, NB blocks, E + 1 offsets
-  // when the plan keeps them) for down and the cast. E: experts; block rows kSegRows.
-  const int32_t* fuse_ids = nullptr;
-  int32_t* align_sorted = nullptr;
-  int32_t* align_eids = nullptr;
-  int32_t* align_ntp = nullptr;
-  int32_t* align_offsets = nullptr;
-  int32_t E = 0, L = 0, NB = 0;
 };
 
 struct Stage {
@@ -429,10 +418,6 @@ constexpr int kPGroupsPerCu = 1;
 constexpr int kPThreads = kPWaves * kWave;
 constexpr int kPWavesPerEu = kPWaves * kPGroupsPerCu / 4;
 constexpr int kPPieces = 1024 / kPThreads;  // 16 B chunk pieces per thread
-// Largest pair count and expert count for which gate_up builds the align result itself
-// (one pair per thread; the tables in LDS).
-constexpr int kFuseMaxPairs = kPThreads;
-constexpr int kFuseMaxExperts = 256;
 static_assert(1024 % kPThreads == 0, "chunk pieces per thread");
 // Groups per batch of a half step: their activation operands and zero-point terms are
 // read from LDS at once and their MFMAs issued back to back before the scale FMAs.
@@ -463,15 +448,11 @@ struct Unit {
 // the MFMAs of all MB blocks, so a pass over the weights serves 16 MB rows.
 // DX: the activation chunks come straight from the rows of x (gate_up), found through the
 // pair ids, instead of from a gathered copy in the operand layout.
-// FA (with DX): the align result is built by the kernel itself from the routed ids
-// (StreamArgs::fuse_ids): every work-group ranks the pairs of each expert in LDS and reads
-// its row blocks' experts and pair ids from there.
-template <Epi EPI, bool MX, bool NV, int MB, bool DX, bool FA = false>
+template <Epi EPI, bool MX, bool NV, int MB, bool DX>
 __global__ void __launch_bounds__(kPThreads)
     __attribute__((amdgpu_waves_per_eu(kPWavesPerEu)))
     w4a16_persist_kernel(StreamArgs a) {
   static_assert(MB == 1 || MB == 2, "LDS holds the activation chunks of at most two blocks");
-  static_assert(!FA || (DX && MB == 1), "the kernel-built align serves one 16-row block per pass");
   __shared__ u32x4 a_lds[2][MB][kChunkGroups][kWave];
   // Zero-point term of each group per activation row: the same for every column, so one
   // float per row (read by the four lanes of a row quarter at once).
@@ -483,97 +464,6 @@ __global__ void __launch_bounds__(kPThreads)
   // once, and without the pad the pieces (512 B apart) would all land on the same LDS
   // banks.
   __shared__ f32x4 s_lds[kPWaves][2][2 * kScaleUnits][kPieceStride];
-  // FA: the align result. f_sorted: pair id of each sorted row (P for padding); f_eid:
-  // expert of each 16-row block; f_wcnt: per wave and expert, the pairs the wave holds,
-  // then those of the earlier waves; f_cnt: pairs per expert; f_off: segment offsets
-  // (f_off[E] = rows in use).
-  constexpr int kFR = FA ? kFuseMaxPairs + kFuseMaxExperts * (kSegRows - 1) : 1;
-  constexpr int kFE = FA ? kFuseMaxExperts : 1;
-  __shared__ __align__(16) int32_t f_ids[FA ? kFuseMaxPairs : 1];
-  __shared__ int32_t f_sorted[kFR];
-  __shared__ int32_t f_eid[(kFR + kSegRows - 1) / kSegRows];
-  __shared__ int32_t f_wcnt[FA ? kPWaves : 1][kFE];
-  __shared__ int32_t f_cnt[kFE];
-  __shared__ int32_t f_off[kFE + 1];
-  if constexpr (FA) {
-    // Pair p = thread p (P <= kPThreads). Its rank among the earlier pairs of its expert:
-    // the lower lanes of its wave holding the same expert (a scan of the wave's 64 ids in
-    // LDS, four per broadcast read), plus that expert's pairs in the earlier waves. Stable
-    // in p, as align's counting sort.
-    const int tid = threadIdx.x, fw = tid / kWave, fl = lane_id();
-    const int P = a.P, E = a.E;
-    const int v = tid < P ? a.fuse_ids[tid] : -1;
-    for (int i = tid; i < kPWaves * E; i += kPThreads) f_wcnt[i / E][i % E] = 0;
-    const bool ok = (unsigned)v < (unsigned)E;  // ids outside [0, E) are dropped
-    f_ids[tid] = ok ? v : -1;
-    __syncthreads();
-    int rank = 0, same = 0;
-#pragma unroll
-    for (int j = 0; j < kWave; j += 4) {
-      const int4 q = *reinterpret_cast<const int4*>(&f_ids[fw * kWave + j]);
-      const int qv[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool eq = qv[i] == v;
-        same += eq;
-        rank += eq && j + i < fl;
-      }
-    }
-    // the wave's first pair of each expert records the wave's count of it
-    if (ok && rank == 0) f_wcnt[fw][v] = same;
-    __syncthreads();
-    if (fw == 0) {
-      // per expert: the waves' counts become exclusive prefixes, their sum the count; an
-      // exclusive scan of the counts padded to kSegRows gives the segment offsets
-      const int per = (E + kWave - 1) / kWave;
-      int mine = 0;
-      for (int j = 0; j < per; ++j) {
-        const int e = fl * per + j;
-        if (e < E) {
-          int run = 0;
-          for (int ww = 0; ww < kPWaves; ++ww) {
-            const int c = f_wcnt[ww][e];
-            f_wcnt[ww][e] = run;
-            run += c;
-          }
-          f_cnt[e] = run;
-          mine += (run + kSegRows - 1) / kSegRows * kSegRows;
-        }
-      }
-      int incl = mine;
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const int n = __shfl_up(incl, d, kWave);
-        if (fl >= d) incl += n;
-      }
-      int base = incl - mine;
-      for (int j = 0; j < per; ++j) {
-        const int e = fl * per + j;
-        if (e < E) {
-          f_off[e] = base;
-          base += (f_cnt[e] + kSegRows - 1) / kSegRows * kSegRows;
-        }
-      }
-      if (fl == kWave - 1) f_off[E] = incl;
-    }
-    __syncthreads();
-    if (ok) f_sorted[f_off[v] + f_wcnt[fw][v] + rank] = tid;
-    for (int e = tid; e < E; e += kPThreads) {
-      const int s0 = f_off[e], s1 = f_off[e + 1];
-      for (int r = s0 + f_cnt[e]; r < s1; ++r) f_sorted[r] = P;
-      for (int b = s0 / kSegRows; b < s1 / kSegRows; ++b) f_eid[b] = e;
-    }
-    __syncthreads();
-    if (blockIdx.x == 0) {
-      const int ntp = f_off[E];
-      for (int r = tid; r < a.L; r += kPThreads) a.align_sorted[r] = r < ntp ? f_sorted[r] : P;
-      for (int b = tid; b < a.NB; b += kPThreads)
-        a.align_eids[b] = b < ntp / kSegRows ? f_eid[b] : -1;
-      if (a.align_offsets)
-        for (int e = tid; e <= E; e += kPThreads) a.align_offsets[e] = f_off[e];
-      if (tid == 0) a.align_ntp[0] = ntp;
-    }
-  }
 
   // gate_up clears the fp32 output that down accumulates into (down starts after the
   // last gate_up work-group has ended).
@@ -598,9 +488,7 @@ __global__ void __launch_bounds__(kPThreads)
   }
   const int K = a.K, G = K / 32, KB = K / 2, N = a.N;
   const int upi = K / 512;  // units per item
-  const int rows_in_use =
-      FA ? __builtin_amdgcn_readfirstlane(f_off[a.E]) : ld_invariant(a.ntp, 0);
-  const int items = (rows_in_use / (kSegRows * MB)) * a.chunks;
+  const int items = (ld_invariant(a.ntp, 0) / (kSegRows * MB)) * a.chunks;
   const int nwg = gridDim.x;  // a multiple of the XCD count
   // XCD-major numbering: the work-groups of one XCD hold consecutive ranges, so the
   // column chunks of one expert (which share its activation rows) meet in one L2.
@@ -652,7 +540,7 @@ __global__ void __launch_bounds__(kPThreads)
     }
     d.rb = item / a.chunks;
     d.cc = item - d.rb * a.chunks;
-    d.e = FA ? __builtin_amdgcn_readfirstlane(f_eid[d.rb]) : ld_invariant(a.expert_ids, d.rb);
+    d.e = ld_invariant(a.expert_ids, d.rb);
     return d;
   };
   // First weight row of tile t of this wave in column chunk cc, and whether the tile
@@ -744,16 +632,12 @@ __global__ void __launch_bounds__(kPThreads)
   // which do not enter the vector memory counter: waiting for them does not wait for the
   // weight loads in flight.
   auto row_token = [&](int rb16) {
+    const int32_t* ids = a.sorted_ids + __builtin_amdgcn_readfirstlane(rb16) * 16;
     int sid = 0;
-    if constexpr (FA) {
-      sid = f_sorted[rb16 * 16 + col];
-    } else {
-      const int32_t* ids = a.sorted_ids + __builtin_amdgcn_readfirstlane(rb16) * 16;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const int v = ld_invariant(ids, m);
-        sid = (col == m) ? v : sid;
-      }
+    for (int m = 0; m < 16; ++m) {
+      const int v = ld_invariant(ids, m);
+      sid = (col == m) ? v : sid;
     }
     return sid < a.P ? sid / a.k : -1;
   };
@@ -1088,9 +972,9 @@ int persistent_grid() {
 
 namespace {
 
-template <Epi EPI, bool MX, bool NV, int MB, bool DX, bool FA = false>
+template <Epi EPI, bool MX, bool NV, int MB, bool DX>
 void launch_persist(const StreamArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, NV, MB, DX, FA>),
+  hipLaunchKernelGGL((w4a16_persist_kernel<EPI, MX, NV, MB, DX>),
                      dim3(persistent_grid() * kPGroupsPerCu), dim3(kPThreads), 0, stream, args);
 }
 
@@ -1108,9 +992,7 @@ hipError_t launch_stream(const StreamArgs& a, int E, int mb, hipStream_t stream)
   if (persist) {
     // gate_up with one block per pass reads the rows of x directly (no gathered copy)
     if constexpr (EPI == Epi::GateUp) {
-      if (mb == 1 && args.fuse_ids)
-        launch_persist<EPI, MX, NV, 1, true, true>(args, stream);
-      else if (mb == 1)
+      if (mb == 1)
         launch_persist<EPI, MX, NV, 1, true>(args, stream);
       else
         launch_persist<EPI, MX, NV, 2, false>(args, stream);
@@ -1152,13 +1034,6 @@ bool w4a16_stream_zeroes_output(int32_t H) { return H % 512 == 0; }
 // MI355X: grouped decode, 48 experts x 32 rows, gate_up 220 us gathered, 232 us direct).
 bool w4a16_stream_reads_rows(int32_t H, int mb) { return H % 512 == 0 && mb == 1; }
 
-// The persistent gate_up that reads the rows of x builds the align result itself when the
-// pairs fit one per thread and the per-expert tables fit its LDS: the separate align
-// launch (about 6 us at 256 pairs on MI355X) and its launch gap are saved.
-bool w4a16_stream_fuses_align(int32_t H, int mb, int64_t P, int32_t E) {
-  return w4a16_stream_reads_rows(H, mb) && P > 0 && P <= kFuseMaxPairs && E <= kFuseMaxExperts;
-}
-
 hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, int mb,
                                       hipStream_t stream) {
   const bool zero = w4a16_stream_zeroes_output(p.H);
@@ -1169,17 +1044,6 @@ hipError_t launch_w4a16_gateup_stream(const W4A16Problem& p, const Routing& r, i
   a.g = p.g13;
   a.x = p.x;
   a.zero_routed = p.routed_rows_only;
-  if (p.fuse_ids) {
-    if (mb != 1 || p.routed_rows_only || p.H % 512) return hipErrorInvalidValue;
-    a.fuse_ids = p.fuse_ids;
-    a.align_sorted = p.align_sorted;
-    a.align_eids = p.align_eids;
-    a.align_ntp = p.align_ntp;
-    a.align_offsets = p.align_offsets;
-    a.E = r.E;
-    a.L = r.L;
-    a.NB = p.align_NB;
-  }
   return p.nv   ? launch_stream<Epi::GateUp, true, true>(a, r.E, mb, stream)
          : p.mx ? launch_stream<Epi::GateUp, true, false>(a, r.E, mb, stream)
                 : launch_stream<Epi::GateUp, false, false>(a, r.E, mb, stream);

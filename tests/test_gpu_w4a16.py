@@ -109,19 +109,18 @@ def test_w4a16_decode_persistent_shapes(oracle_mod, T, H, I, E, k, kind):
     assert report(f"persistent {T}x{H}x{I}x{E}", got, ref).max() <= TOL
 
 
-# The decode gate_up that reads the token rows builds the align result itself (one pair
-# per thread: up to 512 pairs, and up to 256 experts): the forward and the align arrays it
-# leaves in the workspace against the oracle, at those limits, just past them (align then
-# runs as its own launch) and with dropped ids. The workspace starts as 0xFF bytes, so
-# every array must have been written.
+# The align arrays a decode forward leaves in its workspace (sorted rows, block experts,
+# padded row count, offsets) against the oracle's align, with 512 pairs over 256 experts,
+# past both, and with ids outside [0, E). The workspace starts as 0xFF bytes, so every
+# array must have been written.
 @pytest.mark.parametrize("T,H,I,E,k,drop", [
-    (64, 512, 256, 256, 8, True),    # 512 pairs over 256 experts: the largest built in-kernel
-    (65, 512, 256, 128, 8, False),   # 520 pairs: align launch
-    (20, 1024, 512, 257, 4, False),  # 257 experts: align launch
+    (64, 512, 256, 256, 8, True),    # 512 pairs over 256 experts
+    (65, 512, 256, 128, 8, False),   # 520 pairs
+    (20, 1024, 512, 257, 4, False),  # 257 experts
     (9, 512, 256, 8, 3, True),       # a few pairs, some ids outside [0, E)
 ])
-def test_w4a16_decode_align_in_kernel(oracle_mod, T, H, I, E, k, drop):
-    print(f"[w4a16] align in kernel T={T} H={H} I={I} E={E} k={k} drop={drop}", flush=True)
+def test_w4a16_decode_align_arrays(oracle_mod, T, H, I, E, k, drop):
+    print(f"[w4a16] align arrays T={T} H={H} I={I} E={E} k={k} drop={drop}", flush=True)
     case = inputs.custom_w4a16_case(T, H, I, E, k, seed=T * 3 + E)
     if drop:
         case["topk_ids"][::3, -1] = np.resize(np.array([-1, E, E + 7], np.int32),
@@ -136,7 +135,7 @@ def test_w4a16_decode_align_in_kernel(oracle_mod, T, H, I, E, k, drop):
                                     d["topk_weights"], schedule=sch, workspace=ws)
     torch.cuda.synchronize()
     ref = _oracle(oracle_mod, case, None)
-    assert report(f"align in kernel {T}x{E}", bf16_out_to_f64(out), ref).max() <= TOL
+    assert report(f"align arrays {T}x{E}", bf16_out_to_f64(out), ref).max() <= TOL
     sorted_ids, expert_ids, ntp, offsets = oracle_mod.moe_align(case["topk_ids"], E, 16)
     wsn = ws.cpu().numpy()
 
