@@ -35,11 +35,14 @@ def _check(oracle_mod, logits, k, renormalize=True, expert_map=None):
     (256, 48, 8, "uniform", True),
     (8192, 48, 8, "zipf", True),
     (256, 384, 8, "uniform", True),
-    (33, 65, 8, "uniform", False),     # a lane holds one more expert than the rest
-    (5, 600, 4, "zipf", True),         # experts past the register chunks
+    (33, 65, 8, "uniform", False),     # 2 per lane: lane 32 holds one, the lanes past it none
+    (5, 600, 4, "zipf", True),         # more than 512 experts: rescanned from memory
     (4, 4096, 8, "uniform", False),    # the largest expert count
     (3, 200, 100, "uniform", True),    # k > 64: slots written in two batches
     (16, 384, 384, "uniform", False),  # k = E
+    (64, 151, 8, "uniform", True),     # 3 experts per lane (each count 1..8 has its own kernel)
+    (64, 298, 8, "zipf", False),       # 5 per lane, the last used lane partly filled
+    (32, 420, 70, "uniform", True),    # 7 per lane, k > 64
     (64, 512, 8, "zipf", True),        # the largest count held in registers (8 per lane)
     (16, 513, 16, "uniform", False),   # the smallest count scanned from memory
 ])
@@ -48,7 +51,7 @@ def test_router_matches_oracle(oracle_mod, T, E, k, kind, renorm):
     _check(oracle_mod, inputs.router_logits(rng, T, E, kind), k, renorm)
 
 
-@pytest.mark.parametrize("E", [48, 384, 600])
+@pytest.mark.parametrize("E", [48, 151, 298, 384, 420, 600])
 def test_router_ties_and_signed_zeros(oracle_mod, E):
     rng = np.random.default_rng(3 + E)
     # logits on a coarse grid: many exact ties, within a lane's experts and across lanes,
