@@ -31,6 +31,9 @@ def _check(oracle_mod, logits, k, renormalize=True, expert_map=None):
 
 @pytest.mark.parametrize("T,E,k,kind,renorm", [
     (1, 8, 1, "uniform", True),
+    (2, 1, 1, "uniform", False),       # one expert: weight 1 (renormalized or not)
+    (4, 2, 2, "uniform", True),        # k = E = 2, one lane
+    (1, 384, 1, "zipf", False),        # one token, one slot
     (7, 8, 2, "uniform", True),
     (256, 48, 8, "uniform", True),
     (8192, 48, 8, "zipf", True),
