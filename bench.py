@@ -4,8 +4,8 @@
 One step = one full forward (align -> gate_up GEMM + SiLU*up -> down GEMM + weighted
 scatter-add -> bf16 output) on seeded synthetic inputs already resident in HBM. The timed
 steps are plain calls without instrumentation (--launch graph: replays of one captured HIP
-graph); the per-kernel times come from a separate pass of K steps with HIP events recorded
-around every kernel on its launch stream.
+graph); the per-kernel times come from a separate pass of 10 K steps in which every tenth
+step has HIP events recorded around every kernel on its launch stream.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W]
                   [--workload decode|prefill|fp8|full384|tiny|router|grouped_prefill|grouped_decode|
@@ -148,6 +148,10 @@ CPU_ROWS = {"full384": 192, "prefill": 192, "fp8": 32, "prefill_mxfp4": 48,
 ONE_CORE_ROWS = {"tiny": 16, "decode": 8, "decode_mxfp4": 2, "decode_nvfp4": 2}
 
 
+# One forward in this many is recorded with per-stage HIP events in the instrumented pass.
+SAMPLE_EVERY = 10
+
+
 def measure(workload, steps, warmup, launch, cpu_rows, cpu, np, torch, binding, inputs, lib):
     """Times one workload: an instrumented pass (per-stage HIP events on the launch stream,
     for the per-kernel times and the roofline), then K plain steps (`value`,
@@ -248,16 +252,25 @@ def measure(workload, steps, warmup, launch, cpu_rows, cpu, np, torch, binding, 
         step()
     torch.cuda.synchronize()
 
-    # Instrumented pass: K eager steps with HIP events recorded by the library around every
-    # stage launch on the launch stream; the per-kernel times (and the roofline) come from
-    # these events. Room for every launch of a stage: align holds up to three per forward
-    # (the grouped layouts' per-row routing, the sort, the row gather).
-    if lib.qmoe_timing_begin(steps * 3) != 0:
+    # Instrumented pass: K * SAMPLE_EVERY eager steps, of which every SAMPLE_EVERY-th has
+    # HIP events recorded by the library around every stage launch on the launch stream;
+    # the per-kernel times (and the roofline) come from these K sampled forwards. When
+    # every forward is bracketed, the pauses the events add between kernels move the GPU's
+    # power state within a few steps and the HBM-bound kernels slow down by up to a fifth
+    # (decode gate_up 152 -> 182 us in kernel traces); sampled forwards run amid unrecorded
+    # ones, as the timed steps do. Room for every launch of a stage: align holds up to
+    # three per forward (the grouped layouts' per-row routing, the sort, the row gather).
+    if lib.qmoe_timing_begin(steps * 3) != 0 or lib.qmoe_timing_pause(1) != 0:
         raise RuntimeError(lib.qmoe_last_error())
     torch.cuda.synchronize()
     te0 = time.perf_counter()
-    for _ in range(steps):
+    for i in range(steps * SAMPLE_EVERY):
+        sampled = i % SAMPLE_EVERY == SAMPLE_EVERY - 1
+        if sampled:
+            lib.qmoe_timing_pause(0)
         step()
+        if sampled:
+            lib.qmoe_timing_pause(1)
     torch.cuda.synchronize()
     te1 = time.perf_counter()
     ms_sum = (ctypes.c_float * 6)()
@@ -268,7 +281,7 @@ def measure(workload, steps, warmup, launch, cpu_rows, cpu, np, torch, binding, 
     # Per forward: a stage can hold more than one launch (align = sort + row gather).
     stage_ms = {n: (ms_sum[i] / steps if counts[i] else None)
                 for i, n in enumerate(stage_names)}
-    instrumented_ms = (te1 - te0) * 1e3 / steps
+    instrumented_ms = (te1 - te0) * 1e3 / (steps * SAMPLE_EVERY)
 
     # Timed pass: K steps without instrumentation, as one captured graph replayed K times
     # (the forward's kernels are launched on the capturing stream; nothing in it allocates

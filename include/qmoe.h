@@ -425,6 +425,11 @@ qmoe_status qmoe_set_tuning(int32_t tile_rows, int32_t rows_per_pass, int32_t ks
  * qmoe_timing_begin(max_calls): the next max_calls forward calls in this process
  *   record a HIP event pair around each stage's launch, on the forward's stream.
  *   Event handles are created here (host-side objects; no device memory is touched).
+ * qmoe_timing_pause(paused): between begin and end, paused != 0 stops recording and
+ *   paused == 0 resumes it, keeping what was recorded (a caller can time a sample of its
+ *   forwards; a stream in which every launch is bracketed by events runs its kernels
+ *   more slowly, since the pauses the events add between kernels move the GPU's power
+ *   state). QMOE_ERR_INVALID_ARG outside begin / end.
  * qmoe_timing_end(ms_sum, count): stops recording, waits for the recorded events and
  *   writes, per stage, the summed event-to-event milliseconds and the number of
  *   forwards recorded. Both arrays hold QMOE_NUM_STAGES entries.
@@ -440,6 +445,7 @@ enum {
   QMOE_NUM_STAGES = 6
 };
 qmoe_status qmoe_timing_begin(int32_t max_calls);
+qmoe_status qmoe_timing_pause(int32_t paused);
 qmoe_status qmoe_timing_end(float* ms_sum, int32_t* count);
 
 #ifdef __cplusplus

@@ -905,6 +905,14 @@ qmoe_status qmoe_timing_begin(int32_t max_calls) {
   return QMOE_OK;
 }
 
+qmoe_status qmoe_timing_pause(int32_t paused) {
+  g_last_error[0] = 0;
+  std::lock_guard<std::mutex> lk(g_timer.mu);
+  if (g_timer.cap == 0) return fail(QMOE_ERR_INVALID_ARG, "timing not begun");
+  g_timer.on = paused == 0;
+  return QMOE_OK;
+}
+
 qmoe_status qmoe_timing_end(float* ms_sum, int32_t* count) {
   g_last_error[0] = 0;
   if (!ms_sum || !count) return fail(QMOE_ERR_INVALID_ARG, "NULL output");
