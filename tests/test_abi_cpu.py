@@ -27,6 +27,13 @@ def test_exports_every_declared_function(lib):
     assert lib.qmoe_status_string(3) == b"workspace too small"
 
 
+def test_timing_pause_outside_begin_end(lib):
+    # pausing or resuming stage timing needs a begun timing (host-only check)
+    assert lib.qmoe_timing_pause(1) == INVALID
+    assert lib.qmoe_timing_pause(0) == INVALID
+    assert b"timing not begun" in lib.qmoe_last_error()
+
+
 def _w4(lib, T=32, H=7168, I=2048, E=48, k=8, sched=0, ptr=FAKE, ws=None, size=1 << 40, out=FAKE):
     sz = ctypes.c_size_t(size)
     st = lib.moe_w4a16_forward(ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, I, E, k, sched, out, ws,
